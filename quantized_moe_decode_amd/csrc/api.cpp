@@ -1,0 +1,307 @@
+// C ABI of libhfq4moe.so (declared in include/hfq4moe.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// device, and refuses loudly with a detail string that names the argument
+// and, for sizes, both the required and the given amount (the refusal style
+// of the hipfire expert-offload explainer, section "放置算法": say what is
+// short and by how much instead of failing later).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/hfq4moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+char g_arch_override[64] = {0};
+std::mutex g_arch_mu;
+int g_arch_ok[64] = {0};  // per device: 0 unknown, 1 gfx950, -1 other
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return HFQ4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t packed(int64_t rows, int64_t K) { return (size_t)rows * (size_t)((K + 255) / 256) * 136u; }
+
+int check_device() {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_override[0] && std::strncmp(g_arch_override, "gfx950", 6) != 0)
+    return fail(HFQ4_E_DEVICE, "device is %s, this library is built for gfx950 only",
+                g_arch_override);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HFQ4_E_DEVICE, "no usable HIP device: %s", hipGetErrorString(e));
+  if (g_arch_override[0]) return HFQ4_OK;
+  if (dev >= 0 && dev < 64 && g_arch_ok[dev] == 1) return HFQ4_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(HFQ4_E_DEVICE, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) g_arch_ok[dev] = is950 ? 1 : -1;
+  if (!is950)
+    return fail(HFQ4_E_DEVICE, "device %d is %s, this library is built for gfx950 only", dev,
+                prop.gcnArchName);
+  return HFQ4_OK;
+}
+
+int hip_status(int e, const char* what) {
+  if (e != hipSuccess)
+    return fail(HFQ4_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
+  return ok();
+}
+
+int check_layer(const moe_layer* L) {
+  if (!L) return fail(HFQ4_E_INVALID, "layer descriptor is NULL");
+  if (!L->gate || !L->up || !L->down) return fail(HFQ4_E_INVALID, "layer gate/up/down pointer is NULL");
+  if (L->E < 1 || L->E > HFQ4_MAX_EXPERTS)
+    return fail(HFQ4_E_INVALID, "E = %lld outside [1, %d]", (long long)L->E, HFQ4_MAX_EXPERTS);
+  if (L->d < 4 || L->d > 2048 || (L->d & 3))
+    return fail(HFQ4_E_UNSUPPORTED, "d = %lld: need 4 <= d <= 2048 and d %% 4 == 0", (long long)L->d);
+  if (L->F < 4 || L->F > 2048 || (L->F & 3))
+    return fail(HFQ4_E_UNSUPPORTED, "F = %lld: need 4 <= F <= 2048 and F %% 4 == 0", (long long)L->F);
+  const size_t gb = packed(L->F, L->d), db = packed(L->d, L->F);
+  if (L->stride_gate < (int64_t)gb || L->stride_up < (int64_t)gb)
+    return fail(HFQ4_E_INVALID, "gate/up stride must be >= %zu bytes (one F x d HFQ4 matrix), got %lld / %lld",
+                gb, (long long)L->stride_gate, (long long)L->stride_up);
+  if (L->stride_down < (int64_t)db)
+    return fail(HFQ4_E_INVALID, "down stride must be >= %zu bytes (one d x F HFQ4 matrix), got %lld", db,
+                (long long)L->stride_down);
+  if (!aligned16(L->gate) || !aligned16(L->up) || !aligned16(L->down) || (L->stride_gate & 15) ||
+      (L->stride_up & 15) || (L->stride_down & 15))
+    return fail(HFQ4_E_ALIGN, "expert weight pointers and strides must be 16-byte aligned");
+  if (L->flags & ~HFQ4_LAYER_HOST_MAPPED) return fail(HFQ4_E_INVALID, "unknown layer flags 0x%x", L->flags);
+  return HFQ4_OK;
+}
+
+size_t ws_bytes_for(int64_t E, int B, int k, int64_t F) {
+  size_t a, b, c, d;
+  return hq::ws_layout(E, B, k, F, &a, &b, &c, &d);
+}
+
+int check_expert_io(const moe_layer* L, const float* x, int64_t ldx, int batch, const int32_t* idx,
+                    const float* wts, int k, const float* residual, float* y, int64_t ldy) {
+  if (!x || !y) return fail(HFQ4_E_INVALID, "x and y must be non-NULL");
+  if (!idx || !wts) return fail(HFQ4_E_INVALID, "idx and wts must be non-NULL");
+  if (batch < 1 || batch > HFQ4_MAX_BATCH)
+    return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  if (k < 1 || k > HFQ4_MAX_TOPK || k > L->E)
+    return fail(HFQ4_E_INVALID, "k = %d: need 1 <= k <= min(E = %lld, %d)", k, (long long)L->E,
+                HFQ4_MAX_TOPK);
+  if (batch * k > 128)
+    return fail(HFQ4_E_UNSUPPORTED, "batch * k = %d exceeds 128 (token, slot) pairs", batch * k);
+  if (ldx < L->d || (ldx & 3)) return fail(HFQ4_E_ALIGN, "ldx = %lld: need ldx >= d and ldx %% 4 == 0", (long long)ldx);
+  if (ldy < L->d) return fail(HFQ4_E_INVALID, "ldy = %lld < d = %lld", (long long)ldy, (long long)L->d);
+  if (!aligned16(x)) return fail(HFQ4_E_ALIGN, "x must be 16-byte aligned");
+  const size_t xb = sizeof(float) * ((size_t)(batch - 1) * ldx + L->d);
+  const size_t yb = sizeof(float) * ((size_t)(batch - 1) * ldy + L->d);
+  if (overlap(x, xb, y, yb)) return fail(HFQ4_E_INVALID, "y overlaps x");
+  if (residual && residual != y && overlap(residual, yb, y, yb))
+    return fail(HFQ4_E_INVALID, "residual partially overlaps y (it may equal y or be disjoint)");
+  return HFQ4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hfq4_last_error(void) { return g_err.c_str(); }
+
+int hfq4_version(void) { return 100; }
+
+// Testing hook: pretend the current device reports `arch` ("" restores the
+// real query).  Used to exercise the device check without such a device.
+int hfq4_debug_set_arch(const char* arch) {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (!arch) arch = "";
+  std::snprintf(g_arch_override, sizeof g_arch_override, "%s", arch);
+  return ok();
+}
+
+int hfq4_packed_bytes(int64_t rows, int64_t K, size_t* out) {
+  if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
+  if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);
+  if (K < 1) return fail(HFQ4_E_INVALID, "K = %lld < 1", (long long)K);
+  *out = packed(rows, K);
+  return ok();
+}
+
+int hfq4_pack(const float* w, int64_t rows, int64_t K, int64_t ldw, void* out, size_t out_bytes,
+              int32_t* bad, hipStream_t stream) {
+  if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);
+  if (K < 1) return fail(HFQ4_E_INVALID, "K = %lld < 1", (long long)K);
+  if (ldw < K) return fail(HFQ4_E_INVALID, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (rows > 0 && (!w || !out)) return fail(HFQ4_E_INVALID, "w and out must be non-NULL");
+  const size_t need = packed(rows, K);
+  if (out_bytes < need)
+    return fail(HFQ4_E_INVALID, "output needs %zu bytes, got %zu", need, out_bytes);
+  if (rows > 0 && ((reinterpret_cast<uintptr_t>(out) & 7u) || (reinterpret_cast<uintptr_t>(w) & 3u)))
+    return fail(HFQ4_E_ALIGN, "out must be 8-byte aligned and w 4-byte aligned");
+  if (rows > 0 && overlap(w, sizeof(float) * ((size_t)(rows - 1) * ldw + K), out, need))
+    return fail(HFQ4_E_INVALID, "out overlaps w");
+  if (rows == 0) return ok();
+  int r = check_device();
+  if (r) return r;
+  return hip_status(hq::launch_pack(w, rows, K, ldw, out, bad, stream), "hfq4_pack launch");
+}
+
+int hfq4_gemv(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,
+              const float* residual, int64_t ldr, float* y, int64_t ldy, hipStream_t stream) {
+  if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);
+  if (K < 1 || K > 16384) return fail(HFQ4_E_UNSUPPORTED, "K = %lld outside [1, 16384]", (long long)K);
+  if (batch < 1 || batch > HFQ4_MAX_BATCH)
+    return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  if ((int64_t)batch * K > 32768)
+    return fail(HFQ4_E_UNSUPPORTED, "batch * K = %lld exceeds 32768", (long long)batch * K);
+  if (rows == 0) return ok();
+  if (!W || !x || !y) return fail(HFQ4_E_INVALID, "W, x and y must be non-NULL");
+  if (ldx < K || (ldx & 3)) return fail(HFQ4_E_ALIGN, "ldx = %lld: need ldx >= K and ldx %% 4 == 0", (long long)ldx);
+  if (ldy < rows) return fail(HFQ4_E_INVALID, "ldy = %lld < rows = %lld", (long long)ldy, (long long)rows);
+  if (residual && ldr < rows) return fail(HFQ4_E_INVALID, "ldr = %lld < rows = %lld", (long long)ldr, (long long)rows);
+  if (!aligned16(W) || !aligned16(x)) return fail(HFQ4_E_ALIGN, "W and x must be 16-byte aligned");
+  const size_t yb = sizeof(float) * ((size_t)(batch - 1) * ldy + rows);
+  if (overlap(x, sizeof(float) * ((size_t)(batch - 1) * ldx + K), y, yb))
+    return fail(HFQ4_E_INVALID, "y overlaps x");
+  if (overlap(W, packed(rows, K), y, yb)) return fail(HFQ4_E_INVALID, "y overlaps W");
+  if (residual && residual != y && overlap(residual, sizeof(float) * ((size_t)(batch - 1) * ldr + rows), y, yb))
+    return fail(HFQ4_E_INVALID, "residual partially overlaps y");
+  int r = check_device();
+  if (r) return r;
+  return hip_status(hq::launch_gemv(W, rows, K, x, ldx, batch, residual, ldr, y, ldy, stream),
+                    "hfq4_gemv launch");
+}
+
+int moe_route_workspace_bytes(int64_t E, int batch, size_t* out) {
+  if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
+  if (E < 1 || E > HFQ4_MAX_EXPERTS) return fail(HFQ4_E_INVALID, "E = %lld outside [1, %d]", (long long)E, HFQ4_MAX_EXPERTS);
+  if (batch < 1 || batch > HFQ4_MAX_BATCH) return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  *out = ws_bytes_for(E, batch, 0, 0);
+  return ok();
+}
+
+int moe_route_topk(const float* Wr, const float* bias, int64_t E, int64_t d, const float* x,
+                   int64_t ldx, int batch, int k, int32_t* idx, float* wts, float* logits_out,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!Wr || !x || !idx || !wts || !ws)
+    return fail(HFQ4_E_INVALID, "Wr, x, idx, wts and ws must be non-NULL");
+  if (E < 1 || E > HFQ4_MAX_EXPERTS) return fail(HFQ4_E_INVALID, "E = %lld outside [1, %d]", (long long)E, HFQ4_MAX_EXPERTS);
+  if (d < 4 || d > 65536 || (d & 3)) return fail(HFQ4_E_UNSUPPORTED, "d = %lld: need 4 <= d <= 65536, d %% 4 == 0", (long long)d);
+  if (batch < 1 || batch > HFQ4_MAX_BATCH) return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  if (k < 1 || k > E || k > HFQ4_MAX_TOPK)
+    return fail(HFQ4_E_INVALID, "k = %d: need 1 <= k <= min(E = %lld, %d)", k, (long long)E, HFQ4_MAX_TOPK);
+  if (ldx < d || (ldx & 3)) return fail(HFQ4_E_ALIGN, "ldx = %lld: need ldx >= d and ldx %% 4 == 0", (long long)ldx);
+  if (!aligned16(Wr) || !aligned16(x)) return fail(HFQ4_E_ALIGN, "Wr and x must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
+  const size_t need = ws_bytes_for(E, batch, 0, 0);
+  if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  int r = check_device();
+  if (r) return r;
+  hq::Ws w = hq::ws_carve(ws, E, batch, 0, 0);
+  return hip_status(hq::launch_route(Wr, bias, (int)E, (int)d, x, ldx, batch, k, idx, wts, logits_out, w, stream),
+                    "moe_route_topk launch");
+}
+
+int moe_workspace_bytes(const moe_layer* L, int batch, int k, size_t* out) {
+  if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
+  int r = check_layer(L);
+  if (r) return r;
+  if (batch < 1 || batch > HFQ4_MAX_BATCH) return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  if (k < 1 || k > HFQ4_MAX_TOPK || k > L->E) return fail(HFQ4_E_INVALID, "k = %d outside [1, min(E, %d)]", k, HFQ4_MAX_TOPK);
+  *out = ws_bytes_for(L->E, batch, k, L->F);
+  return ok();
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
+  int r = check_device();
+  if (r) return r;
+  return hip_status(hq::launch_fill_zero(ws, ws_bytes, stream), "moe_workspace_init launch");
+}
+
+static hq::LayerDev to_dev(const moe_layer* L) {
+  hq::LayerDev D;
+  D.gate = static_cast<const uint8_t*>(L->gate);
+  D.up = static_cast<const uint8_t*>(L->up);
+  D.down = static_cast<const uint8_t*>(L->down);
+  D.sg = L->stride_gate;
+  D.su = L->stride_up;
+  D.sd = L->stride_down;
+  D.E = (int)L->E;
+  D.d = (int)L->d;
+  D.F = (int)L->F;
+  D.flags = L->flags;
+  return D;
+}
+
+int moe_expert_decode(const moe_layer* L, const float* x, int64_t ldx, int batch,
+                      const int32_t* idx, const float* wts, int k, const float* residual, float* y,
+                      int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int r = check_layer(L);
+  if (r) return r;
+  r = check_expert_io(L, x, ldx, batch, idx, wts, k, residual, y, ldy);
+  if (r) return r;
+  if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
+  const size_t need = ws_bytes_for(L->E, batch, k, L->F);
+  if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  r = check_device();
+  if (r) return r;
+  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->F);
+  return hip_status(hq::launch_experts(to_dev(L), x, ldx, batch, idx, wts, k, residual, y, ldy, w, stream),
+                    "moe_expert_decode launch");
+}
+
+int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias, const float* x,
+                     int64_t ldx, int batch, int k, int32_t* idx, float* wts, const float* residual,
+                     float* y, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int r = check_layer(L);
+  if (r) return r;
+  if (!Wr) return fail(HFQ4_E_INVALID, "Wr is NULL");
+  if (!aligned16(Wr)) return fail(HFQ4_E_ALIGN, "Wr must be 16-byte aligned");
+  r = check_expert_io(L, x, ldx, batch, idx, wts, k, residual, y, ldy);
+  if (r) return r;
+  if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
+  const size_t need = ws_bytes_for(L->E, batch, k, L->F);
+  if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  r = check_device();
+  if (r) return r;
+  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->F);
+  return hip_status(hq::launch_layer(to_dev(L), Wr, bias, x, ldx, batch, k, idx, wts, residual, y, ldy, w, stream),
+                    "moe_layer_decode launch");
+}
+
+int hfq4_host_device_pointer(void* host, void** dev) {
+  if (!host || !dev) return fail(HFQ4_E_INVALID, "host and dev must be non-NULL");
+  int r = check_device();
+  if (r) return r;
+  return hip_status(hipHostGetDevicePointer(dev, host, 0), "hipHostGetDevicePointer");
+}
+
+}  // extern "C"

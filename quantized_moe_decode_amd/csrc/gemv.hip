@@ -1,0 +1,150 @@
+// hfq4_gemv: y = residual + W x for HFQ4 rows, batch 1..16.
+//
+// The dequantizing GEMV is the hot kernel the HFQ4 format was designed for
+// (page "hipfire：为AMD RDNA GPU打造的Rust原生LLM推理引擎", section
+// "2. HFQ量化格式与GEMV优化": few registers per lane so that many waves are
+// in flight to hide memory latency).  On gfx950 the same goal is met by
+// issuing every weight load of a wave before the first use, keeping the
+// activation fragment of the lane's fixed segment in registers, and
+// decoding nibbles straight into f16 pairs for v_dot2 (hfq4_device.h).
+#include "hfq4_device.h"
+#include "launch.h"
+
+namespace hq {
+
+// Rows of nb <= NB blocks (K <= 256*NB); SEGS = 8*NB lanes per row, G =
+// 64/SEGS rows per load instruction, RPW load instructions per wave.  Lanes
+// whose block index is >= nb load nothing and contribute zero.
+template <int NB, int RPW>
+__global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restrict__ W,
+                                                          int64_t rows, int K,
+                                                          const float* __restrict__ x, int64_t ldx,
+                                                          int batch, const float* __restrict__ res,
+                                                          int64_t ldr, float* __restrict__ y,
+                                                          int64_t ldy) {
+  constexpr int SEGS = 8 * NB, G = 64 / SEGS;
+  const int nb = (K + BLK - 1) / BLK;
+  const int64_t ROWB = (int64_t)nb * BLK_BYTES;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane / SEGS, s = lane % SEGS;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
+  const int64_t row0 = wave * (RPW * G);
+
+  // Issue this wave's weight loads first: they do not depend on x.
+  u32x4 codes[RPW];
+  u32x2 hdr[RPW];
+  int64_t nhere = rows - row0;
+  if (nhere > RPW * G) nhere = RPW * G;
+  if (nhere < 0) nhere = 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (nhere ? row0 * ROWB : 0), (uint32_t)(nhere * ROWB));
+  const bool live = (s >> 3) < nb;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const uint32_t off = (uint32_t)((i * G + g) * ROWB + (s >> 3) * BLK_BYTES);
+    hdr[i] = live ? bload8(rs, off) : u32x2{0u, 0u};
+    codes[i] = live ? bload16(rs, off + 8 + 16 * (s & 7)) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int fb = frag_bytes(SEGS);
+  for (int b = 0; b < batch; ++b)
+    stage_vector(x + b * ldx, K, SEGS, lds + b * fb, threadIdx.x, blockDim.x);
+  __syncthreads();
+  if (nhere == 0) return;
+
+  for (int b = 0; b < batch; ++b) {
+    Frag f;
+    frag_load(lds + b * fb, SEGS, s, f);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      float p = dot_seg(codes[i], hdr[i], f);
+      p = group_sum<SEGS>(p);
+      const int64_t row = row0 + i * G + g;
+      if (s == 0 && row < rows) y[b * ldy + row] = (res ? res[b * ldr + row] : 0.f) + p;
+    }
+  }
+}
+
+// Rows wider than 2048: lanes stride over the segments of one row at a time.
+__global__ void __launch_bounds__(256) gemv_wide_kernel(const uint8_t* __restrict__ W, int64_t rows,
+                                                        int K, const float* __restrict__ x,
+                                                        int64_t ldx, int batch,
+                                                        const float* __restrict__ res, int64_t ldr,
+                                                        float* __restrict__ y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int NB = (K + BLK - 1) / BLK;
+  const int S = NB * SEGS_PER_BLK;
+  const int64_t ROWB = (int64_t)NB * BLK_BYTES;
+  const int fb = frag_bytes(S);
+  for (int b = 0; b < batch; ++b)
+    stage_vector(x + b * ldx, K, S, lds + b * fb, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + row * ROWB, (uint32_t)ROWB);
+  float acc[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) acc[b] = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const uint32_t off = (uint32_t)((s >> 3) * BLK_BYTES);
+    const u32x2 hdr = bload8(rs, off);
+    const u32x4 codes = bload16(rs, off + 8 + 16 * (s & 7));
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      if (b < batch) {
+        Frag f;
+        frag_load(lds + b * fb, S, s, f);
+        acc[b] += dot_seg(codes, hdr, f);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    if (b < batch) {
+      const float p = group_sum<64>(acc[b]);
+      if (lane == 0) y[b * ldy + row] = (res ? res[b * ldr + row] : 0.f) + p;
+    }
+  }
+}
+
+template <int NB>
+static int launch_narrow(const void* W, int64_t rows, int K, const float* x, int64_t ldx,
+                         int batch, const float* res, int64_t ldr, float* y, int64_t ldy,
+                         hipStream_t s) {
+  constexpr int RPW = 2;
+  constexpr int G = 64 / (8 * NB);
+  const int64_t waves = (rows + RPW * G - 1) / (RPW * G);
+  const int64_t blocks = (waves + 3) / 4;
+  const size_t shm = (size_t)batch * frag_bytes(8 * NB);
+  if (int e = allow_lds(gemv_narrow_kernel<NB, RPW>, shm)) return e;
+  hipLaunchKernelGGL((gemv_narrow_kernel<NB, RPW>), dim3((unsigned)blocks), dim3(256), shm, s,
+                     static_cast<const uint8_t*>(W), rows, K, x, ldx, batch, res, ldr, y, ldy);
+  return (int)hipGetLastError();
+}
+
+int launch_gemv(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,
+                const float* residual, int64_t ldr, float* y, int64_t ldy, hipStream_t s) {
+  if (rows == 0) return 0;
+  const int NB = (int)((K + BLK - 1) / BLK);
+  const int k = (int)K;
+  switch (NB) {
+    case 1: return launch_narrow<1>(W, rows, k, x, ldx, batch, residual, ldr, y, ldy, s);
+    case 2: return launch_narrow<2>(W, rows, k, x, ldx, batch, residual, ldr, y, ldy, s);
+    case 3:
+    case 4: return launch_narrow<4>(W, rows, k, x, ldx, batch, residual, ldr, y, ldy, s);
+    case 5: case 6: case 7:
+    case 8: return launch_narrow<8>(W, rows, k, x, ldx, batch, residual, ldr, y, ldy, s);
+    default: {
+      const int64_t blocks = (rows + 3) / 4;
+      const size_t shm = (size_t)batch * frag_bytes(NB * SEGS_PER_BLK);
+      if (int e = allow_lds(gemv_wide_kernel, shm)) return e;
+      hipLaunchKernelGGL(gemv_wide_kernel, dim3((unsigned)blocks), dim3(256), shm, s,
+                         static_cast<const uint8_t*>(W), rows, k, x, ldx, batch, residual, ldr, y,
+                         ldy);
+      return (int)hipGetLastError();
+    }
+  }
+}
+
+}  // namespace hq

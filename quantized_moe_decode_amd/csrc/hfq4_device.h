@@ -1,0 +1,243 @@
+// Device-side building blocks shared by the HFQ4 kernels (gfx950, wave64).
+//
+// HFQ4 block (page "hipfire：为AMD RDNA GPU打造的Rust原生LLM推理引擎",
+// section "2. HFQ量化格式与GEMV优化"): 256 weights in 136 bytes =
+// f32 scale | f32 zero | 128 code bytes.  Byte j of the codes holds element
+// 2j in its low nibble and 2j+1 in its high nibble; w = zero + scale*q.
+//
+// Dot-product scheme.  A row is read as "segments": 16 code bytes = 32
+// weights; a block has 8 segments at byte offsets 8 + 16c.  One lane owns
+// one segment position for every row it visits ("column-stationary"), so
+// the activation values it needs stay in registers across rows.  A code
+// dword is turned into four f16 pairs with no conversion instructions:
+// OR-ing a nibble into the mantissa of 1024.0h gives 1024 + q exactly, and
+// OR-ing the next nibble (4 bits higher) gives 1024 + 16q.  The matching
+// activation pairs are pre-arranged (and pre-scaled by 1/16 where needed)
+// once per vector, so each dword costs 4 bit-ops + 1 shift + 4 v_dot2
+// (f16 x f16 products, f32 accumulate).  The constant 1024 terms and the
+// zero point are folded back per segment with pre-computed sums:
+//   sum_i w_i x_i = scale * sum_i (q_i - 8) x_i + (zero + 8 scale) * sum_i x_i
+// where the first sum uses f16-rounded x and the second the exact f32 x.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BLK = 256;          // weights per block
+constexpr int BLK_BYTES = 136;    // bytes per block
+constexpr int SEG = 32;           // weights per segment (16 code bytes)
+constexpr int SEGS_PER_BLK = 8;
+
+#define HFQ4_MAXB_DEV 16      // max tokens per call (matches HFQ4_MAX_BATCH)
+#define HFQ4_MAXE_DEV 1024    // max experts per layer (matches HFQ4_MAX_EXPERTS)
+
+constexpr uint32_t MAGIC = 0x64006400u;   // two f16 1024.0
+constexpr uint32_t LO4 = 0x000F000Fu;
+constexpr uint32_t HI4 = 0x00F000F0u;
+
+// Bit reinterpretation through by-value scalars.  (clang's __builtin_bit_cast
+// applied directly to an ext-vector element such as v.y reads element 0, so
+// vector elements always pass through one of these first.)
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ---------------------------------------------------------------- loads
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // gfx9 family buffer descriptor word 3 (raw dword access, no swizzle)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+
+// ---------------------------------------------------------------- fragments
+
+// Activation fragment for one 32-element segment, in the order dot_seg uses.
+struct Frag {
+  h2 p[16];
+  float off;   // -(1024 * sum of all 32 stored halves + 8 * sum of the f16 x they stand for)
+  float sx;    // exact f32 sum of the 32 activations
+};
+
+// Build a fragment from 32 f32 activations v[0..31] (element order).
+// Dword w of a segment covers elements 8w..8w+7 (element 8w+n at nibble n).
+__device__ __forceinline__ void make_frag(const float* v, Frag& f) {
+  float sum_half = 0.f, sum_x16 = 0.f, sx = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool hi = (p & 1);                 // nibbles 1,3 (and 5,7) carry 16q
+      const int n = p;                         // pair p = elements (8w+p, 8w+p+4)
+      const float a = v[8 * w + n], b = v[8 * w + n + 4];
+      const float s = hi ? 0.0625f : 1.0f;
+      _Float16 ha = (_Float16)(a * s), hb = (_Float16)(b * s);
+      f.p[4 * w + p] = h2{ha, hb};
+      const float fa = (float)ha, fb = (float)hb;
+      sum_half += fa + fb;
+      sum_x16 += hi ? 16.f * (fa + fb) : (fa + fb);
+      sx += a + b;
+    }
+  }
+  f.off = -(1024.f * sum_half + 8.f * sum_x16);
+  f.sx = sx;
+}
+
+// One code dword (8 weights) against 4 fragment pairs.
+__device__ __forceinline__ float dot_dword(uint32_t d, const h2* x, float acc) {
+  const uint32_t p0 = (d & LO4) | MAGIC;
+  const uint32_t p1 = (d & HI4) | MAGIC;
+  const uint32_t d8 = d >> 8;
+  const uint32_t p2 = (d8 & LO4) | MAGIC;
+  const uint32_t p3 = (d8 & HI4) | MAGIC;
+  acc = __builtin_amdgcn_fdot2(as_h2(p0), x[0], acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(p1), x[1], acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(p2), x[2], acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(p3), x[3], acc, false);
+  return acc;
+}
+
+// Contribution of one segment (16 code bytes + its block header) to a row dot.
+__device__ __forceinline__ float dot_seg(u32x4 codes, u32x2 hdr, const Frag& f) {
+  float acc = f.off;
+  acc = dot_dword(codes.x, &f.p[0], acc);
+  acc = dot_dword(codes.y, &f.p[4], acc);
+  acc = dot_dword(codes.z, &f.p[8], acc);
+  acc = dot_dword(codes.w, &f.p[12], acc);
+  const float scale = as_f32(hdr.x);
+  const float zero = as_f32(hdr.y);
+  const float zp8 = __builtin_fmaf(8.f, scale, zero);
+  return __builtin_fmaf(scale, acc, zp8 * f.sx);
+}
+
+// ---------------------------------------------------------------- LDS fragment store
+// Fragments of a vector with S segments live in LDS as 4 planes of S x 16 B
+// (plane w = pairs 4w..4w+3 of every segment; consecutive segments are
+// consecutive 16-byte slots, so a wave reading consecutive segments is
+// conflict-free) followed by S float2 (off, sx).
+__device__ __forceinline__ void frag_store(uint8_t* lds, int S, int s, const Frag& f) {
+  u32x4* planes = reinterpret_cast<u32x4*>(lds);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32x4 v;
+    v.x = as_u32(f.p[4 * w + 0]);
+    v.y = as_u32(f.p[4 * w + 1]);
+    v.z = as_u32(f.p[4 * w + 2]);
+    v.w = as_u32(f.p[4 * w + 3]);
+    planes[w * S + s] = v;
+  }
+  float2* os = reinterpret_cast<float2*>(lds + 64 * S);
+  os[s] = make_float2(f.off, f.sx);
+}
+__device__ __forceinline__ void frag_load(const uint8_t* lds, int S, int s, Frag& f) {
+  const u32x4* planes = reinterpret_cast<const u32x4*>(lds);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const u32x4 v = planes[w * S + s];
+    f.p[4 * w + 0] = as_h2(v.x);
+    f.p[4 * w + 1] = as_h2(v.y);
+    f.p[4 * w + 2] = as_h2(v.z);
+    f.p[4 * w + 3] = as_h2(v.w);
+  }
+  const float2 os = reinterpret_cast<const float2*>(lds + 64 * S)[s];
+  f.off = os.x;
+  f.sx = os.y;
+}
+__host__ __device__ constexpr int frag_bytes(int S) { return 72 * S; }
+
+// Stage n f32 values (n <= 32*S; the rest read as 0) into LDS fragments,
+// one segment per thread of the block (threads beyond S idle).
+__device__ __forceinline__ void stage_vector(const float* __restrict__ v, int n, int S,
+                                             uint8_t* lds, int tid, int nthreads) {
+  for (int s = tid; s < S; s += nthreads) {
+    float buf[32];
+    const int base = s * SEG;
+    if (base + SEG <= n) {
+      const f32x4* v4 = reinterpret_cast<const f32x4*>(v + base);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x4 t = v4[i];
+        buf[4 * i + 0] = t.x; buf[4 * i + 1] = t.y; buf[4 * i + 2] = t.z; buf[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) buf[i] = (base + i < n) ? v[base + i] : 0.f;
+    }
+    Frag f;
+    make_frag(buf, f);
+    frag_store(lds, S, s, f);
+  }
+}
+
+// ---------------------------------------------------------------- reductions
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64);
+// every lane of a group gets the group sum.  Fixed butterfly order.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.f + __expf(-g)) * u;
+}
+
+// ---------------------------------------------------------------- inter-workgroup sync
+// Counters live in caller-provided device memory.  Producers: every thread
+// fences its own writes at agent scope, the workgroup meets at a barrier,
+// then one thread bumps the counter.  Consumers: one thread polls with a
+// time limit (s_memrealtime ticks at 100 MHz), then an acquire fence and a
+// barrier.  A wait that times out sets `err` and returns false, so every
+// wave always leaves the kernel.
+__device__ __forceinline__ void wg_signal(uint32_t* ctr) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool wg_wait(uint32_t* ctr, uint32_t target, uint32_t* err,
+                                        uint64_t limit_ticks) {
+  __shared__ int ok_flag;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > limit_ticks) {
+        __hip_atomic_fetch_or(err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    ok_flag = ok;
+  }
+  __syncthreads();
+  return ok_flag != 0;
+}
+
+// Loads of data written by other workgroups of the same kernel: bypass the
+// (non-coherent across XCDs) L2 by loading at agent scope.
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace hq

@@ -1,0 +1,58 @@
+// Internal launch entry points (host side) behind the C ABI in hfq4moe.h.
+// Every launcher assumes its arguments were validated by api.cpp and
+// returns a hipError_t value (0 = success).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+// Kernel-side view of one MoE layer's expert weights.
+struct LayerDev {
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  int64_t sg, su, sd;   // bytes between consecutive experts
+  int E, d, F;
+  uint32_t flags;
+};
+
+// Workspace carve-up shared by the routing and expert kernels.
+struct Ws {
+  uint32_t* err;      // sticky HFQ4_DEV_ERR_* word
+  uint32_t* ctr;      // inter-workgroup counters [16]
+  float* logits;      // [B][E]
+  int32_t* idx;       // [B][k]  routing (internal copy)
+  float* wts;         // [B][k]
+  float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
+};
+
+// Byte layout of a workspace for (E, B, k, F); returns total bytes.
+size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,
+                 size_t* off_wts, size_t* off_h);
+Ws ws_carve(void* base, int64_t E, int B, int k, int64_t F);
+
+int launch_pack(const float* w, int64_t rows, int64_t K, int64_t ldw, void* out, int32_t* bad,
+                hipStream_t s);
+int launch_gemv(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,
+                const float* residual, int64_t ldr, float* y, int64_t ldy, hipStream_t s);
+int launch_route(const float* Wr, const float* bias, int E, int d, const float* x, int64_t ldx,
+                 int B, int k, int32_t* idx, float* wts, float* logits_out, Ws ws, hipStream_t s);
+int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const int32_t* idx,
+                   const float* wts, int k, const float* residual, float* y, int64_t ldy, Ws ws,
+                   hipStream_t s);
+int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const float* x,
+                 int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
+                 float* y, int64_t ldy, Ws ws, hipStream_t s);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Raise a kernel's dynamic LDS limit when it asks for more than the 64 KiB
+// default (gfx950 has 160 KiB per CU).
+template <typename K>
+inline int allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return 0;
+  return (int)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace hq

@@ -1,0 +1,309 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: HFQ4 bytes and routing indices bit-exact (ties inside the stated
+tolerance may come in either order, and the alternative must be a valid
+top-k); routing weights within 1e-5; layer output relative L2 <= 2e-3 per
+token.  Inputs are seeded and synthetic (synth)."""
+
+import numpy as np
+import pytest
+
+from oracle import hfq4, moe
+import synth
+
+from _parity import (REL_L2_TOL, ExpertCache, check_routing, oracle_layer_check, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def q():
+    _need_gpu()
+    import quantized_moe_decode_amd as q
+    q.lib.hfq4_debug_set_arch(b"")
+    return q
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ pack
+
+@pytest.mark.parametrize("rows,K,std,off", [(1, 256, 0.02, 0.0), (7, 128, 1.0, 0.5),
+                                            (33, 300, 0.02, 0.0), (64, 2048, 0.02, 0.0),
+                                            (5, 2050, 3.0, -1.0), (512, 2048, 0.02, 0.0),
+                                            (2048, 512, 0.02, 0.0), (3, 5000, 1e-3, 0.0)])
+def test_pack_bit_exact(q, rows, K, std, off):
+    say("hfq4_pack", rows, K)
+    rng = np.random.default_rng(rows * 7919 + K)
+    W = (rng.standard_normal((rows, K)) * std + off).astype(np.float32)
+    W[0, : min(K, 4)] = [0.0, 15.0, 2.5, 3.5][: min(K, 4)] if std == 1.0 else W[0, : min(K, 4)]
+    got = q.hfq4_pack(torch.from_numpy(W).cuda()).cpu().numpy()
+    ref = hfq4.quantize_rows(W)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref), "first mismatch at byte %d" % int(np.argmax(got != ref))
+
+
+def test_pack_golden_and_constant_blocks(q):
+    say("hfq4_pack golden")
+    i = np.arange(256)
+    W = np.stack([(i % 16).astype(np.float32), np.full(256, 0.75, np.float32),
+                  (np.float32(-0.25) + ((7 * i) % 16).astype(np.float32) / np.float32(64))])
+    got = q.hfq4_pack(torch.from_numpy(W).cuda()).cpu().numpy().tobytes()
+    assert got[:8] == bytes.fromhex("0000803f00000000")
+    assert got[8:136] == bytes.fromhex("1032547698badcfe") * 16
+    assert got[136:144] == bytes.fromhex("000000000000403f")
+    assert got[272:280] == bytes.fromhex("0000803c000080be")
+    assert got[280:408] == bytes.fromhex("705e3c1af8d6b492") * 16
+
+
+def test_pack_rejects_nonfinite(q):
+    say("hfq4_pack nonfinite")
+    W = np.zeros((3, 512), np.float32)
+    W[1, 300] = np.inf
+    W[2, 5] = np.nan
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = q.hfq4_pack(torch.from_numpy(W).cuda(), bad=bad).cpu().numpy().reshape(3, 2, 136)
+    assert int(bad.item()) == 2
+    assert np.all(out[1, 1] == 0) and np.all(out[2, 0] == 0)
+    with pytest.raises(q.Hfq4Error):
+        q.hfq4_pack(torch.from_numpy(W).cuda())
+
+
+# ------------------------------------------------------------------ gemv
+
+@pytest.mark.parametrize("rows,K,batch,resid", [(1, 256, 1, False), (7, 128, 1, True),
+                                                (64, 2048, 1, False), (2051, 2048, 1, True),
+                                                (300, 300, 4, False), (129, 1000, 16, True),
+                                                (40, 4096, 2, False), (17, 16384, 2, True),
+                                                (2048, 512, 16, False)])
+def test_gemv(q, rows, K, batch, resid):
+    say("hfq4_gemv", rows, K, batch, resid)
+    rng = np.random.default_rng(rows + 31 * K + batch)
+    W = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    P = hfq4.quantize_rows(W)
+    x = rng.standard_normal((batch, K)).astype(np.float32)
+    r = rng.standard_normal((batch, rows)).astype(np.float32) if resid else None
+    Wd = torch.from_numpy(P).cuda()
+    y = q.hfq4_gemv(Wd, rows, K, torch.from_numpy(x).cuda(),
+                    residual=None if r is None else torch.from_numpy(r).cuda()).cpu().numpy()
+    ref = hfq4.matvec(P, rows, K, x)
+    if r is not None:
+        ref = ref + r
+    for b in range(batch):
+        assert rel_l2(y[b], ref[b]) <= REL_L2_TOL, (b, rel_l2(y[b], ref[b]))
+    # run-to-run bitwise determinism
+    y2 = q.hfq4_gemv(Wd, rows, K, torch.from_numpy(x).cuda(),
+                     residual=None if r is None else torch.from_numpy(r).cuda()).cpu().numpy()
+    assert np.array_equal(y, y2)
+
+
+def test_gemv_exact_grid_block(q):
+    # block C dequantizes exactly; with x = ones the sum is exactly -34
+    say("hfq4_gemv exact")
+    i = np.arange(256)
+    w = (np.float32(-0.25) + ((7 * i) % 16).astype(np.float32) / np.float32(64))[None, :]
+    Wd = torch.from_numpy(hfq4.quantize_rows(w)).cuda()
+    y = q.hfq4_gemv(Wd, 1, 256, torch.ones((1, 256), device="cuda")).cpu().numpy()
+    assert abs(y[0, 0] + 34.0) < 1e-4
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("E,d,k,B,zipf", [(8, 256, 2, 1, False), (256, 2048, 8, 16, False),
+                                          (512, 2048, 8, 16, True), (1024, 64, 16, 3, False),
+                                          (5, 8, 5, 2, False), (1, 4, 1, 1, False)])
+def test_route_topk(q, E, d, k, B, zipf):
+    say("moe_route_topk", E, d, k, B, zipf)
+    rng = np.random.default_rng(E + d + k + B)
+    Wr = (rng.standard_normal((E, d)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((B, d)).astype(np.float32)
+    bias = synth.zipf_bias(1, E) if zipf else None
+    logits = torch.empty((B, E), dtype=torch.float32, device="cuda")
+    idx, wts = q.moe_route_topk(torch.from_numpy(Wr).cuda(), torch.from_numpy(x).cuda(), k,
+                                bias=None if bias is None else torch.from_numpy(bias).cuda(),
+                                logits=logits)
+    l64 = moe.router_logits(Wr, x, bias)
+    lg = logits.cpu().numpy()
+    assert np.max(np.abs(lg - l64)) <= 1e-4 * max(1.0, np.max(np.abs(l64)))
+    amb = check_routing(idx.cpu().numpy(), wts.cpu().numpy(), l64, k)
+    assert amb <= max(1, B // 8)
+
+
+def test_route_ties_lower_index(q):
+    say("moe_route_topk ties")
+    E, d, k = 64, 4, 8
+    Wr = np.zeros((E, d), np.float32)
+    Wr[[3, 10, 20, 40], 0] = 1.0       # four tied top logits
+    Wr[[5, 7, 9, 11, 13], 0] = 0.5     # five tied next
+    x = np.ones((1, d), np.float32)
+    idx, wts = q.moe_route_topk(torch.from_numpy(Wr).cuda(), torch.from_numpy(x).cuda(), k)
+    assert idx.cpu().numpy().tolist() == [[3, 10, 20, 40, 5, 7, 9, 11]]
+    w = wts.cpu().numpy()[0]
+    e1, e2 = 1.0, np.exp(-0.5)
+    ref = np.array([e1] * 4 + [e2] * 4) / (4 * e1 + 4 * e2)
+    assert np.allclose(w, ref, atol=1e-6)
+
+
+# ------------------------------------------------------------------ expert decode + layer
+
+def _tiny_inputs(q, seed=0):
+    layer, L = q.synthetic.tiny_layer(torch, seed)
+    exps = [moe.PackedExpert.from_f32(L["gate"][e], L["up"][e], L["down"][e]) for e in range(L["E"])]
+    return layer, L, exps
+
+
+@pytest.fixture(scope="module")
+def qs(q):
+    import quantized_moe_decode_amd.synthetic  # noqa: F401
+    return q
+
+
+def test_tiny_layer_packs_match_oracle(qs):
+    say("tiny layer packs")
+    layer, L, exps = _tiny_inputs(qs)
+    g = layer.gate.cpu().numpy().reshape(8, -1)
+    dn = layer.down.cpu().numpy().reshape(8, -1)
+    for e in range(8):
+        assert np.array_equal(g[e], exps[e].gate)
+        assert np.array_equal(dn[e], exps[e].down)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_layer(qs, fused):
+    say("tiny layer fused=%s" % fused)
+    q = qs
+    layer, L, exps = _tiny_inputs(q)
+    x = torch.from_numpy(L["x"]).cuda()
+    ws = q.new_workspace(layer, 1, 2)
+    if fused:
+        idx, wts, y = q.moe_layer_decode(layer, x, 2, ws)
+    else:
+        idx, wts = q.moe_route_topk(layer.Wr, x, 2, ws=ws)
+        y = q.moe_expert_decode(layer, x, idx, wts, ws)
+    torch.cuda.synchronize()
+    assert q.workspace_error(ws) == 0
+    err, amb = oracle_layer_check(L["x"], L["Wr"], None, exps, 2, idx.cpu().numpy(),
+                                  wts.cpu().numpy(), y.cpu().numpy())
+    assert amb == 0 and err <= REL_L2_TOL, err
+
+
+def test_tiny_all_k_and_batches(qs):
+    q = qs
+    layer, L, exps = _tiny_inputs(q, 5)
+    rng = np.random.default_rng(9)
+    for B in (1, 3, 16):
+        for k in (1, 2, 8):
+            say("tiny layer B=%d k=%d" % (B, k))
+            x = rng.standard_normal((B, 256)).astype(np.float32)
+            r = rng.standard_normal((B, 256)).astype(np.float32)
+            ws = q.new_workspace(layer, B, k)
+            idx, wts, y = q.moe_layer_decode(layer, torch.from_numpy(x).cuda(), k, ws,
+                                             residual=torch.from_numpy(r).cuda())
+            torch.cuda.synchronize()
+            assert q.workspace_error(ws) == 0
+            err, amb = oracle_layer_check(x, L["Wr"], None, exps, k, idx.cpu().numpy(),
+                                          wts.cpu().numpy(), y.cpu().numpy(), residual=r)
+            assert amb == 0 and err <= REL_L2_TOL, (B, k, err)
+
+
+def test_expert_decode_bad_index_skipped(qs):
+    q = qs
+    say("expert decode bad index")
+    layer, L, exps = _tiny_inputs(q)
+    x = torch.from_numpy(L["x"]).cuda()
+    idx = torch.tensor([[3, 99]], dtype=torch.int32, device="cuda")
+    wts = torch.tensor([[0.6, 0.4]], dtype=torch.float32, device="cuda")
+    ws = q.new_workspace(layer, 1, 2)
+    y = q.moe_expert_decode(layer, x, idx, wts, ws).cpu().numpy()
+    assert q.workspace_error(ws) & q.HFQ4_DEV_ERR_INDEX
+    ref = 0.6 * moe.expert_forward(exps[3], L["x"][0])
+    assert rel_l2(y[0], ref) <= REL_L2_TOL
+
+
+@pytest.fixture(scope="module")
+def c2(qs):
+    say("building 256-expert layer d=2048 F=512")
+    layer = qs.synthetic.build_layer(torch, seed=0, layer_id=0, E=256, d=2048, F=512)
+    return layer, ExpertCache(torch, "cuda", 0, 0, 2048, 512)
+
+
+def test_c2_packed_experts_match_oracle(qs, c2):
+    layer, cache = c2
+    gb = qs.hfq4_packed_bytes(512, 2048)
+    for e in (0, 137, 255):
+        say("c2 pack parity expert", e)
+        ex = cache(e)
+        assert np.array_equal(layer.gate[e * gb:(e + 1) * gb].cpu().numpy(), ex.gate)
+        assert np.array_equal(layer.up[e * gb:(e + 1) * gb].cpu().numpy(), ex.up)
+        assert np.array_equal(layer.down[e * gb:(e + 1) * gb].cpu().numpy(), ex.down)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_c2_single_token(qs, c2, fused):
+    q = qs
+    layer, cache = c2
+    xs = synth.activations(torch, "cuda", 1, 3, 2048)
+    ws = q.new_workspace(layer, 1, 8)
+    Wr = layer.Wr.cpu().numpy()
+    for t in range(3):
+        say("c2 token", t, "fused", fused)
+        x = xs[t:t + 1].contiguous()
+        if fused:
+            idx, wts, y = q.moe_layer_decode(layer, x, 8, ws)
+        else:
+            idx, wts = q.moe_route_topk(layer.Wr, x, 8, ws=ws)
+            y = q.moe_expert_decode(layer, x, idx, wts, ws)
+        torch.cuda.synchronize()
+        assert q.workspace_error(ws) == 0
+        err, amb = oracle_layer_check(x.cpu().numpy(), Wr, None, cache, 8, idx.cpu().numpy(),
+                                      wts.cpu().numpy(), y.cpu().numpy())
+        assert err <= REL_L2_TOL, err
+
+
+def test_c2_fused_equals_two_call_bitwise(qs, c2):
+    q = qs
+    layer, _ = c2
+    say("c2 fused vs two-call, B=4")
+    x = synth.activations(torch, "cuda", 2, 4, 2048)
+    ws = q.new_workspace(layer, 4, 8)
+    i1, w1, y1 = q.moe_layer_decode(layer, x, 8, ws)
+    i2, w2 = q.moe_route_topk(layer.Wr, x, 8, ws=ws)
+    y2 = q.moe_expert_decode(layer, x, i2, w2, ws)
+    i3, w3, y3 = q.moe_layer_decode(layer, x, 8, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1, w2) and torch.equal(y1, y2)
+    assert torch.equal(y1, y3)
+
+
+def test_c3_skewed_batch(qs):
+    q = qs
+    say("building 512-expert zipf layer")
+    bias = synth.zipf_bias(7, 512)
+    layer = q.synthetic.build_layer(torch, seed=3, layer_id=0, E=512, d=2048, F=512, bias=bias)
+    cache = ExpertCache(torch, "cuda", 3, 0, 2048, 512)
+    for B in (4, 16):
+        say("c3 B=%d" % B)
+        x = synth.activations(torch, "cuda", 10 + B, B, 2048)
+        ws = q.new_workspace(layer, B, 8)
+        idx, wts, y = q.moe_layer_decode(layer, x, 8, ws)
+        torch.cuda.synchronize()
+        assert q.workspace_error(ws) == 0
+        ii = idx.cpu().numpy()
+        if B == 16:   # the oracle evaluates a subset of tokens to stay within seconds
+            sel = [0, 5, 15]
+            err, amb = oracle_layer_check(x.cpu().numpy()[sel], layer.Wr.cpu().numpy(), bias,
+                                          cache, 8, ii[sel], wts.cpu().numpy()[sel],
+                                          y.cpu().numpy()[sel])
+        else:
+            err, amb = oracle_layer_check(x.cpu().numpy(), layer.Wr.cpu().numpy(), bias, cache, 8,
+                                          ii, wts.cpu().numpy(), y.cpu().numpy())
+        assert err <= REL_L2_TOL, err
