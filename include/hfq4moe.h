@@ -192,6 +192,11 @@ int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias,
  * non-gfx950 device be exercised without such a device. */
 int hfq4_debug_set_arch(const char* arch);
 
+/* Diagnostics: register a device buffer (>= 256 KiB) that later decode
+ * launches fill with per-workgroup phase timestamps (s_memrealtime, 100
+ * MHz), slot [(kernel*1024 + workgroup)*8 + point]; NULL turns it off. */
+int hfq4_debug_set_trace(void* dev, size_t bytes);
+
 /* Device address of pinned host memory allocated with hipHostMalloc
  * (mapped), for use in moe_layer with HFQ4_LAYER_HOST_MAPPED [PCIE]. */
 int hfq4_host_device_pointer(void* host, void** dev);

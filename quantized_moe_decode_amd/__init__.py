@@ -35,6 +35,7 @@ EXPORTS = [
     "hfq4_last_error", "hfq4_version", "hfq4_debug_set_arch", "hfq4_packed_bytes", "hfq4_pack",
     "hfq4_gemv", "moe_route_workspace_bytes", "moe_route_topk", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_decode", "moe_layer_decode", "hfq4_host_device_pointer",
+    "hfq4_debug_set_trace",
 ]
 
 
@@ -74,6 +75,7 @@ def _load():
         "moe_layer_decode": (I32, [ctypes.POINTER(MoeLayerC), P, P, P, I64, I32, I32, P, P, P, P,
                                    I64, P, SZ, P]),
         "hfq4_host_device_pointer": (I32, [P, ctypes.POINTER(P)]),
+        "hfq4_debug_set_trace": (I32, [P, SZ]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -1,6 +1,8 @@
 """Build libhfq4moe.so in-tree with hipcc for gfx950.
 
-    python -m quantized_moe_decode_amd.build   (or build() from Python)
+    python quantized_moe_decode_amd/build.py   (or build() from Python)
+
+(Run it as a script: importing the package would load the library first.)
 
 Every source under csrc/ is compiled into one shared library next to this
 file.  All HIP code is built with packed-FP32 instructions disabled.

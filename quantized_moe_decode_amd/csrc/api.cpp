@@ -96,6 +96,11 @@ int check_layer(const moe_layer* L) {
       (L->stride_up & 15) || (L->stride_down & 15))
     return fail(HFQ4_E_ALIGN, "expert weight pointers and strides must be 16-byte aligned");
   if (L->flags & ~HFQ4_LAYER_HOST_MAPPED) return fail(HFQ4_E_INVALID, "unknown layer flags 0x%x", L->flags);
+  const int64_t lim = ((int64_t)1 << 32) - 256;
+  if (L->E * L->stride_gate > lim || L->E * L->stride_up > lim || L->E * L->stride_down > lim)
+    return fail(HFQ4_E_UNSUPPORTED, "E * stride must stay below 4 GiB per tensor (%lld / %lld / %lld bytes)",
+                (long long)(L->E * L->stride_gate), (long long)(L->E * L->stride_up),
+                (long long)(L->E * L->stride_down));
   return HFQ4_OK;
 }
 
@@ -140,6 +145,16 @@ int hfq4_debug_set_arch(const char* arch) {
   std::lock_guard<std::mutex> lk(g_arch_mu);
   if (!arch) arch = "";
   std::snprintf(g_arch_override, sizeof g_arch_override, "%s", arch);
+  return ok();
+}
+
+// Diagnostics: register (or with NULL, clear) a device buffer of at least
+// 4 * 1024 * 8 * 8 bytes that the decode kernels fill with per-workgroup
+// phase timestamps.  Not for production use: it adds stores to every launch.
+int hfq4_debug_set_trace(void* dev, size_t bytes) {
+  if (dev && bytes < (size_t)4 * 1024 * 8 * 8)
+    return fail(HFQ4_E_INVALID, "trace buffer needs %zu bytes, got %zu", (size_t)4 * 1024 * 8 * 8, bytes);
+  hq::set_trace(static_cast<uint64_t*>(dev));
   return ok();
 }
 
@@ -256,6 +271,9 @@ static hq::LayerDev to_dev(const moe_layer* L) {
   D.d = (int)L->d;
   D.F = (int)L->F;
   D.flags = L->flags;
+  D.gate_bytes = (uint32_t)(L->E * L->stride_gate);
+  D.up_bytes = (uint32_t)(L->E * L->stride_up);
+  D.down_bytes = (uint32_t)(L->E * L->stride_down);
   return D;
 }
 

@@ -31,19 +31,23 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
   const int64_t row0 = wave * (RPW * G);
 
-  // Issue this wave's weight loads first: they do not depend on x.
+  // Issue this wave's weight loads first: they do not depend on x.  One
+  // wave-uniform descriptor covers the matrix (rows * ROWB < 2^31, split by
+  // the launcher); rows past the end and dead lanes read zeros.
   u32x4 codes[RPW];
   u32x2 hdr[RPW];
   int64_t nhere = rows - row0;
   if (nhere > RPW * G) nhere = RPW * G;
   if (nhere < 0) nhere = 0;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (nhere ? row0 * ROWB : 0), (uint32_t)(nhere * ROWB));
+  const uint32_t wbytes = (uint32_t)(rows * ROWB);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, wbytes);
   const bool live = (s >> 3) < nb;
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    const uint32_t off = (uint32_t)((i * G + g) * ROWB + (s >> 3) * BLK_BYTES);
-    hdr[i] = live ? bload8(rs, off) : u32x2{0u, 0u};
-    codes[i] = live ? bload16(rs, off + 8 + 16 * (s & 7)) : u32x4{0u, 0u, 0u, 0u};
+    const int64_t row = row0 + i * G + g;
+    const uint32_t off = (live && row < rows) ? (uint32_t)(row * ROWB + (s >> 3) * BLK_BYTES) : wbytes;
+    hdr[i] = bload8(rs, off);
+    codes[i] = bload16(rs, off + 8 + 16 * (s & 7));
   }
 
   const int fb = frag_bytes(SEGS);
@@ -82,12 +86,13 @@ __global__ void __launch_bounds__(256) gemv_wide_kernel(const uint8_t* __restric
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + row * ROWB, (uint32_t)ROWB);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, (uint32_t)(rows * ROWB));
+  const uint32_t rbase = (uint32_t)(row * ROWB);
   float acc[16];
 #pragma unroll
   for (int b = 0; b < 16; ++b) acc[b] = 0.f;
   for (int s = lane; s < S; s += 64) {
-    const uint32_t off = (uint32_t)((s >> 3) * BLK_BYTES);
+    const uint32_t off = rbase + (uint32_t)((s >> 3) * BLK_BYTES);
     const u32x2 hdr = bload8(rs, off);
     const u32x4 codes = bload16(rs, off + 8 + 16 * (s & 7));
 #pragma unroll
@@ -123,8 +128,28 @@ static int launch_narrow(const void* W, int64_t rows, int K, const float* x, int
   return (int)hipGetLastError();
 }
 
+static int launch_gemv_rows(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx,
+                            int batch, const float* residual, int64_t ldr, float* y, int64_t ldy,
+                            hipStream_t s);
+
+// Rows are processed in chunks whose packed size stays below 2^31 bytes, the
+// reach of one buffer descriptor.
 int launch_gemv(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,
                 const float* residual, int64_t ldr, float* y, int64_t ldy, hipStream_t s) {
+  const int64_t rowb = ((K + BLK - 1) / BLK) * BLK_BYTES;
+  const int64_t chunk = ((int64_t)1 << 31) / rowb;
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int64_t n = rows - r0 < chunk ? rows - r0 : chunk;
+    const int e = launch_gemv_rows(static_cast<const uint8_t*>(W) + r0 * rowb, n, K, x, ldx, batch,
+                                   residual ? residual + r0 : nullptr, ldr, y + r0, ldy, s);
+    if (e) return e;
+  }
+  return 0;
+}
+
+static int launch_gemv_rows(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx,
+                            int batch, const float* residual, int64_t ldr, float* y, int64_t ldy,
+                            hipStream_t s) {
   if (rows == 0) return 0;
   const int NB = (int)((K + BLK - 1) / BLK);
   const int k = (int)K;

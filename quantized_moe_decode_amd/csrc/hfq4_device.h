@@ -191,6 +191,57 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---- DPP / permlane reductions (VALU only, fixed order, no LDS traffic)
+template <int CTL>
+__device__ __forceinline__ float dpp(float v) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__builtin_bit_cast(uint32_t, v), CTL,
+                                                      0xf, 0xf, false));
+}
+// All-reduce over each 16-lane row: xor 1, xor 2, rotate 4, rotate 8.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  return v;
+}
+// All-reduce over each 8-lane half-row: xor 1, xor 2, mirror within 8.
+__device__ __forceinline__ float row_sum8(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v;
+}
+// gfx950 cross-row swaps.  a, b must be distinct values.
+// swap32: returns {a.lo32 | b.lo32, a.hi32 | b.hi32} summed -> lanes 0-31 hold
+// a reduced over xor 32, lanes 32-63 hold b reduced over xor 32.
+__device__ __forceinline__ float fold32(float a, float b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                            __builtin_bit_cast(uint32_t, b), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+// swap16: rows {a.r0, b.r0, a.r2, b.r2} + {a.r1, b.r1, a.r3, b.r3}: rows 0 and 2
+// hold a reduced over xor 16, rows 1 and 3 hold b.
+__device__ __forceinline__ float fold16(float a, float b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                            __builtin_bit_cast(uint32_t, b), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+// Full 64-lane sum, result uniform (fixed order: rows, then row 0+1+2+3).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ void trace_point(uint64_t* trace, int kernel, int point) {
+  if (trace && threadIdx.x == 0 && blockIdx.x < 1024)
+    trace[((size_t)kernel * 1024 + blockIdx.x) * 8 + point] = __builtin_amdgcn_s_memrealtime();
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.f + __expf(-g)) * u;
 }

@@ -15,6 +15,9 @@ struct LayerDev {
   int64_t sg, su, sd;   // bytes between consecutive experts
   int E, d, F;
   uint32_t flags;
+  // extent of each tensor (E * stride, < 2^32): one buffer descriptor per
+  // tensor, with expert and row in the per-lane offset
+  uint32_t gate_bytes, up_bytes, down_bytes;
 };
 
 // Workspace carve-up shared by the routing and expert kernels.
@@ -25,7 +28,15 @@ struct Ws {
   int32_t* idx;       // [B][k]  routing (internal copy)
   float* wts;         // [B][k]
   float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
+  uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
+
+// Phase tracing: when a trace buffer is registered, thread 0 of every
+// workgroup stamps s_memrealtime (100 MHz) at fixed points.  Slot layout:
+// trace[(kernel * 1024 + workgroup) * 8 + point].
+enum TraceKernel { TK_LOGITS = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_TOPK = 3 };
+void set_trace(uint64_t* p);
+uint64_t* get_trace();
 
 // Byte layout of a workspace for (E, B, k, F); returns total bytes.
 size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,

@@ -21,8 +21,13 @@
 //   down_kernel    down dequant-GEMV for every (token, slot), weighted by the
 //                  routing weight and summed per lane before one cross-lane
 //                  reduction per output row (fixed order, no atomics).
-//   layer_kernel   all of the above in one launch: one workgroup per CU,
-//                  phases separated by counters in the workspace.
+//   fast path      (d = 2048, F = 512, k <= 8): K2 = per-workgroup top-k +
+//                  grouped gate/up, K3 = down + combine, reductions by DPP and
+//                  gfx950 permlane swaps.  A kernel boundary is the cheapest
+//                  grid-wide synchronisation on MI355X (about 1.5 us inside a
+//                  HIP graph, against 2.4-10 us for an in-kernel barrier over
+//                  256 workgroups), so the layer is three dependent launches:
+//                  router logits -> top-k + gate/up -> down + combine.
 #include "hfq4_device.h"
 #include "launch.h"
 
@@ -58,146 +63,264 @@ struct ExpertArgs {
 
 // ====================================================================== routing
 
-// Logits of rows e = gw, gw + nw, ... for every token; one wave per row.
-__device__ void router_rows(const RouteArgs& a, const Ws& ws, int gw, int nw) {
-  const int lane = threadIdx.x & 63;
+// Router logits, one workgroup per expert row: the four waves split the row
+// into quarters, each lane keeps up to 8 float4 loads in flight, partial
+// sums meet in LDS and are added in a fixed order.
+__global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restrict__ logits,
+                                                     uint64_t* trace) {
+  __shared__ float part[4][HFQ4_MAXB_DEV];
+  trace_point(trace, TK_LOGITS, 0);
+  const int e = blockIdx.x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nq = a.d >> 2;
-  for (int e = gw; e < a.E; e += nw) {
-    const f32x4* wr = reinterpret_cast<const f32x4*>(a.Wr + (int64_t)e * a.d);
-    float acc[HFQ4_MAXB_DEV];
+  const int qw = (nq + 3) >> 2;
+  const int q_lo = wv * qw;
+  const int q_hi = q_lo + qw < nq ? q_lo + qw : nq;
+  const f32x4* wr = reinterpret_cast<const f32x4*>(a.Wr + (int64_t)e * a.d);
+  float acc[HFQ4_MAXB_DEV];
 #pragma unroll
-    for (int b = 0; b < HFQ4_MAXB_DEV; ++b) acc[b] = 0.f;
-    for (int q0 = 0; q0 < nq; q0 += 64 * 8) {
-      f32x4 w[8];
+  for (int b = 0; b < HFQ4_MAXB_DEV; ++b) acc[b] = 0.f;
+  for (int q0 = q_lo; q0 < q_hi; q0 += 64 * 8) {
+    f32x4 w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * 64 + lane;
-        w[u] = q < nq ? wr[q] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int b = 0; b < HFQ4_MAXB_DEV; ++b) {
-        if (b < a.B) {
-          const f32x4* xb = reinterpret_cast<const f32x4*>(a.x + b * a.ldx);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int q = q0 + u * 64 + lane;
-            const f32x4 xv = q < nq ? xb[q] : f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[b] = __builtin_fmaf(w[u].x, xv.x, acc[b]);
-            acc[b] = __builtin_fmaf(w[u].y, xv.y, acc[b]);
-            acc[b] = __builtin_fmaf(w[u].z, xv.z, acc[b]);
-            acc[b] = __builtin_fmaf(w[u].w, xv.w, acc[b]);
-          }
-        }
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u * 64 + lane;
+      w[u] = q < q_hi ? wr[q] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float bias = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
     for (int b = 0; b < HFQ4_MAXB_DEV; ++b) {
       if (b < a.B) {
-        const float l = group_sum<64>(acc[b]) + bias;
-        if (lane == 0) {
-          ws.logits[b * a.E + e] = l;
-          if (a.logits_out) a.logits_out[b * a.E + e] = l;
+        const f32x4* xb = reinterpret_cast<const f32x4*>(a.x + b * a.ldx);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = q0 + u * 64 + lane;
+          const f32x4 xv = q < q_hi ? xb[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[b] = __builtin_fmaf(w[u].x, xv.x, acc[b]);
+          acc[b] = __builtin_fmaf(w[u].y, xv.y, acc[b]);
+          acc[b] = __builtin_fmaf(w[u].z, xv.z, acc[b]);
+          acc[b] = __builtin_fmaf(w[u].w, xv.w, acc[b]);
         }
       }
     }
   }
-}
-
-// (value, index) order for top-k: larger value first, equal values -> lower index.
-__device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
-  if (ae < 0) return false;
-  if (be < 0) return true;
-  return av > bv || (av == bv && ae < be);
-}
-
-// Top-k of one token by one wave.  Logits are read from the workspace at
-// agent scope (they were written by other workgroups).  On return lanes
-// j < k hold (sel_e, sel_w); all lanes see the same selection.
-__device__ void topk_wave(const float* logits, int E, int k, uint32_t* err, int& sel_e,
-                          float& sel_w) {
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = HFQ4_MAXE_DEV / 64;
-  float v[PER];
-  int nonfinite = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    float t = -INFINITY;
-    if (e < E) {
-      t = ld_agent(logits + e);
-      if (__builtin_isnan(t)) {
-        nonfinite = 1;
-        t = -INFINITY;
-      }
+  for (int b = 0; b < HFQ4_MAXB_DEV; ++b)
+    if (b < a.B) {
+      const float t = wave_sum(acc[b]);
+      if (lane == 0) part[wv][b] = t;
     }
-    v[i] = t;
+  __syncthreads();
+  if (threadIdx.x < a.B) {
+    const int b = threadIdx.x;
+    const float l = ((part[0][b] + part[1][b]) + (part[2][b] + part[3][b])) + (a.bias ? a.bias[e] : 0.f);
+    logits[b * a.E + e] = l;
+    if (a.logits_out) a.logits_out[b * a.E + e] = l;
   }
-  if (__any(nonfinite) && lane == 0)
-    __hip_atomic_fetch_or(err, 4u /*HFQ4_DEV_ERR_NONFINITE*/, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t taken = 0;
-  sel_e = -1;
-  float my_v = -INFINITY;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = -1;
+  trace_point(trace, TK_LOGITS, 1);
+}
+
+// Order-preserving 32-bit key of a logit: a larger float gives a larger key,
+// -0 and +0 give the same key, NaN sorts below -inf (key 1), and key 0 is
+// reserved for "no expert" (padding lanes).
+__device__ __forceinline__ uint32_t okey(float f) {
+  if (__builtin_isnan(f)) return 1u;
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u << 1) == 0u) u = 0u;                     // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float okey_value(uint32_t k) {
+  return as_f32((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+template <int CTL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x124>(v));
+  v = max(v, dpp_u<0x128>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<0xB1>(v));
+  v = min(v, dpp_u<0x4E>(v));
+  v = min(v, dpp_u<0x124>(v));
+  v = min(v, dpp_u<0x128>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+// (key, index) order of the top-k: larger key first, equal keys -> lower index.
+__device__ __forceinline__ bool before(uint32_t ak, uint32_t ae, uint32_t bk, uint32_t be) {
+  return (ak > bk) | ((ak == bk) & (ae < be));
+}
+template <int CTL>
+__device__ __forceinline__ void bitonic_step(uint32_t& key, uint32_t& e, bool keep_first) {
+  const uint32_t pk = dpp_u<CTL>(key), pe = dpp_u<CTL>(e);
+  const bool mine_first = before(key, e, pk, pe);
+  const bool take = keep_first != mine_first;   // keep the partner's entry
+  key = take ? pk : key;
+  e = take ? pe : e;
+}
+
+// Top-k of one token's E logits by one wave, exactly in f32 order with ties
+// to the lower expert index (PER >= ceil(E/64) logits per lane, expert e =
+// lane*PER + i).
+//  1. radix select of T, the k-th largest key, two bits per step: three
+//     candidate thresholds are counted at once with ballot + popcount; the
+//     search stops as soon as exactly k keys are >= a candidate (exact ties
+//     at the boundary run all 32 bits);
+//  2. the winners are every key > T plus the lowest-index keys == T, up to
+//     k; they are compacted (in index order) into lanes 0..k-1 through a
+//     64-entry LDS table (`scratch`, 256 bytes per wave);
+//  3. a bitonic network on DPP (mirror/xor partners inside 8 or 16 lanes)
+//     sorts them by (key desc, index asc);
+//  4. weights exp(l_j - l_0) / sum_m exp(l_m - l_0), the sum taken by DPP in a
+//     fixed order.
+// Lanes j < k end with the j-th expert and its weight.  Returns whether a
+// NaN logit was seen.  k <= 16.
+template <int PER>
+__device__ bool topk_wave(const float* __restrict__ logits, int E, int k, int& sel_e, float& sel_w,
+                          uint32_t* scratch, uint64_t* trace) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[PER];
+  int nan_seen = 0;
+  // bounded descriptor over the E logits: lanes past the end read zeros
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits, (uint32_t)E * 4u);
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const int e0 = lane * PER + i;
+    const u32x4 raw = bload16(rl, (uint32_t)e0 * 4u);
+    const uint32_t rv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float f = as_f32(rv[t]);
+      const bool valid = e0 + t < E;
+      key[i + t] = valid ? okey(f) : 0u;
+      nan_seen |= valid & __builtin_isnan(f);
+    }
+  }
+  trace_point(trace, TK_TOPK, 0);
+  // 1. threshold
+  uint32_t T = 0;
+  for (int b = 30; b >= 0; b -= 2) {
+    const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (be < 0 || v[i] > bv)) {
-        bv = v[i];
-        be = e;
-      }
+      n1 += __builtin_popcountll(__ballot(key[i] >= c1));
+      n2 += __builtin_popcountll(__ballot(key[i] >= c2));
+      n3 += __builtin_popcountll(__ballot(key[i] >= c3));
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oe = __shfl_xor(be, m, 64);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      sel_e = be;
-      my_v = bv;
-    }
+    T = (n3 >= k) ? c3 : (n2 >= k) ? c2 : (n1 >= k) ? c1 : T;
+    if (n1 == k || n2 == k || n3 == k) break;   // exactly k keys >= T: done
   }
-  // weights: k-term softmax in selection order (max is the first selected)
-  const float v0 = __shfl(my_v, 0, 64);
+  trace_point(trace, TK_TOPK, 2);
+  // 2. winners: keys > T, then keys == T in index order up to k
+  int n_gt = 0, below_eq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    n_gt += __builtin_popcountll(__ballot(key[i] > T));
+    const uint64_t eq = __ballot(key[i] == T);
+    below_eq += __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+  }
+  const int need = k - n_gt;
+  int own_eq = 0, below_sel = 0, own_sel = 0;
+  bool sel[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool is_eq = key[i] == T;
+    sel[i] = key[i] > T || (is_eq && below_eq + own_eq < need);
+    own_eq += is_eq;
+    const uint64_t sm = __ballot(sel[i]);
+    below_sel += __builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (sel[i]) {
+      const int slot = below_sel + own_sel;
+      scratch[slot] = key[i];
+      scratch[32 + slot] = (uint32_t)(lane * PER + i);
+    }
+    own_sel += sel[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written
+  __builtin_amdgcn_wave_barrier();
+  uint32_t mk = 0, me = 0xFFFFFFFFu;     // lanes >= k hold "after everything"
+  if (lane < k) {
+    mk = scratch[lane];
+    me = scratch[32 + lane];
+  }
+  trace_point(trace, TK_TOPK, 3);
+  // 3. bitonic sort (descending) of lanes 0..15, flip variant: the first
+  //    step of each merge compares mirrored partners, later steps xor
+  //    partners; the lower lane of each pair keeps the entry that comes first
+  const bool lo1 = (lane & 1) == 0, lo2 = (lane & 2) == 0, lo4 = (lane & 4) == 0,
+             lo8 = (lane & 8) == 0;
+  bitonic_step<0xB1>(mk, me, lo1);    // size 2: xor 1
+  bitonic_step<0x1B>(mk, me, lo2);    // size 4: mirror in 4
+  bitonic_step<0xB1>(mk, me, lo1);
+  bitonic_step<0x141>(mk, me, lo4);   // size 8: mirror in 8
+  bitonic_step<0x4E>(mk, me, lo2);
+  bitonic_step<0xB1>(mk, me, lo1);
+  if (k > 8) {
+    bitonic_step<0x140>(mk, me, lo8); // size 16: mirror in 16
+    // xor 4 inside 16 lanes: rotate by 4 for the upper, by 12 for the lower half of each 8
+    {
+      const uint32_t ak = dpp_u<0x12C>(mk), ae = dpp_u<0x12C>(me);   // lane i <- i+4 (mod 16)
+      const uint32_t bk = dpp_u<0x124>(mk), be = dpp_u<0x124>(me);   // lane i <- i-4 (mod 16)
+      const uint32_t pk = lo4 ? ak : bk, pe = lo4 ? ae : be;
+      const bool take = lo4 != before(mk, me, pk, pe);
+      mk = take ? pk : mk;
+      me = take ? pe : me;
+    }
+    bitonic_step<0x4E>(mk, me, lo2);
+    bitonic_step<0xB1>(mk, me, lo1);
+  }
+  trace_point(trace, TK_TOPK, 4);
+  // 4. weights
+  const float l = okey_value(mk);
+  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), 0));
   float ex = 0.f;
-  if (lane < k) ex = (v0 == -INFINITY) ? 1.f : expf(my_v - v0);
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 64);
+  if (lane < k) ex = (l0 == -INFINITY) ? 1.f : expf(l - l0);
+  float sum = ex + dpp<0xB1>(ex);
+  sum += dpp<0x4E>(sum);
+  sum += dpp<0x141>(sum);
+  if (k > 8) sum += dpp<0x128>(sum);   // lanes 0-7 add lanes 8-15
+  sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 0));
+  sel_e = lane < k ? (int)me : -1;
   sel_w = ex / sum;
+  trace_point(trace, TK_TOPK, 1);
+  return __any(nan_seen);
 }
 
-__global__ void __launch_bounds__(256) route_kernel(RouteArgs a, Ws ws) {
-  const int nw = gridDim.x * (blockDim.x >> 6);
-  const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  router_rows(a, ws, gw, nw);
-  // last workgroup to finish selects the experts
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  __shared__ uint32_t ticket;
-  if (threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(&ws.ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (ticket != gridDim.x - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ bool topk_any(const float* logits, int E, int k, int& e, float& w, uint32_t* scratch,
+                         uint64_t* trace) {
+  if (E <= 256) return topk_wave<4>(logits, E, k, e, w, scratch, trace);
+  if (E <= 512) return topk_wave<8>(logits, E, k, e, w, scratch, trace);
+  return topk_wave<16>(logits, E, k, e, w, scratch, trace);
+}
+
+// Standalone top-k: one wave per token.
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int E, int B,
+                                                   int k, int32_t* idx, float* wts, uint32_t* err) {
+  __shared__ uint32_t scratch[4][64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int b = wv; b < a.B; b += (blockDim.x >> 6)) {
+  for (int b = wv; b < B; b += (blockDim.x >> 6)) {
     int e;
     float w;
-    topk_wave(ws.logits + b * a.E, a.E, a.k, ws.err, e, w);
-    if (lane < a.k) {
-      a.idx_out[b * a.k + lane] = e;
-      a.wts_out[b * a.k + lane] = w;
+    const bool nan_seen = topk_any(logits + b * E, E, k, e, w, scratch[wv], nullptr);
+    if (lane < k) {
+      idx[b * k + lane] = e;
+      wts[b * k + lane] = w;
     }
+    if (nan_seen && lane == 0)
+      __hip_atomic_fetch_or(err, 4u /*HFQ4_DEV_ERR_NONFINITE*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&ws.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ====================================================================== grouping
@@ -291,20 +414,23 @@ __device__ void gateup_item(const ExpertArgs& a, const Ws& ws, const Groups& G,
   const int f0 = chunk * ROWS;
   int nrows = F - f0;
   if (nrows > ROWS) nrows = ROWS;
-  const uint32_t span = (uint32_t)(nrows * rowb);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate + e * a.L.sg + f0 * rowb, span);
-  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up + e * a.L.su + f0 * rowb, span);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate, a.L.gate_bytes);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up, a.L.up_bytes);
   const bool live = (s >> 3) < nb;
   u32x4 cg[RPW], cu[RPW];
   u32x2 hg[RPW], hu[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    const uint32_t off = (uint32_t)((i * GR + g) * rowb + (s >> 3) * BLK_BYTES);
-    const uint32_t coff = off + 8 + 16 * (s & 7);
-    hg[i] = live ? bload8(rg, off) : u32x2{0u, 0u};
-    cg[i] = live ? bload16(rg, coff) : u32x4{0u, 0u, 0u, 0u};
-    hu[i] = live ? bload8(ru, off) : u32x2{0u, 0u};
-    cu[i] = live ? bload16(ru, coff) : u32x4{0u, 0u, 0u, 0u};
+    const int rl = i * GR + g;
+    const bool ok = live && rl < nrows;
+    const uint32_t off = (uint32_t)((f0 + rl) * rowb + (s >> 3) * BLK_BYTES);
+    const uint32_t og = ok ? (uint32_t)(e * a.L.sg) + off : a.L.gate_bytes;
+    const uint32_t ou = ok ? (uint32_t)(e * a.L.su) + off : a.L.up_bytes;
+    const uint32_t cc = 8 + 16 * (s & 7);
+    hg[i] = bload8(rg, og);
+    cg[i] = bload16(rg, og + cc);
+    hu[i] = bload8(ru, ou);
+    cu[i] = bload16(ru, ou + cc);
   }
   const int fb = frag_bytes(SEGS);
   const int n = G.gcnt[u], st = G.gstart[u];
@@ -348,16 +474,17 @@ __device__ void down_rows(const ExpertArgs& a, const Ws& ws, const uint8_t* hfr,
     const int p = b * k + j;
     const int e = (j < k) ? pexp[p] : -1;
     const bool use = live && e >= 0;
-    const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(a.L.down + (e >= 0 ? e : 0) * a.L.sd, (uint32_t)(d * rowb));
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
     u32x4 c[ROUT];
     u32x2 hd[ROUT];
 #pragma unroll
     for (int r = 0; r < ROUT; ++r) {
       const int row = r0 + r;
-      const uint32_t off = (uint32_t)(row * rowb + (s >> 3) * BLK_BYTES);
-      hd[r] = (use && row < d) ? bload8(rd, off) : u32x2{0u, 0u};
-      c[r] = (use && row < d) ? bload16(rd, off + 8 + 16 * (s & 7)) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t off = (use && row < d)
+                               ? (uint32_t)(e * a.L.sd + row * rowb + (s >> 3) * BLK_BYTES)
+                               : a.L.down_bytes;
+      hd[r] = bload8(rd, off);
+      c[r] = bload16(rd, off + 8 + 16 * (s & 7));
     }
     const float w = (j < k && e >= 0) ? a.wts[p] : 0.f;
     Frag f;
@@ -434,86 +561,251 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a, Ws ws) {
   }
 }
 
-// ====================================================================== fused layer
+// ====================================================================== fast path: d = 2048, F = 512, k <= 8
 
-// One launch per layer, one workgroup per CU.  Phases:
-//  0  stage x (LDS); router rows of this workgroup -> workspace logits
-//  1  wait for all logits; top-k for every token (redundantly per WG, so no
-//     second hop); WG 0 writes idx/wts; build groups
-//  2  gate/up items -> h in workspace; signal
-//  3  wait for all h; stage h (LDS); down rows + combine -> y
-//  4  last workgroup out resets the counters.
-template <int NBD, int NBF, int RPW, int ROUT>
-__global__ void __launch_bounds__(256) layer_kernel(RouteArgs ra, ExpertArgs a, Ws ws) {
-  constexpr int SEGS_D = 8 * NBD;
-  extern __shared__ __align__(16) uint8_t lds[];
+// Shapes of the workloads this build is tuned for: a gate/up row is 8 blocks
+// = 64 segments (one per lane), a down row is 2 blocks = 16 segments (16
+// lanes), up to 8 experts per token.
+constexpr int FAST_SEGS_D = 64;
+constexpr int FAST_SEGS_F = 16;
+constexpr int FAST_RP = 4;        // gate/up row pairs per wave item
+constexpr int FAST_ROWS = 2;      // down output rows per wave
+
+__host__ __device__ inline bool fast_shape(int d, int F, int k) {
+  return d > 1792 && d <= 2048 && F == 512 && k <= 8;
+}
+
+// K2: routing (top-k from logits, or idx/wts from memory), groups, then the
+// grouped gate/up dequant-GEMV.  A wave item is FAST_RP consecutive row
+// pairs of one expert; each lane owns one 32-weight segment of every row.
+// The 2*FAST_RP row partials of a token are reduced together: two permlane
+// folds (xor 32, xor 16) and one 16-lane DPP sum leave row r's gate and up
+// sums in lanes 16r..16r+15.
+template <bool FROM_LOGITS>
+__global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
+                                                          const float* __restrict__ logits,
+                                                          int32_t* idx_out, float* wts_out) {
+  extern __shared__ __align__(16) uint8_t xfr[];
   __shared__ Groups G;
-  __shared__ int sel_idx[HFQ4_MAXB_DEV * MAXK];
-  __shared__ float sel_w[HFQ4_MAXB_DEV * MAXK];
-  const int nwg = gridDim.x;
+  __shared__ int s_idx[HFQ4_MAXB_DEV * MAXK];
+  __shared__ float s_w[HFQ4_MAXB_DEV * MAXK];
+  __shared__ uint32_t tk_scratch[4][64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = nwg * (blockDim.x >> 6);
+  const int B = a.B, k = a.k, P = B * k, E = a.L.E, F = a.L.F;
+  const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
-  const int B = a.B, k = a.k, P = B * k;
-  uint8_t* xfr = lds;
-  uint8_t* hfr = lds + B * frag_bytes(SEGS_D);
+  const int fb = frag_bytes(FAST_SEGS_D);
+  trace_point(ws.trace, TK_GATEUP, 0);
 
-  // phase 0
-  router_rows(ra, ws, gw, nw);
-  for (int b = 0; b < B; ++b)
-    stage_vector(a.x + b * a.ldx, a.L.d, SEGS_D, xfr + b * frag_bytes(SEGS_D), threadIdx.x,
-                 blockDim.x);
-  wg_signal(&ws.ctr[0]);
-  // phase 1
-  if (!wg_wait(&ws.ctr[0], (uint32_t)nwg, ws.err, WAIT_TICKS)) goto done;
-  for (int b = wv; b < B; b += (blockDim.x >> 6)) {
-    int e;
-    float w;
-    topk_wave(ws.logits + b * ra.E, ra.E, k, ws.err, e, w);
-    if (lane < k) {
-      sel_idx[b * k + lane] = e;
-      sel_w[b * k + lane] = w;
-      if (blockIdx.x == 0) {
-        ra.idx_out[b * k + lane] = e;
-        ra.wts_out[b * k + lane] = w;
+  // 1. routing; waves without a token to route stage x meanwhile
+  if (FROM_LOGITS) {
+    for (int b = wv; b < B; b += 4) {
+      int e;
+      float w;
+      const bool nan_seen = topk_any(logits + b * E, E, k, e, w, tk_scratch[wv], ws.trace);
+      if (lane < k) {
+        s_idx[b * k + lane] = e;
+        s_w[b * k + lane] = w;
+      }
+      if (nan_seen && lane == 0 && blockIdx.x == 0)
+        __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    if (threadIdx.x < P) {
+      s_idx[threadIdx.x] = a.idx[threadIdx.x];
+      s_w[threadIdx.x] = a.wts[threadIdx.x];
+    }
+  }
+  const int stagers = FROM_LOGITS ? (B >= 4 ? 0 : (4 - B) * 64) : 256;
+  const int stage_tid = threadIdx.x - (256 - stagers);
+  if (stagers > 0 && stage_tid >= 0)
+    for (int b = 0; b < B; ++b)
+      stage_vector(a.x + b * a.ldx, a.L.d, FAST_SEGS_D, xfr + b * fb, stage_tid, stagers);
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 1);
+  if (FROM_LOGITS && blockIdx.x == 0 && threadIdx.x < P) {
+    idx_out[threadIdx.x] = s_idx[threadIdx.x];
+    wts_out[threadIdx.x] = s_w[threadIdx.x];
+    ws.idx[threadIdx.x] = s_idx[threadIdx.x];
+    ws.wts[threadIdx.x] = s_w[threadIdx.x];
+  }
+  if (B == 1) {
+    // one token: its k experts are distinct, so every slot is its own group
+    if (threadIdx.x < k) {
+      const int e = s_idx[threadIdx.x];
+      const bool ok = e >= 0 && e < E;
+      if (!ok && blockIdx.x == 0)
+        __hip_atomic_fetch_or(ws.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int u = threadIdx.x;
+      G.gexp[u] = ok ? e : 0;
+      G.gcnt[u] = ok ? 1 : 0;
+      G.gstart[u] = u;
+      G.gmem[u] = u;
+    }
+    if (threadIdx.x == 0) G.U = k;
+    __syncthreads();
+  } else {
+    build_groups(s_idx, P, E, G, ws.err, false);
+  }
+  trace_point(ws.trace, TK_GATEUP, 2);
+
+  // 2. first item's weight loads go out before x is staged (when needed)
+  const int nchunk = F / FAST_RP;
+  const int items = G.U * nchunk;
+  constexpr int64_t ROWB = 8 * BLK_BYTES;
+  const uint32_t hoff = (uint32_t)((lane >> 3) * BLK_BYTES);
+  const uint32_t coff = hoff + 8 + 16 * (lane & 7);
+  int it = gw;
+  u32x4 cg[FAST_RP], cu[FAST_RP];
+  u32x2 hg[FAST_RP], hu[FAST_RP];
+  // one wave-uniform descriptor per tensor (kernel arguments); the expert
+  // and row go into the per-lane offset
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate, a.L.gate_bytes);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up, a.L.up_bytes);
+  auto issue = [&](int item) {
+    const int u = item / nchunk, c = item - u * nchunk;
+    const int e = G.gexp[u];
+    const uint32_t bg = (uint32_t)(e * a.L.sg + (int64_t)c * FAST_RP * ROWB);
+    const uint32_t bu = (uint32_t)(e * a.L.su + (int64_t)c * FAST_RP * ROWB);
+#pragma unroll
+    for (int r = 0; r < FAST_RP; ++r) {
+      hg[r] = bload8(rg, bg + r * ROWB + hoff);
+      cg[r] = bload16(rg, bg + r * ROWB + coff);
+    }
+#pragma unroll
+    for (int r = 0; r < FAST_RP; ++r) {
+      hu[r] = bload8(ru, bu + r * ROWB + hoff);
+      cu[r] = bload16(ru, bu + r * ROWB + coff);
+    }
+  };
+  if (it < items) issue(it);
+  if (FROM_LOGITS && B >= 4) {
+    for (int b = 0; b < B; ++b)
+      stage_vector(a.x + b * a.ldx, a.L.d, FAST_SEGS_D, xfr + b * fb, threadIdx.x, 256);
+    __syncthreads();
+  }
+
+  // 3. compute
+  const int row = lane >> 4;
+  trace_point(ws.trace, TK_GATEUP, 3);
+  bool first = true;
+  while (it < items) {
+    const int u = it / nchunk, c = it - u * nchunk;
+    const int n = G.gcnt[u], st = G.gstart[u];
+    for (int m = 0; m < n; ++m) {
+      const int p = G.gmem[st + m];
+      Frag f;
+      frag_load(xfr + (p / k) * fb, FAST_SEGS_D, lane, f);
+      float g[FAST_RP], v[FAST_RP];
+#pragma unroll
+      for (int r = 0; r < FAST_RP; ++r) {
+        g[r] = dot_seg(cg[r], hg[r], f);
+        v[r] = dot_seg(cu[r], hu[r], f);
+      }
+      const float tg = row_sum16(fold16(fold32(g[0], g[2]), fold32(g[1], g[3])));
+      const float tu = row_sum16(fold16(fold32(v[0], v[2]), fold32(v[1], v[3])));
+      if ((lane & 15) == 0) ws.h[(int64_t)p * F + c * FAST_RP + row] = silu_mul(tg, tu);
+    }
+    if (first) {
+      trace_point(ws.trace, TK_GATEUP, 4);
+      first = false;
+    }
+    it += nw;
+    if (it < items) issue(it);
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 5);
+}
+
+// K3: down dequant-GEMV + routing-weighted combine.  A wave owns FAST_ROWS
+// output rows; lane group g (16 lanes) takes slots g and g + 4 of the
+// token, so every lane sums w_j * partial over its two slots first and one
+// 64-lane reduction per row finishes the sum over segments and slots.
+__global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
+  extern __shared__ __align__(16) uint8_t hfr[];
+  __shared__ int s_e[HFQ4_MAXB_DEV * MAXK];
+  __shared__ float s_w[HFQ4_MAXB_DEV * MAXK];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int B = a.B, k = a.k, P = B * k, d = a.L.d, F = a.L.F;
+  const int g = lane >> 4, s = lane & 15;
+  constexpr int64_t ROWB = 2 * BLK_BYTES;
+  const int fb = frag_bytes(FAST_SEGS_F);
+  trace_point(ws.trace, TK_DOWN, 0);
+  if (threadIdx.x < P) {
+    const int e = a.idx[threadIdx.x];
+    const bool ok = e >= 0 && e < a.L.E;
+    s_e[threadIdx.x] = ok ? e : -1;
+    s_w[threadIdx.x] = ok ? a.wts[threadIdx.x] : 0.f;
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_DOWN, 1);
+  const int r0 = (blockIdx.x * (blockDim.x >> 6) + wv) * FAST_ROWS;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  const uint32_t hoff = (uint32_t)((s >> 3) * BLK_BYTES);
+  const uint32_t coff = hoff + 8 + 16 * (s & 7);
+  for (int b = 0; b < B; ++b) {
+    // h(b, j) for the k slots (one 32-value segment per thread) is loaded
+    // first, the weights of slots g and g+4 second, so that staging can
+    // start as soon as h arrives while the weight loads are still in flight
+    const int t_h = threadIdx.x;
+    const bool stager = t_h < k * FAST_SEGS_F;
+    const int j_h = t_h / FAST_SEGS_F, sg_h = t_h - j_h * FAST_SEGS_F;
+    f32x4 hv[8];
+    if (stager) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)(b * k + j_h) * F + sg_h * SEG);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hv[i] = src[i];
+    }
+    u32x4 c[2][FAST_ROWS];
+    u32x2 hd[2][FAST_ROWS];
+    float w[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = g + 4 * t;
+      const int e = j < k ? s_e[b * k + j] : -1;
+      w[t] = e >= 0 ? s_w[b * k + j] : 0.f;
+      // dead slots read past the end of the descriptor and get zeros
+      const uint32_t base = (e >= 0 && r0 < d) ? (uint32_t)(e * a.L.sd + (int64_t)r0 * ROWB)
+                                               : a.L.down_bytes;
+#pragma unroll
+      for (int r = 0; r < FAST_ROWS; ++r) {
+        hd[t][r] = bload8(rd, base + r * ROWB + hoff);
+        c[t][r] = bload16(rd, base + r * ROWB + coff);
       }
     }
-  }
-  __syncthreads();
-  build_groups(sel_idx, P, a.L.E, G, ws.err, false);
-  {
-    // phase 2
-    constexpr int ROWS = (64 / SEGS_D) * RPW;
-    const int nchunk = (a.L.F + ROWS - 1) / ROWS;
-    const int items = G.U * nchunk;
-    for (int it = gw; it < items; it += nw) gateup_item<NBD, RPW>(a, ws, G, xfr, it);
-  }
-  wg_signal(&ws.ctr[1]);
-  if (!wg_wait(&ws.ctr[1], (uint32_t)nwg, ws.err, WAIT_TICKS)) goto done;
-  {
-    // phase 3: routing weights for the down pass come from LDS
-    ExpertArgs ad = a;
-    ad.wts = sel_w;
-    for (int b = 0; b < B; ++b) {
-      stage_h<NBF>(ad, ws, b, hfr, true);
-      __syncthreads();
-      for (int r0 = gw * ROUT; r0 < a.L.d; r0 += nw * ROUT)
-        down_rows<NBF, ROUT>(ad, ws, hfr, b, r0, G.pexp);
-      __syncthreads();
+    if (stager) {
+      float buf[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        buf[4 * i] = hv[i].x; buf[4 * i + 1] = hv[i].y; buf[4 * i + 2] = hv[i].z; buf[4 * i + 3] = hv[i].w;
+      }
+      Frag fr;
+      make_frag(buf, fr);
+      frag_store(hfr + j_h * fb, FAST_SEGS_F, sg_h, fr);
+      if (b == 0) trace_point(ws.trace, TK_DOWN, 4);
     }
-  }
-done:
-  // phase 4: the last workgroup out clears the counters for the next call
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t =
-        __hip_atomic_fetch_add(&ws.ctr[2], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == (uint32_t)nwg - 1) {
-      __hip_atomic_store(&ws.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws.ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws.ctr[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (b == 0) trace_point(ws.trace, TK_DOWN, 2);
+    float acc[FAST_ROWS];
+#pragma unroll
+    for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = g + 4 * t;
+      Frag f;
+      frag_load(hfr + (j < k ? j : 0) * fb, FAST_SEGS_F, s, f);
+#pragma unroll
+      for (int r = 0; r < FAST_ROWS; ++r) acc[r] = __builtin_fmaf(w[t], dot_seg(c[t][r], hd[t][r], f), acc[r]);
     }
+    // rows 0 and 2 of t hold output rows r0 and r0+1
+    const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
+    if ((lane == 0 || lane == 32)) {
+      const int rr = r0 + (lane >> 5);
+      if (rr < d) a.y[b * a.ldy + rr] = (a.res ? a.res[b * a.ldy + rr] : 0.f) + t;
+    }
+    __syncthreads();
   }
+  trace_point(ws.trace, TK_DOWN, 3);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
@@ -525,6 +817,10 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 // ====================================================================== host side
 
 static inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static uint64_t* g_trace = nullptr;
+void set_trace(uint64_t* p) { g_trace = p; }
+uint64_t* get_trace() { return g_trace; }
 
 size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,
                  size_t* off_wts, size_t* off_h) {
@@ -551,6 +847,7 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t F) {
   w.idx = reinterpret_cast<int32_t*>(p + oi);
   w.wts = reinterpret_cast<float*>(p + ow);
   w.h = reinterpret_cast<float*>(p + oh);
+  w.trace = get_trace();
   return w;
 }
 
@@ -569,9 +866,11 @@ static int num_cus() {
 int launch_route(const float* Wr, const float* bias, int E, int d, const float* x, int64_t ldx,
                  int B, int k, int32_t* idx, float* wts, float* logits_out, Ws ws, hipStream_t s) {
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
-  const int waves = E;
-  int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(256), 0, s, a, ws);
+  hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(256), 0, s, (const float*)ws.logits, E, B, k, idx,
+                     wts, ws.err);
   return (int)hipGetLastError();
 }
 
@@ -601,11 +900,8 @@ static int nb_class(int64_t K) {
   return nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8;
 }
 
-int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const int32_t* idx,
-                   const float* wts, int k, const float* residual, float* y, int64_t ldy, Ws ws,
-                   hipStream_t s) {
-  ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
-  const int cd = nb_class(L.d), cf = nb_class(L.F);
+static int launch_generic_experts(const ExpertArgs& a, Ws ws, hipStream_t s) {
+  const int cd = nb_class(a.L.d), cf = nb_class(a.L.F);
 #define HQ_CASE(D, FF) \
   if (cd == D && cf == FF) return launch_experts_t<D, FF>(a, ws, s);
   HQ_CASE(1, 1) HQ_CASE(1, 2) HQ_CASE(1, 4) HQ_CASE(1, 8)
@@ -616,31 +912,58 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
   return (int)hipErrorInvalidValue;
 }
 
-template <int NBD, int NBF>
-static int launch_layer_t(const RouteArgs& ra, const ExpertArgs& a, Ws ws, hipStream_t s) {
-  constexpr int RPW = (NBD >= 8) ? 2 : 1;
-  constexpr int ROUT = 2;
+// Fast path: K2 (optionally routing from logits) then K3.
+static int launch_fast(const ExpertArgs& a, Ws ws, const float* logits, int32_t* idx_out,
+                       float* wts_out, hipStream_t s) {
   const int nwg = num_cus();
-  const size_t shm = (size_t)a.B * frag_bytes(8 * NBD) + (size_t)a.k * frag_bytes(8 * NBF);
-  if (int e = allow_lds(layer_kernel<NBD, NBF, RPW, ROUT>, shm)) return e;
-  hipLaunchKernelGGL((layer_kernel<NBD, NBF, RPW, ROUT>), dim3(nwg), dim3(256), shm, s, ra, a, ws);
+  const size_t shm = (size_t)a.B * frag_bytes(FAST_SEGS_D);
+  if (logits) {
+    if (int e = allow_lds(gateup_fast_kernel<true>, shm)) return e;
+    hipLaunchKernelGGL(gateup_fast_kernel<true>, dim3(nwg), dim3(256), shm, s, a, ws, logits,
+                       idx_out, wts_out);
+  } else {
+    if (int e = allow_lds(gateup_fast_kernel<false>, shm)) return e;
+    hipLaunchKernelGGL(gateup_fast_kernel<false>, dim3(nwg), dim3(256), shm, s, a, ws,
+                       (const float*)nullptr, (int32_t*)nullptr, (float*)nullptr);
+  }
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  ExpertArgs ad = a;
+  if (logits) {   // the down pass reads the routing K2 just wrote
+    ad.idx = ws.idx;
+    ad.wts = ws.wts;
+  }
+  const int waves = (a.L.d + FAST_ROWS - 1) / FAST_ROWS;
+  hipLaunchKernelGGL(down_fast_kernel, dim3((waves + 3) / 4), dim3(256),
+                     (size_t)a.k * frag_bytes(FAST_SEGS_F), s, ad, ws);
   return (int)hipGetLastError();
+}
+
+int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const int32_t* idx,
+                   const float* wts, int k, const float* residual, float* y, int64_t ldy, Ws ws,
+                   hipStream_t s) {
+  ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
+  if (fast_shape(L.d, L.F, k)) return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
+  return launch_generic_experts(a, ws, s);
 }
 
 int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const float* x,
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s) {
   RouteArgs ra{Wr, bias, L.E, L.d, x, ldx, B, k, idx, wts, nullptr};
+  hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(256), 0, s, ra, ws.logits, ws.trace);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  if (fast_shape(L.d, L.F, k)) {
+    ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
+    return launch_fast(a, ws, ws.logits, idx, wts, s);
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(256), 0, s, (const float*)ws.logits, L.E, B, k,
+                     idx, wts, ws.err);
+  err = (int)hipGetLastError();
+  if (err) return err;
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
-  const int cd = nb_class(L.d), cf = nb_class(L.F);
-#define HQ_CASE(D, FF) \
-  if (cd == D && cf == FF) return launch_layer_t<D, FF>(ra, a, ws, s);
-  HQ_CASE(1, 1) HQ_CASE(1, 2) HQ_CASE(1, 4) HQ_CASE(1, 8)
-  HQ_CASE(2, 1) HQ_CASE(2, 2) HQ_CASE(2, 4) HQ_CASE(2, 8)
-  HQ_CASE(4, 1) HQ_CASE(4, 2) HQ_CASE(4, 4) HQ_CASE(4, 8)
-  HQ_CASE(8, 1) HQ_CASE(8, 2) HQ_CASE(8, 4) HQ_CASE(8, 8)
-#undef HQ_CASE
-  return (int)hipErrorInvalidValue;
+  return launch_generic_experts(a, ws, s);
 }
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
