@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernel-samples", type=int, default=40)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (counter calibration)")
     args = ap.parse_args()
@@ -198,6 +199,39 @@ def main():
     if err:
         raise SystemExit("device error word %d after timed run" % err)
 
+    # Live duration of each kernel of the step, from the library's phase
+    # stamps (s_memrealtime at 100 MHz, thread 0 of every workgroup): a second
+    # graph of the same steps is captured with stamping on, and after each
+    # replay the last step's kernels give first-workgroup-start to
+    # last-workgroup-end.  The stamps cost a few stores per workgroup.
+    kern = None
+    if args.mode == "graph" and args.path == "fused":
+        import ctypes
+        tr = torch.zeros(4 * 1024 * 8, dtype=torch.int64, device=dev)
+        q.lib.hfq4_debug_set_trace(ctypes.c_void_p(tr.data_ptr()), tr.numel() * 8)
+        gt = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gt):
+            for i in range(G):
+                step(i)
+        q.lib.hfq4_debug_set_trace(None, 0)
+        samples = {"logits": [], "gateup": [], "down": [], "step": []}
+        nwg = {0: E, 1: torch.cuda.get_device_properties(0).multi_processor_count, 2: D // 8}
+        for rep in range(args.kernel_samples):
+            gt.replay()
+            torch.cuda.synchronize()
+            t = tr.view(4, 1024, 8).cpu().numpy()
+            st, en = {}, {}
+            for kk, last in ((0, 1), (1, 5), (2, 3)):
+                n = min(nwg[kk], 1024)
+                st[kk] = int(t[kk, :n, 0].min())
+                en[kk] = int(t[kk, :n, last].max())
+            samples["logits"].append((en[0] - st[0]) / 100.0)
+            samples["gateup"].append((en[1] - st[1]) / 100.0)
+            samples["down"].append((en[2] - st[2]) / 100.0)
+            samples["step"].append((en[2] - st[0]) / 100.0)
+        kern = {k: (sum(v) / len(v), sorted(v)[len(v) // 2]) for k, v in samples.items()}
+        del gt
+
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -212,6 +246,9 @@ def main():
     value = expert_bytes / per_step_s / 1e9
     achieved = algo_bytes / per_step_s / 1e9
     traffic = load_traffic()
+    # algorithmic bytes of one gate/up launch: the selected experts' gate and
+    # up rows, the logits, x, and the h it writes (plus idx/wts)
+    gu_bytes = K_TOP * 2 * q.hfq4_packed_bytes(F, D) + E * 4 + D * 4 + K_TOP * F * 4 + 2 * K_TOP * 4
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -232,11 +269,22 @@ def main():
         "tokens_per_s": round(1.0 / per_step_s, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "layer_kernel" if args.path == "fused" else "gateup+down+route",
-                     "algorithmic_bytes_per_launch": algo_bytes},
+        "roofline": ({"bound": "hbm",
+                      "achieved": round(gu_bytes / (kern["gateup"][0] * 1e-6) / 1e9, 2),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gu_bytes / (kern["gateup"][0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": traffic,
+                      "kernel": "gateup_fast_kernel<true> (top-k + grouped gate/up dequant-GEMV)",
+                      "algorithmic_bytes_per_launch": gu_bytes,
+                      "avg_launch_us": round(kern["gateup"][0], 3),
+                      "median_launch_us": round(kern["gateup"][1], 3),
+                      "samples": args.kernel_samples,
+                      "kernel_us": {k: round(v[0], 3) for k, v in kern.items()}}
+                     if kern else None),
+        "layer_roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes_per_step": algo_bytes,
+                           "kernels_per_step": 3 if args.path == "fused" else 4},
     }
     if not args.no_cpu:
         xs_host = xs[:64].cpu().numpy()

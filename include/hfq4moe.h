@@ -197,6 +197,12 @@ int hfq4_debug_set_arch(const char* arch);
  * MHz), slot [(kernel*1024 + workgroup)*8 + point]; NULL turns it off. */
 int hfq4_debug_set_trace(void* dev, size_t bytes);
 
+/* Diagnostics: hipEvent_t handles (cast to void*) recorded when each
+ * later launch of the expert gate/up kernel starts and ends, so a caller
+ * can time that kernel alone with hipEventElapsedTime; NULL, NULL turns it
+ * off.  Not for use under HIP graph capture. */
+int hfq4_debug_set_events(void* start, void* stop);
+
 /* Device address of pinned host memory allocated with hipHostMalloc
  * (mapped), for use in moe_layer with HFQ4_LAYER_HOST_MAPPED [PCIE]. */
 int hfq4_host_device_pointer(void* host, void** dev);

@@ -35,7 +35,7 @@ EXPORTS = [
     "hfq4_last_error", "hfq4_version", "hfq4_debug_set_arch", "hfq4_packed_bytes", "hfq4_pack",
     "hfq4_gemv", "moe_route_workspace_bytes", "moe_route_topk", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_decode", "moe_layer_decode", "hfq4_host_device_pointer",
-    "hfq4_debug_set_trace",
+    "hfq4_debug_set_trace", "hfq4_debug_set_events",
 ]
 
 
@@ -76,6 +76,7 @@ def _load():
                                    I64, P, SZ, P]),
         "hfq4_host_device_pointer": (I32, [P, ctypes.POINTER(P)]),
         "hfq4_debug_set_trace": (I32, [P, SZ]),
+        "hfq4_debug_set_events": (I32, [P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

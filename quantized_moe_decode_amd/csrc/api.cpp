@@ -158,6 +158,15 @@ int hfq4_debug_set_trace(void* dev, size_t bytes) {
   return ok();
 }
 
+// Diagnostics: hipEvent_t handles recorded at the start and the end of every
+// later launch of the expert gate/up kernel (NULL, NULL turns it off).
+int hfq4_debug_set_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(HFQ4_E_INVALID, "give both events or neither");
+  hq::set_timing_events(start, stop);
+  return ok();
+}
+
 int hfq4_packed_bytes(int64_t rows, int64_t K, size_t* out) {
   if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
   if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);

@@ -37,6 +37,7 @@ struct Ws {
 enum TraceKernel { TK_LOGITS = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_TOPK = 3 };
 void set_trace(uint64_t* p);
 uint64_t* get_trace();
+void set_timing_events(void* start, void* stop);
 
 // Byte layout of a workspace for (E, B, k, F); returns total bytes.
 size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,

@@ -28,6 +28,8 @@
 //                  HIP graph, against 2.4-10 us for an in-kernel barrier over
 //                  256 workgroups), so the layer is three dependent launches:
 //                  router logits -> top-k + gate/up -> down + combine.
+#include <hip/hip_ext.h>
+
 #include "hfq4_device.h"
 #include "launch.h"
 
@@ -822,6 +824,14 @@ static uint64_t* g_trace = nullptr;
 void set_trace(uint64_t* p) { g_trace = p; }
 uint64_t* get_trace() { return g_trace; }
 
+// Diagnostics: events recorded at the start and end of the next launches of
+// the gate/up kernel (hipExtLaunchKernel), for live kernel timing.
+static hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+void set_timing_events(void* start, void* stop) {
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+}
+
 size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,
                  size_t* off_wts, size_t* off_h) {
   size_t o = 256;  // err word + 16 counters + padding
@@ -919,12 +929,13 @@ static int launch_fast(const ExpertArgs& a, Ws ws, const float* logits, int32_t*
   const size_t shm = (size_t)a.B * frag_bytes(FAST_SEGS_D);
   if (logits) {
     if (int e = allow_lds(gateup_fast_kernel<true>, shm)) return e;
-    hipLaunchKernelGGL(gateup_fast_kernel<true>, dim3(nwg), dim3(256), shm, s, a, ws, logits,
-                       idx_out, wts_out);
+    hipExtLaunchKernelGGL(gateup_fast_kernel<true>, dim3(nwg), dim3(256), shm, s, g_ev_start,
+                          g_ev_stop, 0, a, ws, logits, idx_out, wts_out);
   } else {
     if (int e = allow_lds(gateup_fast_kernel<false>, shm)) return e;
-    hipLaunchKernelGGL(gateup_fast_kernel<false>, dim3(nwg), dim3(256), shm, s, a, ws,
-                       (const float*)nullptr, (int32_t*)nullptr, (float*)nullptr);
+    hipExtLaunchKernelGGL(gateup_fast_kernel<false>, dim3(nwg), dim3(256), shm, s, g_ev_start,
+                          g_ev_stop, 0, a, ws, (const float*)nullptr, (int32_t*)nullptr,
+                          (float*)nullptr);
   }
   int err = (int)hipGetLastError();
   if (err) return err;
