@@ -98,6 +98,249 @@ def cpu_baseline(torch, layers_f32_seed, xs_host, routers_host, budget_s):
             "tokens_per_s": round(1.0 / per_tok, 4)}
 
 
+def _base(args, steps, warm, per_step_s, value, workload, extra_cfg=None):
+    cfg = {"workload": workload, "global_batch": 1, "mode": "graph"}
+    cfg.update(extra_cfg or {})
+    return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warm, "ms_per_step": round(per_step_s * 1e3, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u4 weights, f16 products, f32 accumulate (router f32)",
+            "data": "synthetic (seeded N(0,0.02) weights HFQ4-packed on device; x ~ N(0,1))",
+            "config": cfg, "cpu_baseline": None}
+
+
+def _graphs(torch, step, n_steps, per_graph):
+    """Capture n_steps calls of step(i) into graphs of per_graph steps."""
+    s = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    s.wait_stream(cur)
+    with torch.cuda.stream(s):
+        step(0)
+    cur.wait_stream(s)
+    torch.cuda.synchronize()
+    gs = []
+    for g0 in range(0, n_steps, per_graph):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(g0, min(n_steps, g0 + per_graph)):
+                step(i)
+        gs.append(g)
+    torch.cuda.synchronize()
+    return gs
+
+
+def _time_graphs(torch, gs, reps_warm, reps):
+    for _ in range(reps_warm):
+        for g in gs:
+            g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        for g in gs:
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / 1e3
+
+
+def bench_stack(args, torch, q):
+    """40 MoE layers (d=2048, F=512, E=256, top-8), each preceded by a dense
+    2048 x 2048 HFQ4 GEMV with residual; 1 token; 256 fresh tokens cycled."""
+    from quantized_moe_decode_amd.stack import build_stack
+    import synth
+    NL, POOL = 40, 256
+    t0 = time.time()
+    st = build_stack(torch, 0, NL, E, D, F, K_TOP, 1, dense=True)
+    xs = synth.activations(torch, "cuda", 2, POOL, D)
+    outs = torch.empty((POOL, D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log("built the %d-layer stack in %.1f s" % (NL, time.time() - t0))
+
+    def step(i):
+        outs[i:i + 1].copy_(st.step(xs[i:i + 1]))
+
+    gs = _graphs(torch, step, POOL, 32)
+    reps = max(1, args.steps // POOL)
+    secs = _time_graphs(torch, gs, 1, reps)
+    steps = reps * POOL
+    err = q.workspace_error(st.ws)
+    if err or not bool(torch.isfinite(outs).all()):
+        raise SystemExit("stack run: device error word %d, finite outputs %s"
+                         % (err, bool(torch.isfinite(outs).all())))
+    per = secs / steps
+    eb = NL * K_TOP * st.layers[0].expert_bytes()
+    dense_b = NL * q.hfq4_packed_bytes(D, D)
+    router_b = NL * E * D * 4
+    algo = eb + dense_b + router_b
+    out = _base(args, steps, POOL, per, eb / per / 1e9,
+                "40-layer expert stack decode: per layer a dense 2048x2048 HFQ4 GEMV + residual, "
+                "then a MoE layer (d=2048, FFN 512, 256 experts, top-8) + residual; 1 token; "
+                "%d fresh tokens cycled" % POOL)
+    out["tokens_per_s"] = round(1.0 / per, 2)
+    out["pct_hbm_peak"] = round(100.0 * eb / per / 1e9 / HBM_PEAK_GBS, 2)
+    out["roofline"] = {"bound": "hbm", "achieved": round(algo / per / 1e9, 2),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(algo / per / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                       "kernel": "whole step: 40 x (dense GEMV, router logits, top-k + gate/up, "
+                                 "down + combine)",
+                       "algorithmic_bytes_per_step": algo,
+                       "expert_bytes_per_step": eb, "dense_bytes_per_step": dense_b,
+                       "router_bytes_per_step": router_b, "kernels_per_step": 4 * NL}
+    return out
+
+
+def _zero_copy_rate(torch, q, nbytes):
+    """PCIe rates: a kernel reading a pinned host HFQ4 matrix zero-copy
+    (hfq4_gemv over it, batch 1) and a host-to-device DMA copy."""
+    rows = nbytes // q.hfq4_packed_bytes(1, D)
+    host = torch.empty(rows * q.hfq4_packed_bytes(1, D), dtype=torch.uint8, pin_memory=True)
+    host.zero_()
+    x = torch.zeros((1, D), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+    q.hfq4_gemv(host, rows, D, x, y=y)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    best_zc = 0.0
+    for _ in range(3):
+        ev0.record()
+        q.hfq4_gemv(host, rows, D, x, y=y)
+        ev1.record()
+        torch.cuda.synchronize()
+        best_zc = max(best_zc, host.numel() / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    dst = torch.empty(host.numel(), dtype=torch.uint8, device="cuda")
+    best_dma = 0.0
+    for _ in range(3):
+        ev0.record()
+        dst.copy_(host, non_blocking=True)
+        ev1.record()
+        torch.cuda.synchronize()
+        best_dma = max(best_dma, host.numel() / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    del host, dst
+    return best_zc, best_dma
+
+
+def bench_hostmapped(args, torch, q):
+    """48 MoE layers (d=2048, F=512, E=512, top-8), residual between layers;
+    experts of layers 0-23 in HBM, of layers 24-47 in pinned host memory
+    read zero-copy by the same kernels."""
+    from quantized_moe_decode_amd.stack import build_stack
+    import synth
+    NL, HOST_FROM, EH, POOL = 48, 24, 512, 64
+    zc, dma = _zero_copy_rate(torch, q, 1 << 29)
+    log("PCIe: zero-copy kernel read %.1f GB/s, DMA host->device %.1f GB/s" % (zc, dma))
+    t0 = time.time()
+    st = build_stack(torch, 0, NL, EH, D, F, K_TOP, 1, dense=False, host_from=HOST_FROM)
+    xs = synth.activations(torch, "cuda", 2, POOL, D)
+    outs = torch.empty((POOL, D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log("built the %d-layer host-mapped stack in %.1f s" % (NL, time.time() - t0))
+
+    def step(i):
+        outs[i:i + 1].copy_(st.step(xs[i:i + 1]))
+
+    gs = _graphs(torch, step, POOL, 16)
+    reps = max(1, min(args.steps, 256) // POOL)
+    secs = _time_graphs(torch, gs, 1, reps)
+    steps = reps * POOL
+    err = q.workspace_error(st.ws)
+    if err or not bool(torch.isfinite(outs).all()):
+        raise SystemExit("host-mapped run: device error word %d, finite outputs %s"
+                         % (err, bool(torch.isfinite(outs).all())))
+    per = secs / steps
+    eb_layer = K_TOP * st.layers[0].expert_bytes()
+    host_b = (NL - HOST_FROM) * eb_layer
+    hbm_b = HOST_FROM * eb_layer + NL * EH * D * 4
+    pcie_peak = max(zc, dma)
+    t_bound = hbm_b / (HBM_PEAK_GBS * 1e9) + host_b / (pcie_peak * 1e9)
+    out = _base(args, steps, POOL, per, NL * eb_layer / per / 1e9,
+                "host-mapped expert mode: 48 MoE layers (d=2048, FFN 512, 512 experts, top-8) + "
+                "residual; experts of layers 0-23 in HBM, 24-47 in pinned host memory read "
+                "zero-copy; 1 token; %d fresh tokens cycled" % POOL)
+    out["tokens_per_s"] = round(1.0 / per, 2)
+    out["roofline"] = {"bound": "hbm+pcie", "achieved": round((hbm_b + host_b) / per / 1e9, 2),
+                       "peak": round((hbm_b + host_b) / t_bound / 1e9, 2), "unit": "GB/s",
+                       "frac": round(t_bound / per, 4), "traffic": None,
+                       "kernel": "whole step: 48 x (router logits, top-k + gate/up, down + combine)",
+                       "hbm_bytes_per_step": hbm_b, "host_bytes_per_step": host_b,
+                       "pcie_zero_copy_gbs": round(zc, 2), "pcie_dma_gbs": round(dma, 2),
+                       "pcie_peak_used_gbs": round(pcie_peak, 2),
+                       "bound_ms_per_step": round(t_bound * 1e3, 4),
+                       "host_gbs_if_hbm_at_peak": round(
+                           host_b / max(per - hbm_b / (HBM_PEAK_GBS * 1e9), 1e-12) / 1e9, 2)}
+    return out
+
+
+def bench_skewed(args, torch, q):
+    """One layer shape (d=2048, F=512, E=512, top-8) with Zipf(1.1)-biased
+    router logits; token batches of 1, 4 and 16.  16 replicas of the layer
+    (13.7 GB) and a 4096-token pool keep the Infinity Cache from serving
+    repeats."""
+    import numpy as np
+    import quantized_moe_decode_amd.synthetic as syn
+    import synth
+    EH, NREP, POOL = 512, 16, 4096
+    bias = synth.zipf_bias(0, EH)
+    t0 = time.time()
+    layers = [syn.build_layer(torch, 0, r, EH, D, F, bias=bias) for r in range(NREP)]
+    xs = synth.activations(torch, "cuda", 3, POOL, D)
+    torch.cuda.synchronize()
+    log("built %d skewed replicas in %.1f s" % (NREP, time.time() - t0))
+    eb = layers[0].expert_bytes()
+    res = {}
+    for B in (1, 4, 16):
+        ws = q.new_workspace(layers[0], B, K_TOP)
+        y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, K_TOP), dtype=torch.int32, device="cuda")
+        wts = torch.empty((B, K_TOP), dtype=torch.float32, device="cuda")
+        nsteps = POOL // B
+        G = 256
+
+        def step(i):
+            j = (i * B) % POOL
+            q.moe_layer_decode(layers[i % NREP], xs[j:j + B], K_TOP, ws, y=y, idx=idx, wts=wts)
+
+        gs = _graphs(torch, step, G, G)
+        reps = max(1, args.steps // (4 * G))
+        secs = _time_graphs(torch, gs, 1, reps)
+        err = q.workspace_error(ws)
+        if err:
+            raise SystemExit("device error word %d after the skewed run (B=%d)" % (err, B))
+        per = secs / (reps * G)
+        # distinct experts per step, from the routing of the same steps
+        uni = []
+        rws = torch.empty(q.moe_route_workspace_bytes(EH, B), dtype=torch.uint8,
+                                             device="cuda")
+        for i in range(G):
+            j = (i * B) % POOL
+            L = layers[i % NREP]
+            ii, _ = q.moe_route_topk(L.Wr, xs[j:j + B], K_TOP, bias=L.bias, ws=rws)
+            uni.append(len(np.unique(ii.cpu().numpy())))
+        u = float(np.mean(uni))
+        res[str(B)] = {"ms_per_step": round(per * 1e3, 5), "tokens_per_s": round(B / per, 1),
+                       "mean_distinct_experts": round(u, 2),
+                       "expert_gbs": round(u * eb / per / 1e9, 2),
+                       "pct_hbm_peak": round(100 * u * eb / per / 1e9 / HBM_PEAK_GBS, 2),
+                       "steps": reps * G}
+        del ws
+    b1 = res["1"]
+    out = _base(args, sum(r["steps"] for r in res.values()), 0, b1["ms_per_step"] / 1e3,
+                b1["expert_gbs"],
+                "skewed-routing layer: d=2048, FFN 512, 512 experts, top-8, Zipf(s=1.1) router "
+                "bias, token batches 1/4/16; %d replicas, %d-token pool" % (NREP, POOL),
+                {"global_batch": [1, 4, 16]})
+    out["per_batch"] = res
+    out["tokens_per_s"] = b1["tokens_per_s"]
+    out["roofline"] = {"bound": "hbm", "achieved": b1["expert_gbs"], "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(b1["expert_gbs"] / HBM_PEAK_GBS, 4),
+                       "traffic": None, "kernel": "whole layer step at B=1 (expert bytes of the "
+                                                  "distinct selected experts)"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +356,11 @@ def main():
     ap.add_argument("--kernel-samples", type=int, default=40)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed"],
+                    default="layer",
+                    help="layer: one MoE layer (the headline line); stack: 40 layers with a dense "
+                         "GEMV each; hostmapped: 48 layers, experts of 24 in pinned host memory; "
+                         "skewed: 512 experts, Zipf-biased routing, token batches 1/4/16")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -129,6 +377,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.workload != "layer":
+        out = {"stack": bench_stack, "hostmapped": bench_hostmapped,
+               "skewed": bench_skewed}[args.workload](args, torch, q)
+        print(json.dumps(out), flush=True)
+        return
 
     t0 = time.time()
     layers = [syn.build_layer(torch, seed=0, layer_id=r, E=E, d=D, F=F, device=dev)

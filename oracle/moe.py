@@ -160,16 +160,19 @@ def moe_layer(x, Wr, experts, k, bias=None, logit_dtype=np.float64, idx=None):
     return r_idx, r_wts, y, logits
 
 
-def stack_step(x, layers, k):
+def stack_step(x, layers, k, trace=None):
     """One decode step through a stack (reading; parity unpinned against the
-    pages).  layers: list of dicts with keys 'Wr', 'experts', optional
+    pages).  layers: iterable of dicts with keys 'Wr', 'experts', optional
     'bias', optional 'dense' (packed HFQ4 d x d).  Per layer:
-    t = x + D x (when a dense matrix is present), then x' = t + MoE(t)."""
+    t = x + D x (when a dense matrix is present), then x' = t + MoE(t).
+    With trace (a list), every layer appends (x', idx, wts, logits)."""
     x = np.asarray(x, dtype=np.float64).reshape(-1)
     d = x.size
     for L in layers:
         if L.get("dense") is not None:
             x = x + hfq4.matvec(L["dense"], d, d, x)
-        _, _, y, _ = moe_layer(x, L["Wr"], L["experts"], k, L.get("bias"))
+        idx, wts, y, logits = moe_layer(x, L["Wr"], L["experts"], k, L.get("bias"))
         x = x + y[0]
+        if trace is not None:
+            trace.append((x.copy(), idx[0], wts[0], logits[0]))
     return x

@@ -138,14 +138,16 @@ def hfq4_pack(w, out=None, bad=None, stream=None):
 
 
 def hfq4_gemv(W, rows, K, x, residual=None, y=None, stream=None):
-    """y[b] = residual[b] + W x[b] for x [batch, K] f32 (device)."""
+    """y[b] = residual[b] + W x[b] for x [batch, K] f32 (device).  W is a
+    device tensor or a pinned host tensor (read zero-copy over PCIe)."""
     import torch
     x2 = x if x.dim() == 2 else x.view(1, -1)
     batch = x2.shape[0]
     if y is None:
         y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
     ldr = residual.stride(0) if (residual is not None and residual.dim() == 2) else rows
-    _check(lib.hfq4_gemv(_ptr(W), rows, K, _ptr(x2), x2.stride(0), batch, _ptr(residual), ldr,
+    wp = _ptr(W) if W.is_cuda else ctypes.c_void_p(host_device_pointer(W))
+    _check(lib.hfq4_gemv(wp, rows, K, _ptr(x2), x2.stride(0), batch, _ptr(residual), ldr,
                          _ptr(y), y.stride(0) if y.dim() == 2 else rows, _stream(stream)))
     return y
 
@@ -175,6 +177,15 @@ def moe_route_topk(Wr, x, k, bias=None, ws=None, logits=None, idx=None, wts=None
     return idx, wts
 
 
+def host_device_pointer(t):
+    """Device address of a pinned host tensor (torch pin_memory=True)."""
+    if t.is_cuda or not t.is_pinned():
+        raise Hfq4Error(HFQ4_E_INVALID, "host-mapped tensors must be pinned host memory")
+    out = ctypes.c_void_p()
+    _check(lib.hfq4_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)))
+    return out.value
+
+
 # ------------------------------------------------------------------ experts
 
 class MoeLayer:
@@ -189,7 +200,15 @@ class MoeLayer:
         self.Wr, self.bias = Wr, bias
         gb = hfq4_packed_bytes(F, d)
         db = hfq4_packed_bytes(d, F)
-        self.c = MoeLayerC(gate.data_ptr(), up.data_ptr(), down.data_ptr(), E, d, F,
+        if host_mapped:
+            ptrs = [host_device_pointer(t) for t in (gate, up, down)]
+        else:
+            for t in (gate, up, down):
+                if not t.is_cuda:
+                    raise Hfq4Error(HFQ4_E_INVALID, "expert tensors must be on the device "
+                                    "(or pinned host memory with host_mapped=True)")
+            ptrs = [t.data_ptr() for t in (gate, up, down)]
+        self.c = MoeLayerC(ptrs[0], ptrs[1], ptrs[2], E, d, F,
                            stride_gate or gb, stride_up or gb, stride_down or db,
                            HFQ4_LAYER_HOST_MAPPED if host_mapped else 0, 0)
 

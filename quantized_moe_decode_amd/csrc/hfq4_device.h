@@ -64,15 +64,31 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // ---------------------------------------------------------------- fragments
 
 // Activation fragment for one 32-element segment, in the order dot_seg uses.
+// The segment is first scaled by a power of two, xs, chosen so that its
+// largest magnitude lies in [2, 4): the f16 pairs then keep the same relative
+// precision whatever the activations' range (a 40-layer residual stack grows
+// them far beyond f16's maximum), and the f32 sums that cancel the 1024
+// offsets stay small.  Scaling by a power of two is exact.
 struct Frag {
   h2 p[16];
-  float off;   // -(1024 * sum of all 32 stored halves + 8 * sum of the f16 x they stand for)
-  float sx;    // exact f32 sum of the 32 activations
+  float off;   // -(1024 * sum of all 32 stored halves + 8 * sum of the f16 values they stand for)
+  float sx;    // exact f32 sum of the 32 (unscaled) activations
+  float xs;    // the power-of-two scale: activation = xs * (stored value)
 };
 
 // Build a fragment from 32 f32 activations v[0..31] (element order).
 // Dword w of a segment covers elements 8w..8w+7 (element 8w+n at nibble n).
 __device__ __forceinline__ void make_frag(const float* v, Frag& f) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = 0;
+  if (amax > 0.f && amax < INFINITY) {
+    int ex;
+    frexpf(amax, &ex);           // amax = m * 2^ex, m in [0.5, 1)
+    e = ex - 2;                  // amax * 2^-e in [2, 4)
+  }
+  const float inv = ldexpf(1.0f, -e);
   float sum_half = 0.f, sum_x16 = 0.f, sx = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -82,7 +98,7 @@ __device__ __forceinline__ void make_frag(const float* v, Frag& f) {
       const int n = p;                         // pair p = elements (8w+p, 8w+p+4)
       const float a = v[8 * w + n], b = v[8 * w + n + 4];
       const float s = hi ? 0.0625f : 1.0f;
-      _Float16 ha = (_Float16)(a * s), hb = (_Float16)(b * s);
+      _Float16 ha = (_Float16)(a * inv * s), hb = (_Float16)(b * inv * s);
       f.p[4 * w + p] = h2{ha, hb};
       const float fa = (float)ha, fb = (float)hb;
       sum_half += fa + fb;
@@ -92,6 +108,7 @@ __device__ __forceinline__ void make_frag(const float* v, Frag& f) {
   }
   f.off = -(1024.f * sum_half + 8.f * sum_x16);
   f.sx = sx;
+  f.xs = ldexpf(1.0f, e);
 }
 
 // One code dword (8 weights) against 4 fragment pairs.
@@ -118,14 +135,14 @@ __device__ __forceinline__ float dot_seg(u32x4 codes, u32x2 hdr, const Frag& f) 
   const float scale = as_f32(hdr.x);
   const float zero = as_f32(hdr.y);
   const float zp8 = __builtin_fmaf(8.f, scale, zero);
-  return __builtin_fmaf(scale, acc, zp8 * f.sx);
+  return __builtin_fmaf(scale * f.xs, acc, zp8 * f.sx);
 }
 
 // ---------------------------------------------------------------- LDS fragment store
 // Fragments of a vector with S segments live in LDS as 4 planes of S x 16 B
 // (plane w = pairs 4w..4w+3 of every segment; consecutive segments are
 // consecutive 16-byte slots, so a wave reading consecutive segments is
-// conflict-free) followed by S float2 (off, sx).
+// conflict-free) followed by S x 16 B of (off, sx, xs, 0).
 __device__ __forceinline__ void frag_store(uint8_t* lds, int S, int s, const Frag& f) {
   u32x4* planes = reinterpret_cast<u32x4*>(lds);
 #pragma unroll
@@ -137,8 +154,8 @@ __device__ __forceinline__ void frag_store(uint8_t* lds, int S, int s, const Fra
     v.w = as_u32(f.p[4 * w + 3]);
     planes[w * S + s] = v;
   }
-  float2* os = reinterpret_cast<float2*>(lds + 64 * S);
-  os[s] = make_float2(f.off, f.sx);
+  f32x4* os = reinterpret_cast<f32x4*>(lds + 64 * S);
+  os[s] = f32x4{f.off, f.sx, f.xs, 0.f};
 }
 __device__ __forceinline__ void frag_load(const uint8_t* lds, int S, int s, Frag& f) {
   const u32x4* planes = reinterpret_cast<const u32x4*>(lds);
@@ -150,11 +167,12 @@ __device__ __forceinline__ void frag_load(const uint8_t* lds, int S, int s, Frag
     f.p[4 * w + 2] = as_h2(v.z);
     f.p[4 * w + 3] = as_h2(v.w);
   }
-  const float2 os = reinterpret_cast<const float2*>(lds + 64 * S)[s];
+  const f32x4 os = reinterpret_cast<const f32x4*>(lds + 64 * S)[s];
   f.off = os.x;
   f.sx = os.y;
+  f.xs = os.z;
 }
-__host__ __device__ constexpr int frag_bytes(int S) { return 72 * S; }
+__host__ __device__ constexpr int frag_bytes(int S) { return 80 * S; }
 
 // Stage n f32 values (n <= 32*S; the rest read as 0) into LDS fragments,
 // one segment per thread of the block (threads beyond S idle).

@@ -16,6 +16,8 @@ Recipes (the shapes and distributions of the workloads; all f32):
   device that drew it (torch Philox on the GPU, torch CPU generator on the
   host).  Router Wr ~ N(0, 0.02) [E, d], expert weights ~ N(0, 0.02),
   x ~ N(0, 1).
+* stack          -- per layer the same expert/router recipe plus a dense
+  d x d matrix ~ N(0, 0.1/sqrt(d)) (dense_f32).
 * skew           -- a per-expert Zipf(s) log-offset added to the router
   logits: bias[e] = -s * ln(rank[e]) with rank a seeded permutation of
   1..E (the hot set is the experts of low rank).
@@ -77,7 +79,14 @@ def router_f32(torch, device, seed, layer, E, d, std=0.02):
     return device_matrix(torch, device, seed, layer, 0, ROUTER, E, d, std)
 
 
-def dense_f32(torch, device, seed, layer, d, std=0.02):
+def dense_f32(torch, device, seed, layer, d, std=None):
+    """Dense d x d matrix of a stack layer, N(0, std) with std = 0.1/sqrt(d)
+    by default: its update D x then has a tenth of the residual's norm, so a
+    40-layer residual stack stays near unit scale (N(0, 0.02) at d = 2048
+    would grow the residual 1.35x per layer and, through the experts'
+    quadratic SiLU(gate)*up term, overflow f32 within about 20 layers)."""
+    if std is None:
+        std = 0.1 / float(np.sqrt(d))
     return device_matrix(torch, device, seed, layer, 0, DENSE, d, d, std)
 
 

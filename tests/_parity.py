@@ -17,11 +17,11 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def tie_tol(l):
-    return TIE_REL * max(1.0, abs(float(l)))
+def tie_tol(l, rel=TIE_REL):
+    return rel * max(1.0, abs(float(l)))
 
 
-def routing_valid(sel, logits, k):
+def routing_valid(sel, logits, k, rel=TIE_REL):
     """Is `sel` (k expert ids, in order) a top-k of `logits` (float64) when
     logits closer than the tie tolerance may come in either order?"""
     sel = [int(e) for e in sel]
@@ -29,12 +29,12 @@ def routing_valid(sel, logits, k):
     if len(sel) != k or len(set(sel)) != k or min(sel) < 0 or max(sel) >= E:
         return False
     for a, c in zip(sel, sel[1:]):          # order: non-increasing up to ties
-        if logits[a] < logits[c] - tie_tol(logits[c]):
+        if logits[a] < logits[c] - tie_tol(logits[c], rel):
             return False
     chosen = set(sel)
     worst = min(logits[s] for s in sel)
     for u in range(E):                      # no unselected expert strictly better
-        if u not in chosen and logits[u] > worst + tie_tol(worst):
+        if u not in chosen and logits[u] > worst + tie_tol(worst, rel):
             return False
     return True
 
