@@ -291,7 +291,7 @@ def bench_skewed(args, torch, q):
     log("built %d skewed replicas in %.1f s" % (NREP, time.time() - t0))
     eb = layers[0].expert_bytes()
     res = {}
-    for B in (1, 4, 16):
+    for B in [int(v) for v in args.batches.split(",")]:
         ws = q.new_workspace(layers[0], B, K_TOP)
         y = torch.empty((B, D), dtype=torch.float32, device="cuda")
         idx = torch.empty((B, K_TOP), dtype=torch.int32, device="cuda")
@@ -326,12 +326,12 @@ def bench_skewed(args, torch, q):
                        "pct_hbm_peak": round(100 * u * eb / per / 1e9 / HBM_PEAK_GBS, 2),
                        "steps": reps * G}
         del ws
-    b1 = res["1"]
+    b1 = res[min(res, key=int)]
     out = _base(args, sum(r["steps"] for r in res.values()), 0, b1["ms_per_step"] / 1e3,
                 b1["expert_gbs"],
                 "skewed-routing layer: d=2048, FFN 512, 512 experts, top-8, Zipf(s=1.1) router "
                 "bias, token batches 1/4/16; %d replicas, %d-token pool" % (NREP, POOL),
-                {"global_batch": [1, 4, 16]})
+                {"global_batch": [int(v) for v in res]})
     out["per_batch"] = res
     out["tokens_per_s"] = b1["tokens_per_s"]
     out["roofline"] = {"bound": "hbm", "achieved": b1["expert_gbs"], "peak": HBM_PEAK_GBS,
@@ -356,6 +356,8 @@ def main():
     ap.add_argument("--kernel-samples", type=int, default=40)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--batches", default="1,4,16",
+                    help="token batch sizes of the skewed workload")
     ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed"],
                     default="layer",
                     help="layer: one MoE layer (the headline line); stack: 40 layers with a dense "

@@ -60,6 +60,9 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 
 // ---------------------------------------------------------------- fragments
 
@@ -255,9 +258,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+__device__ __forceinline__ void trace_point_at(uint64_t* trace, int kernel, int wg, int point) {
+  if (trace && threadIdx.x == 0 && wg < 1024)
+    trace[((size_t)kernel * 1024 + wg) * 8 + point] = __builtin_amdgcn_s_memrealtime();
+}
 __device__ __forceinline__ void trace_point(uint64_t* trace, int kernel, int point) {
-  if (trace && threadIdx.x == 0 && blockIdx.x < 1024)
-    trace[((size_t)kernel * 1024 + blockIdx.x) * 8 + point] = __builtin_amdgcn_s_memrealtime();
+  trace_point_at(trace, kernel, (int)blockIdx.x, point);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

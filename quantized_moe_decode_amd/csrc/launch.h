@@ -20,16 +20,33 @@ struct LayerDev {
   uint32_t gate_bytes, up_bytes, down_bytes;
 };
 
+// Token groups of a batched call: the pairs (token, slot) that selected the
+// same expert.  Group ids follow the first pair of each group; members are
+// in token order.
+constexpr int GT_MAXU = 128;   // max groups (= max pairs B*k)
+constexpr int GT_MAXM = 16;    // max members (= max tokens)
+struct GroupTab {
+  int U;
+  int gexp[GT_MAXU];
+  int gcnt[GT_MAXU];
+  uint8_t gmem[GT_MAXU][GT_MAXM];   // member m of group u: pair id
+};
+
 // Workspace carve-up shared by the routing and expert kernels.
 struct Ws {
   uint32_t* err;      // sticky HFQ4_DEV_ERR_* word
-  uint32_t* ctr;      // inter-workgroup counters [16]
+  uint32_t* ctr;      // inter-workgroup counters [WS_COUNTERS], zero between calls
   float* logits;      // [B][E]
   int32_t* idx;       // [B][k]  routing (internal copy)
   float* wts;         // [B][k]
-  float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
+  float* h;           // [B*k][F] SiLU(gate)*up per (token, slot); batched: gate outputs [2][B*k][F]
+  float* u;           // batched: up outputs [2][B*k][F] (two K halves); null otherwise
+  float* ypart;       // [B*k][d] weighted expert outputs (batched path; null otherwise)
+  GroupTab* groups;   // batched path; null otherwise
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
+constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
+constexpr int WS_COUNTERS = 240;
 
 // Phase tracing: when a trace buffer is registered, thread 0 of every
 // workgroup stamps s_memrealtime (100 MHz) at fixed points.  Slot layout:
@@ -39,10 +56,12 @@ void set_trace(uint64_t* p);
 uint64_t* get_trace();
 void set_timing_events(void* start, void* stop);
 
-// Byte layout of a workspace for (E, B, k, F); returns total bytes.
-size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,
-                 size_t* off_wts, size_t* off_h);
-Ws ws_carve(void* base, int64_t E, int B, int k, int64_t F);
+// Byte layout of a workspace for (E, B, k, d, F) (k = 0: routing only).
+struct WsLayout {
+  size_t logits, idx, wts, h, u, ypart, groups, total;
+};
+WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F);
+Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F);
 
 int launch_pack(const float* w, int64_t rows, int64_t K, int64_t ldw, void* out, int32_t* bad,
                 hipStream_t s);
@@ -58,11 +77,11 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  float* y, int64_t ldy, Ws ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
-// Raise a kernel's dynamic LDS limit when it asks for more than the 64 KiB
-// default (gfx950 has 160 KiB per CU).
+// Raise a kernel's dynamic LDS limit when its static plus dynamic use may
+// pass the 64 KiB default (gfx950 has 160 KiB per CU).
 template <typename K>
 inline int allow_lds(K kernel, size_t bytes) {
-  if (bytes <= 65536) return 0;
+  if (bytes <= 32768) return 0;
   return (int)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }

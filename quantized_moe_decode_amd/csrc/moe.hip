@@ -32,36 +32,10 @@
 
 #include "hfq4_device.h"
 #include "launch.h"
+#include "moe_common.h"
+#include "topk_device.h"
 
 namespace hq {
-
-constexpr uint64_t WAIT_TICKS = 20000000ull;   // 200 ms of s_memrealtime (100 MHz)
-constexpr int MAXP = 128;                      // max (token, slot) pairs: 16 x 8... up to B*k
-constexpr int MAXK = 16;
-
-struct RouteArgs {
-  const float* Wr;
-  const float* bias;
-  int E, d;
-  const float* x;
-  int64_t ldx;
-  int B, k;
-  int32_t* idx_out;
-  float* wts_out;
-  float* logits_out;
-};
-
-struct ExpertArgs {
-  LayerDev L;
-  const float* x;
-  int64_t ldx;
-  int B, k;
-  const int32_t* idx;   // [B][k]
-  const float* wts;     // [B][k]
-  const float* res;     // [B][ldy] or null
-  float* y;
-  int64_t ldy;
-};
 
 // ====================================================================== routing
 
@@ -119,192 +93,6 @@ __global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restr
     if (a.logits_out) a.logits_out[b * a.E + e] = l;
   }
   trace_point(trace, TK_LOGITS, 1);
-}
-
-// Order-preserving 32-bit key of a logit: a larger float gives a larger key,
-// -0 and +0 give the same key, NaN sorts below -inf (key 1), and key 0 is
-// reserved for "no expert" (padding lanes).
-__device__ __forceinline__ uint32_t okey(float f) {
-  if (__builtin_isnan(f)) return 1u;
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u << 1) == 0u) u = 0u;                     // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float okey_value(uint32_t k) {
-  return as_f32((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-template <int CTL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTL, 0xf, 0xf, false);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u<0xB1>(v));
-  v = max(v, dpp_u<0x4E>(v));
-  v = max(v, dpp_u<0x124>(v));
-  v = max(v, dpp_u<0x128>(v));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp_u<0xB1>(v));
-  v = min(v, dpp_u<0x4E>(v));
-  v = min(v, dpp_u<0x124>(v));
-  v = min(v, dpp_u<0x128>(v));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return min(min(r0, r1), min(r2, r3));
-}
-
-// (key, index) order of the top-k: larger key first, equal keys -> lower index.
-__device__ __forceinline__ bool before(uint32_t ak, uint32_t ae, uint32_t bk, uint32_t be) {
-  return (ak > bk) | ((ak == bk) & (ae < be));
-}
-template <int CTL>
-__device__ __forceinline__ void bitonic_step(uint32_t& key, uint32_t& e, bool keep_first) {
-  const uint32_t pk = dpp_u<CTL>(key), pe = dpp_u<CTL>(e);
-  const bool mine_first = before(key, e, pk, pe);
-  const bool take = keep_first != mine_first;   // keep the partner's entry
-  key = take ? pk : key;
-  e = take ? pe : e;
-}
-
-// Top-k of one token's E logits by one wave, exactly in f32 order with ties
-// to the lower expert index (PER >= ceil(E/64) logits per lane, expert e =
-// lane*PER + i).
-//  1. radix select of T, the k-th largest key, two bits per step: three
-//     candidate thresholds are counted at once with ballot + popcount; the
-//     search stops as soon as exactly k keys are >= a candidate (exact ties
-//     at the boundary run all 32 bits);
-//  2. the winners are every key > T plus the lowest-index keys == T, up to
-//     k; they are compacted (in index order) into lanes 0..k-1 through a
-//     64-entry LDS table (`scratch`, 256 bytes per wave);
-//  3. a bitonic network on DPP (mirror/xor partners inside 8 or 16 lanes)
-//     sorts them by (key desc, index asc);
-//  4. weights exp(l_j - l_0) / sum_m exp(l_m - l_0), the sum taken by DPP in a
-//     fixed order.
-// Lanes j < k end with the j-th expert and its weight.  Returns whether a
-// NaN logit was seen.  k <= 16.
-template <int PER>
-__device__ bool topk_wave(const float* __restrict__ logits, int E, int k, int& sel_e, float& sel_w,
-                          uint32_t* scratch, uint64_t* trace) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[PER];
-  int nan_seen = 0;
-  // bounded descriptor over the E logits: lanes past the end read zeros
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits, (uint32_t)E * 4u);
-#pragma unroll
-  for (int i = 0; i < PER; i += 4) {
-    const int e0 = lane * PER + i;
-    const u32x4 raw = bload16(rl, (uint32_t)e0 * 4u);
-    const uint32_t rv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float f = as_f32(rv[t]);
-      const bool valid = e0 + t < E;
-      key[i + t] = valid ? okey(f) : 0u;
-      nan_seen |= valid & __builtin_isnan(f);
-    }
-  }
-  trace_point(trace, TK_TOPK, 0);
-  // 1. threshold
-  uint32_t T = 0;
-  for (int b = 30; b >= 0; b -= 2) {
-    const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
-    int n1 = 0, n2 = 0, n3 = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      n1 += __builtin_popcountll(__ballot(key[i] >= c1));
-      n2 += __builtin_popcountll(__ballot(key[i] >= c2));
-      n3 += __builtin_popcountll(__ballot(key[i] >= c3));
-    }
-    T = (n3 >= k) ? c3 : (n2 >= k) ? c2 : (n1 >= k) ? c1 : T;
-    if (n1 == k || n2 == k || n3 == k) break;   // exactly k keys >= T: done
-  }
-  trace_point(trace, TK_TOPK, 2);
-  // 2. winners: keys > T, then keys == T in index order up to k
-  int n_gt = 0, below_eq = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    n_gt += __builtin_popcountll(__ballot(key[i] > T));
-    const uint64_t eq = __ballot(key[i] == T);
-    below_eq += __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
-  }
-  const int need = k - n_gt;
-  int own_eq = 0, below_sel = 0, own_sel = 0;
-  bool sel[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const bool is_eq = key[i] == T;
-    sel[i] = key[i] > T || (is_eq && below_eq + own_eq < need);
-    own_eq += is_eq;
-    const uint64_t sm = __ballot(sel[i]);
-    below_sel += __builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (sel[i]) {
-      const int slot = below_sel + own_sel;
-      scratch[slot] = key[i];
-      scratch[32 + slot] = (uint32_t)(lane * PER + i);
-    }
-    own_sel += sel[i];
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written
-  __builtin_amdgcn_wave_barrier();
-  uint32_t mk = 0, me = 0xFFFFFFFFu;     // lanes >= k hold "after everything"
-  if (lane < k) {
-    mk = scratch[lane];
-    me = scratch[32 + lane];
-  }
-  trace_point(trace, TK_TOPK, 3);
-  // 3. bitonic sort (descending) of lanes 0..15, flip variant: the first
-  //    step of each merge compares mirrored partners, later steps xor
-  //    partners; the lower lane of each pair keeps the entry that comes first
-  const bool lo1 = (lane & 1) == 0, lo2 = (lane & 2) == 0, lo4 = (lane & 4) == 0,
-             lo8 = (lane & 8) == 0;
-  bitonic_step<0xB1>(mk, me, lo1);    // size 2: xor 1
-  bitonic_step<0x1B>(mk, me, lo2);    // size 4: mirror in 4
-  bitonic_step<0xB1>(mk, me, lo1);
-  bitonic_step<0x141>(mk, me, lo4);   // size 8: mirror in 8
-  bitonic_step<0x4E>(mk, me, lo2);
-  bitonic_step<0xB1>(mk, me, lo1);
-  if (k > 8) {
-    bitonic_step<0x140>(mk, me, lo8); // size 16: mirror in 16
-    // xor 4 inside 16 lanes: rotate by 4 for the upper, by 12 for the lower half of each 8
-    {
-      const uint32_t ak = dpp_u<0x12C>(mk), ae = dpp_u<0x12C>(me);   // lane i <- i+4 (mod 16)
-      const uint32_t bk = dpp_u<0x124>(mk), be = dpp_u<0x124>(me);   // lane i <- i-4 (mod 16)
-      const uint32_t pk = lo4 ? ak : bk, pe = lo4 ? ae : be;
-      const bool take = lo4 != before(mk, me, pk, pe);
-      mk = take ? pk : mk;
-      me = take ? pe : me;
-    }
-    bitonic_step<0x4E>(mk, me, lo2);
-    bitonic_step<0xB1>(mk, me, lo1);
-  }
-  trace_point(trace, TK_TOPK, 4);
-  // 4. weights
-  const float l = okey_value(mk);
-  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), 0));
-  float ex = 0.f;
-  if (lane < k) ex = (l0 == -INFINITY) ? 1.f : expf(l - l0);
-  float sum = ex + dpp<0xB1>(ex);
-  sum += dpp<0x4E>(sum);
-  sum += dpp<0x141>(sum);
-  if (k > 8) sum += dpp<0x128>(sum);   // lanes 0-7 add lanes 8-15
-  sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 0));
-  sel_e = lane < k ? (int)me : -1;
-  sel_w = ex / sum;
-  trace_point(trace, TK_TOPK, 1);
-  return __any(nan_seen);
-}
-
-__device__ bool topk_any(const float* logits, int E, int k, int& e, float& w, uint32_t* scratch,
-                         uint64_t* trace) {
-  if (E <= 256) return topk_wave<4>(logits, E, k, e, w, scratch, trace);
-  if (E <= 512) return topk_wave<8>(logits, E, k, e, w, scratch, trace);
-  return topk_wave<16>(logits, E, k, e, w, scratch, trace);
 }
 
 // Standalone top-k: one wave per token.
@@ -565,18 +353,6 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a, Ws ws) {
 
 // ====================================================================== fast path: d = 2048, F = 512, k <= 8
 
-// Shapes of the workloads this build is tuned for: a gate/up row is 8 blocks
-// = 64 segments (one per lane), a down row is 2 blocks = 16 segments (16
-// lanes), up to 8 experts per token.
-constexpr int FAST_SEGS_D = 64;
-constexpr int FAST_SEGS_F = 16;
-constexpr int FAST_RP = 4;        // gate/up row pairs per wave item
-constexpr int FAST_ROWS = 2;      // down output rows per wave
-
-__host__ __device__ inline bool fast_shape(int d, int F, int k) {
-  return d > 1792 && d <= 2048 && F == 512 && k <= 8;
-}
-
 // K2: routing (top-k from logits, or idx/wts from memory), groups, then the
 // grouped gate/up dequant-GEMV.  A wave item is FAST_RP consecutive row
 // pairs of one expert; each lane owns one 32-weight segment of every row.
@@ -832,31 +608,43 @@ void set_timing_events(void* start, void* stop) {
   g_ev_stop = static_cast<hipEvent_t>(stop);
 }
 
-size_t ws_layout(int64_t E, int B, int k, int64_t F, size_t* off_logits, size_t* off_idx,
-                 size_t* off_wts, size_t* off_h) {
-  size_t o = 256;  // err word + 16 counters + padding
-  *off_logits = o;
-  o = al256(o + sizeof(float) * (size_t)B * E);
-  *off_idx = o;
+WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F) {
+  WsLayout l{};
+  size_t o = WS_HEADER;
+  l.logits = o;   // batched calls keep LG_KS partial logit sets
+  o = al256(o + sizeof(float) * (size_t)(B >= 2 ? LG_KS : 1) * B * E);
+  l.idx = o;
   o = al256(o + sizeof(int32_t) * (size_t)B * k);
-  *off_wts = o;
+  l.wts = o;
   o = al256(o + sizeof(float) * (size_t)B * k);
-  *off_h = o;
-  o = al256(o + sizeof(float) * (size_t)B * k * F);
-  return o;
+  l.h = o;
+  const size_t halves = (B >= 2) ? 2 : 1;   // batched: gate outputs in two K halves
+  o = al256(o + sizeof(float) * halves * (size_t)B * k * F);
+  if (B >= 2 && k > 0) {          // batched expert path
+    l.u = o;
+    o = al256(o + sizeof(float) * 2 * (size_t)B * k * F);
+    l.ypart = o;
+    o = al256(o + sizeof(float) * (size_t)B * k * d);
+    l.groups = o;
+    o = al256(o + sizeof(GroupTab));
+  }
+  l.total = o;
+  return l;
 }
 
-Ws ws_carve(void* base, int64_t E, int B, int k, int64_t F) {
-  size_t ol, oi, ow, oh;
-  ws_layout(E, B, k, F, &ol, &oi, &ow, &oh);
+Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F) {
+  const WsLayout l = ws_layout(E, B, k, d, F);
   uint8_t* p = static_cast<uint8_t*>(base);
   Ws w;
   w.err = reinterpret_cast<uint32_t*>(p);
   w.ctr = reinterpret_cast<uint32_t*>(p + 64);
-  w.logits = reinterpret_cast<float*>(p + ol);
-  w.idx = reinterpret_cast<int32_t*>(p + oi);
-  w.wts = reinterpret_cast<float*>(p + ow);
-  w.h = reinterpret_cast<float*>(p + oh);
+  w.logits = reinterpret_cast<float*>(p + l.logits);
+  w.idx = reinterpret_cast<int32_t*>(p + l.idx);
+  w.wts = reinterpret_cast<float*>(p + l.wts);
+  w.h = reinterpret_cast<float*>(p + l.h);
+  w.u = l.u ? reinterpret_cast<float*>(p + l.u) : nullptr;
+  w.ypart = l.ypart ? reinterpret_cast<float*>(p + l.ypart) : nullptr;
+  w.groups = l.groups ? reinterpret_cast<GroupTab*>(p + l.groups) : nullptr;
   w.trace = get_trace();
   return w;
 }
@@ -876,6 +664,10 @@ static int num_cus() {
 int launch_route(const float* Wr, const float* bias, int E, int d, const float* x, int64_t ldx,
                  int B, int k, int32_t* idx, float* wts, float* logits_out, Ws ws, hipStream_t s) {
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
+  if (B >= 2) {
+    if (int e = launch_logits_batched(a, ws.logits, s)) return e;
+    return launch_route_batched(a, ws.logits, nullptr, nullptr, nullptr, nullptr, ws.err, s);
+  }
   hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
   if (err) return err;
@@ -954,7 +746,15 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
                    const float* wts, int k, const float* residual, float* y, int64_t ldy, Ws ws,
                    hipStream_t s) {
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
-  if (fast_shape(L.d, L.F, k)) return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
+  if (fast_shape(L.d, L.F, k)) {
+    if (B >= 2) {
+      RouteArgs ra{nullptr, nullptr, L.E, L.d, x, ldx, B, k, nullptr, nullptr, nullptr};
+      if (int e = launch_route_batched(ra, nullptr, idx, nullptr, nullptr, ws.groups, ws.err, s))
+        return e;
+      return launch_experts_batched(a, ws, num_cus(), s);
+    }
+    return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
+  }
   return launch_generic_experts(a, ws, s);
 }
 
@@ -962,10 +762,21 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s) {
   RouteArgs ra{Wr, bias, L.E, L.d, x, ldx, B, k, idx, wts, nullptr};
+  const bool fast = fast_shape(L.d, L.F, k);
+  if (B >= 2) {
+    // same routing kernels as moe_route_topk, so the two-call path gives
+    // the same bits
+    if (int e = launch_logits_batched(ra, ws.logits, s)) return e;
+    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, nullptr,
+                                     fast ? ws.groups : nullptr, ws.err, s))
+      return e;
+    ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
+    return fast ? launch_experts_batched(a, ws, num_cus(), s) : launch_generic_experts(a, ws, s);
+  }
   hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(256), 0, s, ra, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
   if (err) return err;
-  if (fast_shape(L.d, L.F, k)) {
+  if (fast) {
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
     return launch_fast(a, ws, ws.logits, idx, wts, s);
   }

@@ -1,0 +1,59 @@
+// Argument blocks and shape constants shared by the MoE decode kernels.
+#pragma once
+#include "hfq4_device.h"
+#include "launch.h"
+
+namespace hq {
+
+constexpr uint64_t WAIT_TICKS = 20000000ull;   // 200 ms of s_memrealtime (100 MHz)
+constexpr int MAXP = 128;                      // max (token, slot) pairs: 16 x 8... up to B*k
+constexpr int MAXK = 16;
+
+struct RouteArgs {
+  const float* Wr;
+  const float* bias;
+  int E, d;
+  const float* x;
+  int64_t ldx;
+  int B, k;
+  int32_t* idx_out;
+  float* wts_out;
+  float* logits_out;
+};
+
+struct ExpertArgs {
+  LayerDev L;
+  const float* x;
+  int64_t ldx;
+  int B, k;
+  const int32_t* idx;   // [B][k]
+  const float* wts;     // [B][k]
+  const float* res;     // [B][ldy] or null
+  float* y;
+  int64_t ldy;
+};
+
+// Shapes of the workloads this build is tuned for: a gate/up row is 8 blocks
+// = 64 segments (one per lane), a down row is 2 blocks = 16 segments (16
+// lanes), up to 8 experts per token.
+constexpr int FAST_SEGS_D = 64;
+constexpr int FAST_SEGS_F = 16;
+constexpr int FAST_RP = 4;        // gate/up row pairs per wave item
+constexpr int FAST_ROWS = 2;      // down output rows per wave
+
+__host__ __device__ inline bool fast_shape(int d, int F, int k) {
+  return d > 1792 && d <= 2048 && F == 512 && k <= 8;
+}
+
+// Batched path (2 <= B <= 16) on MFMA matrix cores.
+constexpr int LG_KS = 4;   // K splits of the batched router GEMV (partial logit sets)
+int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
+// Top-k from the partial logits (idx_in null) or the caller's routing
+// (idx_in), optionally followed by the token groups.
+int launch_route_batched(const RouteArgs& ra, const float* part, const int32_t* idx_in,
+                         int32_t* idx_copy, float* wts_copy, GroupTab* groups, uint32_t* err,
+                         hipStream_t s);
+// gate/up, down and combine for the fast shape; groups already in ws.
+int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s);
+
+}  // namespace hq

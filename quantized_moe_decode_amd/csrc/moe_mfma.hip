@@ -1,0 +1,730 @@
+// Batched decode (2..16 tokens) of the d = 2048, F = 512 layer shape on
+// MFMA matrix cores (gfx950 v_mfma_f32_16x16x32_f16).
+//
+// With several tokens, an expert picked by n tokens is a small GEMM: its
+// rows times an n-column activation matrix.  On the VALU path every extra
+// token repeats the nibble decode and four v_dot2 per code dword, so the
+// cost per weight grows with n; here each code dword is decoded once into
+// an f16 operand and the matrix core multiplies it against all n tokens.
+//
+// Operands.  A = activations (16 rows = tokens or (token, slot) pairs of
+// one expert group, 32 K per step), B = weights (16 rows of the matrix, the
+// same 32 K).  Lane l of the wave carries row l%16 and K chunk l/16 of both
+// (8 values each), so a lane decodes exactly the code dword it loaded, and
+// the output lane (g = l/16, n = l%16) holds pairs 4g..4g+3 of row n --
+// the row whose block headers it loaded itself.  Inside a block the K order
+// is a permutation of the block's elements (the nibble order the decode
+// produces, with the odd nibbles' activations pre-divided by 16) applied to
+// both operands alike.  Weights enter as 1024 + q (1024 + 16q for odd
+// nibbles) straight from the bit trick of the VALU path; per block and
+// column the 1024 terms and the zero point are folded back in the epilogue:
+//   sum_i w_i x_i = scale * xs * (C + off) + (zero + 8 scale) * sum_i x_i
+// with off = -(1024 * sum of the stored halves + 8 * sum of the f16 values
+// they stand for) and xs the column's power-of-two scale.  Each block's
+// product starts from a zero accumulator, so scale and zero apply exactly.
+//
+// Kernels (one HIP graph node each; kernel boundaries are the only
+// grid-wide synchronisation, so no workgroup ever waits on another):
+//   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32):
+//                        16 experts x 16 tokens per tile, K split over 4
+//                        workgroups x 4 waves; writes 4 partial logit sets.
+//   route_groups_kernel  one workgroup: per token (one wave each) the partial
+//                        sums + bias, top-k and weights; then the token groups
+//                        (pairs that chose the same expert), published for
+//                        the expert kernels.
+//   gateup_mfma_kernel   items of (group, 16 rows, gate or up, K half) in
+//                        contiguous runs per workgroup, so a workgroup stages
+//                        only the tokens of the groups it serves.
+//   down_mfma_kernel     work items of (group, 128 output rows): stages
+//                        h = SiLU(g) * u of the group's pairs, writes
+//                        w_p * (down h_p) per pair.
+//   combine_kernel       y[b] = residual[b] + sum over the k slots of token b,
+//                        in slot order.
+#include "hfq4_device.h"
+#include "launch.h"
+#include "moe_common.h"
+#include "topk_device.h"
+
+namespace hq {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+constexpr int XT_STRIDE = 4096 + 16;   // bytes per staged token (256 entries of 16 B + pad)
+constexpr int HT_STRIDE = 1024 + 16;   // bytes per staged h vector (64 entries + pad)
+constexpr int MM_ROWS = 16;            // rows per item
+constexpr int DOWN_TILES = 2;          // 16-row tiles per wave in the down kernel
+constexpr int DOWN_CHUNK = 64 * DOWN_TILES;   // output rows per down work item (4 waves)
+
+// Code dword -> B operand: 1024+q0, 1024+q4, 1024+16q1, 1024+16q5,
+// 1024+q2, 1024+q6, 1024+16q3, 1024+16q7.
+__device__ __forceinline__ h8 dec8(uint32_t d) {
+  const uint32_t d8 = d >> 8;
+  const u32x4 v = {(d & LO4) | MAGIC, (d & HI4) | MAGIC, (d8 & LO4) | MAGIC, (d8 & HI4) | MAGIC};
+  return __builtin_bit_cast(h8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(h8 a, h8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float lane_bcast(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Max over each 16-lane row (result in every lane of the row).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  return v;
+}
+
+// Power-of-two scale putting the largest magnitude in [2, 4) (1 for 0 or
+// non-finite maxima); returns 2^-e, sets xs = 2^e.
+__device__ __forceinline__ float pow2_scale(float amax, float& xs) {
+  int e = 0;
+  if (amax > 0.f && amax < INFINITY) {
+    int ex;
+    frexpf(amax, &ex);
+    e = ex - 2;
+  }
+  xs = ldexpf(1.f, e);
+  return ldexpf(1.f, -e);
+}
+
+// Write the 8 elements of one code dword's entry (scaled by inv) as 16 B at
+// dst in the order dec8 produces -- pair q holds elements q and q+4, odd
+// pairs divided by 16 -- and add to (sum of the stored halves, sum of the
+// f16 values they stand for).
+__device__ __forceinline__ void put_entry(const float* v, float inv, uint8_t* dst, float& sh,
+                                          float& s16) {
+  h2 p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool hi = q & 1;
+    const float s = hi ? 0.0625f : 1.0f;
+    const _Float16 a = (_Float16)(v[q] * inv * s), b = (_Float16)(v[q + 4] * inv * s);
+    p[q] = h2{a, b};
+    const float fa = (float)a, fb = (float)b;
+    sh += fa + fb;
+    s16 += hi ? 16.f * (fa + fb) : (fa + fb);
+  }
+  const u32x4 e = {as_u32(p[0]), as_u32(p[1]), as_u32(p[2]), as_u32(p[3])};
+  *reinterpret_cast<u32x4*>(dst) = e;
+}
+
+// Deterministic token groups from the k selections of B tokens (in LDS):
+// group ids in order of each group's first pair, members in token order, at
+// most one pair per token in a group (so <= 16 members, one MFMA column
+// each).  A slot repeating an expert already chosen earlier by the same
+// token (possible only with caller-supplied indices) forms a group of its
+// own.  Pairs with an index outside [0, E) join no group (and set `err`
+// when report is true).  P <= 128 <= blockDim.x.
+struct GroupScratch {
+  int first[HFQ4_MAXE_DEV];
+  uint32_t tokmask[GT_MAXU];
+  uint64_t lead[2];
+};
+
+__device__ void build_groups_mm(const int* s_idx, int P, int k, int E, GroupTab& G,
+                                GroupScratch& S, uint32_t* err, bool report) {
+  const int t = threadIdx.x;
+  for (int i = t; i < E; i += blockDim.x) S.first[i] = 0x7FFFFFFF;
+  if (t < GT_MAXU) S.tokmask[t] = 0u;
+  __syncthreads();
+  int e = -1;
+  bool repeat = false;
+  if (t < P) {
+    e = s_idx[t];
+    if (e < 0 || e >= E) {
+      if (report)
+        __hip_atomic_fetch_or(err, 1u /*HFQ4_DEV_ERR_INDEX*/, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      e = -1;
+    } else {
+      for (int q = t - t % k; q < t; ++q) repeat |= (s_idx[q] == e);
+      if (!repeat) atomicMin(&S.first[e], t);
+    }
+  }
+  __syncthreads();
+  const bool lead = t < P && e >= 0 && (repeat || S.first[e] == t);
+  if (t < 128) {
+    const uint64_t m = __ballot(lead);
+    if ((t & 63) == 0) S.lead[t >> 6] = m;
+  }
+  __syncthreads();
+  auto rank = [&](int f) {   // number of group leaders before pair f
+    const uint64_t m0 = S.lead[0], m1 = S.lead[1];
+    if (f < 64) return __builtin_popcountll(m0 & ((1ull << f) - 1ull));
+    return __builtin_popcountll(m0) + __builtin_popcountll(m1 & ((1ull << (f - 64)) - 1ull));
+  };
+  int u = -1;
+  if (t < P && e >= 0) {
+    u = rank(repeat ? t : S.first[e]);
+    atomicOr(&S.tokmask[u], 1u << (t / k));
+    if (lead) G.gexp[u] = e;
+  }
+  if (t == 0) G.U = __builtin_popcountll(S.lead[0]) + __builtin_popcountll(S.lead[1]);
+  __syncthreads();
+  if (u >= 0) {
+    const uint32_t tm = S.tokmask[u];
+    const int b = t / k;
+    G.gmem[u][__builtin_popcount(tm & ((1u << b) - 1u))] = (uint8_t)t;
+    if (lead) G.gcnt[u] = __builtin_popcount(tm);
+  }
+  __syncthreads();
+}
+
+// ====================================================================== router
+
+// Partial router logits: part[ks][b][e] = sum over K split ks of
+// Wr[e][i] * x[b][i].  A = x (16 tokens; rows past B read zeros), B = Wr
+// (16 experts), 4 K per MFMA: lane (n, c) loads a float4 at K offset 4c of
+// every 16-wide K step and feeds element j to the j-th MFMA, so both
+// operands use the same K assignment.  The four waves of a workgroup take
+// consecutive quarters of the split and meet in LDS in a fixed order.
+__global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __restrict__ part,
+                                                          uint64_t* trace) {
+  __shared__ f32x4 red[4][64];
+  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  trace_point_at(trace, TK_LOGITS, wg, 0);
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, c = lane >> 4;
+  const int rt = blockIdx.x, ks = blockIdx.y;
+  const int Kq = ((a.d + LG_KS * 64 - 1) / (LG_KS * 64)) * 64;   // per split, multiple of 64
+  const int Kw = Kq / 4;                                          // per wave, multiple of 16
+  const int k_lo = ks * Kq + wv * Kw;
+  const int row = rt * 16 + n16;
+  const uint32_t xbytes = (uint32_t)(((int64_t)(a.B - 1) * a.ldx + a.d) * 4);
+  const uint32_t wbytes = (uint32_t)((int64_t)a.E * a.d * 4);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, xbytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr, wbytes);
+  const bool tok_ok = n16 < a.B, row_ok = row < a.E;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = k_lo; k0 < k_lo + Kw; k0 += 8 * 16) {
+    u32x4 xv[8], wv4[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int ki = k0 + 16 * s + 4 * c;
+      const bool kin = ki < a.d && ki < k_lo + Kw;
+      xv[s] = bload16(rx, (tok_ok && kin) ? (uint32_t)(((int64_t)n16 * a.ldx + ki) * 4) : xbytes);
+      wv4[s] = bload16(rw, (row_ok && kin) ? (uint32_t)(((int64_t)row * a.d + ki) * 4) : wbytes);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(xv[s].x), as_f32(wv4[s].x), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(xv[s].y), as_f32(wv4[s].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(xv[s].z), as_f32(wv4[s].z), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(xv[s].w), as_f32(wv4[s].w), acc, 0, 0, 0);
+    }
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    const f32x4 t = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    const float tv[4] = {t.x, t.y, t.z, t.w};
+    // lane (c, n16) holds tokens 4c..4c+3 of expert row
+    if (row_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * c + i;
+        if (b < a.B) part[((int64_t)ks * a.B + b) * a.E + row] = tv[i];
+      }
+    }
+  }
+  trace_point_at(trace, TK_LOGITS, wg, 1);
+}
+
+struct BatchRouteArgs {
+  const float* part;      // [LG_KS][B][E] partial logits
+  const float* bias;      // [E] or null
+  int E, B, k;
+  const int32_t* idx_in;  // routing given by the caller (no top-k) or null
+  int32_t* idx_out;       // [B][k]
+  float* wts_out;         // [B][k]
+  float* logits_out;      // [B][E] or null
+  int32_t* idx_copy;      // workspace copies or null
+  float* wts_copy;
+  GroupTab* groups;       // or null
+  uint32_t* err;
+  uint64_t* trace;
+};
+
+template <int PER>
+__device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t* scratch,
+                            float* lg) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, (uint32_t)((int64_t)LG_KS * r.B * r.E * 4));
+  // coalesced pass: lane l sums expert 64c + l over the partial sets (+ bias)
+  // into LDS; the top-k then reads its own PER consecutive experts
+  int nan_seen = 0;
+  uint32_t raw[LG_KS][PER];   // every load in flight before the first add
+#pragma unroll
+  for (int p = 0; p < LG_KS; ++p)
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int e = 64 * c + lane;
+      raw[p][c] = bload4(rp, e < r.E ? (uint32_t)((((int64_t)p * r.B + b) * r.E + e) * 4)
+                                     : 0xFFFFFFF0u);
+    }
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int e = 64 * c + lane;
+    if (e < r.E) {
+      float l = 0.f;
+#pragma unroll
+      for (int p = 0; p < LG_KS; ++p) l += as_f32(raw[p][c]);
+      if (r.bias) l += r.bias[e];
+      if (r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
+      lg[e] = l;
+      nan_seen |= __builtin_isnan(l);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane * PER + i;
+    key[i] = e < r.E ? okey(lg[e]) : 0u;
+  }
+  int e;
+  float w;
+  topk_keys<PER>(key, r.E, r.k, e, w, scratch, nullptr);
+  if (lane < r.k) {
+    const int p = b * r.k + lane;
+    r.idx_out[p] = e;
+    r.wts_out[p] = w;
+    if (r.idx_copy) {
+      r.idx_copy[p] = e;
+      r.wts_copy[p] = w;
+    }
+    s_idx[p] = e;
+  }
+  if (__any(nan_seen) && lane == 0)
+    __hip_atomic_fetch_or(r.err, 4u /*HFQ4_DEV_ERR_NONFINITE*/, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup of 16 waves: routing of token b by wave b (partial sums,
+// bias, top-k, weights), then the token groups.
+template <bool WITH_TOPK>
+__global__ void __launch_bounds__(1024) route_groups_kernel(BatchRouteArgs r) {
+  extern __shared__ float lgs[];   // [B][E] summed logits
+  __shared__ GroupTab G;
+  __shared__ GroupScratch GS;
+  __shared__ int s_idx[MAXP];
+  __shared__ uint32_t tk_scratch[16][64];
+  const int wv = threadIdx.x >> 6;
+  const int P = r.B * r.k;
+  trace_point(r.trace, TK_TOPK, 0);
+  if (WITH_TOPK) {
+    if (wv < r.B) {
+      float* lg = lgs + wv * r.E;
+      if (r.E <= 256) route_token<4>(r, wv, s_idx, tk_scratch[wv], lg);
+      else if (r.E <= 512) route_token<8>(r, wv, s_idx, tk_scratch[wv], lg);
+      else route_token<16>(r, wv, s_idx, tk_scratch[wv], lg);
+    }
+  } else if ((int)threadIdx.x < P) {
+    s_idx[threadIdx.x] = r.idx_in[threadIdx.x];
+  }
+  if (!r.groups) {
+    trace_point(r.trace, TK_TOPK, 1);
+    return;
+  }
+  __syncthreads();
+  build_groups_mm(s_idx, P, r.k, r.E, G, GS, r.err, true);
+  int* dst = reinterpret_cast<int*>(r.groups);
+  const int* src = reinterpret_cast<const int*>(&G);
+  for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  trace_point(r.trace, TK_TOPK, 1);
+}
+
+// ====================================================================== gate / up
+
+__global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) {
+  extern __shared__ __align__(16) uint8_t xt[];      // [B][XT_STRIDE]
+  __shared__ GroupTab G;
+  __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
+  __shared__ float s_xs[HFQ4_MAXB_DEV];
+  __shared__ uint32_t s_need;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int B = a.B, k = a.k, P = B * k, F = a.L.F, d = a.L.d;
+  trace_point(ws.trace, TK_GATEUP, 0);
+  {
+    const int* src = reinterpret_cast<const int*>(ws.groups);
+    int* dst = reinterpret_cast<int*>(&G);
+    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 1);
+
+  // 3. this workgroup's items: a contiguous run of (group, matrix, 16-row
+  //    tile, K half); an item covers 4 of the 8 blocks of its rows, and the
+  //    down kernel adds the two halves
+  const int tiles = F / MM_ROWS;                 // 32
+  const int per_u = 2 * tiles * 2;               // items per group
+  const int items = G.U * per_u;
+  const int per = (items + gridDim.x - 1) / gridDim.x;
+  const int i0 = blockIdx.x * per;
+  const int i1 = min(items, i0 + per);
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    if (i0 < i1)
+      for (int u = i0 / per_u; u <= (i1 - 1) / per_u; ++u) {
+        for (int q = 0; q < G.gcnt[u]; ++q) m |= 1u << (G.gmem[u][q] / k);
+      }
+    s_need = m;
+  }
+  __syncthreads();
+
+  constexpr int64_t ROWB = 8 * BLK_BYTES;
+  const int n16 = lane & 15, c = lane >> 4;
+  u32x4 cd[4][2];
+  u32x2 hd[4];
+  auto issue = [&](int it) {
+    const int u = it / per_u, r = it - u * per_u;
+    const int mat = r / (2 * tiles), tile = (r >> 1) % tiles, kh = r & 1;
+    const int e = G.gexp[u];
+    const uint8_t* base = mat ? a.L.up : a.L.gate;
+    const uint32_t bytes = mat ? a.L.up_bytes : a.L.gate_bytes;
+    const int64_t stride = mat ? a.L.su : a.L.sg;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+    const uint32_t rowoff = (uint32_t)(e * stride + (int64_t)(tile * MM_ROWS + n16) * ROWB +
+                                       kh * 4 * BLK_BYTES);
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      hd[bk] = bload8(rs, rowoff + bk * BLK_BYTES);
+      cd[bk][0] = bload16(rs, rowoff + bk * BLK_BYTES + 8 + 16 * c);
+      cd[bk][1] = bload16(rs, rowoff + bk * BLK_BYTES + 8 + 64 + 16 * c);
+    }
+  };
+  int it = i0 + wv;
+  // 4. stage the tokens this workgroup needs: wave b stages token b.  Waves
+  //    that stage issue their first item's weight loads afterwards (the
+  //    registers would not hold both), the others at once.
+  const bool stager = wv < B && ((s_need >> wv) & 1u);
+  if (!stager && it < i1) issue(it);
+  if (stager) {
+    // lane l takes entries o = l + 64m (8 consecutive elements each), so a
+    // load instruction covers 2 KB of x contiguously; entry o belongs to
+    // block o / 32, i.e. block 2m for lanes 0-31 and 2m+1 for lanes 32-63
+    const float* xb = a.x + (int64_t)wv * a.ldx;
+    float v[4][8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e0 = 8 * (lane + 64 * m);
+      f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
+      if (e0 < d) t0 = *reinterpret_cast<const f32x4*>(xb + e0);
+      if (e0 + 4 < d) t1 = *reinterpret_cast<const f32x4*>(xb + e0 + 4);
+      v[m][0] = t0.x; v[m][1] = t0.y; v[m][2] = t0.z; v[m][3] = t0.w;
+      v[m][4] = t1.x; v[m][5] = t1.y; v[m][6] = t1.z; v[m][7] = t1.w;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[m][i]));
+    float xs;
+    const float inv = pow2_scale(wave_max_f(am), xs);
+    uint8_t* dst = xt + wv * XT_STRIDE;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float sh = 0.f, s16 = 0.f, sx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sx += v[m][i];
+      put_entry(v[m], inv, dst + 16 * (lane + 64 * m), sh, s16);
+      // block sums over 32 lanes, fixed order
+      sh = row_sum16(sh);
+      s16 = row_sum16(s16);
+      sx = row_sum16(sx);
+      const float lo_sh = lane_bcast(sh, 0) + lane_bcast(sh, 16);
+      const float hi_sh = lane_bcast(sh, 32) + lane_bcast(sh, 48);
+      const float lo_16 = lane_bcast(s16, 0) + lane_bcast(s16, 16);
+      const float hi_16 = lane_bcast(s16, 32) + lane_bcast(s16, 48);
+      const float lo_sx = lane_bcast(sx, 0) + lane_bcast(sx, 16);
+      const float hi_sx = lane_bcast(sx, 32) + lane_bcast(sx, 48);
+      if (lane == 0) {
+        s_blk[wv][2 * m] = make_float2(-(1024.f * lo_sh + 8.f * lo_16), lo_sx);
+        s_blk[wv][2 * m + 1] = make_float2(-(1024.f * hi_sh + 8.f * hi_16), hi_sx);
+      }
+    }
+    if (lane == 0) s_xs[wv] = xs;
+    if (it < i1) issue(it);
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 3);
+
+  // 5. items
+  while (it < i1) {
+    const int u = it / per_u, r = it - u * per_u;
+    const int mat = r / (2 * tiles), tile = (r >> 1) % tiles, kh = r & 1;
+    const int n = G.gcnt[u];
+    // A operand source: member n16 of the group (zeros past the group)
+    const int tok_a = n16 < n ? G.gmem[u][n16] / k : -1;
+    const uint8_t* arow = xt + (tok_a >= 0 ? tok_a : 0) * XT_STRIDE + 16 * (4 * c) + kh * 4 * 512;
+    // epilogue columns: members 4c..4c+3
+    int tok_c[4];
+    float xs_c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * c + i;
+      tok_c[i] = m < n ? G.gmem[u][m] / k : -1;
+      xs_c[i] = tok_c[i] >= 0 ? s_xs[tok_c[i]] : 0.f;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 q = cd[bk][t];
+        const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // entry 32 (4 kh + bk) + 16t + 4c + i of the token
+          h8 av = h8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (tok_a >= 0) av = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+          cb = mfma16(av, dec8(qv[i]), cb);
+        }
+      }
+      const float scale = as_f32(hd[bk].x), zero = as_f32(hd[bk].y);
+      const float zp8 = __builtin_fmaf(8.f, scale, zero);
+      const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+      float accv[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tok_c[i] >= 0) {
+          const float2 ob = s_blk[tok_c[i]][4 * kh + bk];
+          accv[i] += __builtin_fmaf(scale * xs_c[i], cbv[i] + ob.x, zp8 * ob.y);
+        }
+      }
+      acc = f32x4{accv[0], accv[1], accv[2], accv[3]};
+    }
+    float* out = (mat ? ws.u : ws.h) + (int64_t)kh * P * F;
+    const int row = tile * MM_ROWS + n16;
+    const float accv[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * c + i;
+      if (m < n) out[(int64_t)G.gmem[u][m] * F + row] = accv[i];
+    }
+    it += 16;
+    if (it < i1) issue(it);
+  }
+  trace_point(ws.trace, TK_GATEUP, 5);
+}
+
+// ====================================================================== down + combine
+
+__global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
+  __shared__ __align__(16) uint8_t ht[GT_MAXM * HT_STRIDE];   // [member][HT_STRIDE]
+  __shared__ float2 s_blk[GT_MAXM][2];
+  __shared__ float s_xs[GT_MAXM];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int B = a.B, k = a.k, d = a.L.d, F = a.L.F;
+  const GroupTab& G = *ws.groups;
+  const int nch = (d + DOWN_CHUNK - 1) / DOWN_CHUNK;
+  const int U = G.U;
+  const int items = U * nch;
+  constexpr int64_t ROWB = 2 * BLK_BYTES;
+  const int n16 = lane & 15, c = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  trace_point(ws.trace, TK_DOWN, 0);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int u = it / nch, ch = it - u * nch;
+    const int n = G.gcnt[u], e = G.gexp[u];
+
+    // 1. weight loads: wave wv owns rows ch*DOWN_CHUNK + 16*DOWN_TILES*wv .. (DOWN_TILES tiles)
+    u32x4 cd[DOWN_TILES][2][2];
+    u32x2 hd[DOWN_TILES][2];
+#pragma unroll
+    for (int tl = 0; tl < DOWN_TILES; ++tl) {
+      const int row = ch * DOWN_CHUNK + 16 * (DOWN_TILES * wv + tl) + n16;
+      const uint32_t ro = row < d ? (uint32_t)(e * a.L.sd + (int64_t)row * ROWB) : a.L.down_bytes;
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        hd[tl][bk] = bload8(rd, ro + bk * BLK_BYTES);
+        cd[tl][bk][0] = bload16(rd, ro + bk * BLK_BYTES + 8 + 16 * c);
+        cd[tl][bk][1] = bload16(rd, ro + bk * BLK_BYTES + 8 + 64 + 16 * c);
+      }
+    }
+
+    // 2. stage h = SiLU(g) * u of the members: 16 threads per member, thread
+    //    s takes entries o = s + 16q (q < 4; block q / 2), so 16 threads read
+    //    512 contiguous bytes; scale per member over its F values
+    {
+      const int m = threadIdx.x >> 4, s = threadIdx.x & 15;
+      const bool live = m < n;
+      const int p = live ? G.gmem[u][m] : 0;
+      const int64_t half = (int64_t)B * k * F;   // gate/up outputs come in two K halves
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e0 = (int64_t)p * F + 8 * (s + 16 * q);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f}, uv = gv;
+          if (live) {
+            gv = *reinterpret_cast<const f32x4*>(ws.h + e0 + 4 * h) +
+                 *reinterpret_cast<const f32x4*>(ws.h + half + e0 + 4 * h);
+            uv = *reinterpret_cast<const f32x4*>(ws.u + e0 + 4 * h) +
+                 *reinterpret_cast<const f32x4*>(ws.u + half + e0 + 4 * h);
+          }
+          v[q][4 * h] = silu_mul(gv.x, uv.x);
+          v[q][4 * h + 1] = silu_mul(gv.y, uv.y);
+          v[q][4 * h + 2] = silu_mul(gv.z, uv.z);
+          v[q][4 * h + 3] = silu_mul(gv.w, uv.w);
+        }
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[q][i]));
+      float xs;
+      const float inv = pow2_scale(row_max16(am), xs);
+      float sh[2] = {0.f, 0.f}, s16[2] = {0.f, 0.f}, sx[2] = {0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sx[q >> 1] += v[q][i];
+        put_entry(v[q], inv, ht + m * HT_STRIDE + 16 * (s + 16 * q), sh[q >> 1], s16[q >> 1]);
+      }
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        const float a_sh = row_sum16(sh[bk]), a_16 = row_sum16(s16[bk]), a_sx = row_sum16(sx[bk]);
+        if (s == 0) s_blk[m][bk] = make_float2(-(1024.f * a_sh + 8.f * a_16), a_sx);
+      }
+      if (s == 0) s_xs[m] = xs;
+    }
+    __syncthreads();
+    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 1);
+
+    // 3. MFMA per tile, epilogue per block, weighted partial per member
+    const bool a_live = n16 < n;
+    const uint8_t* arow = ht + (a_live ? n16 : 0) * HT_STRIDE + 16 * (4 * c);
+    int pc[4];
+    float wc[4], xsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * c + i;
+      pc[i] = m < n ? G.gmem[u][m] : -1;
+      wc[i] = pc[i] >= 0 ? a.wts[pc[i]] : 0.f;
+      xsc[i] = pc[i] >= 0 ? s_xs[m] : 0.f;
+    }
+#pragma unroll
+    for (int tl = 0; tl < DOWN_TILES; ++tl) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 q = cd[tl][bk][t];
+          const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h8 av = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (a_live) av = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+            cb = mfma16(av, dec8(qv[i]), cb);
+          }
+        }
+        const float scale = as_f32(hd[tl][bk].x), zero = as_f32(hd[tl][bk].y);
+        const float zp8 = __builtin_fmaf(8.f, scale, zero);
+        const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (pc[i] >= 0) {
+            const float2 ob = s_blk[4 * c + i][bk];
+            acc[i] += __builtin_fmaf(scale * xsc[i], cbv[i] + ob.x, zp8 * ob.y);
+          }
+        }
+      }
+      const int row = ch * DOWN_CHUNK + 16 * (DOWN_TILES * wv + tl) + n16;
+      if (row < d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (pc[i] >= 0) ws.ypart[(int64_t)pc[i] * d + row] = wc[i] * acc[i];
+      }
+    }
+    __syncthreads();   // ht is restaged by the next item
+  }
+  trace_point(ws.trace, TK_DOWN, 2);
+}
+
+// y[b][r] = residual[b][r] + sum_j w_j y_{e_j}[r] over the valid slots, in
+// slot order (the weights are already in ypart).
+__global__ void __launch_bounds__(256) combine_kernel(ExpertArgs a, Ws ws) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
+  const int d = a.L.d, k = a.k;
+  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  trace_point_at(ws.trace, TK_DOWN, wg, 5);
+  if (r >= d) return;
+  float part[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    const int p = b * k + j;
+    const int e = j < k ? a.idx[p] : -1;
+    part[j] = (e >= 0 && e < a.L.E) ? ws.ypart[(int64_t)p * d + r] : 0.f;
+  }
+  float y = a.res ? a.res[b * a.ldy + r] : 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j)
+    if (j < k) y += part[j];
+  a.y[b * a.ldy + r] = y;
+  trace_point_at(ws.trace, TK_DOWN, wg, 6);
+}
+
+// ====================================================================== host
+
+int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
+  hipLaunchKernelGGL(logits_mfma_kernel, dim3((ra.E + 15) / 16, LG_KS), dim3(256), 0, s, ra, part,
+                     get_trace());
+  return (int)hipGetLastError();
+}
+
+int launch_route_batched(const RouteArgs& ra, const float* part, const int32_t* idx_in,
+                         int32_t* idx_copy, float* wts_copy, GroupTab* groups, uint32_t* err,
+                         hipStream_t s) {
+  BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, idx_in, ra.idx_out, ra.wts_out,
+                   ra.logits_out, idx_copy, wts_copy, groups, err, get_trace()};
+  if (idx_in) {
+    hipLaunchKernelGGL(route_groups_kernel<false>, dim3(1), dim3(1024), 0, s, r);
+  } else {
+    const size_t shm = sizeof(float) * (size_t)ra.B * ra.E;
+    if (int e = allow_lds(route_groups_kernel<true>, shm)) return e;
+    hipLaunchKernelGGL(route_groups_kernel<true>, dim3(1), dim3(1024), shm, s, r);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s) {
+  const size_t shm = (size_t)a.B * XT_STRIDE;
+  if (int e = allow_lds(gateup_mfma_kernel, shm)) return e;
+  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(nwg), dim3(1024), shm, s, a, ws);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  const int P = a.B * a.k;
+  const int umax = P < a.L.E ? P : a.L.E;
+  const int nch = (a.L.d + DOWN_CHUNK - 1) / DOWN_CHUNK;
+  const int grid = umax * nch < 4 * nwg ? umax * nch : 4 * nwg;
+  hipLaunchKernelGGL(down_mfma_kernel, dim3(grid), dim3(256), 0, s, a, ws);
+  err = (int)hipGetLastError();
+  if (err) return err;
+  hipLaunchKernelGGL(combine_kernel, dim3((a.L.d + 255) / 256, a.B), dim3(256), 0, s, a, ws);
+  return (int)hipGetLastError();
+}
+
+}  // namespace hq
