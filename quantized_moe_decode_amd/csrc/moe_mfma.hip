@@ -270,14 +270,17 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
   // into LDS; the top-k then reads its own PER consecutive experts
   int nan_seen = 0;
   uint32_t raw[LG_KS][PER];   // every load in flight before the first add
+  uint32_t rb[PER];
+  const __amdgpu_buffer_rsrc_t rbias = make_rsrc(r.bias, r.bias ? (uint32_t)r.E * 4u : 0u);
 #pragma unroll
-  for (int p = 0; p < LG_KS; ++p)
+  for (int c = 0; c < PER; ++c) {
+    const int e = 64 * c + lane;
 #pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int e = 64 * c + lane;
+    for (int p = 0; p < LG_KS; ++p)
       raw[p][c] = bload4(rp, e < r.E ? (uint32_t)((((int64_t)p * r.B + b) * r.E + e) * 4)
                                      : 0xFFFFFFF0u);
-    }
+    rb[c] = bload4(rbias, (uint32_t)e * 4u);   // zero without a bias or past E
+  }
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int e = 64 * c + lane;
@@ -285,7 +288,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
       float l = 0.f;
 #pragma unroll
       for (int p = 0; p < LG_KS; ++p) l += as_f32(raw[p][c]);
-      if (r.bias) l += r.bias[e];
+      if (r.bias) l += as_f32(rb[c]);
       if (r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
       lg[e] = l;
       nan_seen |= __builtin_isnan(l);
@@ -293,6 +296,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
+  trace_point(r.trace, TK_TOPK, 2);
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -302,6 +306,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
   int e;
   float w;
   topk_keys<PER>(key, r.E, r.k, e, w, scratch, nullptr);
+  trace_point(r.trace, TK_TOPK, 3);
   if (lane < r.k) {
     const int p = b * r.k + lane;
     r.idx_out[p] = e;
@@ -345,6 +350,7 @@ __global__ void __launch_bounds__(1024) route_groups_kernel(BatchRouteArgs r) {
   }
   __syncthreads();
   build_groups_mm(s_idx, P, r.k, r.E, G, GS, r.err, true);
+  trace_point(r.trace, TK_TOPK, 4);
   int* dst = reinterpret_cast<int*>(r.groups);
   const int* src = reinterpret_cast<const int*>(&G);
   for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
@@ -461,6 +467,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
       }
     }
     if (lane == 0) s_xs[wv] = xs;
+    trace_point(ws.trace, TK_GATEUP, 2);
     if (it < i1) issue(it);
   }
   __syncthreads();
@@ -532,9 +539,15 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t ht[GT_MAXM * HT_STRIDE];   // [member][HT_STRIDE]
   __shared__ float2 s_blk[GT_MAXM][2];
   __shared__ float s_xs[GT_MAXM];
+  __shared__ GroupTab G;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int B = a.B, k = a.k, d = a.L.d, F = a.L.F;
-  const GroupTab& G = *ws.groups;
+  {   // one round trip for the whole table instead of a chain of dependent loads
+    const int* src = reinterpret_cast<const int*>(ws.groups);
+    int* dst = reinterpret_cast<int*>(&G);
+    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  }
+  __syncthreads();
   const int nch = (d + DOWN_CHUNK - 1) / DOWN_CHUNK;
   const int U = G.U;
   const int items = U * nch;
@@ -615,6 +628,7 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
     // 3. MFMA per tile, epilogue per block, weighted partial per member
     const bool a_live = n16 < n;
     const uint8_t* arow = ht + (a_live ? n16 : 0) * HT_STRIDE + 16 * (4 * c);
+    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 3);
     int pc[4];
     float wc[4], xsc[4];
 #pragma unroll
@@ -659,6 +673,7 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
           if (pc[i] >= 0) ws.ypart[(int64_t)pc[i] * d + row] = wc[i] * acc[i];
       }
     }
+    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 4);
     __syncthreads();   // ht is restaged by the next item
   }
   trace_point(ws.trace, TK_DOWN, 2);
@@ -672,17 +687,19 @@ __global__ void __launch_bounds__(256) combine_kernel(ExpertArgs a, Ws ws) {
   const int wg = blockIdx.x + gridDim.x * blockIdx.y;
   trace_point_at(ws.trace, TK_DOWN, wg, 5);
   if (r >= d) return;
+  // every load at once: ypart rows of invalid slots are read but not added
   float part[MAXK];
+  int ej[MAXK];
 #pragma unroll
   for (int j = 0; j < MAXK; ++j) {
-    const int p = b * k + j;
-    const int e = j < k ? a.idx[p] : -1;
-    part[j] = (e >= 0 && e < a.L.E) ? ws.ypart[(int64_t)p * d + r] : 0.f;
+    const int p = b * k + (j < k ? j : 0);
+    ej[j] = a.idx[p];
+    part[j] = ws.ypart[(int64_t)p * d + r];
   }
   float y = a.res ? a.res[b * a.ldy + r] : 0.f;
 #pragma unroll
   for (int j = 0; j < MAXK; ++j)
-    if (j < k) y += part[j];
+    if (j < k && ej[j] >= 0 && ej[j] < a.L.E) y += part[j];
   a.y[b * a.ldy + r] = y;
   trace_point_at(ws.trace, TK_DOWN, wg, 6);
 }

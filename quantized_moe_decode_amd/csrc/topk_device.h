@@ -97,107 +97,83 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Sorting networks (Batcher's odd-even merge sort) for a lane's PER keys.
+__device__ constexpr int SORT4[][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};
+__device__ constexpr int SORT8[][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6},
+                                       {5, 7}, {1, 2}, {5, 6}, {0, 4}, {1, 5}, {2, 6}, {3, 7},
+                                       {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
+__device__ constexpr int SORT16[][2] = {
+    {0, 1},  {2, 3},   {4, 5},   {6, 7},   {8, 9},   {10, 11}, {12, 13}, {14, 15}, {0, 2},
+    {1, 3},  {4, 6},   {5, 7},   {8, 10},  {9, 11},  {12, 14}, {13, 15}, {1, 2},   {5, 6},
+    {9, 10}, {13, 14}, {0, 4},   {1, 5},   {2, 6},   {3, 7},   {8, 12},  {9, 13},  {10, 14},
+    {11, 15}, {2, 4},  {3, 5},   {10, 12}, {11, 13}, {1, 2},   {3, 4},   {5, 6},   {9, 10},
+    {11, 12}, {13, 14}, {0, 8},  {1, 9},   {2, 10},  {3, 11},  {4, 12},  {5, 13},  {6, 14},
+    {7, 15}, {4, 8},   {5, 9},   {6, 10},  {7, 11},  {2, 4},   {3, 5},   {6, 8},   {7, 9},
+    {10, 12}, {11, 13}, {1, 2},  {3, 4},   {5, 6},   {7, 8},   {9, 10},  {11, 12}, {13, 14}};
+
+template <int PER>
+__device__ __forceinline__ void local_sort(uint32_t* kk, uint32_t* ii) {
+  constexpr int N = PER == 4 ? 5 : PER == 8 ? 19 : 63;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const int a = PER == 4 ? SORT4[c][0] : PER == 8 ? SORT8[c][0] : SORT16[c][0];
+    const int b = PER == 4 ? SORT4[c][1] : PER == 8 ? SORT8[c][1] : SORT16[c][1];
+    const bool keep = before(kk[a], ii[a], kk[b], ii[b]);
+    const uint32_t ka = kk[a], ia = ii[a];
+    kk[a] = keep ? ka : kk[b];
+    ii[a] = keep ? ia : ii[b];
+    kk[b] = keep ? kk[b] : ka;
+    ii[b] = keep ? ii[b] : ia;
+  }
+}
+
 // Top-k of one token's E logits by one wave, exactly in f32 order with ties
 // to the lower expert index (PER >= ceil(E/64) logits per lane, expert e =
 // lane*PER + i).
-//  1. radix select of T, the k-th largest key, two bits per step: three
-//     candidate thresholds are counted at once (per-lane counts, DPP sums);
-//     the search stops as soon as exactly k keys are >= a candidate (exact ties
-//     at the boundary run all 32 bits);
-//  2. the winners are every key > T plus the lowest-index keys == T, up to
-//     k; they are compacted (in index order) into lanes 0..k-1 through a
-//     64-entry LDS table (`scratch`, 256 bytes per wave);
-//  3. a bitonic network on DPP (mirror/xor partners inside 8 or 16 lanes)
-//     sorts them by (key desc, index asc);
-//  4. weights exp(l_j - l_0) / sum_m exp(l_m - l_0), the sum taken by DPP in a
+//  1. every lane sorts its PER (key, expert) entries by (key desc, expert
+//     asc) with a sorting network;
+//  2. k rounds: the wave maximum of the lanes' heads (DPP), the lowest lane
+//     holding it wins (lower lanes hold lower experts), lane j records the
+//     round-j winner and the winning lane drops its head;
+//  3. weights exp(l_j - l_0) / sum_m exp(l_m - l_0), the sum taken by DPP in a
 //     fixed order.
+// k rounds of one reduction each replace a bit-serial threshold search:
+// the dependent chain per token is k wave reductions long.
 // Lanes j < k end with the j-th expert and its weight.  k <= 16.
 template <int PER>
 __device__ void topk_keys(const uint32_t* key, int E, int k, int& sel_e, float& sel_w,
                           uint32_t* scratch, uint64_t* trace) {
   const int lane = threadIdx.x & 63;
-  // 1. threshold
-  uint32_t T = 0;
-  for (int b = 30; b >= 0; b -= 2) {
-    const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
-    // counts per lane on the VALU (n1 | n2 << 16, and n3), then two DPP sums:
-    // ballot + popcount per key would queue on the scalar unit the CU's
-    // waves share
-    uint32_t p12 = 0, p3 = 0;
+  (void)scratch;
+  uint32_t kk[PER], ii[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      p12 += (key[i] >= c1 ? 1u : 0u) + (key[i] >= c2 ? 0x10000u : 0u);
-      p3 += key[i] >= c3 ? 1u : 0u;
-    }
-    p12 = wave_sum_u32(p12);
-    const int n1 = (int)(p12 & 0xFFFFu), n2 = (int)(p12 >> 16), n3 = (int)wave_sum_u32(p3);
-    T = (n3 >= k) ? c3 : (n2 >= k) ? c2 : (n1 >= k) ? c1 : T;
-    if (n1 == k || n2 == k || n3 == k) break;   // exactly k keys >= T: done
+  for (int i = 0; i < PER; ++i) {
+    kk[i] = key[i];
+    ii[i] = (uint32_t)(lane * PER + i);
   }
+  local_sort<PER>(kk, ii);
   trace_point(trace, TK_TOPK, 2);
-  // 2. winners: keys > T, then keys == T in index order up to k
-  int n_gt = 0, below_eq = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    n_gt += __builtin_popcountll(__ballot(key[i] > T));
-    const uint64_t eq = __ballot(key[i] == T);
-    below_eq += __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
-  }
-  const int need = k - n_gt;
-  int own_eq = 0, below_sel = 0, own_sel = 0;
-  bool sel[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const bool is_eq = key[i] == T;
-    sel[i] = key[i] > T || (is_eq && below_eq + own_eq < need);
-    own_eq += is_eq;
-    const uint64_t sm = __ballot(sel[i]);
-    below_sel += __builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (sel[i]) {
-      const int slot = below_sel + own_sel;
-      scratch[slot] = key[i];
-      scratch[32 + slot] = (uint32_t)(lane * PER + i);
-    }
-    own_sel += sel[i];
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written
-  __builtin_amdgcn_wave_barrier();
   uint32_t mk = 0, me = 0xFFFFFFFFu;     // lanes >= k hold "after everything"
-  if (lane < k) {
-    mk = scratch[lane];
-    me = scratch[32 + lane];
-  }
-  trace_point(trace, TK_TOPK, 3);
-  // 3. bitonic sort (descending) of lanes 0..15, flip variant: the first
-  //    step of each merge compares mirrored partners, later steps xor
-  //    partners; the lower lane of each pair keeps the entry that comes first
-  const bool lo1 = (lane & 1) == 0, lo2 = (lane & 2) == 0, lo4 = (lane & 4) == 0,
-             lo8 = (lane & 8) == 0;
-  bitonic_step<0xB1>(mk, me, lo1);    // size 2: xor 1
-  bitonic_step<0x1B>(mk, me, lo2);    // size 4: mirror in 4
-  bitonic_step<0xB1>(mk, me, lo1);
-  bitonic_step<0x141>(mk, me, lo4);   // size 8: mirror in 8
-  bitonic_step<0x4E>(mk, me, lo2);
-  bitonic_step<0xB1>(mk, me, lo1);
-  if (k > 8) {
-    bitonic_step<0x140>(mk, me, lo8); // size 16: mirror in 16
-    // xor 4 inside 16 lanes: rotate by 4 for the upper, by 12 for the lower half of each 8
-    {
-      const uint32_t ak = dpp_u<0x12C>(mk), ae = dpp_u<0x12C>(me);   // lane i <- i+4 (mod 16)
-      const uint32_t bk = dpp_u<0x124>(mk), be = dpp_u<0x124>(me);   // lane i <- i-4 (mod 16)
-      const uint32_t pk = lo4 ? ak : bk, pe = lo4 ? ae : be;
-      const bool take = lo4 != before(mk, me, pk, pe);
-      mk = take ? pk : mk;
-      me = take ? pe : me;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t m = wave_max_u32(kk[0]);
+    const uint64_t who = __ballot(kk[0] == m);
+    const int wl = (int)__builtin_ctzll(who);
+    const uint32_t we = (uint32_t)__builtin_amdgcn_readlane((int)ii[0], wl);
+    if (lane == j) {
+      mk = m;
+      me = we;
     }
-    bitonic_step<0x4E>(mk, me, lo2);
-    bitonic_step<0xB1>(mk, me, lo1);
+    const bool pop = lane == wl;
+#pragma unroll
+    for (int i = 0; i < PER - 1; ++i) {
+      kk[i] = pop ? kk[i + 1] : kk[i];
+      ii[i] = pop ? ii[i + 1] : ii[i];
+    }
+    kk[PER - 1] = pop ? 0u : kk[PER - 1];
+    ii[PER - 1] = pop ? 0xFFFFFFFFu : ii[PER - 1];
   }
   trace_point(trace, TK_TOPK, 4);
-  // 4. weights
+  // 3. weights
   const float l = okey_value(mk);
   const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), 0));
   float ex = 0.f;
