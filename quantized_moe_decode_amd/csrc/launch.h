@@ -42,7 +42,6 @@ struct Ws {
   float* h;           // [B*k][F] SiLU(gate)*up per (token, slot); batched: gate outputs [2][B*k][F]
   float* u;           // batched: up outputs [2][B*k][F] (two K halves); null otherwise
   float* ypart;       // [B*k][d] weighted expert outputs (batched path; null otherwise)
-  GroupTab* groups;   // batched path; null otherwise
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
 constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
@@ -58,7 +57,7 @@ void set_timing_events(void* start, void* stop);
 
 // Byte layout of a workspace for (E, B, k, d, F) (k = 0: routing only).
 struct WsLayout {
-  size_t logits, idx, wts, h, u, ypart, groups, total;
+  size_t logits, idx, wts, h, u, ypart, total;
 };
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F);
 Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F);

@@ -625,8 +625,6 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F) {
     o = al256(o + sizeof(float) * 2 * (size_t)B * k * F);
     l.ypart = o;
     o = al256(o + sizeof(float) * (size_t)B * k * d);
-    l.groups = o;
-    o = al256(o + sizeof(GroupTab));
   }
   l.total = o;
   return l;
@@ -644,7 +642,6 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F) {
   w.h = reinterpret_cast<float*>(p + l.h);
   w.u = l.u ? reinterpret_cast<float*>(p + l.u) : nullptr;
   w.ypart = l.ypart ? reinterpret_cast<float*>(p + l.ypart) : nullptr;
-  w.groups = l.groups ? reinterpret_cast<GroupTab*>(p + l.groups) : nullptr;
   w.trace = get_trace();
   return w;
 }
@@ -666,7 +663,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
   if (B >= 2) {
     if (int e = launch_logits_batched(a, ws.logits, s)) return e;
-    return launch_route_batched(a, ws.logits, nullptr, nullptr, nullptr, nullptr, ws.err, s);
+    return launch_route_batched(a, ws.logits, nullptr, nullptr, ws.err, s);
   }
   hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
@@ -747,12 +744,7 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
                    hipStream_t s) {
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
   if (fast_shape(L.d, L.F, k)) {
-    if (B >= 2) {
-      RouteArgs ra{nullptr, nullptr, L.E, L.d, x, ldx, B, k, nullptr, nullptr, nullptr};
-      if (int e = launch_route_batched(ra, nullptr, idx, nullptr, nullptr, ws.groups, ws.err, s))
-        return e;
-      return launch_experts_batched(a, ws, num_cus(), s);
-    }
+    if (B >= 2) return launch_experts_batched(a, ws, num_cus(), s);
     return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
   }
   return launch_generic_experts(a, ws, s);
@@ -767,9 +759,7 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
     // same routing kernels as moe_route_topk, so the two-call path gives
     // the same bits
     if (int e = launch_logits_batched(ra, ws.logits, s)) return e;
-    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, nullptr,
-                                     fast ? ws.groups : nullptr, ws.err, s))
-      return e;
+    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, ws.err, s)) return e;
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
     return fast ? launch_experts_batched(a, ws, num_cus(), s) : launch_generic_experts(a, ws, s);
   }

@@ -48,12 +48,10 @@ __host__ __device__ inline bool fast_shape(int d, int F, int k) {
 // Batched path (2 <= B <= 16) on MFMA matrix cores.
 constexpr int LG_KS = 4;   // K splits of the batched router GEMV (partial logit sets)
 int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
-// Top-k from the partial logits (idx_in null) or the caller's routing
-// (idx_in), optionally followed by the token groups.
-int launch_route_batched(const RouteArgs& ra, const float* part, const int32_t* idx_in,
-                         int32_t* idx_copy, float* wts_copy, GroupTab* groups, uint32_t* err,
-                         hipStream_t s);
-// gate/up, down and combine for the fast shape; groups already in ws.
+// Top-k and weights from the partial logits, one wave per token.
+int launch_route_batched(const RouteArgs& ra, const float* part, int32_t* idx_copy,
+                         float* wts_copy, uint32_t* err, hipStream_t s);
+// gate/up, down and combine for the fast shape (token groups built in-kernel).
 int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s);
 
 }  // namespace hq

@@ -28,10 +28,9 @@
 //   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32):
 //                        16 experts x 16 tokens per tile, K split over 4
 //                        workgroups x 4 waves; writes 4 partial logit sets.
-//   route_groups_kernel  one workgroup: per token (one wave each) the partial
-//                        sums + bias, top-k and weights; then the token groups
-//                        (pairs that chose the same expert), published for
-//                        the expert kernels.
+//   route_topk_kernel    one wave per token (each on its own CU): partial
+//                        sums + bias, top-k and weights.  The expert kernels
+//                        group the (token, slot) pairs by expert themselves.
 //   gateup_mfma_kernel   items of (group, 16 rows, gate or up, K half) in
 //                        contiguous runs per workgroup, so a workgroup stages
 //                        only the tokens of the groups it serves.
@@ -250,20 +249,17 @@ struct BatchRouteArgs {
   const float* part;      // [LG_KS][B][E] partial logits
   const float* bias;      // [E] or null
   int E, B, k;
-  const int32_t* idx_in;  // routing given by the caller (no top-k) or null
   int32_t* idx_out;       // [B][k]
   float* wts_out;         // [B][k]
   float* logits_out;      // [B][E] or null
   int32_t* idx_copy;      // workspace copies or null
   float* wts_copy;
-  GroupTab* groups;       // or null
   uint32_t* err;
   uint64_t* trace;
 };
 
 template <int PER>
-__device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t* scratch,
-                            float* lg) {
+__device__ void route_token(const BatchRouteArgs& r, int b, float* lg) {
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, (uint32_t)((int64_t)LG_KS * r.B * r.E * 4));
   // coalesced pass: lane l sums expert 64c + l over the partial sets (+ bias)
@@ -305,7 +301,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
   }
   int e;
   float w;
-  topk_keys<PER>(key, r.E, r.k, e, w, scratch, nullptr);
+  topk_keys<PER>(key, r.E, r.k, e, w, nullptr, nullptr);
   trace_point(r.trace, TK_TOPK, 3);
   if (lane < r.k) {
     const int p = b * r.k + lane;
@@ -315,45 +311,23 @@ __device__ void route_token(const BatchRouteArgs& r, int b, int* s_idx, uint32_t
       r.idx_copy[p] = e;
       r.wts_copy[p] = w;
     }
-    s_idx[p] = e;
   }
   if (__any(nan_seen) && lane == 0)
     __hip_atomic_fetch_or(r.err, 4u /*HFQ4_DEV_ERR_NONFINITE*/, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup of 16 waves: routing of token b by wave b (partial sums,
-// bias, top-k, weights), then the token groups.
-template <bool WITH_TOPK>
-__global__ void __launch_bounds__(1024) route_groups_kernel(BatchRouteArgs r) {
-  extern __shared__ float lgs[];   // [B][E] summed logits
-  __shared__ GroupTab G;
-  __shared__ GroupScratch GS;
-  __shared__ int s_idx[MAXP];
-  __shared__ uint32_t tk_scratch[16][64];
-  const int wv = threadIdx.x >> 6;
-  const int P = r.B * r.k;
+// One single-wave workgroup per token: partial sums + bias, top-k, weights.
+// Tokens run on different CUs in parallel; the expert kernels build the
+// token groups themselves from the indices (deterministically, so every
+// workgroup sees the same groups).
+__global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
+  __shared__ float lg[HFQ4_MAXE_DEV];
   trace_point(r.trace, TK_TOPK, 0);
-  if (WITH_TOPK) {
-    if (wv < r.B) {
-      float* lg = lgs + wv * r.E;
-      if (r.E <= 256) route_token<4>(r, wv, s_idx, tk_scratch[wv], lg);
-      else if (r.E <= 512) route_token<8>(r, wv, s_idx, tk_scratch[wv], lg);
-      else route_token<16>(r, wv, s_idx, tk_scratch[wv], lg);
-    }
-  } else if ((int)threadIdx.x < P) {
-    s_idx[threadIdx.x] = r.idx_in[threadIdx.x];
-  }
-  if (!r.groups) {
-    trace_point(r.trace, TK_TOPK, 1);
-    return;
-  }
-  __syncthreads();
-  build_groups_mm(s_idx, P, r.k, r.E, G, GS, r.err, true);
-  trace_point(r.trace, TK_TOPK, 4);
-  int* dst = reinterpret_cast<int*>(r.groups);
-  const int* src = reinterpret_cast<const int*>(&G);
-  for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  const int b = blockIdx.x;
+  if (r.E <= 256) route_token<4>(r, b, lg);
+  else if (r.E <= 512) route_token<8>(r, b, lg);
+  else route_token<16>(r, b, lg);
   trace_point(r.trace, TK_TOPK, 1);
 }
 
@@ -362,18 +336,17 @@ __global__ void __launch_bounds__(1024) route_groups_kernel(BatchRouteArgs r) {
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) {
   extern __shared__ __align__(16) uint8_t xt[];      // [B][XT_STRIDE]
   __shared__ GroupTab G;
+  __shared__ GroupScratch GS;
+  __shared__ int s_idx[MAXP];
   __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
   __shared__ float s_xs[HFQ4_MAXB_DEV];
   __shared__ uint32_t s_need;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int B = a.B, k = a.k, P = B * k, F = a.L.F, d = a.L.d;
   trace_point(ws.trace, TK_GATEUP, 0);
-  {
-    const int* src = reinterpret_cast<const int*>(ws.groups);
-    int* dst = reinterpret_cast<int*>(&G);
-    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
-  }
+  if ((int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
+  build_groups_mm(s_idx, P, k, a.L.E, G, GS, ws.err, blockIdx.x == 0);
   trace_point(ws.trace, TK_GATEUP, 1);
 
   // 3. this workgroup's items: a contiguous run of (group, matrix, 16-row
@@ -493,19 +466,25 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
-      f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+      // the block's 8 A operands first, then two independent MFMA chains
+      h8 av[2][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 q = cd[bk][t];
-        const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // entry 32 (4 kh + bk) + 16t + 4c + i of the token
-          h8 av = h8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (tok_a >= 0) av = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
-          cb = mfma16(av, dec8(qv[i]), cb);
+          av[t][i] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (tok_a >= 0) av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
         }
+      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q0[4] = {cd[bk][0].x, cd[bk][0].y, cd[bk][0].z, cd[bk][0].w};
+        const uint32_t q1[4] = {cd[bk][1].x, cd[bk][1].y, cd[bk][1].z, cd[bk][1].w};
+        c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
+        c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
       }
+      const f32x4 cb = c2[0] + c2[1];
       const float scale = as_f32(hd[bk].x), zero = as_f32(hd[bk].y);
       const float zp8 = __builtin_fmaf(8.f, scale, zero);
       const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
@@ -531,6 +510,11 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
     if (it < i1) issue(it);
   }
   trace_point(ws.trace, TK_GATEUP, 5);
+  if (ws.trace) {   // diagnostics: when this workgroup's stores have completed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    trace_point(ws.trace, TK_GATEUP, 6);
+  }
 }
 
 // ====================================================================== down + combine
@@ -540,14 +524,13 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
   __shared__ float2 s_blk[GT_MAXM][2];
   __shared__ float s_xs[GT_MAXM];
   __shared__ GroupTab G;
+  __shared__ GroupScratch GS;
+  __shared__ int s_idx[MAXP];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int B = a.B, k = a.k, d = a.L.d, F = a.L.F;
-  {   // one round trip for the whole table instead of a chain of dependent loads
-    const int* src = reinterpret_cast<const int*>(ws.groups);
-    int* dst = reinterpret_cast<int*>(&G);
-    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
-  }
+  if ((int)threadIdx.x < B * k) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
+  build_groups_mm(s_idx, B * k, k, a.L.E, G, GS, ws.err, false);
   const int nch = (d + DOWN_CHUNK - 1) / DOWN_CHUNK;
   const int U = G.U;
   const int items = U * nch;
@@ -643,18 +626,23 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk) {
-        f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+        h8 av[2][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 q = cd[tl][bk][t];
-          const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            h8 av = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (a_live) av = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
-            cb = mfma16(av, dec8(qv[i]), cb);
+            av[t][i] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (a_live) av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
           }
+        f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t q0[4] = {cd[tl][bk][0].x, cd[tl][bk][0].y, cd[tl][bk][0].z, cd[tl][bk][0].w};
+          const uint32_t q1[4] = {cd[tl][bk][1].x, cd[tl][bk][1].y, cd[tl][bk][1].z, cd[tl][bk][1].w};
+          c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
+          c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
         }
+        const f32x4 cb = c2[0] + c2[1];
         const float scale = as_f32(hd[tl][bk].x), zero = as_f32(hd[tl][bk].y);
         const float zp8 = __builtin_fmaf(8.f, scale, zero);
         const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
@@ -712,18 +700,11 @@ int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-int launch_route_batched(const RouteArgs& ra, const float* part, const int32_t* idx_in,
-                         int32_t* idx_copy, float* wts_copy, GroupTab* groups, uint32_t* err,
-                         hipStream_t s) {
-  BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, idx_in, ra.idx_out, ra.wts_out,
-                   ra.logits_out, idx_copy, wts_copy, groups, err, get_trace()};
-  if (idx_in) {
-    hipLaunchKernelGGL(route_groups_kernel<false>, dim3(1), dim3(1024), 0, s, r);
-  } else {
-    const size_t shm = sizeof(float) * (size_t)ra.B * ra.E;
-    if (int e = allow_lds(route_groups_kernel<true>, shm)) return e;
-    hipLaunchKernelGGL(route_groups_kernel<true>, dim3(1), dim3(1024), shm, s, r);
-  }
+int launch_route_batched(const RouteArgs& ra, const float* part, int32_t* idx_copy,
+                         float* wts_copy, uint32_t* err, hipStream_t s) {
+  BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, ra.idx_out, ra.wts_out,
+                   ra.logits_out, idx_copy, wts_copy, err, get_trace()};
+  hipLaunchKernelGGL(route_topk_kernel, dim3(ra.B), dim3(64), 0, s, r);
   return (int)hipGetLastError();
 }
 
@@ -736,7 +717,7 @@ int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s) {
   const int P = a.B * a.k;
   const int umax = P < a.L.E ? P : a.L.E;
   const int nch = (a.L.d + DOWN_CHUNK - 1) / DOWN_CHUNK;
-  const int grid = umax * nch < 4 * nwg ? umax * nch : 4 * nwg;
+  const int grid = umax * nch < 2 * nwg ? umax * nch : 2 * nwg;
   hipLaunchKernelGGL(down_mfma_kernel, dim3(grid), dim3(256), 0, s, a, ws);
   err = (int)hipGetLastError();
   if (err) return err;
