@@ -98,6 +98,15 @@ def cpu_baseline(torch, layers_f32_seed, xs_host, routers_host, budget_s):
             "tokens_per_s": round(1.0 / per_tok, 4)}
 
 
+def _calib_copy(torch):
+    """One 1 GiB device copy: the reference the counter runs scale by."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def _base(args, steps, warm, per_step_s, value, workload, extra_cfg=None):
     cfg = {"workload": workload, "global_batch": 1, "mode": "graph"}
     cfg.update(extra_cfg or {})
@@ -326,6 +335,8 @@ def bench_skewed(args, torch, q):
                        "pct_hbm_peak": round(100 * u * eb / per / 1e9 / HBM_PEAK_GBS, 2),
                        "steps": reps * G}
         del ws
+    if args.calib_copy:
+        _calib_copy(torch)
     b1 = res[min(res, key=int)]
     out = _base(args, sum(r["steps"] for r in res.values()), 0, b1["ms_per_step"] / 1e3,
                 b1["expert_gbs"],
@@ -488,11 +499,7 @@ def main():
         del gt
 
     if args.calib_copy:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        _calib_copy(torch)
 
     per_step_s = gpu_ms / 1e3 / steps
     expert_bytes = K_TOP * layers[0].expert_bytes()

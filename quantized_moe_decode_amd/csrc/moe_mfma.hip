@@ -34,7 +34,7 @@
 //   gateup_mfma_kernel   items of (group, 16 rows, gate or up, K half) in
 //                        contiguous runs per workgroup, so a workgroup stages
 //                        only the tokens of the groups it serves.
-//   down_mfma_kernel     work items of (group, 128 output rows): stages
+//   down_mfma_kernel     work items of (group, 256 output rows): stages
 //                        h = SiLU(g) * u of the group's pairs, writes
 //                        w_p * (down h_p) per pair.
 //   combine_kernel       y[b] = residual[b] + sum over the k slots of token b,
@@ -52,7 +52,8 @@ constexpr int XT_STRIDE = 4096 + 16;   // bytes per staged token (256 entries of
 constexpr int HT_STRIDE = 1024 + 16;   // bytes per staged h vector (64 entries + pad)
 constexpr int MM_ROWS = 16;            // rows per item
 constexpr int DOWN_TILES = 2;          // 16-row tiles per wave in the down kernel
-constexpr int DOWN_CHUNK = 64 * DOWN_TILES;   // output rows per down work item (4 waves)
+constexpr int DOWN_WAVES = 8;          // waves per down workgroup
+constexpr int DOWN_CHUNK = 16 * DOWN_TILES * DOWN_WAVES;   // output rows per down work item
 
 // Code dword -> B operand: 1024+q0, 1024+q4, 1024+16q1, 1024+16q5,
 // 1024+q2, 1024+q6, 1024+16q3, 1024+16q7.
@@ -519,7 +520,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
 
 // ====================================================================== down + combine
 
-__global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
+__global__ void __launch_bounds__(64 * DOWN_WAVES) down_mfma_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t ht[GT_MAXM * HT_STRIDE];   // [member][HT_STRIDE]
   __shared__ float2 s_blk[GT_MAXM][2];
   __shared__ float s_xs[GT_MAXM];
@@ -557,18 +558,18 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
       }
     }
 
-    // 2. stage h = SiLU(g) * u of the members: 16 threads per member, thread
-    //    s takes entries o = s + 16q (q < 4; block q / 2), so 16 threads read
-    //    512 contiguous bytes; scale per member over its F values
+    // 2. stage h = SiLU(g) * u of the members: 32 threads per member (half a
+    //    wave), thread s takes entries o = s + 32q (q < 2, block q), so the
+    //    32 threads read 1 KB contiguously; scale per member over its F values
     {
-      const int m = threadIdx.x >> 4, s = threadIdx.x & 15;
+      const int m = threadIdx.x >> 5, s = threadIdx.x & 31;
       const bool live = m < n;
       const int p = live ? G.gmem[u][m] : 0;
       const int64_t half = (int64_t)B * k * F;   // gate/up outputs come in two K halves
-      float v[4][8];
+      float v[2][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t e0 = (int64_t)p * F + 8 * (s + 16 * q);
+      for (int q = 0; q < 2; ++q) {
+        const int64_t e0 = (int64_t)p * F + 8 * (s + 32 * q);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f}, uv = gv;
@@ -586,22 +587,26 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(ExpertArgs a, Ws ws) {
       }
       float am = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[q][i]));
+      am = row_max16(am);
+      am = fmaxf(am, __shfl_xor(am, 16, 64));   // the member's 32 lanes
       float xs;
-      const float inv = pow2_scale(row_max16(am), xs);
-      float sh[2] = {0.f, 0.f}, s16[2] = {0.f, 0.f}, sx[2] = {0.f, 0.f};
+      const float inv = pow2_scale(am, xs);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2; ++q) {
+        float sh = 0.f, s16 = 0.f, sx = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sx[q >> 1] += v[q][i];
-        put_entry(v[q], inv, ht + m * HT_STRIDE + 16 * (s + 16 * q), sh[q >> 1], s16[q >> 1]);
-      }
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        const float a_sh = row_sum16(sh[bk]), a_16 = row_sum16(s16[bk]), a_sx = row_sum16(sx[bk]);
-        if (s == 0) s_blk[m][bk] = make_float2(-(1024.f * a_sh + 8.f * a_16), a_sx);
+        for (int i = 0; i < 8; ++i) sx += v[q][i];
+        put_entry(v[q], inv, ht + m * HT_STRIDE + 16 * (s + 32 * q), sh, s16);
+        sh = row_sum16(sh);
+        s16 = row_sum16(s16);
+        sx = row_sum16(sx);
+        sh += __shfl_xor(sh, 16, 64);
+        s16 += __shfl_xor(s16, 16, 64);
+        sx += __shfl_xor(sx, 16, 64);
+        if (s == 0) s_blk[m][q] = make_float2(-(1024.f * sh + 8.f * s16), sx);
       }
       if (s == 0) s_xs[m] = xs;
     }
@@ -718,7 +723,7 @@ int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s) {
   const int umax = P < a.L.E ? P : a.L.E;
   const int nch = (a.L.d + DOWN_CHUNK - 1) / DOWN_CHUNK;
   const int grid = umax * nch < 2 * nwg ? umax * nch : 2 * nwg;
-  hipLaunchKernelGGL(down_mfma_kernel, dim3(grid), dim3(256), 0, s, a, ws);
+  hipLaunchKernelGGL(down_mfma_kernel, dim3(grid), dim3(64 * DOWN_WAVES), 0, s, a, ws);
   err = (int)hipGetLastError();
   if (err) return err;
   hipLaunchKernelGGL(combine_kernel, dim3((a.L.d + 255) / 256, a.B), dim3(256), 0, s, a, ws);
