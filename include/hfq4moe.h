@@ -70,11 +70,13 @@ extern "C" {
 /* Sticky device-side error bits, OR-ed into the first 4 bytes of a MoE
  * workspace (see moe_workspace_bytes) or into hfq4_pack's `bad` counter. */
 #define HFQ4_DEV_ERR_INDEX     1u  /* an expert index outside [0, E); its slot is skipped */
-#define HFQ4_DEV_ERR_TIMEOUT   2u  /* an inter-workgroup wait exceeded its time limit */
+#define HFQ4_DEV_ERR_TIMEOUT   2u  /* reserved: no kernel of this build waits on another */
 #define HFQ4_DEV_ERR_NONFINITE 4u  /* a non-finite router logit was seen */
 
 /* Layer flags */
-#define HFQ4_LAYER_HOST_MAPPED 1u  /* expert weights live in pinned host memory [PCIE] */
+#define HFQ4_LAYER_HOST_MAPPED 1u  /* expert weights live in pinned host memory [PCIE];
+                                      informational: the kernels read host and device
+                                      weights through the same code, with the same bits */
 
 /* Limits of this build */
 #define HFQ4_MAX_BATCH   16
@@ -111,8 +113,9 @@ int hfq4_pack(const float* w, int64_t rows, int64_t K, int64_t ldw,
  * for b < batch (1..HFQ4_MAX_BATCH), r < rows.  W: HFQ4 rows (device or
  * mapped host), x: f32 [batch][ldx], residual: f32 [batch][ldr] or NULL,
  * y: f32 [batch][ldy].  y must not overlap x or W.  Products are taken
- * with x rounded to f16 and accumulated in f32 (error well inside 1e-3
- * relative L2 for K <= 16384).  K <= 16384; batch*K <= 32768. */
+ * with x scaled by a power of two per 32-element segment and rounded to
+ * f16, accumulated in f32 (error well inside 1e-3 relative L2 for K <=
+ * 16384, at any activation scale).  K <= 16384; batch*K <= 32768. */
 int hfq4_gemv(const void* W, int64_t rows, int64_t K,
               const float* x, int64_t ldx, int batch,
               const float* residual, int64_t ldr,
@@ -148,7 +151,7 @@ int moe_route_topk(const float* Wr, const float* bias, int64_t E, int64_t d,
  *   down = (const uint8_t*)down + e*stride_down : HFQ4 [d rows][K = F]
  * Strides >= the matrix size (so gate and up may be interleaved).
  * flags: HFQ4_LAYER_HOST_MAPPED when the pointers are pinned host memory
- * [PCIE] (results are identical; only the launch shape differs). */
+ * [PCIE] (same kernels, same results: the reads simply cross PCIe). */
 typedef struct moe_layer {
     const void* gate;
     const void* up;
@@ -169,11 +172,16 @@ int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 /* Expert half of the layer, given the routing:
  *   y[b] = residual[b] + sum_{j<k} wts[b][j] * down_e( SiLU(gate_e x[b]) * (up_e x[b]) ),
  *   e = idx[b][j].
- * Tokens that share an expert read its weights once (grouping).  An index
- * outside [0, E) sets HFQ4_DEV_ERR_INDEX and contributes nothing.
+ * Tokens that share an expert read its weights once (grouping); an index
+ * repeated within one token counts once per slot.  An index outside
+ * [0, E) sets HFQ4_DEV_ERR_INDEX and contributes nothing.
  * x: f32 [batch][ldx]; idx: int32 [batch][k]; wts: f32 [batch][k];
  * residual: f32 [batch][ldy] or NULL; y: f32 [batch][ldy], must not
- * overlap x.  d <= 2048, F <= 2048, d % 4 == 0, F % 4 == 0. */
+ * overlap x.  d <= 2048, F <= 2048, d % 4 == 0, F % 4 == 0.
+ * For 1792 < d <= 2048, F = 512, k <= 8 the work runs on tuned kernels:
+ * one token on the VALU (f16 dot products), 2..16 tokens on MFMA matrix
+ * cores (each expert a small GEMM over the tokens that chose it).  The two
+ * agree within the stated error, not bit for bit. */
 int moe_expert_decode(const moe_layer* L, const float* x, int64_t ldx, int batch,
                       const int32_t* idx, const float* wts, int k,
                       const float* residual, float* y, int64_t ldy,

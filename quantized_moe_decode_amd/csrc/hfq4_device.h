@@ -271,49 +271,4 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
 }
 
-// ---------------------------------------------------------------- inter-workgroup sync
-// Counters live in caller-provided device memory.  Producers: every thread
-// fences its own writes at agent scope, the workgroup meets at a barrier,
-// then one thread bumps the counter.  Consumers: one thread polls with a
-// time limit (s_memrealtime ticks at 100 MHz), then an acquire fence and a
-// barrier.  A wait that times out sets `err` and returns false, so every
-// wave always leaves the kernel.
-__device__ __forceinline__ void wg_signal(uint32_t* ctr) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ bool wg_wait(uint32_t* ctr, uint32_t target, uint32_t* err,
-                                        uint64_t limit_ticks) {
-  __shared__ int ok_flag;
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > limit_ticks) {
-        __hip_atomic_fetch_or(err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    ok_flag = ok;
-  }
-  __syncthreads();
-  return ok_flag != 0;
-}
-
-// Loads of data written by other workgroups of the same kernel: bypass the
-// (non-coherent across XCDs) L2 by loading at agent scope.
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_agent(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace hq

@@ -130,11 +130,10 @@ struct Groups {
   int first[MAXP];  // first pair with the same expert
 };
 
-__device__ void build_groups(const int32_t* idx, int P, int E, Groups& G, uint32_t* err,
-                             bool idx_agent) {
+__device__ void build_groups(const int32_t* idx, int P, int E, Groups& G, uint32_t* err) {
   const int t = threadIdx.x;
   if (t < P) {
-    int e = idx_agent ? ld_agent(idx + t) : idx[t];
+    int e = idx[t];
     if (e < 0 || e >= E) {
       __hip_atomic_fetch_or(err, 1u /*HFQ4_DEV_ERR_INDEX*/, __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
@@ -293,7 +292,7 @@ __device__ void down_rows(const ExpertArgs& a, const Ws& ws, const uint8_t* hfr,
 
 // Stage h(token b, slot j) for j < k into LDS fragments (F values each).
 template <int NBF>
-__device__ void stage_h(const ExpertArgs& a, const Ws& ws, int b, uint8_t* hfr, bool agent) {
+__device__ void stage_h(const ExpertArgs& a, const Ws& ws, int b, uint8_t* hfr) {
   constexpr int SEGS = 8 * NBF;
   const int F = a.L.F, k = a.k;
   const int fb = frag_bytes(SEGS);
@@ -305,7 +304,7 @@ __device__ void stage_h(const ExpertArgs& a, const Ws& ws, int b, uint8_t* hfr, 
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int f = base + i;
-      buf[i] = (f < F) ? (agent ? ld_agent(src + f) : src[f]) : 0.f;
+      buf[i] = (f < F) ? src[f] : 0.f;
     }
     Frag fr;
     make_frag(buf, fr);
@@ -320,7 +319,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a, Ws ws) {
   constexpr int SEGS = 8 * NBD, ROWS = (64 / SEGS) * RPW;
   extern __shared__ __align__(16) uint8_t xfr[];
   __shared__ Groups G;
-  build_groups(a.idx, a.B * a.k, a.L.E, G, ws.err, false);
+  build_groups(a.idx, a.B * a.k, a.L.E, G, ws.err);
   const int fb = frag_bytes(SEGS);
   for (int b = 0; b < a.B; ++b)
     stage_vector(a.x + b * a.ldx, a.L.d, SEGS, xfr + b * fb, threadIdx.x, blockDim.x);
@@ -345,7 +344,7 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a, Ws ws) {
   const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   for (int b = 0; b < a.B; ++b) {
     __syncthreads();
-    stage_h<NBF>(a, ws, b, hfr, false);
+    stage_h<NBF>(a, ws, b, hfr);
     __syncthreads();
     for (int r0 = gw * ROUT; r0 < a.L.d; r0 += nw * ROUT) down_rows<NBF, ROUT>(a, ws, hfr, b, r0, pexp);
   }
@@ -423,7 +422,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
     if (threadIdx.x == 0) G.U = k;
     __syncthreads();
   } else {
-    build_groups(s_idx, P, E, G, ws.err, false);
+    build_groups(s_idx, P, E, G, ws.err);
   }
   trace_point(ws.trace, TK_GATEUP, 2);
 

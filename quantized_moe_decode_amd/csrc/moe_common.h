@@ -5,7 +5,6 @@
 
 namespace hq {
 
-constexpr uint64_t WAIT_TICKS = 20000000ull;   // 200 ms of s_memrealtime (100 MHz)
 constexpr int MAXP = 128;                      // max (token, slot) pairs: 16 x 8... up to B*k
 constexpr int MAXK = 16;
 
