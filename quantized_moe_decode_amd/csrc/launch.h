@@ -39,12 +39,13 @@ struct Ws {
   float* logits;      // [B][E]
   int32_t* idx;       // [B][k]  routing (internal copy)
   float* wts;         // [B][k]
-  float* h;           // [B*k][F] SiLU(gate)*up per (token, slot); batched: gate outputs [2][B*k][F]
-  float* u;           // batched: up outputs [2][B*k][F] (two K halves); null otherwise
+  float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
+  uint8_t* xg;        // batched: [B][XG_STRIDE] staged activations; null otherwise
   float* ypart;       // [B*k][d] weighted expert outputs (batched path; null otherwise)
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
 constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
+constexpr int XG_STRIDE = 4224;    // bytes per staged token of the batched path
 constexpr int WS_COUNTERS = 240;
 
 // Phase tracing: when a trace buffer is registered, thread 0 of every
@@ -57,7 +58,7 @@ void set_timing_events(void* start, void* stop);
 
 // Byte layout of a workspace for (E, B, k, d, F) (k = 0: routing only).
 struct WsLayout {
-  size_t logits, idx, wts, h, u, ypart, total;
+  size_t logits, idx, wts, h, xg, ypart, total;
 };
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F);
 Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F);

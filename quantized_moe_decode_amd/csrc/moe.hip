@@ -617,11 +617,10 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F) {
   l.wts = o;
   o = al256(o + sizeof(float) * (size_t)B * k);
   l.h = o;
-  const size_t halves = (B >= 2) ? 2 : 1;   // batched: gate outputs in two K halves
-  o = al256(o + sizeof(float) * halves * (size_t)B * k * F);
+  o = al256(o + sizeof(float) * (size_t)B * k * F);
   if (B >= 2 && k > 0) {          // batched expert path
-    l.u = o;
-    o = al256(o + sizeof(float) * 2 * (size_t)B * k * F);
+    l.xg = o;
+    o = al256(o + (size_t)XG_STRIDE * B);
     l.ypart = o;
     o = al256(o + sizeof(float) * (size_t)B * k * d);
   }
@@ -639,7 +638,7 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F) {
   w.idx = reinterpret_cast<int32_t*>(p + l.idx);
   w.wts = reinterpret_cast<float*>(p + l.wts);
   w.h = reinterpret_cast<float*>(p + l.h);
-  w.u = l.u ? reinterpret_cast<float*>(p + l.u) : nullptr;
+  w.xg = l.xg ? p + l.xg : nullptr;
   w.ypart = l.ypart ? reinterpret_cast<float*>(p + l.ypart) : nullptr;
   w.trace = get_trace();
   return w;
@@ -662,7 +661,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
   if (B >= 2) {
     if (int e = launch_logits_batched(a, ws.logits, s)) return e;
-    return launch_route_batched(a, ws.logits, nullptr, nullptr, ws.err, s);
+    return launch_route_batched(a, ws.logits, nullptr, nullptr, nullptr, ws.err, s);
   }
   hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
@@ -743,7 +742,10 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
                    hipStream_t s) {
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
   if (fast_shape(L.d, L.F, k)) {
-    if (B >= 2) return launch_experts_batched(a, ws, num_cus(), s);
+    if (B >= 2) {
+      if (int e = launch_stage_batched(x, ldx, B, L.d, ws.xg, s)) return e;
+      return launch_experts_batched(a, ws, num_cus(), s);
+    }
     return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
   }
   return launch_generic_experts(a, ws, s);
@@ -758,7 +760,9 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
     // same routing kernels as moe_route_topk, so the two-call path gives
     // the same bits
     if (int e = launch_logits_batched(ra, ws.logits, s)) return e;
-    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, ws.err, s)) return e;
+    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, fast ? ws.xg : nullptr,
+                                     ws.err, s))
+      return e;
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
     return fast ? launch_experts_batched(a, ws, num_cus(), s) : launch_generic_experts(a, ws, s);
   }

@@ -29,13 +29,17 @@
 //                        16 experts x 16 tokens per tile, K split over 4
 //                        workgroups x 4 waves; writes 4 partial logit sets.
 //   route_topk_kernel    one wave per token (each on its own CU): partial
-//                        sums + bias, top-k and weights.  The expert kernels
-//                        group the (token, slot) pairs by expert themselves.
-//   gateup_mfma_kernel   items of (group, 16 rows, gate or up, K half) in
-//                        contiguous runs per workgroup, so a workgroup stages
-//                        only the tokens of the groups it serves.
+//                        sums + bias, top-k and weights, and the token's
+//                        activations staged once in the MFMA operand format.
+//                        The expert kernels group the (token, slot) pairs by
+//                        expert themselves.
+//   gateup_mfma_kernel   items of (group, 16 rows) in contiguous runs per
+//                        workgroup; a quad of waves computes gate and up over
+//                        both K halves, reduces through LDS and writes
+//                        h = SiLU(g) * u.  The workgroup copies in only the
+//                        staged activations of the tokens its groups need.
 //   down_mfma_kernel     work items of (group, 256 output rows): stages
-//                        h = SiLU(g) * u of the group's pairs, writes
+//                        h of the group's pairs, writes
 //                        w_p * (down h_p) per pair.
 //   combine_kernel       y[b] = residual[b] + sum over the k slots of token b,
 //                        in slot order.
@@ -257,35 +261,51 @@ struct BatchRouteArgs {
   float* wts_copy;
   uint32_t* err;
   uint64_t* trace;
+  const float* x;         // [B][ldx] activations to stage, or null
+  int64_t ldx;
+  int d;
+  uint8_t* xg;            // [B][XG_STRIDE] staged activations (see stage_token)
 };
 
 template <int PER>
-__device__ void route_token(const BatchRouteArgs& r, int b, float* lg) {
+struct RouteLoads {
+  uint32_t raw[LG_KS][PER];
+  uint32_t rb[PER];
+};
+
+// Issue every load of one token's routing: the LG_KS partial logits and the
+// bias of expert 64c + lane (coalesced).
+template <int PER>
+__device__ __forceinline__ void route_load(const BatchRouteArgs& r, int b, RouteLoads<PER>& L) {
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, (uint32_t)((int64_t)LG_KS * r.B * r.E * 4));
-  // coalesced pass: lane l sums expert 64c + l over the partial sets (+ bias)
-  // into LDS; the top-k then reads its own PER consecutive experts
-  int nan_seen = 0;
-  uint32_t raw[LG_KS][PER];   // every load in flight before the first add
-  uint32_t rb[PER];
   const __amdgpu_buffer_rsrc_t rbias = make_rsrc(r.bias, r.bias ? (uint32_t)r.E * 4u : 0u);
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int e = 64 * c + lane;
 #pragma unroll
     for (int p = 0; p < LG_KS; ++p)
-      raw[p][c] = bload4(rp, e < r.E ? (uint32_t)((((int64_t)p * r.B + b) * r.E + e) * 4)
-                                     : 0xFFFFFFF0u);
-    rb[c] = bload4(rbias, (uint32_t)e * 4u);   // zero without a bias or past E
+      L.raw[p][c] = bload4(rp, e < r.E ? (uint32_t)((((int64_t)p * r.B + b) * r.E + e) * 4)
+                                       : 0xFFFFFFF0u);
+    L.rb[c] = bload4(rbias, (uint32_t)e * 4u);   // zero without a bias or past E
   }
+}
+
+// Sum, top-k and weights of one token from its loads.
+template <int PER>
+__device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER>& L, float* lg) {
+  const int lane = threadIdx.x & 63;
+  // lane l sums expert 64c + l over the partial sets (+ bias) into LDS; the
+  // top-k then reads its own PER consecutive experts
+  int nan_seen = 0;
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int e = 64 * c + lane;
     if (e < r.E) {
       float l = 0.f;
 #pragma unroll
-      for (int p = 0; p < LG_KS; ++p) l += as_f32(raw[p][c]);
-      if (r.bias) l += as_f32(rb[c]);
+      for (int p = 0; p < LG_KS; ++p) l += as_f32(L.raw[p][c]);
+      if (r.bias) l += as_f32(L.rb[c]);
       if (r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
       lg[e] = l;
       nan_seen |= __builtin_isnan(l);
@@ -318,22 +338,96 @@ __device__ void route_token(const BatchRouteArgs& r, int b, float* lg) {
                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One single-wave workgroup per token: partial sums + bias, top-k, weights.
-// Tokens run on different CUs in parallel; the expert kernels build the
-// token groups themselves from the indices (deterministically, so every
-// workgroup sees the same groups).
+// Stage one token's activations (one wave) into the MFMA A-operand format
+// at dst: 256 entries of 16 B (entry o = elements 8o..8o+7 scaled by 2^-e,
+// in dec8 order), then per block (off, sx) as 8 float2, then xs = 2^e.
+// Lane l takes entries o = l + 64m, so one load instruction covers 2 KB of
+// x; entry o belongs to block o / 32 (2m for lanes 0-31, 2m+1 above).
+constexpr int XG_ENTRIES = 4096, XG_BLK = 4096, XG_XS = 4096 + 64;
+static_assert(XG_STRIDE >= XG_XS + 4, "staged token layout");
+
+__device__ void stage_token(const float* __restrict__ xb, int d, uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+  float v[4][8];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e0 = 8 * (lane + 64 * m);
+    f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
+    if (e0 < d) t0 = *reinterpret_cast<const f32x4*>(xb + e0);
+    if (e0 + 4 < d) t1 = *reinterpret_cast<const f32x4*>(xb + e0 + 4);
+    v[m][0] = t0.x; v[m][1] = t0.y; v[m][2] = t0.z; v[m][3] = t0.w;
+    v[m][4] = t1.x; v[m][5] = t1.y; v[m][6] = t1.z; v[m][7] = t1.w;
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[m][i]));
+  float xs;
+  const float inv = pow2_scale(wave_max_f(am), xs);
+  float2* blk = reinterpret_cast<float2*>(dst + XG_BLK);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float sh = 0.f, s16 = 0.f, sx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sx += v[m][i];
+    put_entry(v[m], inv, dst + XG_ENTRIES * 0 + 16 * (lane + 64 * m), sh, s16);
+    // block sums over 32 lanes, fixed order
+    sh = row_sum16(sh);
+    s16 = row_sum16(s16);
+    sx = row_sum16(sx);
+    const float lo_sh = lane_bcast(sh, 0) + lane_bcast(sh, 16);
+    const float hi_sh = lane_bcast(sh, 32) + lane_bcast(sh, 48);
+    const float lo_16 = lane_bcast(s16, 0) + lane_bcast(s16, 16);
+    const float hi_16 = lane_bcast(s16, 32) + lane_bcast(s16, 48);
+    const float lo_sx = lane_bcast(sx, 0) + lane_bcast(sx, 16);
+    const float hi_sx = lane_bcast(sx, 32) + lane_bcast(sx, 48);
+    if (lane == 0) {
+      blk[2 * m] = make_float2(-(1024.f * lo_sh + 8.f * lo_16), lo_sx);
+      blk[2 * m + 1] = make_float2(-(1024.f * hi_sh + 8.f * hi_16), hi_sx);
+    }
+  }
+  if (lane == 0) *reinterpret_cast<float*>(dst + XG_XS) = xs;
+}
+
+// One single-wave workgroup per token: partial sums + bias, top-k, weights
+// (WITH_TOPK), and the token's activations staged for the expert kernels
+// (when r.xg is set).  Tokens run on different CUs in parallel; the expert
+// kernels build the token groups themselves from the indices
+// (deterministically, so every workgroup sees the same groups).
+template <bool WITH_TOPK>
 __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
   __shared__ float lg[HFQ4_MAXE_DEV];
   trace_point(r.trace, TK_TOPK, 0);
   const int b = blockIdx.x;
-  if (r.E <= 256) route_token<4>(r, b, lg);
-  else if (r.E <= 512) route_token<8>(r, b, lg);
-  else route_token<16>(r, b, lg);
+  // the routing loads go out first, the activation staging overlaps them
+  if (!WITH_TOPK) {
+    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
+  } else if (r.E <= 256) {
+    RouteLoads<4> L;
+    route_load<4>(r, b, L);
+    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
+    route_token<4>(r, b, L, lg);
+  } else if (r.E <= 512) {
+    RouteLoads<8> L;
+    route_load<8>(r, b, L);
+    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
+    route_token<8>(r, b, L, lg);
+  } else {
+    RouteLoads<16> L;
+    route_load<16>(r, b, L);
+    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
+    route_token<16>(r, b, L, lg);
+  }
   trace_point(r.trace, TK_TOPK, 1);
 }
 
 // ====================================================================== gate / up
 
+// A workgroup of 16 waves = 4 quads; a quad takes one (group, 16-row tile)
+// item at a time: its waves compute gate K-half 0, gate K-half 1, up K-half
+// 0 and up K-half 1 (4 blocks each, all loads in flight at once), the
+// partial tiles meet in LDS, and the first wave writes h = SiLU(g) * u.
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) {
   extern __shared__ __align__(16) uint8_t xt[];      // [B][XT_STRIDE]
   __shared__ GroupTab G;
@@ -342,47 +436,45 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
   __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
   __shared__ float s_xs[HFQ4_MAXB_DEV];
   __shared__ uint32_t s_need;
+  __shared__ f32x4 red[4][3][64];                    // partial tiles of roles 1..3
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int B = a.B, k = a.k, P = B * k, F = a.L.F, d = a.L.d;
+  const int quad = wv >> 2, role = wv & 3;
+  const int B = a.B, k = a.k, P = B * k, F = a.L.F;
   trace_point(ws.trace, TK_GATEUP, 0);
   if ((int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
   build_groups_mm(s_idx, P, k, a.L.E, G, GS, ws.err, blockIdx.x == 0);
   trace_point(ws.trace, TK_GATEUP, 1);
 
-  // 3. this workgroup's items: a contiguous run of (group, matrix, 16-row
-  //    tile, K half); an item covers 4 of the 8 blocks of its rows, and the
-  //    down kernel adds the two halves
+  // 1. this workgroup's items: a contiguous run of (group, 16-row tile)
   const int tiles = F / MM_ROWS;                 // 32
-  const int per_u = 2 * tiles * 2;               // items per group
-  const int items = G.U * per_u;
+  const int items = G.U * tiles;
   const int per = (items + gridDim.x - 1) / gridDim.x;
   const int i0 = blockIdx.x * per;
   const int i1 = min(items, i0 + per);
   if (threadIdx.x == 0) {
     uint32_t m = 0;
     if (i0 < i1)
-      for (int u = i0 / per_u; u <= (i1 - 1) / per_u; ++u) {
+      for (int u = i0 / tiles; u <= (i1 - 1) / tiles; ++u) {
         for (int q = 0; q < G.gcnt[u]; ++q) m |= 1u << (G.gmem[u][q] / k);
       }
     s_need = m;
   }
   __syncthreads();
 
+  // 2. the wave's first item: its role's 4 blocks, every load in flight
   constexpr int64_t ROWB = 8 * BLK_BYTES;
   const int n16 = lane & 15, c = lane >> 4;
+  const int mat = role >> 1, kh = role & 1;
+  const uint8_t* base = mat ? a.L.up : a.L.gate;
+  const int64_t stride = mat ? a.L.su : a.L.sg;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, mat ? a.L.up_bytes : a.L.gate_bytes);
   u32x4 cd[4][2];
   u32x2 hd[4];
   auto issue = [&](int it) {
-    const int u = it / per_u, r = it - u * per_u;
-    const int mat = r / (2 * tiles), tile = (r >> 1) % tiles, kh = r & 1;
-    const int e = G.gexp[u];
-    const uint8_t* base = mat ? a.L.up : a.L.gate;
-    const uint32_t bytes = mat ? a.L.up_bytes : a.L.gate_bytes;
-    const int64_t stride = mat ? a.L.su : a.L.sg;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
-    const uint32_t rowoff = (uint32_t)(e * stride + (int64_t)(tile * MM_ROWS + n16) * ROWB +
-                                       kh * 4 * BLK_BYTES);
+    const int u = it / tiles, tile = it - u * tiles;
+    const uint32_t rowoff = (uint32_t)(G.gexp[u] * stride +
+                                       (int64_t)(tile * MM_ROWS + n16) * ROWB + kh * 4 * BLK_BYTES);
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
       hd[bk] = bload8(rs, rowoff + bk * BLK_BYTES);
@@ -390,132 +482,116 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
       cd[bk][1] = bload16(rs, rowoff + bk * BLK_BYTES + 8 + 64 + 16 * c);
     }
   };
-  int it = i0 + wv;
-  // 4. stage the tokens this workgroup needs: wave b stages token b.  Waves
-  //    that stage issue their first item's weight loads afterwards (the
-  //    registers would not hold both), the others at once.
-  const bool stager = wv < B && ((s_need >> wv) & 1u);
-  if (!stager && it < i1) issue(it);
-  if (stager) {
-    // lane l takes entries o = l + 64m (8 consecutive elements each), so a
-    // load instruction covers 2 KB of x contiguously; entry o belongs to
-    // block o / 32, i.e. block 2m for lanes 0-31 and 2m+1 for lanes 32-63
-    const float* xb = a.x + (int64_t)wv * a.ldx;
-    float v[4][8];
+  // 3. the needed tokens' staged activations: every 16-byte chunk load in
+  //    flight first (ahead of the weights in the memory queue), then the
+  //    first item's weight loads, then the chunks go to LDS
+  constexpr int XG_CHUNKS = (XG_XS + 4 + 15) / 16;   // 261 chunks of a staged token
+  constexpr int XG_ITERS = (HFQ4_MAXB_DEV * XG_CHUNKS + 1023) / 1024;
+  u32x4 xc[XG_ITERS];
+  const uint32_t need = s_need;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e0 = 8 * (lane + 64 * m);
-      f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
-      if (e0 < d) t0 = *reinterpret_cast<const f32x4*>(xb + e0);
-      if (e0 + 4 < d) t1 = *reinterpret_cast<const f32x4*>(xb + e0 + 4);
-      v[m][0] = t0.x; v[m][1] = t0.y; v[m][2] = t0.z; v[m][3] = t0.w;
-      v[m][4] = t1.x; v[m][5] = t1.y; v[m][6] = t1.z; v[m][7] = t1.w;
-    }
-    float am = 0.f;
+  for (int j = 0; j < XG_ITERS; ++j) {
+    const int ci = threadIdx.x + 1024 * j;
+    const int tb = ci / XG_CHUNKS, ch = ci - tb * XG_CHUNKS;
+    xc[j] = u32x4{0u, 0u, 0u, 0u};
+    if (tb < B && ((need >> tb) & 1u))
+      xc[j] = *reinterpret_cast<const u32x4*>(ws.xg + (int64_t)tb * XG_STRIDE + 16 * ch);
+  }
+  int it = i0 + quad;
+  if (it < i1) issue(it);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[m][i]));
-    float xs;
-    const float inv = pow2_scale(wave_max_f(am), xs);
-    uint8_t* dst = xt + wv * XT_STRIDE;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float sh = 0.f, s16 = 0.f, sx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sx += v[m][i];
-      put_entry(v[m], inv, dst + 16 * (lane + 64 * m), sh, s16);
-      // block sums over 32 lanes, fixed order
-      sh = row_sum16(sh);
-      s16 = row_sum16(s16);
-      sx = row_sum16(sx);
-      const float lo_sh = lane_bcast(sh, 0) + lane_bcast(sh, 16);
-      const float hi_sh = lane_bcast(sh, 32) + lane_bcast(sh, 48);
-      const float lo_16 = lane_bcast(s16, 0) + lane_bcast(s16, 16);
-      const float hi_16 = lane_bcast(s16, 32) + lane_bcast(s16, 48);
-      const float lo_sx = lane_bcast(sx, 0) + lane_bcast(sx, 16);
-      const float hi_sx = lane_bcast(sx, 32) + lane_bcast(sx, 48);
-      if (lane == 0) {
-        s_blk[wv][2 * m] = make_float2(-(1024.f * lo_sh + 8.f * lo_16), lo_sx);
-        s_blk[wv][2 * m + 1] = make_float2(-(1024.f * hi_sh + 8.f * hi_16), hi_sx);
+  for (int j = 0; j < XG_ITERS; ++j) {
+    const int ci = threadIdx.x + 1024 * j;
+    const int tb = ci / XG_CHUNKS, ch = ci - tb * XG_CHUNKS;
+    if (tb < B && ((need >> tb) & 1u)) {
+      if (ch < 256) {
+        *reinterpret_cast<u32x4*>(xt + tb * XT_STRIDE + 16 * ch) = xc[j];
+      } else if (ch < 260) {   // (off, sx) of blocks 2(ch-256), 2(ch-256)+1
+        s_blk[tb][2 * (ch - 256)] = make_float2(as_f32(xc[j].x), as_f32(xc[j].y));
+        s_blk[tb][2 * (ch - 256) + 1] = make_float2(as_f32(xc[j].z), as_f32(xc[j].w));
+      } else {
+        s_xs[tb] = as_f32(xc[j].x);
       }
     }
-    if (lane == 0) s_xs[wv] = xs;
-    trace_point(ws.trace, TK_GATEUP, 2);
-    if (it < i1) issue(it);
   }
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 3);
 
-  // 5. items
-  while (it < i1) {
-    const int u = it / per_u, r = it - u * per_u;
-    const int mat = r / (2 * tiles), tile = (r >> 1) % tiles, kh = r & 1;
-    const int n = G.gcnt[u];
-    // A operand source: member n16 of the group (zeros past the group)
-    const int tok_a = n16 < n ? G.gmem[u][n16] / k : -1;
-    const uint8_t* arow = xt + (tok_a >= 0 ? tok_a : 0) * XT_STRIDE + 16 * (4 * c) + kh * 4 * 512;
-    // epilogue columns: members 4c..4c+3
-    int tok_c[4];
-    float xs_c[4];
+  // 4. rounds of one item per quad (uniform trip count: every wave meets
+  //    every barrier)
+  const int rounds = (i1 - i0 + 3) / 4;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const bool live = it < i1;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int n = 0, u = 0, tile = 0;
+    if (live) {
+      u = it / tiles;
+      tile = it - u * tiles;
+      n = G.gcnt[u];
+      // A operand source: member n16 of the group (zeros past the group)
+      const int tok_a = n16 < n ? G.gmem[u][n16] / k : -1;
+      const uint8_t* arow = xt + (tok_a >= 0 ? tok_a : 0) * XT_STRIDE + 16 * (4 * c) + kh * 4 * 512;
+      int tok_c[4];
+      float xs_c[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * c + i;
-      tok_c[i] = m < n ? G.gmem[u][m] / k : -1;
-      xs_c[i] = tok_c[i] >= 0 ? s_xs[tok_c[i]] : 0.f;
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * c + i;
+        tok_c[i] = m < n ? G.gmem[u][m] / k : -1;
+        xs_c[i] = tok_c[i] >= 0 ? s_xs[tok_c[i]] : 0.f;
+      }
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      // the block's 8 A operands first, then two independent MFMA chains
-      h8 av[2][4];
+      for (int bk = 0; bk < 4; ++bk) {
+        // the block's 8 A operands first, then two independent MFMA chains
+        h8 av[2][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // entry 32 (4 kh + bk) + 16t + 4c + i of the token; rows past the
+            // group read token 0's slot: their output rows are never used
+            av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+          }
+        f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // entry 32 (4 kh + bk) + 16t + 4c + i of the token
-          av[t][i] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (tok_a >= 0) av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+          const uint32_t q0[4] = {cd[bk][0].x, cd[bk][0].y, cd[bk][0].z, cd[bk][0].w};
+          const uint32_t q1[4] = {cd[bk][1].x, cd[bk][1].y, cd[bk][1].z, cd[bk][1].w};
+          c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
+          c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
         }
-      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const f32x4 cb = c2[0] + c2[1];
+        const float scale = as_f32(hd[bk].x), zero = as_f32(hd[bk].y);
+        const float zp8 = __builtin_fmaf(8.f, scale, zero);
+        const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t q0[4] = {cd[bk][0].x, cd[bk][0].y, cd[bk][0].z, cd[bk][0].w};
-        const uint32_t q1[4] = {cd[bk][1].x, cd[bk][1].y, cd[bk][1].z, cd[bk][1].w};
-        c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
-        c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
-      }
-      const f32x4 cb = c2[0] + c2[1];
-      const float scale = as_f32(hd[bk].x), zero = as_f32(hd[bk].y);
-      const float zp8 = __builtin_fmaf(8.f, scale, zero);
-      const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-      float accv[4] = {acc.x, acc.y, acc.z, acc.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tok_c[i] >= 0) {
-          const float2 ob = s_blk[tok_c[i]][4 * kh + bk];
-          accv[i] += __builtin_fmaf(scale * xs_c[i], cbv[i] + ob.x, zp8 * ob.y);
+        for (int i = 0; i < 4; ++i) {
+          if (tok_c[i] >= 0) {
+            const float2 ob = s_blk[tok_c[i]][4 * kh + bk];
+            acc[i] += __builtin_fmaf(scale * xs_c[i], cbv[i] + ob.x, zp8 * ob.y);
+          }
         }
       }
-      acc = f32x4{accv[0], accv[1], accv[2], accv[3]};
     }
-    float* out = (mat ? ws.u : ws.h) + (int64_t)kh * P * F;
-    const int row = tile * MM_ROWS + n16;
-    const float accv[4] = {acc.x, acc.y, acc.z, acc.w};
+    // next item's loads go out before the exchange
+    const int next = it + 4;
+    if (next < i1) issue(next);
+    if (role > 0) red[quad][role - 1][lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    __syncthreads();
+    if (role == 0 && live) {
+      const f32x4 g1 = red[quad][0][lane], u0 = red[quad][1][lane], u1 = red[quad][2][lane];
+      const float gv[4] = {acc[0] + g1.x, acc[1] + g1.y, acc[2] + g1.z, acc[3] + g1.w};
+      const float uv[4] = {u0.x + u1.x, u0.y + u1.y, u0.z + u1.z, u0.w + u1.w};
+      const int row = tile * MM_ROWS + n16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * c + i;
-      if (m < n) out[(int64_t)G.gmem[u][m] * F + row] = accv[i];
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * c + i;
+        if (m < n) ws.h[(int64_t)G.gmem[u][m] * F + row] = silu_mul(gv[i], uv[i]);
+      }
     }
-    it += 16;
-    if (it < i1) issue(it);
+    __syncthreads();   // red is reused by the next round
+    it = next;
   }
   trace_point(ws.trace, TK_GATEUP, 5);
-  if (ws.trace) {   // diagnostics: when this workgroup's stores have completed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    trace_point(ws.trace, TK_GATEUP, 6);
-  }
 }
 
 // ====================================================================== down + combine
@@ -558,32 +634,24 @@ __global__ void __launch_bounds__(64 * DOWN_WAVES) down_mfma_kernel(ExpertArgs a
       }
     }
 
-    // 2. stage h = SiLU(g) * u of the members: 32 threads per member (half a
-    //    wave), thread s takes entries o = s + 32q (q < 2, block q), so the
-    //    32 threads read 1 KB contiguously; scale per member over its F values
+    // 2. stage h of the members: 32 threads per member (half a wave), thread
+    //    s takes entries o = s + 32q (q < 2, block q), so the 32 threads read
+    //    1 KB contiguously; scale per member over its F values
     {
       const int m = threadIdx.x >> 5, s = threadIdx.x & 31;
       const bool live = m < n;
       const int p = live ? G.gmem[u][m] : 0;
-      const int64_t half = (int64_t)B * k * F;   // gate/up outputs come in two K halves
       float v[2][8];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int64_t e0 = (int64_t)p * F + 8 * (s + 32 * q);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f}, uv = gv;
-          if (live) {
-            gv = *reinterpret_cast<const f32x4*>(ws.h + e0 + 4 * h) +
-                 *reinterpret_cast<const f32x4*>(ws.h + half + e0 + 4 * h);
-            uv = *reinterpret_cast<const f32x4*>(ws.u + e0 + 4 * h) +
-                 *reinterpret_cast<const f32x4*>(ws.u + half + e0 + 4 * h);
-          }
-          v[q][4 * h] = silu_mul(gv.x, uv.x);
-          v[q][4 * h + 1] = silu_mul(gv.y, uv.y);
-          v[q][4 * h + 2] = silu_mul(gv.z, uv.z);
-          v[q][4 * h + 3] = silu_mul(gv.w, uv.w);
+        f32x4 h0 = f32x4{0.f, 0.f, 0.f, 0.f}, h1 = h0;
+        if (live) {
+          h0 = *reinterpret_cast<const f32x4*>(ws.h + e0);
+          h1 = *reinterpret_cast<const f32x4*>(ws.h + e0 + 4);
         }
+        v[q][0] = h0.x; v[q][1] = h0.y; v[q][2] = h0.z; v[q][3] = h0.w;
+        v[q][4] = h1.x; v[q][5] = h1.y; v[q][6] = h1.z; v[q][7] = h1.w;
       }
       float am = 0.f;
 #pragma unroll
@@ -636,8 +704,7 @@ __global__ void __launch_bounds__(64 * DOWN_WAVES) down_mfma_kernel(ExpertArgs a
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            av[t][i] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (a_live) av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+            av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
           }
         f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -706,10 +773,22 @@ int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
 }
 
 int launch_route_batched(const RouteArgs& ra, const float* part, int32_t* idx_copy,
-                         float* wts_copy, uint32_t* err, hipStream_t s) {
-  BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, ra.idx_out, ra.wts_out,
-                   ra.logits_out, idx_copy, wts_copy, err, get_trace()};
-  hipLaunchKernelGGL(route_topk_kernel, dim3(ra.B), dim3(64), 0, s, r);
+                         float* wts_copy, uint8_t* xg, uint32_t* err, hipStream_t s) {
+  BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, ra.idx_out, ra.wts_out, ra.logits_out,
+                   idx_copy, wts_copy, err, get_trace(), ra.x, ra.ldx, ra.d, xg};
+  hipLaunchKernelGGL(route_topk_kernel<true>, dim3(ra.B), dim3(64), 0, s, r);
+  return (int)hipGetLastError();
+}
+
+int launch_stage_batched(const float* x, int64_t ldx, int B, int d, uint8_t* xg, hipStream_t s) {
+  BatchRouteArgs r{};
+  r.B = B;
+  r.x = x;
+  r.ldx = ldx;
+  r.d = d;
+  r.xg = xg;
+  r.trace = get_trace();
+  hipLaunchKernelGGL(route_topk_kernel<false>, dim3(B), dim3(64), 0, s, r);
   return (int)hipGetLastError();
 }
 
