@@ -74,9 +74,12 @@ extern "C" {
 #define HFQ4_DEV_ERR_NONFINITE 4u  /* a non-finite router logit was seen */
 
 /* Layer flags */
-#define HFQ4_LAYER_HOST_MAPPED 1u  /* expert weights live in pinned host memory [PCIE];
-                                      informational: the kernels read host and device
-                                      weights through the same code, with the same bits */
+#define HFQ4_LAYER_HOST_MAPPED 1u  /* expert weights live in pinned host memory [PCIE].
+                                      Results are bit-identical to the same layer in
+                                      HBM.  With one token the gate/up kernel also copies
+                                      the k selected down matrices into the workspace
+                                      while the link is busy, so the down pass reads HBM
+                                      (moe_workspace_bytes accounts for it). */
 
 /* Limits of this build */
 #define HFQ4_MAX_BATCH   16
@@ -151,7 +154,7 @@ int moe_route_topk(const float* Wr, const float* bias, int64_t E, int64_t d,
  *   down = (const uint8_t*)down + e*stride_down : HFQ4 [d rows][K = F]
  * Strides >= the matrix size (so gate and up may be interleaved).
  * flags: HFQ4_LAYER_HOST_MAPPED when the pointers are pinned host memory
- * [PCIE] (same kernels, same results: the reads simply cross PCIe). */
+ * [PCIE] (same results; the reads cross PCIe, see the flag above). */
 typedef struct moe_layer {
     const void* gate;
     const void* up;

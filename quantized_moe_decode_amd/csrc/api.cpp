@@ -104,8 +104,8 @@ int check_layer(const moe_layer* L) {
   return HFQ4_OK;
 }
 
-size_t ws_bytes_for(int64_t E, int B, int k, int64_t d, int64_t F) {
-  return hq::ws_layout(E, B, k, d, F).total;
+size_t ws_bytes_for(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags) {
+  return hq::ws_layout(E, B, k, d, F, flags).total;
 }
 
 int check_expert_io(const moe_layer* L, const float* x, int64_t ldx, int batch, const int32_t* idx,
@@ -223,7 +223,7 @@ int moe_route_workspace_bytes(int64_t E, int batch, size_t* out) {
   if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
   if (E < 1 || E > HFQ4_MAX_EXPERTS) return fail(HFQ4_E_INVALID, "E = %lld outside [1, %d]", (long long)E, HFQ4_MAX_EXPERTS);
   if (batch < 1 || batch > HFQ4_MAX_BATCH) return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
-  *out = ws_bytes_for(E, batch, 0, 0, 0);
+  *out = ws_bytes_for(E, batch, 0, 0, 0, 0);
   return ok();
 }
 
@@ -240,11 +240,11 @@ int moe_route_topk(const float* Wr, const float* bias, int64_t E, int64_t d, con
   if (ldx < d || (ldx & 3)) return fail(HFQ4_E_ALIGN, "ldx = %lld: need ldx >= d and ldx %% 4 == 0", (long long)ldx);
   if (!aligned16(Wr) || !aligned16(x)) return fail(HFQ4_E_ALIGN, "Wr and x must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
-  const size_t need = ws_bytes_for(E, batch, 0, 0, 0);
+  const size_t need = ws_bytes_for(E, batch, 0, 0, 0, 0);
   if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   int r = check_device();
   if (r) return r;
-  hq::Ws w = hq::ws_carve(ws, E, batch, 0, 0, 0);
+  hq::Ws w = hq::ws_carve(ws, E, batch, 0, 0, 0, 0);
   return hip_status(hq::launch_route(Wr, bias, (int)E, (int)d, x, ldx, batch, k, idx, wts, logits_out, w, stream),
                     "moe_route_topk launch");
 }
@@ -255,7 +255,7 @@ int moe_workspace_bytes(const moe_layer* L, int batch, int k, size_t* out) {
   if (r) return r;
   if (batch < 1 || batch > HFQ4_MAX_BATCH) return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
   if (k < 1 || k > HFQ4_MAX_TOPK || k > L->E) return fail(HFQ4_E_INVALID, "k = %d outside [1, min(E, %d)]", k, HFQ4_MAX_TOPK);
-  *out = ws_bytes_for(L->E, batch, k, L->d, L->F);
+  *out = ws_bytes_for(L->E, batch, k, L->d, L->F, L->flags);
   return ok();
 }
 
@@ -294,11 +294,11 @@ int moe_expert_decode(const moe_layer* L, const float* x, int64_t ldx, int batch
   if (r) return r;
   if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
-  const size_t need = ws_bytes_for(L->E, batch, k, L->d, L->F);
+  const size_t need = ws_bytes_for(L->E, batch, k, L->d, L->F, L->flags);
   if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   r = check_device();
   if (r) return r;
-  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->d, L->F);
+  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->d, L->F, L->flags);
   return hip_status(hq::launch_experts(to_dev(L), x, ldx, batch, idx, wts, k, residual, y, ldy, w, stream),
                     "moe_expert_decode launch");
 }
@@ -314,11 +314,11 @@ int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias, con
   if (r) return r;
   if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
-  const size_t need = ws_bytes_for(L->E, batch, k, L->d, L->F);
+  const size_t need = ws_bytes_for(L->E, batch, k, L->d, L->F, L->flags);
   if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   r = check_device();
   if (r) return r;
-  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->d, L->F);
+  hq::Ws w = hq::ws_carve(ws, L->E, batch, k, L->d, L->F, L->flags);
   return hip_status(hq::launch_layer(to_dev(L), Wr, bias, x, ldx, batch, k, idx, wts, residual, y, ldy, w, stream),
                     "moe_layer_decode launch");
 }

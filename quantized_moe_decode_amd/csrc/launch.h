@@ -41,6 +41,9 @@ struct Ws {
   float* wts;         // [B][k]
   float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
   uint8_t* xg;        // batched: [B][XG_STRIDE] staged activations; null otherwise
+  uint8_t* dstage;    // one token, host-mapped layer: [k][dslot] HBM copies of the
+                      // selected experts' down matrices; null otherwise
+  uint32_t dslot;     // bytes per staged down matrix
   float* ypart;       // [B*k][d] weighted expert outputs (batched path; null otherwise)
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
@@ -56,12 +59,14 @@ void set_trace(uint64_t* p);
 uint64_t* get_trace();
 void set_timing_events(void* start, void* stop);
 
-// Byte layout of a workspace for (E, B, k, d, F) (k = 0: routing only).
+// Byte layout of a workspace for (E, B, k, d, F, layer flags) (k = 0:
+// routing only).
+constexpr uint32_t LAYER_HOST_MAPPED = 1u;
 struct WsLayout {
-  size_t logits, idx, wts, h, xg, ypart, total;
+  size_t logits, idx, wts, h, xg, ypart, dstage, dslot, total;
 };
-WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F);
-Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F);
+WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
+Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
 
 int launch_pack(const float* w, int64_t rows, int64_t K, int64_t ldw, void* out, int32_t* bad,
                 hipStream_t s);

@@ -490,6 +490,32 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
     it += nw;
     if (it < items) issue(it);
   }
+  // Host-mapped layer, one token: copy the k selected experts' down
+  // matrices into the workspace (HBM), so that the down kernel reads them at
+  // HBM speed.  Waves that finish their gate/up items early start at once,
+  // which keeps the PCIe link busy through the tail of this kernel.
+  if (ws.dstage) {
+    const int per_slot = (int)(ws.dslot / 16);
+    const int total = k * per_slot;
+    const int nth = gridDim.x * blockDim.x;
+    const __amdgpu_buffer_rsrc_t rdn = make_rsrc(a.L.down, a.L.down_bytes);
+    for (int c0 = blockIdx.x * blockDim.x + threadIdx.x; c0 < total; c0 += 4 * nth) {
+      u32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ci = c0 + q * nth;
+        const int j = ci / per_slot, o = ci - j * per_slot;
+        const int e = ci < total ? s_idx[j] : -1;
+        v[q] = bload16(rdn, (e >= 0 && e < E) ? (uint32_t)(e * a.L.sd + (int64_t)o * 16)
+                                              : a.L.down_bytes);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ci = c0 + q * nth;
+        if (ci < total) *reinterpret_cast<u32x4*>(ws.dstage + (int64_t)ci * 16) = v[q];
+      }
+    }
+  }
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 5);
 }
@@ -517,7 +543,11 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 1);
   const int r0 = (blockIdx.x * (blockDim.x >> 6) + wv) * FAST_ROWS;
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  // host-mapped layer, one token: the selected down matrices were staged in
+  // HBM by the gate/up kernel, slot j at j * dslot
+  const bool staged = ws.dstage != nullptr;
+  const uint32_t dbytes = staged ? ws.dslot * (uint32_t)k : a.L.down_bytes;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(staged ? ws.dstage : a.L.down, dbytes);
   const uint32_t hoff = (uint32_t)((s >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (s & 7);
   for (int b = 0; b < B; ++b) {
@@ -542,8 +572,10 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
       const int e = j < k ? s_e[b * k + j] : -1;
       w[t] = e >= 0 ? s_w[b * k + j] : 0.f;
       // dead slots read past the end of the descriptor and get zeros
-      const uint32_t base = (e >= 0 && r0 < d) ? (uint32_t)(e * a.L.sd + (int64_t)r0 * ROWB)
-                                               : a.L.down_bytes;
+      const uint32_t base = (e >= 0 && r0 < d)
+                                ? (staged ? (uint32_t)(j * ws.dslot + (int64_t)r0 * ROWB)
+                                          : (uint32_t)(e * a.L.sd + (int64_t)r0 * ROWB))
+                                : dbytes;
 #pragma unroll
       for (int r = 0; r < FAST_ROWS; ++r) {
         hd[t][r] = bload8(rd, base + r * ROWB + hoff);
@@ -607,7 +639,7 @@ void set_timing_events(void* start, void* stop) {
   g_ev_stop = static_cast<hipEvent_t>(stop);
 }
 
-WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F) {
+WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags) {
   WsLayout l{};
   size_t o = WS_HEADER;
   l.logits = o;   // batched calls keep LG_KS partial logit sets
@@ -624,12 +656,17 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F) {
     l.ypart = o;
     o = al256(o + sizeof(float) * (size_t)B * k * d);
   }
+  if (B == 1 && k > 0 && (flags & LAYER_HOST_MAPPED)) {   // staged down matrices
+    l.dslot = (size_t)d * ((F + BLK - 1) / BLK) * BLK_BYTES;
+    l.dstage = o;
+    o = al256(o + l.dslot * k);
+  }
   l.total = o;
   return l;
 }
 
-Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F) {
-  const WsLayout l = ws_layout(E, B, k, d, F);
+Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags) {
+  const WsLayout l = ws_layout(E, B, k, d, F, flags);
   uint8_t* p = static_cast<uint8_t*>(base);
   Ws w;
   w.err = reinterpret_cast<uint32_t*>(p);
@@ -639,6 +676,8 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F) {
   w.wts = reinterpret_cast<float*>(p + l.wts);
   w.h = reinterpret_cast<float*>(p + l.h);
   w.xg = l.xg ? p + l.xg : nullptr;
+  w.dstage = l.dstage ? p + l.dstage : nullptr;
+  w.dslot = (uint32_t)l.dslot;
   w.ypart = l.ypart ? reinterpret_cast<float*>(p + l.ypart) : nullptr;
   w.trace = get_trace();
   return w;

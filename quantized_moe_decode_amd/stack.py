@@ -13,7 +13,7 @@ reads cross PCIe (hipfire expert-offload explainer, section "PCIe 直通").
 
 import synth
 
-from . import hfq4_gemv, hfq4_pack, moe_layer_decode, new_workspace
+from . import hfq4_gemv, hfq4_pack, moe_layer_decode, moe_workspace_bytes, new_workspace
 from .synthetic import build_layer
 
 
@@ -27,7 +27,10 @@ class Stack:
         d = layers[0].d
         self.d = d
         self.buf = [torch.empty((batch, d), dtype=torch.float32, device=device) for _ in range(2)]
-        self.ws = new_workspace(max(layers, key=lambda L: L.E), batch, k, device)
+        # one workspace serves every layer: size it for the largest need
+        # (host-mapped layers also stage their selected down matrices)
+        big = max(layers, key=lambda L: moe_workspace_bytes(L, batch, k))
+        self.ws = new_workspace(big, batch, k, device)
         self.idx = torch.empty((batch, k), dtype=torch.int32, device=device)
         self.wts = torch.empty((batch, k), dtype=torch.float32, device=device)
 
