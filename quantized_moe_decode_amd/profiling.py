@@ -110,7 +110,7 @@ if __name__ == "__main__":
         v = trace_durations(sys.argv[2], sys.argv[3])
         n = int(sys.argv[4])
         tail = v[-n:]
-        print("%s: %d dispatches, avg %.3f us; last %d (the stamped ones): avg %.3f us, "
+        print("%s: %d dispatches, avg %.3f us; last %d: avg %.3f us, "
               "median %.3f us" % (sys.argv[3], len(v), sum(v) / len(v), len(tail),
                                   sum(tail) / len(tail), sorted(tail)[len(tail) // 2]))
     elif sys.argv[1] == "traffic":
