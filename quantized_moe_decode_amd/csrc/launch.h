@@ -40,15 +40,13 @@ struct Ws {
   int32_t* idx;       // [B][k]  routing (internal copy)
   float* wts;         // [B][k]
   float* h;           // [B*k][F] SiLU(gate)*up per (token, slot)
-  uint8_t* xg;        // batched: [B][XG_STRIDE] staged activations; null otherwise
   uint8_t* dstage;    // one token, host-mapped layer: [k][dslot] HBM copies of the
                       // selected experts' down matrices; null otherwise
   uint32_t dslot;     // bytes per staged down matrix
-  float* ypart;       // [B*k][d] weighted expert outputs (batched path; null otherwise)
+  GroupTab* gtab;     // batched: the token groups, published by the gate/up kernel
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
 };
 constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
-constexpr int XG_STRIDE = 4224;    // bytes per staged token of the batched path
 constexpr int WS_COUNTERS = 240;
 
 // Phase tracing: when a trace buffer is registered, thread 0 of every
@@ -63,7 +61,7 @@ void set_timing_events(void* start, void* stop);
 // routing only).
 constexpr uint32_t LAYER_HOST_MAPPED = 1u;
 struct WsLayout {
-  size_t logits, idx, wts, h, xg, ypart, dstage, dslot, total;
+  size_t logits, idx, wts, h, gtab, dstage, dslot, total;
 };
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
 Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);

@@ -650,11 +650,9 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags
   o = al256(o + sizeof(float) * (size_t)B * k);
   l.h = o;
   o = al256(o + sizeof(float) * (size_t)B * k * F);
-  if (B >= 2 && k > 0) {          // batched expert path
-    l.xg = o;
-    o = al256(o + (size_t)XG_STRIDE * B);
-    l.ypart = o;
-    o = al256(o + sizeof(float) * (size_t)B * k * d);
+  if (B >= 2 && k > 0) {          // batched expert path: the token groups
+    l.gtab = o;
+    o = al256(o + sizeof(GroupTab));
   }
   if (B == 1 && k > 0 && (flags & LAYER_HOST_MAPPED)) {   // staged down matrices
     l.dslot = (size_t)d * ((F + BLK - 1) / BLK) * BLK_BYTES;
@@ -675,10 +673,9 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t 
   w.idx = reinterpret_cast<int32_t*>(p + l.idx);
   w.wts = reinterpret_cast<float*>(p + l.wts);
   w.h = reinterpret_cast<float*>(p + l.h);
-  w.xg = l.xg ? p + l.xg : nullptr;
   w.dstage = l.dstage ? p + l.dstage : nullptr;
+  w.gtab = l.gtab ? reinterpret_cast<GroupTab*>(p + l.gtab) : nullptr;
   w.dslot = (uint32_t)l.dslot;
-  w.ypart = l.ypart ? reinterpret_cast<float*>(p + l.ypart) : nullptr;
   w.trace = get_trace();
   return w;
 }
@@ -700,7 +697,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
   if (B >= 2) {
     if (int e = launch_logits_batched(a, ws.logits, s)) return e;
-    return launch_route_batched(a, ws.logits, nullptr, nullptr, nullptr, ws.err, s);
+    return launch_route_batched(a, ws.logits, ws.err, s);
   }
   hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
@@ -781,10 +778,7 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
                    hipStream_t s) {
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
   if (fast_shape(L.d, L.F, k)) {
-    if (B >= 2) {
-      if (int e = launch_stage_batched(x, ldx, B, L.d, ws.xg, s)) return e;
-      return launch_experts_batched(a, ws, num_cus(), s);
-    }
+    if (B >= 2) return launch_experts_batched(a, ws, num_cus(), nullptr, s);
     return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
   }
   return launch_generic_experts(a, ws, s);
@@ -796,14 +790,14 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
   RouteArgs ra{Wr, bias, L.E, L.d, x, ldx, B, k, idx, wts, nullptr};
   const bool fast = fast_shape(L.d, L.F, k);
   if (B >= 2) {
-    // same routing kernels as moe_route_topk, so the two-call path gives
-    // the same bits
+    // the same router and routing functions as moe_route_topk, so the
+    // two-call path gives the same bits; on the fast shape the gate/up
+    // kernel routes the tokens itself
     if (int e = launch_logits_batched(ra, ws.logits, s)) return e;
-    if (int e = launch_route_batched(ra, ws.logits, nullptr, nullptr, fast ? ws.xg : nullptr,
-                                     ws.err, s))
-      return e;
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
-    return fast ? launch_experts_batched(a, ws, num_cus(), s) : launch_generic_experts(a, ws, s);
+    if (fast) return launch_experts_batched(a, ws, num_cus(), &ra, s);
+    if (int e = launch_route_batched(ra, ws.logits, ws.err, s)) return e;
+    return launch_generic_experts(a, ws, s);
   }
   hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(256), 0, s, ra, ws.logits, ws.trace);
   int err = (int)hipGetLastError();

@@ -47,13 +47,12 @@ __host__ __device__ inline bool fast_shape(int d, int F, int k) {
 // Batched path (2 <= B <= 16) on MFMA matrix cores.
 constexpr int LG_KS = 4;   // K splits of the batched router GEMV (partial logit sets)
 int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
-// Top-k and weights from the partial logits, one wave per token; with xg
-// set, each token's activations are also staged there (fast shape).
-int launch_route_batched(const RouteArgs& ra, const float* part, int32_t* idx_copy,
-                         float* wts_copy, uint8_t* xg, uint32_t* err, hipStream_t s);
-// Only the activation staging (caller-supplied routing).
-int launch_stage_batched(const float* x, int64_t ldx, int B, int d, uint8_t* xg, hipStream_t s);
-// gate/up, down and combine for the fast shape (token groups built in-kernel).
-int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s);
+// Top-k and weights from the partial logits, one wave per token (routing
+// only).
+int launch_route_batched(const RouteArgs& ra, const float* part, uint32_t* err, hipStream_t s);
+// gate/up then down for the fast shape (token groups built in-kernel); with
+// ra set, the gate/up kernel also routes the tokens from the partial logits
+// in ws.logits and publishes idx / wts to ra's outputs.
+int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, const RouteArgs* ra, hipStream_t s);
 
 }  // namespace hq

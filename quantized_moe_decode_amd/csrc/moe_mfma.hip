@@ -18,9 +18,11 @@
 // both operands alike.  Weights enter as 1024 + q (1024 + 16q for odd
 // nibbles) straight from the bit trick of the VALU path; per block and
 // column the 1024 terms and the zero point are folded back in the epilogue:
-//   sum_i w_i x_i = scale * xs * (C + off) + (zero + 8 scale) * sum_i x_i
-// with off = -(1024 * sum of the stored halves + 8 * sum of the f16 values
-// they stand for) and xs the column's power-of-two scale.  Each block's
+//   sum_i w_i x_i = scale * xs * (C + off) + (zero + 8 scale) * sx
+// with Sa = sum of the stored halves, S16 = sum of the values they stand
+// for (odd pairs x16), off = -(1024 Sa + 8 S16), sx = xs * S16 and xs the
+// column's power-of-two scale.  Sa and S16 come from one more MFMA chain
+// per block against constant B rows, once per staged column.  Each block's
 // product starts from a zero accumulator, so scale and zero apply exactly.
 //
 // Kernels (one HIP graph node each; kernel boundaries are the only
@@ -28,21 +30,20 @@
 //   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32):
 //                        16 experts x 16 tokens per tile, K split over 4
 //                        workgroups x 4 waves; writes 4 partial logit sets.
-//   route_topk_kernel    one wave per token (each on its own CU): partial
-//                        sums + bias, top-k and weights, and the token's
-//                        activations staged once in the MFMA operand format.
-//                        The expert kernels group the (token, slot) pairs by
-//                        expert themselves.
-//   gateup_mfma_kernel   items of (group, 16 rows) in contiguous runs per
-//                        workgroup; a quad of waves computes gate and up over
-//                        both K halves, reduces through LDS and writes
-//                        h = SiLU(g) * u.  The workgroup copies in only the
-//                        staged activations of the tokens its groups need.
-//   down_mfma_kernel     work items of (group, 256 output rows): stages
-//                        h of the group's pairs, writes
-//                        w_p * (down h_p) per pair.
-//   combine_kernel       y[b] = residual[b] + sum over the k slots of token b,
-//                        in slot order.
+//   gateup_mfma_kernel   one wave per token routes it from the partial
+//                        logits (sums + bias, top-k, weights) and stages its
+//                        activations in LDS in the MFMA operand format; the
+//                        (token, slot) pairs are grouped by expert; items of
+//                        (group, 16 rows) in contiguous runs per workgroup,
+//                        a quad of waves computes gate and up over both K
+//                        halves, reduces through LDS and writes
+//                        h = SiLU(g) * u.
+//   route_topk_kernel    routing only (moe_route_topk): the same routing
+//                        functions, one single-wave workgroup per token.
+//   down_rows_kernel     16 output rows of every token per workgroup: stages
+//                        h of all pairs, runs every group's down tile and
+//                        sums w_p * (down h_p) over the slots onto the
+//                        residual (no per-slot buffer, no combine kernel).
 #include "hfq4_device.h"
 #include "launch.h"
 #include "moe_common.h"
@@ -55,9 +56,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 constexpr int XT_STRIDE = 4096 + 16;   // bytes per staged token (256 entries of 16 B + pad)
 constexpr int HT_STRIDE = 1024 + 16;   // bytes per staged h vector (64 entries + pad)
 constexpr int MM_ROWS = 16;            // rows per item
-constexpr int DOWN_TILES = 2;          // 16-row tiles per wave in the down kernel
-constexpr int DOWN_WAVES = 8;          // waves per down workgroup
-constexpr int DOWN_CHUNK = 16 * DOWN_TILES * DOWN_WAVES;   // output rows per down work item
 
 // Code dword -> B operand: 1024+q0, 1024+q4, 1024+16q1, 1024+16q5,
 // 1024+q2, 1024+q6, 1024+16q3, 1024+16q7.
@@ -108,24 +106,49 @@ __device__ __forceinline__ float pow2_scale(float amax, float& xs) {
 }
 
 // Write the 8 elements of one code dword's entry (scaled by inv) as 16 B at
-// dst in the order dec8 produces -- pair q holds elements q and q+4, odd
-// pairs divided by 16 -- and add to (sum of the stored halves, sum of the
-// f16 values they stand for).
-__device__ __forceinline__ void put_entry(const float* v, float inv, uint8_t* dst, float& sh,
-                                          float& s16) {
-  h2 p[4];
+// dst in the order dec8 produces: pair q holds elements q and q+4, odd pairs
+// divided by 16.
+__device__ __forceinline__ void put_entry(const float* v, float inv, uint8_t* dst) {
+  const float i16 = inv * 0.0625f;
+  const h2 p0 = {(_Float16)(v[0] * inv), (_Float16)(v[4] * inv)};
+  const h2 p1 = {(_Float16)(v[1] * i16), (_Float16)(v[5] * i16)};
+  const h2 p2 = {(_Float16)(v[2] * inv), (_Float16)(v[6] * inv)};
+  const h2 p3 = {(_Float16)(v[3] * i16), (_Float16)(v[7] * i16)};
+  *reinterpret_cast<u32x4*>(dst) = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
+}
+
+// Per-block sums of staged operand rows on the matrix cores.  For up to 16
+// rows (row n16 of the A operand at base + n16 * stride, in the layout
+// put_entry writes; rows >= nrows repeat row 0 and their sums are
+// meaningless) and block bk (32 entries), a chain of 8 MFMAs against a
+// constant B -- row 0 all ones, row 1 the pattern 1, 1, 16, 16 (the values
+// the stored halves stand for), other rows zero -- gives Sa = sum of the
+// stored halves and S16 = sum of the values they stand for.  Lanes (c, 1)
+// end with (Sa, S16) of rows 4c..4c+3 in sa[i], s16[i].  With them,
+// sum_i w_i v_i = xs (scale (C - 1024 Sa) + zero S16) for the block's
+// dequantized weights w and the row's values v = xs * (stored halves).
+__device__ __forceinline__ void block_sums_mfma(const uint8_t* base, int stride, int nrows, int bk,
+                                                float* sa, float* s16) {
+  const int lane = threadIdx.x & 63, n16 = lane & 15, c = lane >> 4;
+  const _Float16 o1 = n16 < 2 ? (_Float16)1.f : (_Float16)0.f;
+  const _Float16 o16 = n16 == 0 ? (_Float16)1.f : n16 == 1 ? (_Float16)16.f : (_Float16)0.f;
+  const h8 bpat = {o1, o1, o16, o16, o1, o1, o16, o16};
+  const uint8_t* arow = base + (n16 < nrows ? n16 : 0) * stride + 16 * (4 * c);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const bool hi = q & 1;
-    const float s = hi ? 0.0625f : 1.0f;
-    const _Float16 a = (_Float16)(v[q] * inv * s), b = (_Float16)(v[q + 4] * inv * s);
-    p[q] = h2{a, b};
-    const float fa = (float)a, fb = (float)b;
-    sh += fa + fb;
-    s16 += hi ? 16.f * (fa + fb) : (fa + fb);
-  }
-  const u32x4 e = {as_u32(p[0]), as_u32(p[1]), as_u32(p[2]), as_u32(p[3])};
-  *reinterpret_cast<u32x4*>(dst) = e;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = mfma16(*reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i)), bpat, acc);
+  const int src = lane & ~15;   // lane (c, 0) holds Sa
+  sa[0] = __shfl(acc.x, src, 64);
+  sa[1] = __shfl(acc.y, src, 64);
+  sa[2] = __shfl(acc.z, src, 64);
+  sa[3] = __shfl(acc.w, src, 64);
+  s16[0] = acc.x;
+  s16[1] = acc.y;
+  s16[2] = acc.z;
+  s16[3] = acc.w;
 }
 
 // Deterministic token groups from the k selections of B tokens (in LDS):
@@ -142,7 +165,7 @@ struct GroupScratch {
 };
 
 __device__ void build_groups_mm(const int* s_idx, int P, int k, int E, GroupTab& G,
-                                GroupScratch& S, uint32_t* err, bool report) {
+                                GroupScratch& S, uint32_t* err, bool report, bool may_repeat) {
   const int t = threadIdx.x;
   for (int i = t; i < E; i += blockDim.x) S.first[i] = 0x7FFFFFFF;
   if (t < GT_MAXU) S.tokmask[t] = 0u;
@@ -157,7 +180,8 @@ __device__ void build_groups_mm(const int* s_idx, int P, int k, int E, GroupTab&
                               __HIP_MEMORY_SCOPE_AGENT);
       e = -1;
     } else {
-      for (int q = t - t % k; q < t; ++q) repeat |= (s_idx[q] == e);
+      if (may_repeat)
+        for (int q = t - t % k; q < t; ++q) repeat |= (s_idx[q] == e);
       if (!repeat) atomicMin(&S.first[e], t);
     }
   }
@@ -261,10 +285,6 @@ struct BatchRouteArgs {
   float* wts_copy;
   uint32_t* err;
   uint64_t* trace;
-  const float* x;         // [B][ldx] activations to stage, or null
-  int64_t ldx;
-  int d;
-  uint8_t* xg;            // [B][XG_STRIDE] staged activations (see stage_token)
 };
 
 template <int PER>
@@ -291,9 +311,12 @@ __device__ __forceinline__ void route_load(const BatchRouteArgs& r, int b, Route
   }
 }
 
-// Sum, top-k and weights of one token from its loads.
+// Sum, top-k and weights of one token from its loads.  The selection goes
+// to s_idx / s_w (LDS, when given); the global outputs, the logits and the
+// error bit are written only when `write` is set.
 template <int PER>
-__device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER>& L, float* lg) {
+__device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER>& L, float* lg,
+                            int* s_idx, float* s_w, bool write) {
   const int lane = threadIdx.x & 63;
   // lane l sums expert 64c + l over the partial sets (+ bias) into LDS; the
   // top-k then reads its own PER consecutive experts
@@ -306,7 +329,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER
 #pragma unroll
       for (int p = 0; p < LG_KS; ++p) l += as_f32(L.raw[p][c]);
       if (r.bias) l += as_f32(L.rb[c]);
-      if (r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
+      if (write && r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
       lg[e] = l;
       nan_seen |= __builtin_isnan(l);
     }
@@ -326,27 +349,30 @@ __device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER
   trace_point(r.trace, TK_TOPK, 3);
   if (lane < r.k) {
     const int p = b * r.k + lane;
-    r.idx_out[p] = e;
-    r.wts_out[p] = w;
-    if (r.idx_copy) {
-      r.idx_copy[p] = e;
-      r.wts_copy[p] = w;
+    if (s_idx) {
+      s_idx[p] = e;
+      s_w[p] = w;
+    }
+    if (write) {
+      r.idx_out[p] = e;
+      r.wts_out[p] = w;
+      if (r.idx_copy) {
+        r.idx_copy[p] = e;
+        r.wts_copy[p] = w;
+      }
     }
   }
-  if (__any(nan_seen) && lane == 0)
+  if (write && __any(nan_seen) && lane == 0)
     __hip_atomic_fetch_or(r.err, 4u /*HFQ4_DEV_ERR_NONFINITE*/, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stage one token's activations (one wave) into the MFMA A-operand format
-// at dst: 256 entries of 16 B (entry o = elements 8o..8o+7 scaled by 2^-e,
-// in dec8 order), then per block (off, sx) as 8 float2, then xs = 2^e.
-// Lane l takes entries o = l + 64m, so one load instruction covers 2 KB of
-// x; entry o belongs to block o / 32 (2m for lanes 0-31, 2m+1 above).
-constexpr int XG_ENTRIES = 4096, XG_BLK = 4096, XG_XS = 4096 + 64;
-static_assert(XG_STRIDE >= XG_XS + 4, "staged token layout");
-
-__device__ void stage_token(const float* __restrict__ xb, int d, uint8_t* dst) {
+// Stage one token's activations (one wave) in the MFMA A-operand format:
+// 256 entries of 16 B at ent (entry o = elements 8o..8o+7 scaled by 2^-e,
+// in dec8 order) and xs = 2^e (the per-block sums come from
+// block_sums_mfma).  Lane l takes entries o = l + 64m, so one load
+// instruction covers 2 KB of x and one LDS store 1 KB.
+__device__ void stage_token(const float* __restrict__ xb, int d, uint8_t* ent, float* xs_out) {
   const int lane = threadIdx.x & 63;
   float v[4][8];
 #pragma unroll
@@ -365,59 +391,30 @@ __device__ void stage_token(const float* __restrict__ xb, int d, uint8_t* dst) {
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[m][i]));
   float xs;
   const float inv = pow2_scale(wave_max_f(am), xs);
-  float2* blk = reinterpret_cast<float2*>(dst + XG_BLK);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float sh = 0.f, s16 = 0.f, sx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sx += v[m][i];
-    put_entry(v[m], inv, dst + XG_ENTRIES * 0 + 16 * (lane + 64 * m), sh, s16);
-    // block sums over 32 lanes, fixed order
-    sh = row_sum16(sh);
-    s16 = row_sum16(s16);
-    sx = row_sum16(sx);
-    const float lo_sh = lane_bcast(sh, 0) + lane_bcast(sh, 16);
-    const float hi_sh = lane_bcast(sh, 32) + lane_bcast(sh, 48);
-    const float lo_16 = lane_bcast(s16, 0) + lane_bcast(s16, 16);
-    const float hi_16 = lane_bcast(s16, 32) + lane_bcast(s16, 48);
-    const float lo_sx = lane_bcast(sx, 0) + lane_bcast(sx, 16);
-    const float hi_sx = lane_bcast(sx, 32) + lane_bcast(sx, 48);
-    if (lane == 0) {
-      blk[2 * m] = make_float2(-(1024.f * lo_sh + 8.f * lo_16), lo_sx);
-      blk[2 * m + 1] = make_float2(-(1024.f * hi_sh + 8.f * hi_16), hi_sx);
-    }
-  }
-  if (lane == 0) *reinterpret_cast<float*>(dst + XG_XS) = xs;
+  for (int m = 0; m < 4; ++m) put_entry(v[m], inv, ent + 16 * (lane + 64 * m));
+  if (lane == 0) *xs_out = xs;
 }
 
-// One single-wave workgroup per token: partial sums + bias, top-k, weights
-// (WITH_TOPK), and the token's activations staged for the expert kernels
-// (when r.xg is set).  Tokens run on different CUs in parallel; the expert
-// kernels build the token groups themselves from the indices
-// (deterministically, so every workgroup sees the same groups).
-template <bool WITH_TOPK>
+// Routing only (the two-call form): one single-wave workgroup per token,
+// partial sums + bias, top-k and weights.  The fused layer runs the same
+// two functions inside the gate/up kernel, so both forms give the same bits.
 __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
   __shared__ float lg[HFQ4_MAXE_DEV];
   trace_point(r.trace, TK_TOPK, 0);
   const int b = blockIdx.x;
-  // the routing loads go out first, the activation staging overlaps them
-  if (!WITH_TOPK) {
-    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
-  } else if (r.E <= 256) {
+  if (r.E <= 256) {
     RouteLoads<4> L;
     route_load<4>(r, b, L);
-    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
-    route_token<4>(r, b, L, lg);
+    route_token<4>(r, b, L, lg, nullptr, nullptr, true);
   } else if (r.E <= 512) {
     RouteLoads<8> L;
     route_load<8>(r, b, L);
-    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
-    route_token<8>(r, b, L, lg);
+    route_token<8>(r, b, L, lg, nullptr, nullptr, true);
   } else {
     RouteLoads<16> L;
     route_load<16>(r, b, L);
-    if (r.xg) stage_token(r.x + (int64_t)b * r.ldx, r.d, r.xg + (int64_t)b * XG_STRIDE);
-    route_token<16>(r, b, L, lg);
+    route_token<16>(r, b, L, lg, nullptr, nullptr, true);
   }
   trace_point(r.trace, TK_TOPK, 1);
 }
@@ -428,41 +425,88 @@ __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
 // item at a time: its waves compute gate K-half 0, gate K-half 1, up K-half
 // 0 and up K-half 1 (4 blocks each, all loads in flight at once), the
 // partial tiles meet in LDS, and the first wave writes h = SiLU(g) * u.
-__global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) {
-  extern __shared__ __align__(16) uint8_t xt[];      // [B][XT_STRIDE]
+// Before that, wave b < B stages token b's activations in LDS and, with
+// FROM_LOGITS, routes token b from the router's partial logits (every
+// workgroup routes every token, so no launch sits between the router and
+// the experts; workgroup 0 publishes the routing).
+template <bool FROM_LOGITS>
+__global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, BatchRouteArgs r) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  uint8_t* xt = dyn;                                                     // [B][XT_STRIDE]
+  float* lg = reinterpret_cast<float*>(dyn + (size_t)a.B * XT_STRIDE);   // [B][E] (routing)
   __shared__ GroupTab G;
   __shared__ GroupScratch GS;
   __shared__ int s_idx[MAXP];
+  __shared__ float s_wt[MAXP];
   __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
   __shared__ float s_xs[HFQ4_MAXB_DEV];
-  __shared__ uint32_t s_need;
   __shared__ f32x4 red[4][3][64];                    // partial tiles of roles 1..3
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int quad = wv >> 2, role = wv & 3;
-  const int B = a.B, k = a.k, P = B * k, F = a.L.F;
+  const int B = a.B, k = a.k, P = B * k, F = a.L.F, E = a.L.E;
   trace_point(ws.trace, TK_GATEUP, 0);
-  if ((int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
+
+  // 1. one wave per token: routing loads first, then the activations
+  //    (their loads overlap the routing loads), then top-k
+  if (wv < B) {
+    const float* xb = a.x + (int64_t)wv * a.ldx;
+    uint8_t* xe = xt + wv * XT_STRIDE;
+    if (FROM_LOGITS) {
+      const bool pub = blockIdx.x == 0;
+      float* lgw = lg + (size_t)wv * E;
+      if (E <= 256) {
+        RouteLoads<4> L;
+        route_load<4>(r, wv, L);
+        stage_token(xb, a.L.d, xe, &s_xs[wv]);
+        route_token<4>(r, wv, L, lgw, s_idx, s_wt, pub);
+      } else if (E <= 512) {
+        RouteLoads<8> L;
+        route_load<8>(r, wv, L);
+        stage_token(xb, a.L.d, xe, &s_xs[wv]);
+        route_token<8>(r, wv, L, lgw, s_idx, s_wt, pub);
+      } else {   // 16 loads per lane: route first, then stage
+        RouteLoads<16> L;
+        route_load<16>(r, wv, L);
+        route_token<16>(r, wv, L, lgw, s_idx, s_wt, pub);
+        stage_token(xb, a.L.d, xe, &s_xs[wv]);
+      }
+    } else {
+      stage_token(xb, a.L.d, xe, &s_xs[wv]);
+    }
+  }
+  if (!FROM_LOGITS && (int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
-  build_groups_mm(s_idx, P, k, a.L.E, G, GS, ws.err, blockIdx.x == 0);
+  trace_point(ws.trace, TK_GATEUP, 2);
+  // per-block sums of the staged tokens: wave w < 8 takes block w
+  if (wv < 8) {
+    float sa[4], sv[4];
+    block_sums_mfma(xt, XT_STRIDE, B, wv, sa, sv);
+    if ((lane & 15) == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * (lane >> 4) + i;
+        if (b < B) s_blk[b][wv] = make_float2(-(1024.f * sa[i] + 8.f * sv[i]), s_xs[b] * sv[i]);
+      }
+    }
+  }
+  // routing from top-k holds k distinct experts per token
+  build_groups_mm(s_idx, P, k, E, G, GS, ws.err, !FROM_LOGITS && blockIdx.x == 0, !FROM_LOGITS);
+  // workgroup 0 publishes the table for the down kernel
+  if (blockIdx.x == 0) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&G);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(ws.gtab);
+    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  }
   trace_point(ws.trace, TK_GATEUP, 1);
 
-  // 1. this workgroup's items: a contiguous run of (group, 16-row tile)
+  // 2. this workgroup's items: a contiguous run of (group, 16-row tile)
   const int tiles = F / MM_ROWS;                 // 32
   const int items = G.U * tiles;
   const int per = (items + gridDim.x - 1) / gridDim.x;
   const int i0 = blockIdx.x * per;
   const int i1 = min(items, i0 + per);
-  if (threadIdx.x == 0) {
-    uint32_t m = 0;
-    if (i0 < i1)
-      for (int u = i0 / tiles; u <= (i1 - 1) / tiles; ++u) {
-        for (int q = 0; q < G.gcnt[u]; ++q) m |= 1u << (G.gmem[u][q] / k);
-      }
-    s_need = m;
-  }
-  __syncthreads();
 
-  // 2. the wave's first item: its role's 4 blocks, every load in flight
+  // 3. the wave's first item: its role's 4 blocks, every load in flight
   constexpr int64_t ROWB = 8 * BLK_BYTES;
   const int n16 = lane & 15, c = lane >> 4;
   const int mat = role >> 1, kh = role & 1;
@@ -482,39 +526,8 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
       cd[bk][1] = bload16(rs, rowoff + bk * BLK_BYTES + 8 + 64 + 16 * c);
     }
   };
-  // 3. the needed tokens' staged activations: every 16-byte chunk load in
-  //    flight first (ahead of the weights in the memory queue), then the
-  //    first item's weight loads, then the chunks go to LDS
-  constexpr int XG_CHUNKS = (XG_XS + 4 + 15) / 16;   // 261 chunks of a staged token
-  constexpr int XG_ITERS = (HFQ4_MAXB_DEV * XG_CHUNKS + 1023) / 1024;
-  u32x4 xc[XG_ITERS];
-  const uint32_t need = s_need;
-#pragma unroll
-  for (int j = 0; j < XG_ITERS; ++j) {
-    const int ci = threadIdx.x + 1024 * j;
-    const int tb = ci / XG_CHUNKS, ch = ci - tb * XG_CHUNKS;
-    xc[j] = u32x4{0u, 0u, 0u, 0u};
-    if (tb < B && ((need >> tb) & 1u))
-      xc[j] = *reinterpret_cast<const u32x4*>(ws.xg + (int64_t)tb * XG_STRIDE + 16 * ch);
-  }
   int it = i0 + quad;
   if (it < i1) issue(it);
-#pragma unroll
-  for (int j = 0; j < XG_ITERS; ++j) {
-    const int ci = threadIdx.x + 1024 * j;
-    const int tb = ci / XG_CHUNKS, ch = ci - tb * XG_CHUNKS;
-    if (tb < B && ((need >> tb) & 1u)) {
-      if (ch < 256) {
-        *reinterpret_cast<u32x4*>(xt + tb * XT_STRIDE + 16 * ch) = xc[j];
-      } else if (ch < 260) {   // (off, sx) of blocks 2(ch-256), 2(ch-256)+1
-        s_blk[tb][2 * (ch - 256)] = make_float2(as_f32(xc[j].x), as_f32(xc[j].y));
-        s_blk[tb][2 * (ch - 256) + 1] = make_float2(as_f32(xc[j].z), as_f32(xc[j].w));
-      } else {
-        s_xs[tb] = as_f32(xc[j].x);
-      }
-    }
-  }
-  __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 3);
 
   // 4. rounds of one item per quad (uniform trip count: every wave meets
@@ -596,172 +609,201 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws) 
 
 // ====================================================================== down + combine
 
-__global__ void __launch_bounds__(64 * DOWN_WAVES) down_mfma_kernel(ExpertArgs a, Ws ws) {
-  __shared__ __align__(16) uint8_t ht[GT_MAXM * HT_STRIDE];   // [member][HT_STRIDE]
-  __shared__ float2 s_blk[GT_MAXM][2];
-  __shared__ float s_xs[GT_MAXM];
-  __shared__ GroupTab G;
-  __shared__ GroupScratch GS;
-  __shared__ int s_idx[MAXP];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int B = a.B, k = a.k, d = a.L.d, F = a.L.F;
-  if ((int)threadIdx.x < B * k) s_idx[threadIdx.x] = a.idx[threadIdx.x];
-  __syncthreads();
-  build_groups_mm(s_idx, B * k, k, a.L.E, G, GS, ws.err, false);
-  const int nch = (d + DOWN_CHUNK - 1) / DOWN_CHUNK;
-  const int U = G.U;
-  const int items = U * nch;
-  constexpr int64_t ROWB = 2 * BLK_BYTES;
-  const int n16 = lane & 15, c = lane >> 4;
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
-  trace_point(ws.trace, TK_DOWN, 0);
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int u = it / nch, ch = it - u * nch;
-    const int n = G.gcnt[u], e = G.gexp[u];
+// A workgroup owns DR_ROWS = 16 output rows of every token.  It stages h of
+// all (token, slot) pairs once (f16 in the MFMA operand order, one
+// power-of-two scale per pair), then its 16 waves take the expert groups in
+// turn (wave w: groups w, w + 16, ...): per group one 16-row MFMA tile over
+// K = F, A = the group's pairs, B = 16 rows of the expert's down matrix,
+// with the next group's weights in flight while the current one computes.
+// Each wave adds w_p * (down h_p) into its own [token][row] slice of LDS;
+// at the end the slices are summed in wave order onto the residual.  The
+// per-slot sum therefore needs no second kernel and no per-slot buffer.
+constexpr int DR_ROWS = 16;
+constexpr int DR_WAVES = 16;
+constexpr int DR_PAIRS_PER_PASS = 64 * DR_WAVES / 16;   // 16 threads per pair
 
-    // 1. weight loads: wave wv owns rows ch*DOWN_CHUNK + 16*DOWN_TILES*wv .. (DOWN_TILES tiles)
-    u32x4 cd[DOWN_TILES][2][2];
-    u32x2 hd[DOWN_TILES][2];
+__global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, Ws ws) {
+  extern __shared__ __align__(16) uint8_t ht[];            // [P][HT_STRIDE]
+  __shared__ float ys[DR_WAVES][GT_MAXM][DR_ROWS];
+  __shared__ float2 s_blk[MAXP][2];                        // per pair, block: (off, sx)
+  __shared__ float s_xs[MAXP];
+  __shared__ float s_w[MAXP];
+  __shared__ GroupTab G;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int B = a.B, k = a.k, P = B * k, d = a.L.d, F = a.L.F;
+  const int r0 = blockIdx.x * DR_ROWS;
+  const int n16 = lane & 15, c = lane >> 4;
+  trace_point(ws.trace, TK_DOWN, 0);
+
+  // 1. h of every pair: 16 threads per pair, thread s takes entries
+  //    s + 16q (q < 4; q = 0, 1 in block 0, q = 2, 3 in block 1); the loads
+  //    of both passes go out together with the routing loads
+  const int s16 = threadIdx.x & 15;
+  f32x4 hv[2][4][2];
 #pragma unroll
-    for (int tl = 0; tl < DOWN_TILES; ++tl) {
-      const int row = ch * DOWN_CHUNK + 16 * (DOWN_TILES * wv + tl) + n16;
-      const uint32_t ro = row < d ? (uint32_t)(e * a.L.sd + (int64_t)row * ROWB) : a.L.down_bytes;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int p = pass * DR_PAIRS_PER_PASS + (threadIdx.x >> 4);
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        hd[tl][bk] = bload8(rd, ro + bk * BLK_BYTES);
-        cd[tl][bk][0] = bload16(rd, ro + bk * BLK_BYTES + 8 + 16 * c);
-        cd[tl][bk][1] = bload16(rd, ro + bk * BLK_BYTES + 8 + 64 + 16 * c);
+    for (int q = 0; q < 4; ++q) {
+      hv[pass][q][0] = hv[pass][q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p < P) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)p * F + 8 * (s16 + 16 * q));
+        hv[pass][q][0] = src[0];
+        hv[pass][q][1] = src[1];
       }
     }
-
-    // 2. stage h of the members: 32 threads per member (half a wave), thread
-    //    s takes entries o = s + 32q (q < 2, block q), so the 32 threads read
-    //    1 KB contiguously; scale per member over its F values
-    {
-      const int m = threadIdx.x >> 5, s = threadIdx.x & 31;
-      const bool live = m < n;
-      const int p = live ? G.gmem[u][m] : 0;
-      float v[2][8];
+  }
+  // the group table the gate/up kernel published, and the weights
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(ws.gtab);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&G);
+    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
+  }
+  if ((int)threadIdx.x < P) s_w[threadIdx.x] = a.wts[threadIdx.x];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int64_t e0 = (int64_t)p * F + 8 * (s + 32 * q);
-        f32x4 h0 = f32x4{0.f, 0.f, 0.f, 0.f}, h1 = h0;
-        if (live) {
-          h0 = *reinterpret_cast<const f32x4*>(ws.h + e0);
-          h1 = *reinterpret_cast<const f32x4*>(ws.h + e0 + 4);
-        }
+  for (int i = threadIdx.x; i < DR_WAVES * GT_MAXM * DR_ROWS; i += 64 * DR_WAVES)
+    (&ys[0][0][0])[i] = 0.f;
+  __syncthreads();
+  trace_point(ws.trace, TK_DOWN, 4);
+  const int U = G.U;
+  trace_point(ws.trace, TK_DOWN, 5);
+
+  // 2. the wave's first group: its 16 rows x 2 blocks, every load in flight
+  constexpr int64_t ROWB = 2 * BLK_BYTES;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  const int row = r0 + n16;
+  u32x4 cdA[2][2], cdB[2][2];   // [block][half], two buffers
+  u32x2 hdA[2], hdB[2];
+  auto issue = [&](int u, u32x4 (&cd)[2][2], u32x2 (&hd)[2]) {
+    const uint32_t ro = row < d ? (uint32_t)(G.gexp[u] * a.L.sd + (int64_t)row * ROWB) : a.L.down_bytes;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      hd[bk] = bload8(rd, ro + bk * BLK_BYTES);
+      cd[bk][0] = bload16(rd, ro + bk * BLK_BYTES + 8 + 16 * c);
+      cd[bk][1] = bload16(rd, ro + bk * BLK_BYTES + 8 + 64 + 16 * c);
+    }
+  };
+  if (wv < U) issue(wv, cdA, hdA);
+
+  // 3. scale and store h in the operand order of dec8 (per pair one
+  //    power-of-two scale), then the per-block sums the epilogue needs
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int p = pass * DR_PAIRS_PER_PASS + (threadIdx.x >> 4);
+    if (pass * DR_PAIRS_PER_PASS < P) {   // uniform over the workgroup
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 h0 = hv[pass][q][0], h1 = hv[pass][q][1];
         v[q][0] = h0.x; v[q][1] = h0.y; v[q][2] = h0.z; v[q][3] = h0.w;
         v[q][4] = h1.x; v[q][5] = h1.y; v[q][6] = h1.z; v[q][7] = h1.w;
       }
       float am = 0.f;
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[q][i]));
       am = row_max16(am);
-      am = fmaxf(am, __shfl_xor(am, 16, 64));   // the member's 32 lanes
       float xs;
       const float inv = pow2_scale(am, xs);
+      if (p < P) {
+        uint8_t* dst = ht + p * HT_STRIDE;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float sh = 0.f, s16 = 0.f, sx = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sx += v[q][i];
-        put_entry(v[q], inv, ht + m * HT_STRIDE + 16 * (s + 32 * q), sh, s16);
-        sh = row_sum16(sh);
-        s16 = row_sum16(s16);
-        sx = row_sum16(sx);
-        sh += __shfl_xor(sh, 16, 64);
-        s16 += __shfl_xor(s16, 16, 64);
-        sx += __shfl_xor(sx, 16, 64);
-        if (s == 0) s_blk[m][q] = make_float2(-(1024.f * sh + 8.f * s16), sx);
+        for (int q = 0; q < 4; ++q) put_entry(v[q], inv, dst + 16 * (s16 + 16 * q));
+        if (s16 == 0) s_xs[p] = xs;
       }
-      if (s == 0) s_xs[m] = xs;
     }
-    __syncthreads();
-    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 1);
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_DOWN, 6);
+  // per-block sums of the staged pairs: job (16 pairs, block) per wave
+  {
+    const int jobs = 2 * ((P + 15) / 16);
+    for (int job = wv; job < jobs; job += DR_WAVES) {   // wave-uniform
+      const int j = job >> 1, bk = job & 1;
+      float sa[4], sv[4];
+      block_sums_mfma(ht + 16 * j * HT_STRIDE, HT_STRIDE, P - 16 * j, bk, sa, sv);
+      if (n16 == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = 16 * j + 4 * c + i;
+          if (p < P) s_blk[p][bk] = make_float2(-(1024.f * sa[i] + 8.f * sv[i]), s_xs[p] * sv[i]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_DOWN, 1);
 
-    // 3. MFMA per tile, epilogue per block, weighted partial per member
-    const bool a_live = n16 < n;
-    const uint8_t* arow = ht + (a_live ? n16 : 0) * HT_STRIDE + 16 * (4 * c);
-    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 3);
+  // 4. the wave's groups, the next one's weights in flight during each
+  auto compute = [&](int u, const u32x4 (&cd)[2][2], const u32x2 (&hd)[2]) {
+    const int n = G.gcnt[u];
+    const int pa = n16 < n ? G.gmem[u][n16] : G.gmem[u][0];   // A row source
+    const uint8_t* arow = ht + pa * HT_STRIDE + 16 * (4 * c);
     int pc[4];
-    float wc[4], xsc[4];
+    float xsc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * c + i;
       pc[i] = m < n ? G.gmem[u][m] : -1;
-      wc[i] = pc[i] >= 0 ? a.wts[pc[i]] : 0.f;
-      xsc[i] = pc[i] >= 0 ? s_xs[m] : 0.f;
+      xsc[i] = pc[i] >= 0 ? s_xs[pc[i]] : 0.f;
     }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tl = 0; tl < DOWN_TILES; ++tl) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int bk = 0; bk < 2; ++bk) {
+      h8 av[2][4];
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        h8 av[2][4];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 4; ++i) av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
+      const uint32_t q0[4] = {cd[bk][0].x, cd[bk][0].y, cd[bk][0].z, cd[bk][0].w};
+      const uint32_t q1[4] = {cd[bk][1].x, cd[bk][1].y, cd[bk][1].z, cd[bk][1].w};
+      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            av[t][i] = *reinterpret_cast<const h8*>(arow + 16 * (32 * bk + 16 * t + i));
-          }
-        f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int i = 0; i < 4; ++i) {
+        c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
+        c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
+      }
+      const f32x4 cb = c2[0] + c2[1];
+      const float scale = as_f32(hd[bk].x), zero = as_f32(hd[bk].y);
+      const float zp8 = __builtin_fmaf(8.f, scale, zero);
+      const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t q0[4] = {cd[tl][bk][0].x, cd[tl][bk][0].y, cd[tl][bk][0].z, cd[tl][bk][0].w};
-          const uint32_t q1[4] = {cd[tl][bk][1].x, cd[tl][bk][1].y, cd[tl][bk][1].z, cd[tl][bk][1].w};
-          c2[0] = mfma16(av[0][i], dec8(q0[i]), c2[0]);
-          c2[1] = mfma16(av[1][i], dec8(q1[i]), c2[1]);
-        }
-        const f32x4 cb = c2[0] + c2[1];
-        const float scale = as_f32(hd[tl][bk].x), zero = as_f32(hd[tl][bk].y);
-        const float zp8 = __builtin_fmaf(8.f, scale, zero);
-        const float cbv[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (pc[i] >= 0) {
-            const float2 ob = s_blk[4 * c + i][bk];
-            acc[i] += __builtin_fmaf(scale * xsc[i], cbv[i] + ob.x, zp8 * ob.y);
-          }
+      for (int i = 0; i < 4; ++i) {
+        if (pc[i] >= 0) {
+          const float2 ob = s_blk[pc[i]][bk];
+          acc[i] += __builtin_fmaf(scale * xsc[i], cbv[i] + ob.x, zp8 * ob.y);
         }
       }
-      const int row = ch * DOWN_CHUNK + 16 * (DOWN_TILES * wv + tl) + n16;
-      if (row < d) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (pc[i] >= 0) ws.ypart[(int64_t)pc[i] * d + row] = wc[i] * acc[i];
-      }
     }
-    if (it == (int)blockIdx.x) trace_point(ws.trace, TK_DOWN, 4);
-    __syncthreads();   // ht is restaged by the next item
+    // the pairs of a group belong to distinct tokens: the lanes of one
+    // update touch distinct slots
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (pc[i] >= 0) ys[wv][pc[i] / k][n16] += s_w[pc[i]] * acc[i];
+  };
+  for (int u = wv; u < U; u += 2 * DR_WAVES) {   // wave-uniform
+    if (u + DR_WAVES < U) issue(u + DR_WAVES, cdB, hdB);
+    compute(u, cdA, hdA);
+    if (u + DR_WAVES >= U) break;
+    if (u + 2 * DR_WAVES < U) issue(u + 2 * DR_WAVES, cdA, hdA);
+    compute(u + DR_WAVES, cdB, hdB);
+  }
+  trace_point(ws.trace, TK_DOWN, 3);
+  __syncthreads();
+
+  // 5. y = residual + the waves' slices, in wave order
+  if ((int)threadIdx.x < B * DR_ROWS) {
+    const int b = threadIdx.x / DR_ROWS, r = threadIdx.x - b * DR_ROWS;
+    const int rr = r0 + r;
+    if (rr < d) {
+      float y = a.res ? a.res[b * a.ldy + rr] : 0.f;
+#pragma unroll
+      for (int w = 0; w < DR_WAVES; ++w) y += ys[w][b][r];
+      a.y[b * a.ldy + rr] = y;
+    }
   }
   trace_point(ws.trace, TK_DOWN, 2);
-}
-
-// y[b][r] = residual[b][r] + sum_j w_j y_{e_j}[r] over the valid slots, in
-// slot order (the weights are already in ypart).
-__global__ void __launch_bounds__(256) combine_kernel(ExpertArgs a, Ws ws) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
-  const int d = a.L.d, k = a.k;
-  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
-  trace_point_at(ws.trace, TK_DOWN, wg, 5);
-  if (r >= d) return;
-  // every load at once: ypart rows of invalid slots are read but not added
-  float part[MAXK];
-  int ej[MAXK];
-#pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    const int p = b * k + (j < k ? j : 0);
-    ej[j] = a.idx[p];
-    part[j] = ws.ypart[(int64_t)p * d + r];
-  }
-  float y = a.res ? a.res[b * a.ldy + r] : 0.f;
-#pragma unroll
-  for (int j = 0; j < MAXK; ++j)
-    if (j < k && ej[j] >= 0 && ej[j] < a.L.E) y += part[j];
-  a.y[b * a.ldy + r] = y;
-  trace_point_at(ws.trace, TK_DOWN, wg, 6);
 }
 
 // ====================================================================== host
@@ -772,40 +814,32 @@ int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-int launch_route_batched(const RouteArgs& ra, const float* part, int32_t* idx_copy,
-                         float* wts_copy, uint8_t* xg, uint32_t* err, hipStream_t s) {
+int launch_route_batched(const RouteArgs& ra, const float* part, uint32_t* err, hipStream_t s) {
   BatchRouteArgs r{part, ra.bias, ra.E, ra.B, ra.k, ra.idx_out, ra.wts_out, ra.logits_out,
-                   idx_copy, wts_copy, err, get_trace(), ra.x, ra.ldx, ra.d, xg};
-  hipLaunchKernelGGL(route_topk_kernel<true>, dim3(ra.B), dim3(64), 0, s, r);
+                   nullptr, nullptr, err, get_trace()};
+  hipLaunchKernelGGL(route_topk_kernel, dim3(ra.B), dim3(64), 0, s, r);
   return (int)hipGetLastError();
 }
 
-int launch_stage_batched(const float* x, int64_t ldx, int B, int d, uint8_t* xg, hipStream_t s) {
-  BatchRouteArgs r{};
-  r.B = B;
-  r.x = x;
-  r.ldx = ldx;
-  r.d = d;
-  r.xg = xg;
-  r.trace = get_trace();
-  hipLaunchKernelGGL(route_topk_kernel<false>, dim3(B), dim3(64), 0, s, r);
-  return (int)hipGetLastError();
-}
-
-int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, hipStream_t s) {
-  const size_t shm = (size_t)a.B * XT_STRIDE;
-  if (int e = allow_lds(gateup_mfma_kernel, shm)) return e;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3(nwg), dim3(1024), shm, s, a, ws);
+int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, const RouteArgs* ra, hipStream_t s) {
+  const size_t shx = (size_t)a.B * XT_STRIDE;
+  if (ra) {
+    const BatchRouteArgs r{ws.logits, ra->bias, ra->E, ra->B, ra->k, ra->idx_out, ra->wts_out,
+                           ra->logits_out, nullptr, nullptr, ws.err, get_trace()};
+    const size_t shm = shx + (size_t)a.B * a.L.E * sizeof(float);
+    if (int e = allow_lds(gateup_mfma_kernel<true>, shm)) return e;
+    hipLaunchKernelGGL(gateup_mfma_kernel<true>, dim3(nwg), dim3(1024), shm, s, a, ws, r);
+  } else {
+    const BatchRouteArgs r{};
+    if (int e = allow_lds(gateup_mfma_kernel<false>, shx)) return e;
+    hipLaunchKernelGGL(gateup_mfma_kernel<false>, dim3(nwg), dim3(1024), shx, s, a, ws, r);
+  }
   int err = (int)hipGetLastError();
   if (err) return err;
-  const int P = a.B * a.k;
-  const int umax = P < a.L.E ? P : a.L.E;
-  const int nch = (a.L.d + DOWN_CHUNK - 1) / DOWN_CHUNK;
-  const int grid = umax * nch < 2 * nwg ? umax * nch : 2 * nwg;
-  hipLaunchKernelGGL(down_mfma_kernel, dim3(grid), dim3(64 * DOWN_WAVES), 0, s, a, ws);
-  err = (int)hipGetLastError();
-  if (err) return err;
-  hipLaunchKernelGGL(combine_kernel, dim3((a.L.d + 255) / 256, a.B), dim3(256), 0, s, a, ws);
+  const size_t shd = (size_t)a.B * a.k * HT_STRIDE;
+  if (int e = allow_lds(down_rows_kernel, shd)) return e;
+  hipLaunchKernelGGL(down_rows_kernel, dim3((a.L.d + DR_ROWS - 1) / DR_ROWS), dim3(64 * DR_WAVES),
+                     shd, s, a, ws);
   return (int)hipGetLastError();
 }
 

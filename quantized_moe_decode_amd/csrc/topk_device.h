@@ -1,7 +1,7 @@
-// Top-k routing by one wave per token (gfx950, wave64): radix select of
-// the k-th largest logit key, compaction, DPP bitonic sort, renormalised
-// softmax weights.  Shared by the routing kernels of the single-token and
-// the batched decode paths.
+// Top-k routing by one wave per token (gfx950, wave64): a sorting network
+// per lane, then k rounds of a DPP wave maximum over the lanes' heads, and
+// the renormalised softmax weights.  Shared by the routing kernels of the
+// single-token and the batched decode paths.
 //
 // Reading (hipfire expert-offload explainer, section "125GB 的 MoE 模型，
 // 为什么 32GB 显卡也有得跑？": each token activates the top 8 of a layer's
