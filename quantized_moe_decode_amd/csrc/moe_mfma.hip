@@ -635,38 +635,40 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   const int n16 = lane & 15, c = lane >> 4;
   trace_point(ws.trace, TK_DOWN, 0);
 
-  // 1. h of every pair: 16 threads per pair, thread s takes entries
-  //    s + 16q (q < 4; q = 0, 1 in block 0, q = 2, 3 in block 1); the loads
-  //    of both passes go out together with the routing loads
+  // 1. the group table the gate/up kernel published and the routing
+  //    weights first, then h of every pair: 16 threads per pair, thread s
+  //    takes entries s + 16q (q < 4; q = 0, 1 in block 0, q = 2, 3 in block
+  //    1), both passes in flight while the table is stored and the first
+  //    weights are requested
+  constexpr int GT_WORDS = (int)(sizeof(GroupTab) / 4);
+  static_assert(GT_WORDS <= 64 * DR_WAVES, "one table word per thread");
+  const uint32_t gword =
+      (int)threadIdx.x < GT_WORDS ? reinterpret_cast<const uint32_t*>(ws.gtab)[threadIdx.x] : 0u;
+  const float wword = (int)threadIdx.x < P ? a.wts[threadIdx.x] : 0.f;
   const int s16 = threadIdx.x & 15;
-  f32x4 hv[2][4][2];
+  // no branches around the loads (pairs past P read past the descriptor and
+  // get zeros), so the table store below waits for the table loads only
+  const uint32_t hbytes = (uint32_t)(P * F * 4);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(ws.h, hbytes);
+  u32x4 hv[2][4][2];
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int p = pass * DR_PAIRS_PER_PASS + (threadIdx.x >> 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      hv[pass][q][0] = hv[pass][q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (p < P) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)p * F + 8 * (s16 + 16 * q));
-        hv[pass][q][0] = src[0];
-        hv[pass][q][1] = src[1];
-      }
+      const uint32_t o = p < P ? (uint32_t)((p * F + 8 * (s16 + 16 * q)) * 4) : hbytes;
+      hv[pass][q][0] = bload16(rh, o);
+      hv[pass][q][1] = bload16(rh, o + 16);
     }
   }
-  // the group table the gate/up kernel published, and the weights
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(ws.gtab);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&G);
-    for (int i = threadIdx.x; i < (int)(sizeof(GroupTab) / 4); i += blockDim.x) dst[i] = src[i];
-  }
-  if ((int)threadIdx.x < P) s_w[threadIdx.x] = a.wts[threadIdx.x];
+  if ((int)threadIdx.x < GT_WORDS) reinterpret_cast<uint32_t*>(&G)[threadIdx.x] = gword;
+  if ((int)threadIdx.x < P) s_w[threadIdx.x] = wword;
 #pragma unroll
   for (int i = threadIdx.x; i < DR_WAVES * GT_MAXM * DR_ROWS; i += 64 * DR_WAVES)
     (&ys[0][0][0])[i] = 0.f;
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 4);
   const int U = G.U;
-  trace_point(ws.trace, TK_DOWN, 5);
 
   // 2. the wave's first group: its 16 rows x 2 blocks, every load in flight
   constexpr int64_t ROWB = 2 * BLK_BYTES;
@@ -684,6 +686,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     }
   };
   if (wv < U) issue(wv, cdA, hdA);
+  trace_point(ws.trace, TK_DOWN, 5);
 
   // 3. scale and store h in the operand order of dec8 (per pair one
   //    power-of-two scale), then the per-block sums the epilogue needs
@@ -694,9 +697,9 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
       float v[4][8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 h0 = hv[pass][q][0], h1 = hv[pass][q][1];
-        v[q][0] = h0.x; v[q][1] = h0.y; v[q][2] = h0.z; v[q][3] = h0.w;
-        v[q][4] = h1.x; v[q][5] = h1.y; v[q][6] = h1.z; v[q][7] = h1.w;
+        const u32x4 h0 = hv[pass][q][0], h1 = hv[pass][q][1];
+        v[q][0] = as_f32(h0.x); v[q][1] = as_f32(h0.y); v[q][2] = as_f32(h0.z); v[q][3] = as_f32(h0.w);
+        v[q][4] = as_f32(h1.x); v[q][5] = as_f32(h1.y); v[q][6] = as_f32(h1.z); v[q][7] = as_f32(h1.w);
       }
       float am = 0.f;
 #pragma unroll
@@ -714,6 +717,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
       }
     }
   }
+  if (wv + DR_WAVES < U) issue(wv + DR_WAVES, cdB, hdB);   // second group in flight too
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 6);
   // per-block sums of the staged pairs: job (16 pairs, block) per wave
@@ -735,7 +739,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 1);
 
-  // 4. the wave's groups, the next one's weights in flight during each
+  // 4. the wave's groups, the next ones' weights in flight during each
   auto compute = [&](int u, const u32x4 (&cd)[2][2], const u32x2 (&hd)[2]) {
     const int n = G.gcnt[u];
     const int pa = n16 < n ? G.gmem[u][n16] : G.gmem[u][0];   // A row source
@@ -782,12 +786,14 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     for (int i = 0; i < 4; ++i)
       if (pc[i] >= 0) ys[wv][pc[i] / k][n16] += s_w[pc[i]] * acc[i];
   };
+  // buffers A and B hold groups u and u + 16; each is refilled with the
+  // group two steps ahead as soon as it has been used
   for (int u = wv; u < U; u += 2 * DR_WAVES) {   // wave-uniform
-    if (u + DR_WAVES < U) issue(u + DR_WAVES, cdB, hdB);
     compute(u, cdA, hdA);
-    if (u + DR_WAVES >= U) break;
     if (u + 2 * DR_WAVES < U) issue(u + 2 * DR_WAVES, cdA, hdA);
+    if (u + DR_WAVES >= U) break;
     compute(u + DR_WAVES, cdB, hdB);
+    if (u + 3 * DR_WAVES < U) issue(u + 3 * DR_WAVES, cdB, hdB);
   }
   trace_point(ws.trace, TK_DOWN, 3);
   __syncthreads();
