@@ -48,7 +48,7 @@ def _layer(q, seed, E, d, F=512, bias=None):
 
 @pytest.mark.parametrize("B,k,d,E", [(2, 8, 2048, 64), (3, 8, 2048, 256), (8, 8, 2048, 512),
                                      (16, 8, 1920, 32), (5, 1, 2048, 16), (4, 4, 2048, 8),
-                                     (16, 8, 2048, 16)])
+                                     (16, 8, 2048, 16), (6, 8, 2048, 1024), (7, 6, 2000, 100)])
 @pytest.mark.parametrize("fused", [True, False])
 def test_batched_layer_vs_oracle(q, B, k, d, E, fused):
     say("batched B=%d k=%d d=%d E=%d fused=%s" % (B, k, d, E, fused))
@@ -68,6 +68,32 @@ def test_batched_layer_vs_oracle(q, B, k, d, E, fused):
                                   residual=res.cpu().numpy())
     say("max rel-L2 %.3g, tie-ambiguous tokens %d" % (err, amb))
     assert err <= REL_L2_TOL
+
+
+@pytest.mark.parametrize("B,E,skew", [(16, 512, True), (6, 1024, False), (3, 100, False)])
+def test_batched_fused_equals_two_call_bitwise(q, B, E, skew):
+    """The fused layer routes inside the gate/up kernel; moe_route_topk runs
+    the same routing functions in its own kernel.  Indices, weights, logits
+    and outputs of the two forms are identical bit for bit."""
+    d, k = 2048, 8
+    bias = synth.zipf_bias(7, E) if skew else None
+    say("fused vs two-call B=%d E=%d skew=%s" % (B, E, skew))
+    L, _ = _layer(q, 23, E, d, bias=bias)
+    x = synth.activations(torch, "cuda", 300 + B, B, d)
+    res = synth.activations(torch, "cuda", 400 + B, B, d)
+    ws = q.new_workspace(L, B, k)
+    i1, w1, y1 = q.moe_layer_decode(L, x, k, ws, residual=res)
+    i1, w1, y1 = i1.clone(), w1.clone(), y1.clone()
+    lg = torch.empty(B, E, device="cuda")
+    i2, w2 = q.moe_route_topk(L.Wr, x, k, ws=ws, bias=L.bias, logits=lg)
+    y2 = q.moe_expert_decode(L, x, i2, w2, ws, residual=res)
+    torch.cuda.synchronize()
+    assert q.workspace_error(ws) == 0
+    assert torch.equal(i1, i2) and torch.equal(w1, w2) and torch.equal(y1, y2)
+    # the logits the routing saw: the selected experts are their top k
+    top = torch.topk(lg, k, dim=1).values
+    sel = torch.gather(lg, 1, i2.long())
+    assert torch.equal(torch.sort(sel, dim=1, descending=True).values, top)
 
 
 def test_batched_duplicates_and_invalid(q):
