@@ -1,4 +1,5 @@
-"""GPU parity of the batched (2..16 tokens) decode path on MFMA.
+"""GPU parity of the batched (2..16 tokens) decode path on MFMA, and of the
+single-token path at expert counts other than the benchmark's.
 
 Token batches of the d=2048-class, F=512 layer shape run through matrix-core
 kernels that group the (token, slot) pairs by expert.  Every case is checked
@@ -68,6 +69,31 @@ def test_batched_layer_vs_oracle(q, B, k, d, E, fused):
                                   residual=res.cpu().numpy())
     say("max rel-L2 %.3g, tie-ambiguous tokens %d" % (err, amb))
     assert err <= REL_L2_TOL
+
+
+@pytest.mark.parametrize("E,k", [(100, 8), (1024, 8), (1024, 1), (64, 5)])
+def test_single_token_expert_counts(q, E, k):
+    """One token on the VALU path (top-k inside the gate/up kernel) with
+    expert counts that are not 256: 100 (not a multiple of the wave), 1024
+    (16 logits per lane), 64 (one per lane), against the oracle."""
+    d = 2048
+    say("single token E=%d k=%d" % (E, k))
+    L, cache = _layer(q, 25, E, d)
+    x = synth.activations(torch, "cuda", 500 + E + k, 1, d)
+    res = synth.activations(torch, "cuda", 600 + E + k, 1, d)
+    ws = q.new_workspace(L, 1, k)
+    idx, wts, y = q.moe_layer_decode(L, x, k, ws, residual=res)
+    torch.cuda.synchronize()
+    assert q.workspace_error(ws) == 0
+    err, _ = oracle_layer_check(x.cpu().numpy(), L.Wr.cpu().numpy(), None, cache, k,
+                                idx.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy(),
+                                residual=res.cpu().numpy())
+    assert err <= REL_L2_TOL
+    # the two-call form gives the same bits
+    i2, w2 = q.moe_route_topk(L.Wr, x, k, ws=ws)
+    y2 = q.moe_expert_decode(L, x, i2, w2, ws, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, i2) and torch.equal(wts, w2) and torch.equal(y, y2)
 
 
 @pytest.mark.parametrize("B,E,skew", [(16, 512, True), (6, 1024, False), (3, 100, False)])
