@@ -14,8 +14,10 @@
 // output = sum_j w_j y_{e_j} (+ optional residual).
 //
 // Kernels
-//   route_kernel   router GEMV (one wave per expert row) + top-k by the last
-//                  workgroup to finish (atomic ticket).
+//   logits_kernel  router GEMV, one workgroup per expert row (one token, and
+//                  the generic shapes).
+//   topk_kernel    standalone top-k, one wave per token (moe_route_topk for
+//                  one token, and the generic shapes).
 //   gateup_kernel  grouped gate/up dequant-GEMV: tokens that picked the same
 //                  expert share one read of its rows; writes h = SiLU(g)*u.
 //   down_kernel    down dequant-GEMV for every (token, slot), weighted by the
@@ -28,6 +30,7 @@
 //                  HIP graph, against 2.4-10 us for an in-kernel barrier over
 //                  256 workgroups), so the layer is three dependent launches:
 //                  router logits -> top-k + gate/up -> down + combine.
+//   2..16 tokens of the tuned shape run on the matrix cores (moe_mfma.hip).
 #include <hip/hip_ext.h>
 
 #include "hfq4_device.h"
