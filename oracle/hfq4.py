@@ -4,7 +4,7 @@ Format (page "hipfire：为AMD RDNA GPU打造的Rust原生LLM推理引擎", sect
 "2. HFQ量化格式与GEMV优化"): a block holds 256 weights in 136 bytes -- an f32
 scale, an f32 zero point and 128 bytes of packed 4-bit codes.
 
-Readings taken where the page is silent (each one listed in the design doc):
+Readings taken where the page is silent:
 
 * byte order inside a block: scale at byte 0, zero at byte 4 (both
   little-endian IEEE f32), codes at bytes 8..135;
