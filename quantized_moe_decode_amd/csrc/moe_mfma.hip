@@ -37,7 +37,8 @@
 //                        (group, 16 rows) in contiguous runs per workgroup,
 //                        a quad of waves computes gate and up over both K
 //                        halves, reduces through LDS and writes
-//                        h = SiLU(g) * u.
+//                        h = SiLU(g) * u as f16 operand entries with one
+//                        power-of-two exponent per (pair, 16-row tile).
 //   route_topk_kernel    routing only (moe_route_topk): the same routing
 //                        functions, one single-wave workgroup per token.
 //   down_rows_kernel     16 output rows of every token per workgroup: stages
@@ -103,6 +104,24 @@ __device__ __forceinline__ float pow2_scale(float amax, float& xs) {
   }
   xs = ldexpf(1.f, e);
   return ldexpf(1.f, -e);
+}
+
+// Exponent e with amax * 2^-e in [2, 4); H_EMPTY for a zero maximum (so it
+// never wins a maximum over tiles), 0 for a non-finite one.
+constexpr int H_EMPTY = -128;
+__device__ __forceinline__ int pow2_exp(float amax) {
+  if (!(amax > 0.f)) return H_EMPTY;
+  if (!(amax < INFINITY)) return 0;
+  int ex;
+  frexpf(amax, &ex);
+  return ex - 2;
+}
+// 2^d as a pair of f16 (d <= 0; 0 below the smallest subnormal).
+__device__ __forceinline__ h2 f16_pow2_pair(int dlt) {
+  uint32_t b = 0u;
+  if (dlt >= -14) b = (uint32_t)(dlt + 15) << 10;
+  else if (dlt >= -24) b = 1u << (dlt + 24);
+  return as_h2(b | (b << 16));
 }
 
 // Write the 8 elements of one code dword's entry (scaled by inv) as 16 B at
@@ -444,6 +463,8 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int quad = wv >> 2, role = wv & 3;
   const int B = a.B, k = a.k, P = B * k, F = a.L.F, E = a.L.E;
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws.h);   // [P][F] f16 operand entries
+  int8_t* he = reinterpret_cast<int8_t*>(hq + (size_t)P * F * 2);   // [P][F / 16] exponents
   trace_point(ws.trace, TK_GATEUP, 0);
 
   // 1. one wave per token: routing loads first, then the activations
@@ -594,11 +615,24 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
       const f32x4 g1 = red[quad][0][lane], u0 = red[quad][1][lane], u1 = red[quad][2][lane];
       const float gv[4] = {acc[0] + g1.x, acc[1] + g1.y, acc[2] + g1.z, acc[3] + g1.w};
       const float uv[4] = {u0.x + u1.x, u0.y + u1.y, u0.z + u1.z, u0.w + u1.w};
+      // h leaves as f16 in the down kernel's operand order with one
+      // power-of-two exponent per (pair, 16-row tile): element q = row % 8
+      // of entry row / 8 sits at half 2 (q % 4) + q / 4, odd q divided by 16
       const int row = tile * MM_ROWS + n16;
+      const int q8 = row & 7;
+      const int hoff = (row >> 3) * 16 + 2 * (2 * (q8 & 3) + (q8 >> 2));
+      const float odd = (q8 & 1) ? 0.0625f : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * c + i;
-        if (m < n) ws.h[(int64_t)G.gmem[u][m] * F + row] = silu_mul(gv[i], uv[i]);
+        const float hv = m < n ? silu_mul(gv[i], uv[i]) : 0.f;
+        const int e = pow2_exp(row_max16(fabsf(hv)));
+        if (m < n) {
+          const int p = G.gmem[u][m];
+          const float inv = e == H_EMPTY ? 0.f : ldexpf(odd, -e);
+          *reinterpret_cast<_Float16*>(hq + (int64_t)p * (2 * F) + hoff) = (_Float16)(hv * inv);
+          if (n16 == 0) he[(int64_t)p * (F / MM_ROWS) + tile] = (int8_t)e;
+        }
       }
     }
     __syncthreads();   // red is reused by the next round
@@ -610,8 +644,10 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
 // ====================================================================== down + combine
 
 // A workgroup owns DR_ROWS = 16 output rows of every token.  It stages h of
-// all (token, slot) pairs once (f16 in the MFMA operand order, one
-// power-of-two scale per pair), then its 16 waves take the expert groups in
+// all (token, slot) pairs once: the gate/up kernel wrote h as f16 in the
+// MFMA operand order with one power-of-two exponent per 16-row tile; here
+// each entry is brought to its block's exponent (the largest of the
+// block's 16 tiles) and stored in LDS.  Then its 16 waves take the expert groups in
 // turn (wave w: groups w, w + 16, ...): per group one 16-row MFMA tile over
 // K = F, A = the group's pairs, B = 16 rows of the expert's down matrix,
 // with the next group's weights in flight while the current one computes.
@@ -620,55 +656,66 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
 // per-slot sum therefore needs no second kernel and no per-slot buffer.
 constexpr int DR_ROWS = 16;
 constexpr int DR_WAVES = 16;
-constexpr int DR_PAIRS_PER_PASS = 64 * DR_WAVES / 16;   // 16 threads per pair
+constexpr int DR_ENT_ITERS = MAXP * 64 / (64 * DR_WAVES);   // h entries per thread (F = 512)
 
 __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, Ws ws) {
   extern __shared__ __align__(16) uint8_t ht[];            // [P][HT_STRIDE]
   __shared__ float ys[DR_WAVES][GT_MAXM][DR_ROWS];
   __shared__ float2 s_blk[MAXP][2];                        // per pair, block: (off, sx)
-  __shared__ float s_xs[MAXP];
+  __shared__ float s_xs[MAXP][2];                          // per pair, block: 2^e
+  __shared__ int s_eb[MAXP][2];                            // per pair, block: e
+  __shared__ uint32_t s_he[MAXP * 8];                      // per pair: 32 tile exponents
   __shared__ float s_w[MAXP];
   __shared__ GroupTab G;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int B = a.B, k = a.k, P = B * k, d = a.L.d, F = a.L.F;
   const int r0 = blockIdx.x * DR_ROWS;
   const int n16 = lane & 15, c = lane >> 4;
+  const uint8_t* hq = reinterpret_cast<const uint8_t*>(ws.h);   // [P][F] f16 operand entries
+  const int8_t* he = reinterpret_cast<const int8_t*>(hq + (size_t)P * F * 2);
   trace_point(ws.trace, TK_DOWN, 0);
 
-  // 1. the group table the gate/up kernel published and the routing
-  //    weights first, then h of every pair: 16 threads per pair, thread s
-  //    takes entries s + 16q (q < 4; q = 0, 1 in block 0, q = 2, 3 in block
-  //    1), both passes in flight while the table is stored and the first
-  //    weights are requested
+  // 1. the group table the gate/up kernel published, the routing weights
+  //    and the tile exponents first, then every h entry (16 B, entry
+  //    threadIdx.x + 1024 j), in flight while the table is stored and the
+  //    first weights are requested
   constexpr int GT_WORDS = (int)(sizeof(GroupTab) / 4);
   static_assert(GT_WORDS <= 64 * DR_WAVES, "one table word per thread");
   const uint32_t gword =
       (int)threadIdx.x < GT_WORDS ? reinterpret_cast<const uint32_t*>(ws.gtab)[threadIdx.x] : 0u;
   const float wword = (int)threadIdx.x < P ? a.wts[threadIdx.x] : 0.f;
-  const int s16 = threadIdx.x & 15;
-  // no branches around the loads (pairs past P read past the descriptor and
-  // get zeros), so the table store below waits for the table loads only
-  const uint32_t hbytes = (uint32_t)(P * F * 4);
-  const __amdgpu_buffer_rsrc_t rh = make_rsrc(ws.h, hbytes);
-  u32x4 hv[2][4][2];
+  const int EW = P * 8;   // exponent words (32 tiles per pair)
+  const uint32_t eword = (int)threadIdx.x < EW ? reinterpret_cast<const uint32_t*>(he)[threadIdx.x] : 0u;
+  // no branches around the loads (entries past the end read past the
+  // descriptor and get zeros), so the stores below wait for their own loads
+  const int NENT = P * 64;
+  const uint32_t hbytes = (uint32_t)NENT * 16u;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(hq, hbytes);
+  u32x4 hv[DR_ENT_ITERS];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int p = pass * DR_PAIRS_PER_PASS + (threadIdx.x >> 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t o = p < P ? (uint32_t)((p * F + 8 * (s16 + 16 * q)) * 4) : hbytes;
-      hv[pass][q][0] = bload16(rh, o);
-      hv[pass][q][1] = bload16(rh, o + 16);
-    }
+  for (int j = 0; j < DR_ENT_ITERS; ++j) {
+    const int el = threadIdx.x + 64 * DR_WAVES * j;
+    hv[j] = bload16(rh, el < NENT ? (uint32_t)el * 16u : hbytes);
   }
   if ((int)threadIdx.x < GT_WORDS) reinterpret_cast<uint32_t*>(&G)[threadIdx.x] = gword;
   if ((int)threadIdx.x < P) s_w[threadIdx.x] = wword;
+  if ((int)threadIdx.x < EW) s_he[threadIdx.x] = eword;
 #pragma unroll
   for (int i = threadIdx.x; i < DR_WAVES * GT_MAXM * DR_ROWS; i += 64 * DR_WAVES)
     (&ys[0][0][0])[i] = 0.f;
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 4);
   const int U = G.U;
+  const int8_t* he_l = reinterpret_cast<const int8_t*>(s_he);
+  // a block's exponent is the largest of its 16 tiles'
+  if ((int)threadIdx.x < 2 * P) {
+    const int p = threadIdx.x >> 1, bk = threadIdx.x & 1;
+    int m = H_EMPTY;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) m = max(m, (int)he_l[p * 32 + 16 * bk + t]);
+    s_eb[p][bk] = m;
+    s_xs[p][bk] = m == H_EMPTY ? 0.f : ldexpf(1.f, m);
+  }
 
   // 2. the wave's first group: its 16 rows x 2 blocks, every load in flight
   constexpr int64_t ROWB = 2 * BLK_BYTES;
@@ -687,34 +734,21 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   };
   if (wv < U) issue(wv, cdA, hdA);
   trace_point(ws.trace, TK_DOWN, 5);
+  __syncthreads();   // block exponents
 
-  // 3. scale and store h in the operand order of dec8 (per pair one
-  //    power-of-two scale), then the per-block sums the epilogue needs
+  // 3. every entry brought from its tile's exponent to its block's (an
+  //    exact power-of-two product in f16, barring values that fall below
+  //    the f16 normal range), then stored in LDS; the per-block sums follow
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int p = pass * DR_PAIRS_PER_PASS + (threadIdx.x >> 4);
-    if (pass * DR_PAIRS_PER_PASS < P) {   // uniform over the workgroup
-      float v[4][8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 h0 = hv[pass][q][0], h1 = hv[pass][q][1];
-        v[q][0] = as_f32(h0.x); v[q][1] = as_f32(h0.y); v[q][2] = as_f32(h0.z); v[q][3] = as_f32(h0.w);
-        v[q][4] = as_f32(h1.x); v[q][5] = as_f32(h1.y); v[q][6] = as_f32(h1.z); v[q][7] = as_f32(h1.w);
-      }
-      float am = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[q][i]));
-      am = row_max16(am);
-      float xs;
-      const float inv = pow2_scale(am, xs);
-      if (p < P) {
-        uint8_t* dst = ht + p * HT_STRIDE;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) put_entry(v[q], inv, dst + 16 * (s16 + 16 * q));
-        if (s16 == 0) s_xs[p] = xs;
-      }
+  for (int j = 0; j < DR_ENT_ITERS; ++j) {
+    const int el = threadIdx.x + 64 * DR_WAVES * j;
+    if (el < NENT) {
+      const int p = el >> 6, o = el & 63;
+      const h2 f = f16_pow2_pair((int)he_l[p * 32 + (o >> 1)] - s_eb[p][o >> 5]);
+      const u32x4 v = hv[j];
+      *reinterpret_cast<u32x4*>(ht + p * HT_STRIDE + 16 * o) =
+          u32x4{as_u32(as_h2(v.x) * f), as_u32(as_h2(v.y) * f), as_u32(as_h2(v.z) * f),
+                as_u32(as_h2(v.w) * f)};
     }
   }
   if (wv + DR_WAVES < U) issue(wv + DR_WAVES, cdB, hdB);   // second group in flight too
@@ -731,7 +765,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = 16 * j + 4 * c + i;
-          if (p < P) s_blk[p][bk] = make_float2(-(1024.f * sa[i] + 8.f * sv[i]), s_xs[p] * sv[i]);
+          if (p < P) s_blk[p][bk] = make_float2(-(1024.f * sa[i] + 8.f * sv[i]), s_xs[p][bk] * sv[i]);
         }
       }
     }
@@ -745,12 +779,10 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     const int pa = n16 < n ? G.gmem[u][n16] : G.gmem[u][0];   // A row source
     const uint8_t* arow = ht + pa * HT_STRIDE + 16 * (4 * c);
     int pc[4];
-    float xsc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * c + i;
       pc[i] = m < n ? G.gmem[u][m] : -1;
-      xsc[i] = pc[i] >= 0 ? s_xs[pc[i]] : 0.f;
     }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -776,7 +808,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
       for (int i = 0; i < 4; ++i) {
         if (pc[i] >= 0) {
           const float2 ob = s_blk[pc[i]][bk];
-          acc[i] += __builtin_fmaf(scale * xsc[i], cbv[i] + ob.x, zp8 * ob.y);
+          acc[i] += __builtin_fmaf(scale * s_xs[pc[i]][bk], cbv[i] + ob.x, zp8 * ob.y);
         }
       }
     }
