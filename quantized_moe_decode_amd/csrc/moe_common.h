@@ -46,6 +46,8 @@ __host__ __device__ inline bool fast_shape(int d, int F, int k) {
 
 // Batched path (2 <= B <= 16) on MFMA matrix cores.
 constexpr int LG_KS = 4;   // K splits of the batched router GEMV (partial logit sets)
+// Row stride of a partial logit set: E rounded up to 4 experts.
+__host__ __device__ inline int lg_stride(int E) { return (E + 3) & ~3; }
 int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
 // Top-k and weights from the partial logits, one wave per token (routing
 // only).

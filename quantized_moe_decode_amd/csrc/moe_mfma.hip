@@ -235,7 +235,8 @@ __device__ void build_groups_mm(const int* s_idx, int P, int k, int E, GroupTab&
 
 // ====================================================================== router
 
-// Partial router logits: part[ks][b][e] = sum over K split ks of
+// Partial router logits: part[ks][b][e] (rows padded to a multiple of 4
+// experts, so that a lane can read 4 consecutive experts at once) = sum over K split ks of
 // Wr[e][i] * x[b][i].  A = x (16 tokens; rows past B read zeros), B = Wr
 // (16 experts), 4 K per MFMA: lane (n, c) loads a float4 at K offset 4c of
 // every 16-wide K step and feeds element j to the j-th MFMA, so both
@@ -286,7 +287,7 @@ __global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = 4 * c + i;
-        if (b < a.B) part[((int64_t)ks * a.B + b) * a.E + row] = tv[i];
+        if (b < a.B) part[((int64_t)ks * a.B + b) * lg_stride(a.E) + row] = tv[i];
       }
     }
   }
@@ -294,7 +295,7 @@ __global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __
 }
 
 struct BatchRouteArgs {
-  const float* part;      // [LG_KS][B][E] partial logits
+  const float* part;      // [LG_KS][B][lg_stride(E)] partial logits
   const float* bias;      // [E] or null
   int E, B, k;
   int32_t* idx_out;       // [B][k]
@@ -308,60 +309,61 @@ struct BatchRouteArgs {
 
 template <int PER>
 struct RouteLoads {
-  uint32_t raw[LG_KS][PER];
+  u32x4 raw[LG_KS][PER / 4];
   uint32_t rb[PER];
 };
 
-// Issue every load of one token's routing: the LG_KS partial logits and the
-// bias of expert 64c + lane (coalesced).
+// Issue every load of one token's routing: lane l holds experts
+// PER l .. PER l + PER - 1 -- the layout the top-k takes -- read 4 at a
+// time from each of the LG_KS partial sets (rows padded to 4 experts), and
+// their bias.
 template <int PER>
 __device__ __forceinline__ void route_load(const BatchRouteArgs& r, int b, RouteLoads<PER>& L) {
   const int lane = threadIdx.x & 63;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, (uint32_t)((int64_t)LG_KS * r.B * r.E * 4));
+  const int stride = lg_stride(r.E);
+  const uint32_t pbytes = (uint32_t)((int64_t)LG_KS * r.B * stride * 4);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, pbytes);
   const __amdgpu_buffer_rsrc_t rbias = make_rsrc(r.bias, r.bias ? (uint32_t)r.E * 4u : 0u);
 #pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int e = 64 * c + lane;
+  for (int c = 0; c < PER / 4; ++c) {
+    const int e0 = lane * PER + 4 * c;
 #pragma unroll
     for (int p = 0; p < LG_KS; ++p)
-      L.raw[p][c] = bload4(rp, e < r.E ? (uint32_t)((((int64_t)p * r.B + b) * r.E + e) * 4)
-                                       : 0xFFFFFFF0u);
-    L.rb[c] = bload4(rbias, (uint32_t)e * 4u);   // zero without a bias or past E
+      L.raw[p][c] = bload16(rp, e0 < r.E ? (uint32_t)((((int64_t)p * r.B + b) * stride + e0) * 4)
+                                         : pbytes);
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)   // zero without a bias or past E
+    L.rb[i] = bload4(rbias, (uint32_t)(lane * PER + i) * 4u);
 }
 
 // Sum, top-k and weights of one token from its loads.  The selection goes
 // to s_idx / s_w (LDS, when given); the global outputs, the logits and the
 // error bit are written only when `write` is set.
 template <int PER>
-__device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER>& L, float* lg,
+__device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER>& L,
                             int* s_idx, float* s_w, bool write) {
   const int lane = threadIdx.x & 63;
-  // lane l sums expert 64c + l over the partial sets (+ bias) into LDS; the
-  // top-k then reads its own PER consecutive experts
+  // expert PER lane + i: the partial sets in order, then the bias
   int nan_seen = 0;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int e = 64 * c + lane;
-    if (e < r.E) {
-      float l = 0.f;
-#pragma unroll
-      for (int p = 0; p < LG_KS; ++p) l += as_f32(L.raw[p][c]);
-      if (r.bias) l += as_f32(L.rb[c]);
-      if (write && r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
-      lg[e] = l;
-      nan_seen |= __builtin_isnan(l);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  trace_point(r.trace, TK_TOPK, 2);
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane * PER + i;
-    key[i] = e < r.E ? okey(lg[e]) : 0u;
+    float l = 0.f;
+#pragma unroll
+    for (int p = 0; p < LG_KS; ++p) {
+      const u32x4 q = L.raw[p][i / 4];
+      const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+      l += as_f32(qv[i % 4]);
+    }
+    if (r.bias) l += as_f32(L.rb[i]);
+    const bool valid = e < r.E;
+    if (valid && write && r.logits_out) r.logits_out[(int64_t)b * r.E + e] = l;
+    nan_seen |= valid & __builtin_isnan(l);
+    key[i] = valid ? okey(l) : 0u;
   }
+  trace_point(r.trace, TK_TOPK, 2);
   int e;
   float w;
   topk_keys<PER>(key, r.E, r.k, e, w, nullptr, nullptr);
@@ -419,21 +421,20 @@ __device__ void stage_token(const float* __restrict__ xb, int d, uint8_t* ent, f
 // partial sums + bias, top-k and weights.  The fused layer runs the same
 // two functions inside the gate/up kernel, so both forms give the same bits.
 __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
-  __shared__ float lg[HFQ4_MAXE_DEV];
   trace_point(r.trace, TK_TOPK, 0);
   const int b = blockIdx.x;
   if (r.E <= 256) {
     RouteLoads<4> L;
     route_load<4>(r, b, L);
-    route_token<4>(r, b, L, lg, nullptr, nullptr, true);
+    route_token<4>(r, b, L, nullptr, nullptr, true);
   } else if (r.E <= 512) {
     RouteLoads<8> L;
     route_load<8>(r, b, L);
-    route_token<8>(r, b, L, lg, nullptr, nullptr, true);
+    route_token<8>(r, b, L, nullptr, nullptr, true);
   } else {
     RouteLoads<16> L;
     route_load<16>(r, b, L);
-    route_token<16>(r, b, L, lg, nullptr, nullptr, true);
+    route_token<16>(r, b, L, nullptr, nullptr, true);
   }
   trace_point(r.trace, TK_TOPK, 1);
 }
@@ -452,7 +453,6 @@ template <bool FROM_LOGITS>
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, BatchRouteArgs r) {
   extern __shared__ __align__(16) uint8_t dyn[];
   uint8_t* xt = dyn;                                                     // [B][XT_STRIDE]
-  float* lg = reinterpret_cast<float*>(dyn + (size_t)a.B * XT_STRIDE);   // [B][E] (routing)
   __shared__ GroupTab G;
   __shared__ GroupScratch GS;
   __shared__ int s_idx[MAXP];
@@ -474,21 +474,20 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
     uint8_t* xe = xt + wv * XT_STRIDE;
     if (FROM_LOGITS) {
       const bool pub = blockIdx.x == 0;
-      float* lgw = lg + (size_t)wv * E;
       if (E <= 256) {
         RouteLoads<4> L;
         route_load<4>(r, wv, L);
         stage_token(xb, a.L.d, xe, &s_xs[wv]);
-        route_token<4>(r, wv, L, lgw, s_idx, s_wt, pub);
+        route_token<4>(r, wv, L, s_idx, s_wt, pub);
       } else if (E <= 512) {
         RouteLoads<8> L;
         route_load<8>(r, wv, L);
         stage_token(xb, a.L.d, xe, &s_xs[wv]);
-        route_token<8>(r, wv, L, lgw, s_idx, s_wt, pub);
+        route_token<8>(r, wv, L, s_idx, s_wt, pub);
       } else {   // 16 loads per lane: route first, then stage
         RouteLoads<16> L;
         route_load<16>(r, wv, L);
-        route_token<16>(r, wv, L, lgw, s_idx, s_wt, pub);
+        route_token<16>(r, wv, L, s_idx, s_wt, pub);
         stage_token(xb, a.L.d, xe, &s_xs[wv]);
       }
     } else {
@@ -864,9 +863,8 @@ int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, const RouteArgs*
   if (ra) {
     const BatchRouteArgs r{ws.logits, ra->bias, ra->E, ra->B, ra->k, ra->idx_out, ra->wts_out,
                            ra->logits_out, nullptr, nullptr, ws.err, get_trace()};
-    const size_t shm = shx + (size_t)a.B * a.L.E * sizeof(float);
-    if (int e = allow_lds(gateup_mfma_kernel<true>, shm)) return e;
-    hipLaunchKernelGGL(gateup_mfma_kernel<true>, dim3(nwg), dim3(1024), shm, s, a, ws, r);
+    if (int e = allow_lds(gateup_mfma_kernel<true>, shx)) return e;
+    hipLaunchKernelGGL(gateup_mfma_kernel<true>, dim3(nwg), dim3(1024), shx, s, a, ws, r);
   } else {
     const BatchRouteArgs r{};
     if (int e = allow_lds(gateup_mfma_kernel<false>, shx)) return e;
