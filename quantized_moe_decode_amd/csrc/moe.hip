@@ -646,7 +646,7 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags
   WsLayout l{};
   size_t o = WS_HEADER;
   l.logits = o;   // batched calls keep LG_KS partial logit sets
-  o = al256(o + sizeof(float) * (B >= 2 ? (size_t)LG_KS * B * lg_stride((int)E) : (size_t)B * E));
+  o = al256(o + sizeof(float) * (B >= 2 ? (size_t)LG_KS : 1) * B * lg_stride((int)E));
   l.idx = o;
   o = al256(o + sizeof(int32_t) * (size_t)B * k);
   l.wts = o;

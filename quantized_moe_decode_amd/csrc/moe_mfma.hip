@@ -81,9 +81,6 @@ __device__ __forceinline__ float wave_max_f(float v) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
-__device__ __forceinline__ float lane_bcast(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
 // Max over each 16-lane row (result in every lane of the row).
 __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp<0xB1>(v));

@@ -39,37 +39,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
   return max(max(r0, r1), max(r2, r3));
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp_u<0xB1>(v));
-  v = min(v, dpp_u<0x4E>(v));
-  v = min(v, dpp_u<0x124>(v));
-  v = min(v, dpp_u<0x128>(v));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return min(min(r0, r1), min(r2, r3));
-}
 
 // (key, index) order of the top-k: larger key first, equal keys -> lower index.
 __device__ __forceinline__ bool before(uint32_t ak, uint32_t ae, uint32_t bk, uint32_t be) {
   return (ak > bk) | ((ak == bk) & (ae < be));
 }
-template <int CTL>
-__device__ __forceinline__ void bitonic_step(uint32_t& key, uint32_t& e, bool keep_first) {
-  const uint32_t pk = dpp_u<CTL>(key), pe = dpp_u<CTL>(e);
-  const bool mine_first = before(key, e, pk, pe);
-  const bool take = keep_first != mine_first;   // keep the partner's entry
-  key = take ? pk : key;
-  e = take ? pe : e;
-}
-
 // Keys of one token's E logits, PER per lane (expert e = lane*PER + i),
-// read through a bounded descriptor (lanes past the end read zeros).
-// Returns whether a NaN logit was seen by this lane.
+// read 4 at a time through a bounded descriptor.  The bound is E rounded up
+// to 4 (every 16-byte load lies wholly inside or wholly outside it, and the
+// logit areas of the workspace leave that much room); experts past E are
+// masked, lanes past the bound read zeros.  Returns whether a NaN logit was
+// seen by this lane.
 template <int PER>
 __device__ __forceinline__ int load_keys(const float* __restrict__ logits, int E, uint32_t* key) {
   const int lane = threadIdx.x & 63;
   int nan_seen = 0;
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits, (uint32_t)E * 4u);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits, (uint32_t)((E + 3) & ~3) * 4u);
 #pragma unroll
   for (int i = 0; i < PER; i += 4) {
     const int e0 = lane * PER + i;
@@ -84,17 +69,6 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ logits, int E
     }
   }
   return nan_seen;
-}
-
-// Sum over the wave of a per-lane count (uniform result, fixed order).
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += dpp_u<0xB1>(v);
-  v += dpp_u<0x4E>(v);
-  v += dpp_u<0x124>(v);
-  v += dpp_u<0x128>(v);
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return (r0 + r1) + (r2 + r3);
 }
 
 // Sorting networks (Batcher's odd-even merge sort) for a lane's PER keys.
