@@ -353,18 +353,24 @@ def bench_skewed(args, torch, q):
 
 
 def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20000)
-    ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
-    ap.add_argument("--path", choices=["fused", "split"], default="fused")
-    ap.add_argument("--replicas", type=int, default=32)
-    ap.add_argument("--pool", type=int, default=4096)
-    ap.add_argument("--graph-steps", type=int, default=512)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--kernel-samples", type=int, default=40)
+    ap = argparse.ArgumentParser(description="Throughput of the HFQ4 MoE decode path on one MI355X; "
+                                             "prints one JSON line.")
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1 is supported)")
+    ap.add_argument("--steps", type=int, default=20000, help="timed steps (rounded to whole graphs)")
+    ap.add_argument("--warmup", type=int, default=2000, help="untimed steps before timing")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="steps as HIP-graph replays or as eager launches")
+    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+                    help="moe_layer_decode, or moe_route_topk + moe_expert_decode")
+    ap.add_argument("--replicas", type=int, default=32,
+                    help="distinct layer copies cycled through (so caches cannot serve repeats)")
+    ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
+    ap.add_argument("--graph-steps", type=int, default=512, help="steps captured per HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the oracle's CPU baseline sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--kernel-samples", type=int, default=40,
+                    help="single synchronised steps timed with HIP events for the roofline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (counter calibration)")
     ap.add_argument("--batches", default="1,4,16",
@@ -377,7 +383,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: runs on several GPUs are not supported "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
