@@ -366,7 +366,7 @@ def main():
                     help="distinct layer copies cycled through (so caches cannot serve repeats)")
     ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
     ap.add_argument("--graph-steps", type=int, default=512, help="steps captured per HIP graph")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle's CPU baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--kernel-samples", type=int, default=40,
@@ -586,7 +586,7 @@ def main():
                            "kernels_per_step": 3 if args.path == "fused" else 4},
     }
     if not args.no_cpu:
-        xs_host = xs[:64].cpu().numpy()
+        xs_host = xs[:512].cpu().numpy()
         routers_host = [L.Wr.cpu().numpy() for L in layers]
         out["cpu_baseline"] = cpu_baseline(torch, 0, xs_host, routers_host, args.cpu_seconds)
     else:
