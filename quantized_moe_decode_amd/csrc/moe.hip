@@ -278,11 +278,16 @@ __device__ void down_rows(const ExpertArgs& a, const Ws& ws, const uint8_t* hfr,
       hd[r] = bload8(rd, off);
       c[r] = bload16(rd, off + 8 + 16 * (s & 7));
     }
-    const float w = (j < k && e >= 0) ? a.wts[p] : 0.f;
+    // slots past k or out of range add nothing, whatever h holds
+    const bool slot = j < k && e >= 0;
+    const float w = slot ? a.wts[p] : 0.f;
     Frag f;
     frag_load(hfr + (j < k ? j : 0) * fb, SEGS, s, f);
 #pragma unroll
-    for (int r = 0; r < ROUT; ++r) acc[r] = __builtin_fmaf(w, dot_seg(c[r], hd[r], f), acc[r]);
+    for (int r = 0; r < ROUT; ++r) {
+      const float v = __builtin_fmaf(w, dot_seg(c[r], hd[r], f), acc[r]);
+      acc[r] = slot ? v : acc[r];
+    }
   }
 #pragma unroll
   for (int r = 0; r < ROUT; ++r) {
@@ -355,83 +360,73 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a, Ws ws) {
 
 // ====================================================================== fast path: d = 2048, F = 512, k <= 8
 
-// K2: routing (top-k from logits, or idx/wts from memory), groups, then the
-// grouped gate/up dequant-GEMV.  A wave item is FAST_RP consecutive row
-// pairs of one expert; each lane owns one 32-weight segment of every row.
-// The 2*FAST_RP row partials of a token are reduced together: two permlane
-// folds (xor 32, xor 16) and one 16-lane DPP sum leave row r's gate and up
-// sums in lanes 16r..16r+15.
+// K2, one token: routing (top-k from the router logits, or idx/wts from
+// memory), then the gate/up dequant-GEMV of the k selected experts.  A wave
+// item is FAST_RP consecutive row pairs of one expert; each lane owns one
+// 32-weight segment of every row.  The 2*FAST_RP row partials are reduced
+// together: two permlane folds (xor 32, xor 16) and one 16-lane DPP sum
+// leave row r's gate and up sums in lanes 16r..16r+15.
 template <bool FROM_LOGITS>
 __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
                                                           const float* __restrict__ logits,
                                                           int32_t* idx_out, float* wts_out) {
-  extern __shared__ __align__(16) uint8_t xfr[];
-  __shared__ Groups G;
-  __shared__ int s_idx[HFQ4_MAXB_DEV * MAXK];
-  __shared__ float s_w[HFQ4_MAXB_DEV * MAXK];
-  __shared__ uint32_t tk_scratch[4][64];
+  __shared__ __align__(16) uint8_t xfr[frag_bytes(FAST_SEGS_D)];
+  __shared__ int s_idx[MAXK];
+  __shared__ float s_w[MAXK];
+  __shared__ int s_exp[MAXK];       // expert of slot j, -1 if out of range
+  __shared__ uint32_t tk_scratch[64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int B = a.B, k = a.k, P = B * k, E = a.L.E, F = a.L.F;
+  const int k = a.k, E = a.L.E, F = a.L.F;
   const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
-  const int fb = frag_bytes(FAST_SEGS_D);
   trace_point(ws.trace, TK_GATEUP, 0);
 
-  // 1. routing; waves without a token to route stage x meanwhile
+  // 1. routing by wave 0 while waves 1-3 stage x (from logits); otherwise
+  // the given routing, and all four waves stage x
   if (FROM_LOGITS) {
-    for (int b = wv; b < B; b += 4) {
+    if (wv == 0) {
       int e;
       float w;
-      const bool nan_seen = topk_any(logits + b * E, E, k, e, w, tk_scratch[wv], ws.trace);
+      const bool nan_seen = topk_any(logits, E, k, e, w, tk_scratch, ws.trace);
       if (lane < k) {
-        s_idx[b * k + lane] = e;
-        s_w[b * k + lane] = w;
+        s_idx[lane] = e;
+        s_w[lane] = w;
       }
       if (nan_seen && lane == 0 && blockIdx.x == 0)
         __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      stage_vector(a.x, a.L.d, FAST_SEGS_D, xfr, threadIdx.x - 64, 192);
     }
   } else {
-    if (threadIdx.x < P) {
+    if (threadIdx.x < k) {
       s_idx[threadIdx.x] = a.idx[threadIdx.x];
       s_w[threadIdx.x] = a.wts[threadIdx.x];
     }
+    stage_vector(a.x, a.L.d, FAST_SEGS_D, xfr, threadIdx.x, 256);
   }
-  const int stagers = FROM_LOGITS ? (B >= 4 ? 0 : (4 - B) * 64) : 256;
-  const int stage_tid = threadIdx.x - (256 - stagers);
-  if (stagers > 0 && stage_tid >= 0)
-    for (int b = 0; b < B; ++b)
-      stage_vector(a.x + b * a.ldx, a.L.d, FAST_SEGS_D, xfr + b * fb, stage_tid, stagers);
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 1);
-  if (FROM_LOGITS && blockIdx.x == 0 && threadIdx.x < P) {
-    idx_out[threadIdx.x] = s_idx[threadIdx.x];
-    wts_out[threadIdx.x] = s_w[threadIdx.x];
-    ws.idx[threadIdx.x] = s_idx[threadIdx.x];
-    ws.wts[threadIdx.x] = s_w[threadIdx.x];
-  }
-  if (B == 1) {
-    // one token: its k experts are distinct, so every slot is its own group
-    if (threadIdx.x < k) {
-      const int e = s_idx[threadIdx.x];
-      const bool ok = e >= 0 && e < E;
-      if (!ok && blockIdx.x == 0)
-        __hip_atomic_fetch_or(ws.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int u = threadIdx.x;
-      G.gexp[u] = ok ? e : 0;
-      G.gcnt[u] = ok ? 1 : 0;
-      G.gstart[u] = u;
-      G.gmem[u] = u;
+  if (threadIdx.x < k) {
+    const int e = s_idx[threadIdx.x];
+    const bool ok = e >= 0 && e < E;
+    s_exp[threadIdx.x] = ok ? e : -1;
+    if (blockIdx.x == 0) {
+      if (FROM_LOGITS) {
+        idx_out[threadIdx.x] = e;
+        wts_out[threadIdx.x] = s_w[threadIdx.x];
+        ws.idx[threadIdx.x] = e;
+        ws.wts[threadIdx.x] = s_w[threadIdx.x];
+      }
+      if (!ok) __hip_atomic_fetch_or(ws.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (threadIdx.x == 0) G.U = k;
-    __syncthreads();
-  } else {
-    build_groups(s_idx, P, E, G, ws.err);
   }
+  __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 2);
 
-  // 2. first item's weight loads go out before x is staged (when needed)
+  // 2. compute: items (slot u, chunk c of FAST_RP rows); the first item's
+  // weight loads go out before the loop
   const int nchunk = F / FAST_RP;
-  const int items = G.U * nchunk;
+  const int items = k * nchunk;
   constexpr int64_t ROWB = 8 * BLK_BYTES;
   const uint32_t hoff = (uint32_t)((lane >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (lane & 7);
@@ -439,14 +434,14 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   u32x4 cg[FAST_RP], cu[FAST_RP];
   u32x2 hg[FAST_RP], hu[FAST_RP];
   // one wave-uniform descriptor per tensor (kernel arguments); the expert
-  // and row go into the per-lane offset
+  // and row go into the per-lane offset; a slot out of range reads zeros
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate, a.L.gate_bytes);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up, a.L.up_bytes);
   auto issue = [&](int item) {
     const int u = item / nchunk, c = item - u * nchunk;
-    const int e = G.gexp[u];
-    const uint32_t bg = (uint32_t)(e * a.L.sg + (int64_t)c * FAST_RP * ROWB);
-    const uint32_t bu = (uint32_t)(e * a.L.su + (int64_t)c * FAST_RP * ROWB);
+    const int e = s_exp[u];
+    const uint32_t bg = e >= 0 ? (uint32_t)(e * a.L.sg + (int64_t)c * FAST_RP * ROWB) : a.L.gate_bytes;
+    const uint32_t bu = e >= 0 ? (uint32_t)(e * a.L.su + (int64_t)c * FAST_RP * ROWB) : a.L.up_bytes;
 #pragma unroll
     for (int r = 0; r < FAST_RP; ++r) {
       hg[r] = bload8(rg, bg + r * ROWB + hoff);
@@ -459,33 +454,23 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
     }
   };
   if (it < items) issue(it);
-  if (FROM_LOGITS && B >= 4) {
-    for (int b = 0; b < B; ++b)
-      stage_vector(a.x + b * a.ldx, a.L.d, FAST_SEGS_D, xfr + b * fb, threadIdx.x, 256);
-    __syncthreads();
-  }
-
-  // 3. compute
   const int row = lane >> 4;
   trace_point(ws.trace, TK_GATEUP, 3);
+  Frag f;
+  frag_load(xfr, FAST_SEGS_D, lane, f);
   bool first = true;
   while (it < items) {
     const int u = it / nchunk, c = it - u * nchunk;
-    const int n = G.gcnt[u], st = G.gstart[u];
-    for (int m = 0; m < n; ++m) {
-      const int p = G.gmem[st + m];
-      Frag f;
-      frag_load(xfr + (p / k) * fb, FAST_SEGS_D, lane, f);
-      float g[FAST_RP], v[FAST_RP];
+    float g[FAST_RP], v[FAST_RP];
 #pragma unroll
-      for (int r = 0; r < FAST_RP; ++r) {
-        g[r] = dot_seg(cg[r], hg[r], f);
-        v[r] = dot_seg(cu[r], hu[r], f);
-      }
-      const float tg = row_sum16(fold16(fold32(g[0], g[2]), fold32(g[1], g[3])));
-      const float tu = row_sum16(fold16(fold32(v[0], v[2]), fold32(v[1], v[3])));
-      if ((lane & 15) == 0) ws.h[(int64_t)p * F + c * FAST_RP + row] = silu_mul(tg, tu);
+    for (int r = 0; r < FAST_RP; ++r) {
+      g[r] = dot_seg(cg[r], hg[r], f);
+      v[r] = dot_seg(cu[r], hu[r], f);
     }
+    const float tg = row_sum16(fold16(fold32(g[0], g[2]), fold32(g[1], g[3])));
+    const float tu = row_sum16(fold16(fold32(v[0], v[2]), fold32(v[1], v[3])));
+    // a slot out of range gets h = 0
+    if ((lane & 15) == 0) ws.h[(int64_t)u * F + c * FAST_RP + row] = s_exp[u] >= 0 ? silu_mul(tg, tu) : 0.f;
     if (first) {
       trace_point(ws.trace, TK_GATEUP, 4);
       first = false;
@@ -508,9 +493,8 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
       for (int q = 0; q < 4; ++q) {
         const int ci = c0 + q * nth;
         const int j = ci / per_slot, o = ci - j * per_slot;
-        const int e = ci < total ? s_idx[j] : -1;
-        v[q] = bload16(rdn, (e >= 0 && e < E) ? (uint32_t)(e * a.L.sd + (int64_t)o * 16)
-                                              : a.L.down_bytes);
+        const int e = ci < total ? s_exp[j] : -1;
+        v[q] = bload16(rdn, e >= 0 ? (uint32_t)(e * a.L.sd + (int64_t)o * 16) : a.L.down_bytes);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -523,21 +507,22 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   trace_point(ws.trace, TK_GATEUP, 5);
 }
 
-// K3: down dequant-GEMV + routing-weighted combine.  A wave owns FAST_ROWS
-// output rows; lane group g (16 lanes) takes slots g and g + 4 of the
-// token, so every lane sums w_j * partial over its two slots first and one
-// 64-lane reduction per row finishes the sum over segments and slots.
+// K3, one token: down dequant-GEMV + routing-weighted combine.  A wave owns
+// FAST_ROWS output rows; lane group g (16 lanes) takes slots g and g + 4
+// (k <= 8), so every lane sums w_j * partial over its two slots first and
+// one 64-lane reduction per row finishes the sum over segments and slots.
+// Slots past k or out of range add nothing (selected out, whatever h holds).
 __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
-  extern __shared__ __align__(16) uint8_t hfr[];
-  __shared__ int s_e[HFQ4_MAXB_DEV * MAXK];
-  __shared__ float s_w[HFQ4_MAXB_DEV * MAXK];
+  __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
+  __shared__ int s_e[8];
+  __shared__ float s_w[8];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int B = a.B, k = a.k, P = B * k, d = a.L.d, F = a.L.F;
+  const int k = a.k, d = a.L.d, F = a.L.F;
   const int g = lane >> 4, s = lane & 15;
   constexpr int64_t ROWB = 2 * BLK_BYTES;
-  const int fb = frag_bytes(FAST_SEGS_F);
+  constexpr int fb = frag_bytes(FAST_SEGS_F);
   trace_point(ws.trace, TK_DOWN, 0);
-  if (threadIdx.x < P) {
+  if (threadIdx.x < k) {
     const int e = a.idx[threadIdx.x];
     const bool ok = e >= 0 && e < a.L.E;
     s_e[threadIdx.x] = ok ? e : -1;
@@ -546,76 +531,77 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 1);
   const int r0 = (blockIdx.x * (blockDim.x >> 6) + wv) * FAST_ROWS;
-  // host-mapped layer, one token: the selected down matrices were staged in
-  // HBM by the gate/up kernel, slot j at j * dslot
+  // host-mapped layer: the selected down matrices were staged in HBM by the
+  // gate/up kernel, slot j at j * dslot
   const bool staged = ws.dstage != nullptr;
   const uint32_t dbytes = staged ? ws.dslot * (uint32_t)k : a.L.down_bytes;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(staged ? ws.dstage : a.L.down, dbytes);
   const uint32_t hoff = (uint32_t)((s >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (s & 7);
-  for (int b = 0; b < B; ++b) {
-    // h(b, j) for the k slots (one 32-value segment per thread) is loaded
-    // first, the weights of slots g and g+4 second, so that staging can
-    // start as soon as h arrives while the weight loads are still in flight
-    const int t_h = threadIdx.x;
-    const bool stager = t_h < k * FAST_SEGS_F;
-    const int j_h = t_h / FAST_SEGS_F, sg_h = t_h - j_h * FAST_SEGS_F;
-    f32x4 hv[8];
-    if (stager) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)(b * k + j_h) * F + sg_h * SEG);
+  // h(j) for the k slots (one 32-value segment per thread) is loaded first,
+  // the weights of slots g and g+4 second, so that staging can start as
+  // soon as h arrives while the weight loads are still in flight
+  const int j_h = threadIdx.x / FAST_SEGS_F, sg_h = threadIdx.x - j_h * FAST_SEGS_F;
+  const bool stager = j_h < k;
+  f32x4 hv[8];
+  if (stager) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)j_h * F + sg_h * SEG);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hv[i] = src[i];
+    for (int i = 0; i < 8; ++i) hv[i] = src[i];
+  }
+  u32x4 c[2][FAST_ROWS];
+  u32x2 hd[2][FAST_ROWS];
+  float w[2];
+  bool live[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = g + 4 * t;
+    const int e = j < k ? s_e[j] : -1;
+    live[t] = e >= 0;
+    w[t] = live[t] ? s_w[j] : 0.f;
+    // dead slots read past the end of the descriptor and get zeros
+    const uint32_t base = (live[t] && r0 < d)
+                              ? (staged ? (uint32_t)(j * ws.dslot + (int64_t)r0 * ROWB)
+                                        : (uint32_t)(e * a.L.sd + (int64_t)r0 * ROWB))
+                              : dbytes;
+#pragma unroll
+    for (int r = 0; r < FAST_ROWS; ++r) {
+      hd[t][r] = bload8(rd, base + r * ROWB + hoff);
+      c[t][r] = bload16(rd, base + r * ROWB + coff);
     }
-    u32x4 c[2][FAST_ROWS];
-    u32x2 hd[2][FAST_ROWS];
-    float w[2];
+  }
+  if (stager) {
+    float buf[32];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = g + 4 * t;
-      const int e = j < k ? s_e[b * k + j] : -1;
-      w[t] = e >= 0 ? s_w[b * k + j] : 0.f;
-      // dead slots read past the end of the descriptor and get zeros
-      const uint32_t base = (e >= 0 && r0 < d)
-                                ? (staged ? (uint32_t)(j * ws.dslot + (int64_t)r0 * ROWB)
-                                          : (uint32_t)(e * a.L.sd + (int64_t)r0 * ROWB))
-                                : dbytes;
-#pragma unroll
-      for (int r = 0; r < FAST_ROWS; ++r) {
-        hd[t][r] = bload8(rd, base + r * ROWB + hoff);
-        c[t][r] = bload16(rd, base + r * ROWB + coff);
-      }
+    for (int i = 0; i < 8; ++i) {
+      buf[4 * i] = hv[i].x; buf[4 * i + 1] = hv[i].y; buf[4 * i + 2] = hv[i].z; buf[4 * i + 3] = hv[i].w;
     }
-    if (stager) {
-      float buf[32];
+    Frag fr;
+    make_frag(buf, fr);
+    frag_store(hfr + j_h * fb, FAST_SEGS_F, sg_h, fr);
+    trace_point(ws.trace, TK_DOWN, 4);
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_DOWN, 2);
+  float acc[FAST_ROWS];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        buf[4 * i] = hv[i].x; buf[4 * i + 1] = hv[i].y; buf[4 * i + 2] = hv[i].z; buf[4 * i + 3] = hv[i].w;
-      }
-      Frag fr;
-      make_frag(buf, fr);
-      frag_store(hfr + j_h * fb, FAST_SEGS_F, sg_h, fr);
-      if (b == 0) trace_point(ws.trace, TK_DOWN, 4);
+  for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = g + 4 * t;
+    Frag f;
+    frag_load(hfr + (j < k ? j : 0) * fb, FAST_SEGS_F, s, f);
+#pragma unroll
+    for (int r = 0; r < FAST_ROWS; ++r) {
+      const float v = __builtin_fmaf(w[t], dot_seg(c[t][r], hd[t][r], f), acc[r]);
+      acc[r] = live[t] ? v : acc[r];
     }
-    __syncthreads();
-    if (b == 0) trace_point(ws.trace, TK_DOWN, 2);
-    float acc[FAST_ROWS];
-#pragma unroll
-    for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = g + 4 * t;
-      Frag f;
-      frag_load(hfr + (j < k ? j : 0) * fb, FAST_SEGS_F, s, f);
-#pragma unroll
-      for (int r = 0; r < FAST_ROWS; ++r) acc[r] = __builtin_fmaf(w[t], dot_seg(c[t][r], hd[t][r], f), acc[r]);
-    }
-    // rows 0 and 2 of t hold output rows r0 and r0+1
-    const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
-    if ((lane == 0 || lane == 32)) {
-      const int rr = r0 + (lane >> 5);
-      if (rr < d) a.y[b * a.ldy + rr] = (a.res ? a.res[b * a.ldy + rr] : 0.f) + t;
-    }
-    __syncthreads();
+  }
+  // rows 0 and 2 of t hold output rows r0 and r0+1
+  const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
+  if ((lane == 0 || lane == 32)) {
+    const int rr = r0 + (lane >> 5);
+    if (rr < d) a.y[rr] = (a.res ? a.res[rr] : 0.f) + t;
   }
   trace_point(ws.trace, TK_DOWN, 3);
 }
@@ -752,14 +738,12 @@ static int launch_generic_experts(const ExpertArgs& a, Ws ws, hipStream_t s) {
 static int launch_fast(const ExpertArgs& a, Ws ws, const float* logits, int32_t* idx_out,
                        float* wts_out, hipStream_t s) {
   const int nwg = num_cus();
-  const size_t shm = (size_t)a.B * frag_bytes(FAST_SEGS_D);
+  if (a.B != 1 || a.k > 8) return (int)hipErrorInvalidValue;   // one token, k <= 8
   if (logits) {
-    if (int e = allow_lds(gateup_fast_kernel<true>, shm)) return e;
-    hipExtLaunchKernelGGL(gateup_fast_kernel<true>, dim3(nwg), dim3(256), shm, s, g_ev_start,
+    hipExtLaunchKernelGGL(gateup_fast_kernel<true>, dim3(nwg), dim3(256), 0, s, g_ev_start,
                           g_ev_stop, 0, a, ws, logits, idx_out, wts_out);
   } else {
-    if (int e = allow_lds(gateup_fast_kernel<false>, shm)) return e;
-    hipExtLaunchKernelGGL(gateup_fast_kernel<false>, dim3(nwg), dim3(256), shm, s, g_ev_start,
+    hipExtLaunchKernelGGL(gateup_fast_kernel<false>, dim3(nwg), dim3(256), 0, s, g_ev_start,
                           g_ev_stop, 0, a, ws, (const float*)nullptr, (int32_t*)nullptr,
                           (float*)nullptr);
   }
@@ -771,8 +755,7 @@ static int launch_fast(const ExpertArgs& a, Ws ws, const float* logits, int32_t*
     ad.wts = ws.wts;
   }
   const int waves = (a.L.d + FAST_ROWS - 1) / FAST_ROWS;
-  hipLaunchKernelGGL(down_fast_kernel, dim3((waves + 3) / 4), dim3(256),
-                     (size_t)a.k * frag_bytes(FAST_SEGS_F), s, ad, ws);
+  hipLaunchKernelGGL(down_fast_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, ad, ws);
   return (int)hipGetLastError();
 }
 

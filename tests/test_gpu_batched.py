@@ -153,6 +153,31 @@ def test_batched_duplicates_and_invalid(q):
         assert rel_l2(yg[b], ref) <= REL_L2_TOL, b
 
 
+def test_batched_invalid_ignores_stale_h(q):
+    """An out-of-range slot adds nothing when the workspace still holds
+    non-finite h from an earlier call."""
+    B, k, d, E = 3, 8, 2048, 32
+    L, cache = _layer(q, 21, E, d)
+    say("batched invalid, stale h")
+    ws = q.new_workspace(L, B, k)
+    idx0 = torch.arange(k, dtype=torch.int32, device="cuda").repeat(B, 1)
+    wts = torch.full((B, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    xbad = torch.full((B, d), float("nan"), dtype=torch.float32, device="cuda")
+    q.moe_expert_decode(L, xbad, idx0, wts, ws)
+    torch.cuda.synchronize()
+    x = synth.activations(torch, "cuda", 12, B, d)
+    idx = idx0.clone()
+    idx[1, 2] = -5
+    y = q.moe_expert_decode(L, x, idx, wts, ws).cpu().numpy()
+    assert q.workspace_error(ws) & q.HFQ4_DEV_ERR_INDEX
+    assert np.all(np.isfinite(y))
+    xs = x.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        outs = [moe.expert_forward(cache(j), xs[b]) for j in range(k) if not (b == 1 and j == 2)]
+        ref = moe.combine(outs, np.full(len(outs), 1.0 / k))
+        assert rel_l2(y[b], ref) <= REL_L2_TOL, b
+
+
 def test_batched_all_invalid_gives_residual(q):
     B, k, d, E = 3, 8, 2048, 16
     L, _ = _layer(q, 21, E, d)

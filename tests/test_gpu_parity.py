@@ -229,6 +229,34 @@ def test_expert_decode_bad_index_skipped(qs):
     assert rel_l2(y[0], ref) <= REL_L2_TOL
 
 
+@pytest.mark.parametrize("E,d,F,k", [(64, 2048, 512, 8), (16, 256, 128, 2), (40, 1024, 300, 5)])
+def test_bad_index_ignores_stale_h(qs, E, d, F, k):
+    """A slot whose index is out of range adds nothing, also when the
+    workspace still holds non-finite h from an earlier call (one token: the
+    tuned kernels for d = 2048, F = 512, the generic ones otherwise)."""
+    q = qs
+    say("bad index, stale h", E, d, F, k)
+    layer = q.synthetic.build_layer(torch, seed=3, layer_id=0, E=E, d=d, F=F)
+    cache = ExpertCache(torch, "cuda", 3, 0, d, F)
+    ws = q.new_workspace(layer, 1, k)
+    idx0 = torch.arange(k, dtype=torch.int32, device="cuda").view(1, k)
+    wts = torch.full((1, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    xbad = torch.full((1, d), float("nan"), dtype=torch.float32, device="cuda")
+    q.moe_expert_decode(layer, xbad, idx0, wts, ws)        # every h slot now NaN
+    torch.cuda.synchronize()
+    assert q.workspace_error(ws) == 0
+    x = synth.activations(torch, "cuda", 5, 1, d)
+    idx = idx0.clone()
+    idx[0, 1] = E + 7
+    y = q.moe_expert_decode(layer, x, idx, wts, ws).cpu().numpy()
+    assert q.workspace_error(ws) & q.HFQ4_DEV_ERR_INDEX
+    assert np.all(np.isfinite(y))
+    xs = x.cpu().numpy().astype(np.float64)[0]
+    outs = [moe.expert_forward(cache(j), xs) for j in range(k) if j != 1]
+    ref = moe.combine(outs, np.full(len(outs), 1.0 / k))
+    assert rel_l2(y[0], ref) <= REL_L2_TOL
+
+
 @pytest.fixture(scope="module")
 def c2(qs):
     say("building 256-expert layer d=2048 F=512")
