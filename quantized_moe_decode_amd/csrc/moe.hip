@@ -42,12 +42,14 @@ namespace hq {
 
 // ====================================================================== routing
 
-// Router logits, one workgroup per expert row: the four waves split the row
-// into quarters, each lane keeps up to 8 float4 loads in flight, partial
-// sums meet in LDS and are added in a fixed order.
+// Router logits of one token, one workgroup per expert row: the four waves
+// split the row into quarters, each lane keeps up to 8 float4 loads of the
+// row and 8 of x in flight (buffer loads, so lanes past a quarter's end read
+// zeros without a branch), and the wave sums meet in LDS and are added in a
+// fixed order.  (Two or more tokens use the batched router.)
 __global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restrict__ logits,
                                                      uint64_t* trace) {
-  __shared__ float part[4][HFQ4_MAXB_DEV];
+  __shared__ float part[4];
   trace_point(trace, TK_LOGITS, 0);
   const int e = blockIdx.x;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -55,45 +57,35 @@ __global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restr
   const int qw = (nq + 3) >> 2;
   const int q_lo = wv * qw;
   const int q_hi = q_lo + qw < nq ? q_lo + qw : nq;
-  const f32x4* wr = reinterpret_cast<const f32x4*>(a.Wr + (int64_t)e * a.d);
-  float acc[HFQ4_MAXB_DEV];
-#pragma unroll
-  for (int b = 0; b < HFQ4_MAXB_DEV; ++b) acc[b] = 0.f;
+  const uint32_t rowb = 4u * (uint32_t)a.d;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr + (int64_t)e * a.d, rowb);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, rowb);
+  float acc = 0.f;
   for (int q0 = q_lo; q0 < q_hi; q0 += 64 * 8) {
-    f32x4 w[8];
+    u32x4 w[8], xv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int q = q0 + u * 64 + lane;
-      w[u] = q < q_hi ? wr[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint32_t off = q < q_hi ? 16u * (uint32_t)q : rowb;
+      w[u] = bload16(rw, off);
+      xv[u] = bload16(rx, off);
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
 #pragma unroll
-    for (int b = 0; b < HFQ4_MAXB_DEV; ++b) {
-      if (b < a.B) {
-        const f32x4* xb = reinterpret_cast<const f32x4*>(a.x + b * a.ldx);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int q = q0 + u * 64 + lane;
-          const f32x4 xv = q < q_hi ? xb[q] : f32x4{0.f, 0.f, 0.f, 0.f};
-          acc[b] = __builtin_fmaf(w[u].x, xv.x, acc[b]);
-          acc[b] = __builtin_fmaf(w[u].y, xv.y, acc[b]);
-          acc[b] = __builtin_fmaf(w[u].z, xv.z, acc[b]);
-          acc[b] = __builtin_fmaf(w[u].w, xv.w, acc[b]);
-        }
-      }
+    for (int u = 0; u < 8; ++u) {
+      acc = __builtin_fmaf(as_f32(w[u].x), as_f32(xv[u].x), acc);
+      acc = __builtin_fmaf(as_f32(w[u].y), as_f32(xv[u].y), acc);
+      acc = __builtin_fmaf(as_f32(w[u].z), as_f32(xv[u].z), acc);
+      acc = __builtin_fmaf(as_f32(w[u].w), as_f32(xv[u].w), acc);
     }
   }
-#pragma unroll
-  for (int b = 0; b < HFQ4_MAXB_DEV; ++b)
-    if (b < a.B) {
-      const float t = wave_sum(acc[b]);
-      if (lane == 0) part[wv][b] = t;
-    }
+  const float t = wave_sum(acc);
+  if (lane == 0) part[wv] = t;
   __syncthreads();
-  if (threadIdx.x < a.B) {
-    const int b = threadIdx.x;
-    const float l = ((part[0][b] + part[1][b]) + (part[2][b] + part[3][b])) + (a.bias ? a.bias[e] : 0.f);
-    logits[b * a.E + e] = l;
-    if (a.logits_out) a.logits_out[b * a.E + e] = l;
+  if (threadIdx.x == 0) {
+    const float l = ((part[0] + part[1]) + (part[2] + part[3])) + (a.bias ? a.bias[e] : 0.f);
+    logits[e] = l;
+    if (a.logits_out) a.logits_out[e] = l;
   }
   trace_point(trace, TK_LOGITS, 1);
 }
