@@ -506,22 +506,31 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
 // Slots past k or out of range add nothing (selected out, whatever h holds).
 __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
-  __shared__ int s_e[8];
-  __shared__ float s_w[8];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k, d = a.L.d, F = a.L.F;
   const int g = lane >> 4, s = lane & 15;
   constexpr int64_t ROWB = 2 * BLK_BYTES;
   constexpr int fb = frag_bytes(FAST_SEGS_F);
   trace_point(ws.trace, TK_DOWN, 0);
-  if (threadIdx.x < k) {
-    const int e = a.idx[threadIdx.x];
-    const bool ok = e >= 0 && e < a.L.E;
-    s_e[threadIdx.x] = ok ? e : -1;
-    s_w[threadIdx.x] = ok ? a.wts[threadIdx.x] : 0.f;
-  }
-  __syncthreads();
-  trace_point(ws.trace, TK_DOWN, 1);
+  // Every wave reads the routing itself (lane j < k: slot j) and h(j) for
+  // the k slots (one 32-value segment per thread of the workgroup); both go
+  // out at once.  The weights of slots g and g+4 follow as soon as the
+  // routing has arrived, so that staging h overlaps the weight loads.
+  // Buffer loads without branches: lanes past the end read zeros, and all
+  // lanes have the same loads in flight, so the routing can be waited for
+  // alone.
+  const uint32_t rbytes = 4u * (uint32_t)k;
+  const uint32_t ro = lane < k ? 4u * lane : rbytes;
+  const int e_in = (int)bload4(make_rsrc(a.idx, rbytes), ro);
+  const float w_in = as_f32(bload4(make_rsrc(a.wts, rbytes), ro));
+  const int j_h = threadIdx.x / FAST_SEGS_F, sg_h = threadIdx.x - j_h * FAST_SEGS_F;
+  const bool stager = j_h < k;
+  const uint32_t hbytes = 4u * (uint32_t)(k * F);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(ws.h, hbytes);
+  const uint32_t ho = stager ? 4u * (uint32_t)(j_h * F + sg_h * SEG) : hbytes;
+  u32x4 hv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hv[i] = bload16(rh, ho + 16 * i);
   const int r0 = (blockIdx.x * (blockDim.x >> 6) + wv) * FAST_ROWS;
   // host-mapped layer: the selected down matrices were staged in HBM by the
   // gate/up kernel, slot j at j * dslot
@@ -530,17 +539,6 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(staged ? ws.dstage : a.L.down, dbytes);
   const uint32_t hoff = (uint32_t)((s >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (s & 7);
-  // h(j) for the k slots (one 32-value segment per thread) is loaded first,
-  // the weights of slots g and g+4 second, so that staging can start as
-  // soon as h arrives while the weight loads are still in flight
-  const int j_h = threadIdx.x / FAST_SEGS_F, sg_h = threadIdx.x - j_h * FAST_SEGS_F;
-  const bool stager = j_h < k;
-  f32x4 hv[8];
-  if (stager) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(ws.h + (int64_t)j_h * F + sg_h * SEG);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hv[i] = src[i];
-  }
   u32x4 c[2][FAST_ROWS];
   u32x2 hd[2][FAST_ROWS];
   float w[2];
@@ -548,9 +546,9 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int j = g + 4 * t;
-    const int e = j < k ? s_e[j] : -1;
-    live[t] = e >= 0;
-    w[t] = live[t] ? s_w[j] : 0.f;
+    const int e = __shfl(e_in, j, 64);
+    live[t] = j < k && e >= 0 && e < a.L.E;
+    w[t] = __shfl(w_in, j, 64);
     // dead slots read past the end of the descriptor and get zeros
     const uint32_t base = (live[t] && r0 < d)
                               ? (staged ? (uint32_t)(j * ws.dslot + (int64_t)r0 * ROWB)
@@ -562,11 +560,13 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
       c[t][r] = bload16(rd, base + r * ROWB + coff);
     }
   }
+  trace_point(ws.trace, TK_DOWN, 1);
   if (stager) {
     float buf[32];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      buf[4 * i] = hv[i].x; buf[4 * i + 1] = hv[i].y; buf[4 * i + 2] = hv[i].z; buf[4 * i + 3] = hv[i].w;
+      buf[4 * i] = as_f32(hv[i].x); buf[4 * i + 1] = as_f32(hv[i].y);
+      buf[4 * i + 2] = as_f32(hv[i].z); buf[4 * i + 3] = as_f32(hv[i].w);
     }
     Frag fr;
     make_frag(buf, fr);
