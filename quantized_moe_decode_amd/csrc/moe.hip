@@ -383,6 +383,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
       if (lane < k) {
         s_idx[lane] = e;
         s_w[lane] = w;
+        s_exp[lane] = e;   // a selection is always in range
       }
       if (nan_seen && lane == 0 && blockIdx.x == 0)
         __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -391,28 +392,26 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
     }
   } else {
     if (threadIdx.x < k) {
-      s_idx[threadIdx.x] = a.idx[threadIdx.x];
+      const int e = a.idx[threadIdx.x];
+      s_idx[threadIdx.x] = e;
       s_w[threadIdx.x] = a.wts[threadIdx.x];
+      s_exp[threadIdx.x] = e >= 0 && e < E ? e : -1;
     }
     stage_vector(a.x, a.L.d, FAST_SEGS_D, xfr, threadIdx.x, 256);
   }
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 1);
-  if (threadIdx.x < k) {
+  if (blockIdx.x == 0 && threadIdx.x < k) {
     const int e = s_idx[threadIdx.x];
-    const bool ok = e >= 0 && e < E;
-    s_exp[threadIdx.x] = ok ? e : -1;
-    if (blockIdx.x == 0) {
-      if (FROM_LOGITS) {
-        idx_out[threadIdx.x] = e;
-        wts_out[threadIdx.x] = s_w[threadIdx.x];
-        ws.idx[threadIdx.x] = e;
-        ws.wts[threadIdx.x] = s_w[threadIdx.x];
-      }
-      if (!ok) __hip_atomic_fetch_or(ws.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (FROM_LOGITS) {
+      idx_out[threadIdx.x] = e;
+      wts_out[threadIdx.x] = s_w[threadIdx.x];
+      ws.idx[threadIdx.x] = e;
+      ws.wts[threadIdx.x] = s_w[threadIdx.x];
     }
+    if (s_exp[threadIdx.x] < 0)
+      __hip_atomic_fetch_or(ws.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 2);
 
   // 2. compute: items (slot u, chunk c of FAST_RP rows); the first item's

@@ -18,10 +18,10 @@ namespace hq {
 // -0 and +0 give the same key, NaN sorts below -inf (key 1), and key 0 is
 // reserved for "no expert" (padding lanes).
 __device__ __forceinline__ uint32_t okey(float f) {
-  if (__builtin_isnan(f)) return 1u;
   uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u << 1) == 0u) u = 0u;                     // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = (u << 1) == 0u ? 0u : u;                    // -0 -> +0
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return __builtin_isnan(f) ? 1u : k;             // selects, no branches
 }
 __device__ __forceinline__ float okey_value(uint32_t k) {
   return as_f32((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -55,10 +55,14 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ logits, int E
   const int lane = threadIdx.x & 63;
   int nan_seen = 0;
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits, (uint32_t)((E + 3) & ~3) * 4u);
+  u32x4 raw4[PER / 4];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) raw4[i / 4] = bload16(rl, (uint32_t)(lane * PER + i) * 4u);
+  __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first use
 #pragma unroll
   for (int i = 0; i < PER; i += 4) {
     const int e0 = lane * PER + i;
-    const u32x4 raw = bload16(rl, (uint32_t)e0 * 4u);
+    const u32x4 raw = raw4[i / 4];
     const uint32_t rv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
