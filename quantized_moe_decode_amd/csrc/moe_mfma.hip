@@ -266,6 +266,7 @@ __global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __
       xv[s] = bload16(rx, (tok_ok && kin) ? (uint32_t)(((int64_t)n16 * a.ldx + ki) * 4) : xbytes);
       wv4[s] = bload16(rw, (row_ok && kin) ? (uint32_t)(((int64_t)row * a.d + ki) * 4) : wbytes);
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first product
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(xv[s].x), as_f32(wv4[s].x), acc, 0, 0, 0);
