@@ -31,9 +31,18 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
   const int64_t row0 = wave * (RPW * G);
 
-  // Issue this wave's weight loads first: they do not depend on x.  One
-  // wave-uniform descriptor covers the matrix (rows * ROWB < 2^31, split by
-  // the launcher); rows past the end and dead lanes read zeros.
+  // Token 0's activations go out first (eight lanes per segment, one pass:
+  // SEGS <= 64 = 2 x 32 segment groups of the 256 threads), then this
+  // wave's weight loads, so that x is converted while the weights are in
+  // flight.  With K not a multiple of 4 the staging below reads x itself.
+  const bool k4 = (K & 3) == 0;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, 4u * (uint32_t)K);
+  const int j8 = threadIdx.x & 7, s8 = threadIdx.x >> 3, G8 = blockDim.x >> 3;
+  const f32x4 xa = load_seg8(rx, k4 && s8 < SEGS ? s8 : -1, j8);
+  const f32x4 xb = load_seg8(rx, k4 && s8 + G8 < SEGS ? s8 + G8 : -1, j8);
+
+  // One wave-uniform descriptor covers the matrix (rows * ROWB < 2^31,
+  // split by the launcher); rows past the end and dead lanes read zeros.
   u32x4 codes[RPW];
   u32x2 hdr[RPW];
   int64_t nhere = rows - row0;
@@ -51,8 +60,15 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
   }
 
   const int fb = frag_bytes(SEGS);
-  for (int b = 0; b < batch; ++b)
-    stage_vector(x + b * ldx, K, SEGS, lds + b * fb, threadIdx.x, blockDim.x);
+  if (k4) {
+    if (s8 < SEGS) build_seg8(xa, SEGS, s8, j8, lds);            // uniform per lane group
+    if (s8 + G8 < SEGS) build_seg8(xb, SEGS, s8 + G8, j8, lds);
+    for (int b = 1; b < batch; ++b)
+      stage_vector8(x + b * ldx, K, SEGS, lds + b * fb, threadIdx.x, blockDim.x);
+  } else {
+    for (int b = 0; b < batch; ++b)
+      stage_vector(x + b * ldx, K, SEGS, lds + b * fb, threadIdx.x, blockDim.x);
+  }
   __syncthreads();
   if (nhere == 0) return;
 

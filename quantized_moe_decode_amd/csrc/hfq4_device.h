@@ -258,6 +258,92 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// ---------------------------------------------------------------- eight-lane fragment builder
+// Eight lanes (an aligned lane group, all active) build one segment's
+// fragment with the same arithmetic as make_frag, up to the order of the
+// three sums: lane j holds elements 4j..4j+3 of the segment, so one load
+// instruction of a wave covers 1 KB of contiguous input.  Lanes 2w and
+// 2w+1 swap values to form the four f16 pairs of plane dword w (two pairs
+// each); the segment maximum and sums are 8-lane DPP reductions.  The
+// result goes to dst in the frag_store layout.
+//
+// Loads go through a buffer descriptor over the vector's 4n bytes with n a
+// multiple of 4 (a 16-byte load is wholly inside or wholly outside it), so
+// segments past the end, and segment -1, read zeros without a branch.
+__device__ __forceinline__ f32x4 load_seg8(__amdgpu_buffer_rsrc_t rv, int s, int j) {
+  const uint32_t off = s >= 0 ? (uint32_t)(4 * (s * SEG + 4 * j)) : 0xfffffff0u;
+  const u32x4 t = bload16(rv, off);
+  return f32x4{as_f32(t.x), as_f32(t.y), as_f32(t.z), as_f32(t.w)};
+}
+__device__ __forceinline__ float sum8(float v) {   // mirror, xor 1, xor 2
+  v += dpp<0x141>(v);
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v;
+}
+__device__ __forceinline__ void build_seg8(f32x4 xv, int S, int s, int j, uint8_t* dst) {
+  const int w = j >> 1, hf = j & 1;
+  float amax = fmaxf(fmaxf(fabsf(xv.x), fabsf(xv.y)), fmaxf(fabsf(xv.z), fabsf(xv.w)));
+  amax = fmaxf(amax, dpp<0x141>(amax));
+  amax = fmaxf(amax, dpp<0xB1>(amax));
+  amax = fmaxf(amax, dpp<0x4E>(amax));
+  int e = 0;
+  if (amax > 0.f && amax < INFINITY) {
+    int ex;
+    frexpf(amax, &ex);           // amax = m * 2^ex, m in [0.5, 1)
+    e = ex - 2;                  // amax * 2^-e in [2, 4)
+  }
+  const float inv = ldexpf(1.0f, -e);
+  // Lane hf = 0 holds elements 8w..8w+3 (the first of each pair), hf = 1
+  // holds 8w+4..8w+7 (the second).  This lane forms pairs p = 2hf + t
+  // (t = 0, 1), elements (8w+p, 8w+p+4): it keeps its values t (hf = 0) or
+  // 2+t (hf = 1) and receives the partner's values of the same index.
+  const float keep0 = hf ? xv.z : xv.x, keep1 = hf ? xv.w : xv.y;
+  const float send0 = hf ? xv.x : xv.z, send1 = hf ? xv.y : xv.w;
+  const float got0 = dpp<0xB1>(send0), got1 = dpp<0xB1>(send1);
+  float sum_half = 0.f, sum_x16 = 0.f, sx = 0.f;
+  uint32_t out[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float kv = t ? keep1 : keep0, gv = t ? got1 : got0;
+    const float av = hf ? gv : kv, bv = hf ? kv : gv;
+    const float sc = t ? 0.0625f : 1.0f;   // p is odd exactly when t is: pairs 1, 3 meet 16q
+    const _Float16 ha = (_Float16)(av * inv * sc), hb = (_Float16)(bv * inv * sc);
+    out[t] = as_u32(h2{ha, hb});
+    const float fa = (float)ha, fb = (float)hb;
+    sum_half += fa + fb;
+    sum_x16 += t ? 16.f * (fa + fb) : (fa + fb);
+    sx += av + bv;
+  }
+  *reinterpret_cast<u32x2*>(dst + 16 * (w * S + s) + 8 * hf) = u32x2{out[0], out[1]};
+  sum_half = sum8(sum_half);
+  sum_x16 = sum8(sum_x16);
+  sx = sum8(sx);
+  if (j == 0)
+    *reinterpret_cast<f32x4*>(dst + 64 * S + 16 * s) =
+        f32x4{-(1024.f * sum_half + 8.f * sum_x16), sx, ldexpf(1.0f, e), 0.f};
+}
+// All S segments of v (n values, n a multiple of 4, the rest 0) into
+// fragments at dst, eight lanes per segment, with the loads of up to four
+// segments per lane in flight before any is used.  nthreads is a multiple
+// of 64, tid & 63 is the lane.
+__device__ __forceinline__ void stage_vector8(const float* __restrict__ v, int n, int S,
+                                              uint8_t* dst, int tid, int nthreads) {
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v, 4u * (uint32_t)n);
+  const int j = tid & 7;
+  const int G = nthreads >> 3;   // segments per pass
+  for (int s0 = tid >> 3; s0 < S; s0 += 4 * G) {
+    const f32x4 x0 = load_seg8(rv, s0 < S ? s0 : -1, j);
+    const f32x4 x1 = load_seg8(rv, s0 + G < S ? s0 + G : -1, j);
+    const f32x4 x2 = load_seg8(rv, s0 + 2 * G < S ? s0 + 2 * G : -1, j);
+    const f32x4 x3 = load_seg8(rv, s0 + 3 * G < S ? s0 + 3 * G : -1, j);
+    build_seg8(x0, S, s0, j, dst);                   // conditions uniform per group
+    if (s0 + G < S) build_seg8(x1, S, s0 + G, j, dst);
+    if (s0 + 2 * G < S) build_seg8(x2, S, s0 + 2 * G, j, dst);
+    if (s0 + 3 * G < S) build_seg8(x3, S, s0 + 3 * G, j, dst);
+  }
+}
+
 __device__ __forceinline__ void trace_point_at(uint64_t* trace, int kernel, int wg, int point) {
   if (trace && threadIdx.x == 0 && wg < 1024)
     trace[((size_t)kernel * 1024 + wg) * 8 + point] = __builtin_amdgcn_s_memrealtime();
