@@ -14,8 +14,8 @@
 // output = sum_j w_j y_{e_j} (+ optional residual).
 //
 // Kernels
-//   logits_kernel  router GEMV, one workgroup per expert row (one token, and
-//                  the generic shapes).
+//   logits_kernel  router GEMV of one token, one workgroup per expert row
+//                  (every shape; two or more tokens use the batched router).
 //   topk_kernel    standalone top-k, one wave per token (moe_route_topk for
 //                  one token, and the generic shapes).
 //   gateup_kernel  grouped gate/up dequant-GEMV: tokens that picked the same
@@ -23,9 +23,9 @@
 //   down_kernel    down dequant-GEMV for every (token, slot), weighted by the
 //                  routing weight and summed per lane before one cross-lane
 //                  reduction per output row (fixed order, no atomics).
-//   fast path      (d = 2048, F = 512, k <= 8): K2 = per-workgroup top-k +
-//                  grouped gate/up, K3 = down + combine, reductions by DPP and
-//                  gfx950 permlane swaps.  A kernel boundary is the cheapest
+//   fast path      one token, 1792 < d <= 2048, F = 512, k <= 8: K2 =
+//                  per-workgroup top-k + gate/up of the k experts, K3 = down +
+//                  combine, reductions by DPP and gfx950 permlane swaps.  A kernel boundary is the cheapest
 //                  grid-wide synchronisation on MI355X (about 1.5 us inside a
 //                  HIP graph, against 2.4-10 us for an in-kernel barrier over
 //                  256 workgroups), so the layer is three dependent launches:
