@@ -84,7 +84,8 @@ def test_pack_rejects_nonfinite(q):
                                                 (64, 2048, 1, False), (2051, 2048, 1, True),
                                                 (300, 300, 4, False), (129, 1000, 16, True),
                                                 (40, 4096, 2, False), (17, 16384, 2, True),
-                                                (2048, 512, 16, False)])
+                                                (2048, 512, 16, False), (33, 1001, 3, True),
+                                                (5, 257, 1, False), (96, 2046, 1, True)])
 def test_gemv(q, rows, K, batch, resid):
     say("hfq4_gemv", rows, K, batch, resid)
     rng = np.random.default_rng(rows + 31 * K + batch)
