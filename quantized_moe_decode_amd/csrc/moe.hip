@@ -93,12 +93,11 @@ __global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restr
 // Standalone top-k: one wave per token.
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int E, int B,
                                                    int k, int32_t* idx, float* wts, uint32_t* err) {
-  __shared__ uint32_t scratch[4][64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int b = wv; b < B; b += (blockDim.x >> 6)) {
     int e;
     float w;
-    const bool nan_seen = topk_any(logits + b * E, E, k, e, w, scratch[wv], nullptr);
+    const bool nan_seen = topk_any(logits + b * E, E, k, k, e, w, nullptr);
     if (lane < k) {
       idx[b * k + lane] = e;
       wts[b * k + lane] = w;
@@ -366,20 +365,35 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   __shared__ int s_idx[MAXK];
   __shared__ float s_w[MAXK];
   __shared__ int s_exp[MAXK];       // expert of slot j, -1 if out of range
-  __shared__ uint32_t tk_scratch[64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k, E = a.L.E, F = a.L.F;
   const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
+  const int nchunk = F / FAST_RP;
+  const int items = k * nchunk;   // (slot u, chunk c of FAST_RP rows)
   trace_point(ws.trace, TK_GATEUP, 0);
 
   // 1. routing by wave 0 while waves 1-3 stage x (from logits); otherwise
   // the given routing, and all four waves stage x
   if (FROM_LOGITS) {
     if (wv == 0) {
+      // The selection comes out one slot per round and this workgroup's
+      // items need slots up to the last one they touch, so it stops there
+      // and its weight loads go out sooner; workgroup 0 runs all k rounds
+      // and publishes the routing, and a host-mapped layer (every workgroup
+      // copies every slot's down matrix) needs them all too.
+      int need = k;
+      if (blockIdx.x != 0 && !ws.dstage) {
+        int umax = -1;
+        for (int w = 0; w < 4; ++w) {
+          const int g0 = blockIdx.x * 4 + w;
+          if (g0 < items) umax = max(umax, (g0 + ((items - 1 - g0) / nw) * nw) / nchunk);
+        }
+        need = umax + 1;
+      }
       int e;
       float w;
-      const bool nan_seen = topk_any(logits, E, k, e, w, tk_scratch, ws.trace);
+      const bool nan_seen = topk_any(logits, E, k, need, e, w, ws.trace);
       if (lane < k) {
         s_idx[lane] = e;
         s_w[lane] = w;
@@ -414,10 +428,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   }
   trace_point(ws.trace, TK_GATEUP, 2);
 
-  // 2. compute: items (slot u, chunk c of FAST_RP rows); the first item's
-  // weight loads go out before the loop
-  const int nchunk = F / FAST_RP;
-  const int items = k * nchunk;
+  // 2. compute: the first item's weight loads go out before the loop
   constexpr int64_t ROWB = 8 * BLK_BYTES;
   const uint32_t hoff = (uint32_t)((lane >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (lane & 7);

@@ -364,7 +364,7 @@ __device__ void route_token(const BatchRouteArgs& r, int b, const RouteLoads<PER
   trace_point(r.trace, TK_TOPK, 2);
   int e;
   float w;
-  topk_keys<PER>(key, r.E, r.k, e, w, nullptr, nullptr);
+  topk_keys<PER>(key, r.E, r.k, r.k, e, w, nullptr);
   trace_point(r.trace, TK_TOPK, 3);
   if (lane < r.k) {
     const int p = b * r.k + lane;

@@ -117,12 +117,13 @@ __device__ __forceinline__ void local_sort(uint32_t* kk, uint32_t* ii) {
 //     fixed order.
 // k rounds of one reduction each replace a bit-serial threshold search:
 // the dependent chain per token is k wave reductions long.
-// Lanes j < k end with the j-th expert and its weight.  k <= 16.
+// Lanes j < k end with the j-th expert and its weight.  k <= 16.  A caller
+// that needs only the first `rounds` < k experts stops there: lanes
+// j < rounds get them (the same as the full run's), and no weights.
 template <int PER>
-__device__ void topk_keys(const uint32_t* key, int E, int k, int& sel_e, float& sel_w,
-                          uint32_t* scratch, uint64_t* trace) {
+__device__ void topk_keys(const uint32_t* key, int E, int k, int rounds, int& sel_e, float& sel_w,
+                          uint64_t* trace) {
   const int lane = threadIdx.x & 63;
-  (void)scratch;
   uint32_t kk[PER], ii[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -132,7 +133,7 @@ __device__ void topk_keys(const uint32_t* key, int E, int k, int& sel_e, float& 
   local_sort<PER>(kk, ii);
   trace_point(trace, TK_TOPK, 2);
   uint32_t mk = 0, me = 0xFFFFFFFFu;     // lanes >= k hold "after everything"
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < rounds; ++j) {
     const uint32_t m = wave_max_u32(kk[0]);
     const uint64_t who = __ballot(kk[0] == m);
     const int wl = (int)__builtin_ctzll(who);
@@ -151,6 +152,9 @@ __device__ void topk_keys(const uint32_t* key, int E, int k, int& sel_e, float& 
     ii[PER - 1] = pop ? 0xFFFFFFFFu : ii[PER - 1];
   }
   trace_point(trace, TK_TOPK, 4);
+  sel_e = lane < rounds ? (int)me : -1;
+  sel_w = 0.f;
+  if (rounds < k) return;
   // 3. weights
   const float l = okey_value(mk);
   const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), 0));
@@ -161,28 +165,27 @@ __device__ void topk_keys(const uint32_t* key, int E, int k, int& sel_e, float& 
   sum += dpp<0x141>(sum);
   if (k > 8) sum += dpp<0x128>(sum);   // lanes 0-7 add lanes 8-15
   sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 0));
-  sel_e = lane < k ? (int)me : -1;
   sel_w = ex / sum;
   trace_point(trace, TK_TOPK, 1);
 }
 
-// Top-k of one token's E logits (global memory) by one wave.  Returns
-// whether a NaN logit was seen.
+// Top-k of one token's E logits (global memory) by one wave (the first
+// `rounds` of them, see topk_keys).  Returns whether a NaN logit was seen.
 template <int PER>
-__device__ bool topk_wave(const float* __restrict__ logits, int E, int k, int& sel_e, float& sel_w,
-                          uint32_t* scratch, uint64_t* trace) {
+__device__ bool topk_wave(const float* __restrict__ logits, int E, int k, int rounds, int& sel_e,
+                          float& sel_w, uint64_t* trace) {
   uint32_t key[PER];
   const int nan_seen = load_keys<PER>(logits, E, key);
   trace_point(trace, TK_TOPK, 0);
-  topk_keys<PER>(key, E, k, sel_e, sel_w, scratch, trace);
+  topk_keys<PER>(key, E, k, rounds, sel_e, sel_w, trace);
   return __any(nan_seen);
 }
 
-__device__ bool topk_any(const float* logits, int E, int k, int& e, float& w, uint32_t* scratch,
+__device__ bool topk_any(const float* logits, int E, int k, int rounds, int& e, float& w,
                          uint64_t* trace) {
-  if (E <= 256) return topk_wave<4>(logits, E, k, e, w, scratch, trace);
-  if (E <= 512) return topk_wave<8>(logits, E, k, e, w, scratch, trace);
-  return topk_wave<16>(logits, E, k, e, w, scratch, trace);
+  if (E <= 256) return topk_wave<4>(logits, E, k, rounds, e, w, trace);
+  if (E <= 512) return topk_wave<8>(logits, E, k, rounds, e, w, trace);
+  return topk_wave<16>(logits, E, k, rounds, e, w, trace);
 }
 
 }  // namespace hq

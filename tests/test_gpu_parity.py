@@ -94,7 +94,12 @@ def test_gemv(q, rows, K, batch, resid):
     x = rng.standard_normal((batch, K)).astype(np.float32)
     r = rng.standard_normal((batch, rows)).astype(np.float32) if resid else None
     Wd = torch.from_numpy(P).cuda()
-    y = q.hfq4_gemv(Wd, rows, K, torch.from_numpy(x).cuda(),
+    # rows of x padded to a multiple of 4 floats (the ABI's ldx rule)
+    ldx = (K + 3) // 4 * 4
+    xp = np.full((batch, ldx), 7.0, dtype=np.float32)
+    xp[:, :K] = x
+    xd = torch.from_numpy(xp).cuda()[:, :K]
+    y = q.hfq4_gemv(Wd, rows, K, xd,
                     residual=None if r is None else torch.from_numpy(r).cuda()).cpu().numpy()
     ref = hfq4.matvec(P, rows, K, x)
     if r is not None:
@@ -102,7 +107,7 @@ def test_gemv(q, rows, K, batch, resid):
     for b in range(batch):
         assert rel_l2(y[b], ref[b]) <= REL_L2_TOL, (b, rel_l2(y[b], ref[b]))
     # run-to-run bitwise determinism
-    y2 = q.hfq4_gemv(Wd, rows, K, torch.from_numpy(x).cuda(),
+    y2 = q.hfq4_gemv(Wd, rows, K, xd,
                      residual=None if r is None else torch.from_numpy(r).cuda()).cpu().numpy()
     assert np.array_equal(y, y2)
 
