@@ -40,10 +40,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// (key, index) order of the top-k: larger key first, equal keys -> lower index.
-__device__ __forceinline__ bool before(uint32_t ak, uint32_t ae, uint32_t bk, uint32_t be) {
-  return (ak > bk) | ((ak == bk) & (ae < be));
-}
 // Keys of one token's E logits, PER per lane (expert e = lane*PER + i),
 // read 4 at a time through a bounded descriptor.  The bound is E rounded up
 // to 4 (every 16-byte load lies wholly inside or wholly outside it, and the
@@ -89,21 +85,33 @@ __device__ constexpr int SORT16[][2] = {
     {7, 15}, {4, 8},   {5, 9},   {6, 10},  {7, 11},  {2, 4},   {3, 5},   {6, 8},   {7, 9},
     {10, 12}, {11, 13}, {1, 2},  {3, 4},   {5, 6},   {7, 8},   {9, 10},  {11, 12}, {13, 14}};
 
+// One comparator on composite entries (key << 32 | PER-1-i): the larger
+// composite is "before" -- the larger key, or the lower expert on equal
+// keys -- so one 64-bit compare orders (key, expert) pairs.
 template <int PER>
-__device__ __forceinline__ void local_sort(uint32_t* kk, uint32_t* ii) {
+__device__ __forceinline__ void local_sort(uint64_t* c) {
   constexpr int N = PER == 4 ? 5 : PER == 8 ? 19 : 63;
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    const int a = PER == 4 ? SORT4[c][0] : PER == 8 ? SORT8[c][0] : SORT16[c][0];
-    const int b = PER == 4 ? SORT4[c][1] : PER == 8 ? SORT8[c][1] : SORT16[c][1];
-    const bool keep = before(kk[a], ii[a], kk[b], ii[b]);
-    const uint32_t ka = kk[a], ia = ii[a];
-    kk[a] = keep ? ka : kk[b];
-    ii[a] = keep ? ia : ii[b];
-    kk[b] = keep ? kk[b] : ka;
-    ii[b] = keep ? ii[b] : ia;
+  for (int t = 0; t < N; ++t) {
+    const int a = PER == 4 ? SORT4[t][0] : PER == 8 ? SORT8[t][0] : SORT16[t][0];
+    const int b = PER == 4 ? SORT4[t][1] : PER == 8 ? SORT8[t][1] : SORT16[t][1];
+    const bool sw = c[b] > c[a];
+    const uint64_t ca = c[a];
+    c[a] = sw ? c[b] : ca;
+    c[b] = sw ? ca : c[b];
   }
 }
+
+// Four bits per sorted entry: the entry's position in the lane's block of
+// experts (a 32-bit word up to 8 entries, 64-bit for 16).
+template <int PER>
+struct PosPack {
+  typedef uint32_t T;
+};
+template <>
+struct PosPack<16> {
+  typedef uint64_t T;
+};
 
 // Top-k of one token's E logits by one wave, exactly in f32 order with ties
 // to the lower expert index (PER >= ceil(E/64) logits per lane, expert e =
@@ -124,32 +132,36 @@ template <int PER>
 __device__ void topk_keys(const uint32_t* key, int E, int k, int rounds, int& sel_e, float& sel_w,
                           uint64_t* trace) {
   const int lane = threadIdx.x & 63;
-  uint32_t kk[PER], ii[PER];
+  uint64_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c[i] = ((uint64_t)key[i] << 32) | (uint32_t)(PER - 1 - i);
+  local_sort<PER>(c);
+  // keys in order, positions packed (the winner's expert is lane*PER + pos)
+  typedef typename PosPack<PER>::T P;
+  uint32_t kk[PER];
+  P pos = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    kk[i] = key[i];
-    ii[i] = (uint32_t)(lane * PER + i);
+    kk[i] = (uint32_t)(c[i] >> 32);
+    pos |= (P)(PER - 1 - (uint32_t)c[i]) << (4 * i);
   }
-  local_sort<PER>(kk, ii);
   trace_point(trace, TK_TOPK, 2);
   uint32_t mk = 0, me = 0xFFFFFFFFu;     // lanes >= k hold "after everything"
   for (int j = 0; j < rounds; ++j) {
     const uint32_t m = wave_max_u32(kk[0]);
     const uint64_t who = __ballot(kk[0] == m);
     const int wl = (int)__builtin_ctzll(who);
-    const uint32_t we = (uint32_t)__builtin_amdgcn_readlane((int)ii[0], wl);
+    const uint32_t we =
+        (uint32_t)(wl * PER) + ((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pos, wl) & 15u);
     if (lane == j) {
       mk = m;
       me = we;
     }
     const bool pop = lane == wl;
 #pragma unroll
-    for (int i = 0; i < PER - 1; ++i) {
-      kk[i] = pop ? kk[i + 1] : kk[i];
-      ii[i] = pop ? ii[i + 1] : ii[i];
-    }
-    kk[PER - 1] = pop ? 0u : kk[PER - 1];
-    ii[PER - 1] = pop ? 0xFFFFFFFFu : ii[PER - 1];
+    for (int i = 0; i < PER - 1; ++i) kk[i] = pop ? kk[i + 1] : kk[i];
+    kk[PER - 1] = pop ? 0u : kk[PER - 1];   // key 0: no expert
+    pos = pop ? pos >> 4 : pos;
   }
   trace_point(trace, TK_TOPK, 4);
   sel_e = lane < rounds ? (int)me : -1;

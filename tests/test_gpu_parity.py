@@ -159,6 +159,27 @@ def test_route_ties_lower_index(q):
     assert np.allclose(w, ref, atol=1e-6)
 
 
+@pytest.mark.parametrize("E", [64, 200, 300, 512, 700, 1024])
+@pytest.mark.parametrize("B", [1, 3])
+def test_route_heavy_ties(q, E, B):
+    """Logits taking only a few distinct values (ties within a lane's block
+    of experts and across lanes, at every block size the top-k uses): the
+    selection must be exactly the lower-index top-k."""
+    say("moe_route_topk heavy ties", E, B)
+    k = 8
+    rng = np.random.default_rng(E + B)
+    d = 4
+    Wr = np.zeros((E, d), np.float32)
+    Wr[:, 0] = rng.integers(0, 4, size=E).astype(np.float32) * 0.25
+    x = np.zeros((B, d), np.float32)
+    x[:, 0] = np.arange(1, B + 1, dtype=np.float32)
+    idx, wts = q.moe_route_topk(torch.from_numpy(Wr).cuda(), torch.from_numpy(x).cuda(), k)
+    logits = (x.astype(np.float64) @ Wr.astype(np.float64).T).astype(np.float32)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert got[b].tolist() == moe.topk_lower_index(logits[b], k), b
+
+
 # ------------------------------------------------------------------ expert decode + layer
 
 def _tiny_inputs(q, seed=0):
