@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
 struct Frag {
   h2 p[16];
   float off;   // -(1024 * sum of all 32 stored halves + 8 * sum of the f16 values they stand for)
-  float sx;    // exact f32 sum of the 32 (unscaled) activations
+  float sx;    // f32 sum of the 32 (unscaled) activations
   float xs;    // the power-of-two scale: activation = xs * (stored value)
 };
 
