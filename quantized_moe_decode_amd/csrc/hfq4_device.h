@@ -226,13 +226,6 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp<0x128>(v);
   return v;
 }
-// All-reduce over each 8-lane half-row: xor 1, xor 2, mirror within 8.
-__device__ __forceinline__ float row_sum8(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  return v;
-}
 // gfx950 cross-row swaps.  a, b must be distinct values.
 // swap32: returns {a.lo32 | b.lo32, a.hi32 | b.hi32} summed -> lanes 0-31 hold
 // a reduced over xor 32, lanes 32-63 hold b reduced over xor 32.
