@@ -239,7 +239,7 @@ def bench_hostmapped(args, torch, q):
     from quantized_moe_decode_amd.stack import build_stack
     import synth
     NL, HOST_FROM, EH, POOL = 48, 24, 512, 64
-    zc, dma = _zero_copy_rate(torch, q, 1 << 29)
+    zc, dma = _zero_copy_rate(torch, q, 1 << 32)   # 4 GiB of pinned memory
     log("PCIe: zero-copy kernel read %.1f GB/s, DMA host->device %.1f GB/s" % (zc, dma))
     t0 = time.time()
     st = build_stack(torch, 0, NL, EH, D, F, K_TOP, 1, dense=False, host_from=HOST_FROM)
