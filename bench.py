@@ -232,6 +232,28 @@ def _zero_copy_rate(torch, q, nbytes):
     return best_zc, best_dma
 
 
+def _stream_ceiling(torch, q, nbytes):
+    """The same dequant-GEMV machinery where it is not latency-bound: one
+    token through an nbytes HFQ4 matrix in HBM (hfq4_gemv), best of 5."""
+    rows = nbytes // q.hfq4_packed_bytes(1, D)
+    W = torch.zeros(rows * q.hfq4_packed_bytes(1, D), dtype=torch.uint8, device="cuda")
+    x = torch.randn((1, D), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+    q.hfq4_gemv(W, rows, D, x, y=y)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        ev0.record()
+        q.hfq4_gemv(W, rows, D, x, y=y)
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, W.numel() / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    del W, y
+    return best
+
+
 def bench_hostmapped(args, torch, q):
     """48 MoE layers (d=2048, F=512, E=512, top-8), residual between layers;
     experts of layers 0-23 in HBM, of layers 24-47 in pinned host memory
@@ -599,6 +621,11 @@ def main():
                            "algorithmic_bytes_per_step": algo_bytes,
                            "kernels_per_step": 3 if args.path == "fused" else 4},
     }
+    # secondary ratio against the streaming ceiling of the same kernel family
+    ceil = _stream_ceiling(torch, q, 1 << 32)
+    out["stream_ceiling"] = {"kernel": "hfq4_gemv, 1 token, 4 GiB HFQ4 matrix in HBM",
+                             "gbs": round(ceil, 1), "frac_of_peak": round(ceil / HBM_PEAK_GBS, 4),
+                             "layer_value_frac": round(value / ceil, 4)}
     if not args.no_cpu:
         xs_host = xs[:512].cpu().numpy()
         routers_host = [L.Wr.cpu().numpy() for L in layers]

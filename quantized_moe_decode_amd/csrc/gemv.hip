@@ -12,9 +12,15 @@
 
 namespace hq {
 
+constexpr int GEMV_WG_PER_CU = 4;   // resident workgroups per CU of a long GEMV
+
 // Rows of nb <= NB blocks (K <= 256*NB); SEGS = 8*NB lanes per row, G =
-// 64/SEGS rows per load instruction, RPW load instructions per wave.  Lanes
-// whose block index is >= nb load nothing and contribute zero.
+// 64/SEGS rows per load instruction, RPW load instructions per wave: a
+// wave's group is RPW*G rows.  Lanes whose block index is >= nb load
+// nothing and contribute zero.  The grid is capped (a few workgroups per
+// CU), so a wave walks groups wave, wave + (waves in the grid), ... with the
+// next group's loads in flight while it computes the current one; x is
+// staged once per workgroup.
 template <int NB, int RPW>
 __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restrict__ W,
                                                           int64_t rows, int K,
@@ -22,19 +28,20 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
                                                           int batch, const float* __restrict__ res,
                                                           int64_t ldr, float* __restrict__ y,
                                                           int64_t ldy) {
-  constexpr int SEGS = 8 * NB, G = 64 / SEGS;
+  constexpr int SEGS = 8 * NB, G = 64 / SEGS, GROUP = RPW * G;
   const int nb = (K + BLK - 1) / BLK;
   const int64_t ROWB = (int64_t)nb * BLK_BYTES;
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane / SEGS, s = lane % SEGS;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
-  const int64_t row0 = wave * (RPW * G);
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6) * GROUP;
+  int64_t row0 = wave * GROUP;
 
   // Token 0's activations go out first (eight lanes per segment, one pass:
   // SEGS <= 64 = 2 x 32 segment groups of the 256 threads), then this
-  // wave's weight loads, so that x is converted while the weights are in
-  // flight.  With K not a multiple of 4 the staging below reads x itself.
+  // wave's first weight loads, so that x is converted while the weights are
+  // in flight.  With K not a multiple of 4 the staging below reads x itself.
   const bool k4 = (K & 3) == 0;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, 4u * (uint32_t)K);
   const int j8 = threadIdx.x & 7, s8 = threadIdx.x >> 3, G8 = blockDim.x >> 3;
@@ -42,22 +49,28 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
   const f32x4 xb = load_seg8(rx, k4 && s8 + G8 < SEGS ? s8 + G8 : -1, j8);
 
   // One wave-uniform descriptor covers the matrix (rows * ROWB < 2^31,
-  // split by the launcher); rows past the end and dead lanes read zeros.
-  u32x4 codes[RPW];
-  u32x2 hdr[RPW];
-  int64_t nhere = rows - row0;
-  if (nhere > RPW * G) nhere = RPW * G;
-  if (nhere < 0) nhere = 0;
+  // split by the launcher); rows past the end and dead lanes read zeros,
+  // so the loads need no branch.
   const uint32_t wbytes = (uint32_t)(rows * ROWB);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, wbytes);
+  // token 0's residual travels with the weights (a null residual reads 0)
+  const uint32_t rbytes = res ? (uint32_t)(4 * rows) : 0u;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(res, rbytes);
   const bool live = (s >> 3) < nb;
+  auto issue = [&](int64_t r0, u32x4 (&codes)[RPW], u32x2 (&hdr)[RPW], uint32_t (&r)[RPW]) {
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int64_t row = row0 + i * G + g;
-    const uint32_t off = (live && row < rows) ? (uint32_t)(row * ROWB + (s >> 3) * BLK_BYTES) : wbytes;
-    hdr[i] = bload8(rs, off);
-    codes[i] = bload16(rs, off + 8 + 16 * (s & 7));
-  }
+    for (int i = 0; i < RPW; ++i) {
+      const int64_t row = r0 + i * G + g;
+      const uint32_t off = (live && row < rows) ? (uint32_t)(row * ROWB + (s >> 3) * BLK_BYTES) : wbytes;
+      hdr[i] = bload8(rs, off);
+      codes[i] = bload16(rs, off + 8 + 16 * (s & 7));
+      r[i] = bload4(rr, row < rows ? (uint32_t)(4 * row) : rbytes);
+    }
+  };
+  u32x4 codes[RPW];
+  u32x2 hdr[RPW];
+  uint32_t r0v[RPW];
+  issue(row0, codes, hdr, r0v);
 
   const int fb = frag_bytes(SEGS);
   if (k4) {
@@ -70,18 +83,37 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
       stage_vector(x + b * ldx, K, SEGS, lds + b * fb, threadIdx.x, blockDim.x);
   }
   __syncthreads();
-  if (nhere == 0) return;
 
-  for (int b = 0; b < batch; ++b) {
-    Frag f;
-    frag_load(lds + b * fb, SEGS, s, f);
+  auto compute = [&](int64_t r0, const u32x4 (&codes)[RPW], const u32x2 (&hdr)[RPW],
+                     const uint32_t (&r)[RPW]) {
+    for (int b = 0; b < batch; ++b) {
+      Frag f;
+      frag_load(lds + b * fb, SEGS, s, f);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      float p = dot_seg(codes[i], hdr[i], f);
-      p = group_sum<SEGS>(p);
-      const int64_t row = row0 + i * G + g;
-      if (s == 0 && row < rows) y[b * ldy + row] = (res ? res[b * ldr + row] : 0.f) + p;
+      for (int i = 0; i < RPW; ++i) {
+        float p = dot_seg(codes[i], hdr[i], f);
+        p = group_sum<SEGS>(p);
+        const int64_t row = r0 + i * G + g;
+        if (s == 0 && row < rows) {
+          const float rv = b == 0 ? as_f32(r[i]) : (res ? res[b * ldr + row] : 0.f);
+          y[b * ldy + row] = rv + p;
+        }
+      }
     }
+  };
+  // two register sets in turn: the next group's loads go out before the
+  // current group is computed, and no loaded value is copied
+  u32x4 codes2[RPW];
+  u32x2 hdr2[RPW];
+  uint32_t r2v[RPW];
+  while (row0 < rows) {
+    issue(row0 + stride, codes2, hdr2, r2v);
+    compute(row0, codes, hdr, r0v);
+    row0 += stride;
+    if (row0 >= rows) break;
+    issue(row0 + stride, codes, hdr, r0v);
+    compute(row0, codes2, hdr2, r2v);
+    row0 += stride;
   }
 }
 
@@ -136,7 +168,9 @@ static int launch_narrow(const void* W, int64_t rows, int K, const float* x, int
   constexpr int RPW = 2;
   constexpr int G = 64 / (8 * NB);
   const int64_t waves = (rows + RPW * G - 1) / (RPW * G);
-  const int64_t blocks = (waves + 3) / 4;
+  int64_t blocks = (waves + 3) / 4;
+  const int64_t cap = (int64_t)num_cus() * GEMV_WG_PER_CU;   // larger matrices loop
+  if (blocks > cap) blocks = cap;
   const size_t shm = (size_t)batch * frag_bytes(8 * NB);
   if (int e = allow_lds(gemv_narrow_kernel<NB, RPW>, shm)) return e;
   hipLaunchKernelGGL((gemv_narrow_kernel<NB, RPW>), dim3((unsigned)blocks), dim3(256), shm, s,

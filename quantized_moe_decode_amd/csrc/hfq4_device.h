@@ -203,14 +203,6 @@ __device__ __forceinline__ void stage_vector(const float* __restrict__ v, int n,
 
 // ---------------------------------------------------------------- reductions
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64);
-// every lane of a group gets the group sum.  Fixed butterfly order.
-template <int WIDTH>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
 
 // ---- DPP / permlane reductions (VALU only, fixed order, no LDS traffic)
 template <int CTL>
@@ -240,6 +232,30 @@ __device__ __forceinline__ float fold16(float a, float b) {
   auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
                                             __builtin_bit_cast(uint32_t, b), false, false);
   return as_f32(r[0]) + as_f32(r[1]);
+}
+// Sum over aligned groups of WIDTH = 8, 16, 32 or 64 lanes (all active);
+// every lane of a group gets the group sum, in a fixed order: DPP within a
+// row, then the gfx950 row swaps.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "group width");
+  if (WIDTH == 8) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    return v + dpp<0x141>(v);
+  }
+  v = row_sum16(v);
+  if (WIDTH >= 32) {   // rows 0+1 and 2+3
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                    __builtin_bit_cast(uint32_t, v), false, false);
+    v = as_f32(r[0]) + as_f32(r[1]);
+  }
+  if (WIDTH == 64) {   // halves
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                    __builtin_bit_cast(uint32_t, v), false, false);
+    v = as_f32(r[0]) + as_f32(r[1]);
+  }
+  return v;
 }
 // Full 64-lane sum, result uniform (fixed order: rows, then row 0+1+2+3).
 __device__ __forceinline__ float wave_sum(float v) {

@@ -79,6 +79,8 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Compute units of the current device (cached per device).
+int num_cus();
 
 // Raise a kernel's dynamic LDS limit when its static plus dynamic use may
 // pass the 64 KiB default (gfx950 has 160 KiB per CU).

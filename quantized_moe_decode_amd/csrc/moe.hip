@@ -671,7 +671,7 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t 
   return w;
 }
 
-static int num_cus() {
+int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
