@@ -13,6 +13,8 @@
 namespace hq {
 
 constexpr int GEMV_WG_PER_CU = 4;   // resident workgroups per CU of a long GEMV
+constexpr int GEMV_RPW_LONG = 4;    // row loads per wave and group of a long GEMV
+constexpr int GEMV_WG_PER_CU_LONG = 3;   // its resident workgroups per CU (137 VGPRs)
 
 // Rows of nb <= NB blocks (K <= 256*NB); SEGS = 8*NB lanes per row, G =
 // 64/SEGS rows per load instruction, RPW load instructions per wave: a
@@ -161,21 +163,33 @@ __global__ void __launch_bounds__(256) gemv_wide_kernel(const uint8_t* __restric
   }
 }
 
-template <int NB>
-static int launch_narrow(const void* W, int64_t rows, int K, const float* x, int64_t ldx,
-                         int batch, const float* res, int64_t ldr, float* y, int64_t ldy,
-                         hipStream_t s) {
-  constexpr int RPW = 2;
+template <int NB, int RPW>
+static int launch_narrow_rpw(const void* W, int64_t rows, int K, const float* x, int64_t ldx,
+                             int batch, const float* res, int64_t ldr, float* y, int64_t ldy,
+                             hipStream_t s) {
   constexpr int G = 64 / (8 * NB);
   const int64_t waves = (rows + RPW * G - 1) / (RPW * G);
   int64_t blocks = (waves + 3) / 4;
-  const int64_t cap = (int64_t)num_cus() * GEMV_WG_PER_CU;   // larger matrices loop
+  // larger matrices loop; the cap keeps every workgroup resident
+  const int64_t cap = (int64_t)num_cus() * (RPW == 2 ? GEMV_WG_PER_CU : GEMV_WG_PER_CU_LONG);
   if (blocks > cap) blocks = cap;
   const size_t shm = (size_t)batch * frag_bytes(8 * NB);
   if (int e = allow_lds(gemv_narrow_kernel<NB, RPW>, shm)) return e;
   hipLaunchKernelGGL((gemv_narrow_kernel<NB, RPW>), dim3((unsigned)blocks), dim3(256), shm, s,
                      static_cast<const uint8_t*>(W), rows, K, x, ldx, batch, res, ldr, y, ldy);
   return (int)hipGetLastError();
+}
+
+// Two row loads per wave and group (more waves, shorter latency); from
+// 512 MiB of weights on, GEMV_RPW_LONG (more bytes in flight per wave:
+// measured 5.5 against 5.2 TB/s at 2-4 GiB, and slower below 512 MiB).
+template <int NB>
+static int launch_narrow(const void* W, int64_t rows, int K, const float* x, int64_t ldx,
+                         int batch, const float* res, int64_t ldr, float* y, int64_t ldy,
+                         hipStream_t s) {
+  if (rows * (int64_t)(((K + BLK - 1) / BLK) * BLK_BYTES) < ((int64_t)1 << 29))
+    return launch_narrow_rpw<NB, 2>(W, rows, K, x, ldx, batch, res, ldr, y, ldy, s);
+  return launch_narrow_rpw<NB, GEMV_RPW_LONG>(W, rows, K, x, ldx, batch, res, ldr, y, ldy, s);
 }
 
 static int launch_gemv_rows(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx,

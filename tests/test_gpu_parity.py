@@ -112,6 +112,33 @@ def test_gemv(q, rows, K, batch, resid):
     assert np.array_equal(y, y2)
 
 
+def test_gemv_long_matrix(q):
+    """A matrix past the long-GEMV switch (>= 512 MiB of weights: four row
+    loads per wave and group, every wave looping over row groups), with a
+    residual and two tokens; 96 sampled rows against the oracle, the first
+    and last rows among them.  The rows repeat a 4096-row packed block, so
+    the oracle needs only that block."""
+    say("hfq4_gemv long matrix")
+    K, batch, base = 2048, 2, 4096
+    rows = 560_000
+    rng = np.random.default_rng(11)
+    Wb = (rng.standard_normal((base, K)) * 0.02).astype(np.float32)
+    Pb = hfq4.quantize_rows(Wb)
+    Wd = torch.from_numpy(Pb.reshape(base, -1)).cuda().repeat((rows + base - 1) // base, 1)
+    Wd = Wd[:rows].contiguous()
+    assert Wd.numel() * 1 >= (1 << 29)
+    x = rng.standard_normal((batch, K)).astype(np.float32)
+    r = rng.standard_normal((batch, rows)).astype(np.float32)
+    y = q.hfq4_gemv(Wd.view(-1), rows, K, torch.from_numpy(x).cuda(),
+                    residual=torch.from_numpy(r).cuda()).cpu().numpy()
+    sample = np.unique(np.concatenate([[0, 1, rows - 2, rows - 1],
+                                       rng.integers(0, rows, size=92)]))
+    ref_base = hfq4.matvec(Pb, base, K, x)          # [batch][base]
+    for b in range(batch):
+        ref = ref_base[b][sample % base] + r[b][sample]
+        assert rel_l2(y[b][sample], ref) <= REL_L2_TOL, b
+
+
 def test_gemv_exact_grid_block(q):
     # block C dequantizes exactly; with x = ones the sum is exactly -34
     say("hfq4_gemv exact")
