@@ -369,7 +369,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   const int k = a.k, E = a.L.E, F = a.L.F;
   const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
-  const int nchunk = F / FAST_RP;
+  constexpr int nchunk = FAST_F / FAST_RP;   // F == FAST_F on this path
   const int items = k * nchunk;   // (slot u, chunk c of FAST_RP rows)
   trace_point(ws.trace, TK_GATEUP, 0);
 
@@ -382,14 +382,12 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
       // and its weight loads go out sooner; workgroup 0 runs all k rounds
       // and publishes the routing, and a host-mapped layer (every workgroup
       // copies every slot's down matrix) needs them all too.
+      // (with at most one item per wave, the usual case, the workgroup's
+      // last item is its last wave's; otherwise all k rounds)
       int need = k;
-      if (blockIdx.x != 0 && !ws.dstage) {
-        int umax = -1;
-        for (int w = 0; w < 4; ++w) {
-          const int g0 = blockIdx.x * 4 + w;
-          if (g0 < items) umax = max(umax, (g0 + ((items - 1 - g0) / nw) * nw) / nchunk);
-        }
-        need = umax + 1;
+      if (blockIdx.x != 0 && !ws.dstage && items <= nw) {
+        const int g0 = blockIdx.x * 4;
+        need = g0 < items ? min(g0 + 3, items - 1) / nchunk + 1 : 0;
       }
       int e;
       float w;

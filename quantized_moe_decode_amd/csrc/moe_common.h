@@ -37,11 +37,12 @@ struct ExpertArgs {
 // lanes), up to 8 experts per token.
 constexpr int FAST_SEGS_D = 64;
 constexpr int FAST_SEGS_F = 16;
+constexpr int FAST_F = 512;       // expert width of the tuned shape
 constexpr int FAST_RP = 4;        // gate/up row pairs per wave item
 constexpr int FAST_ROWS = 2;      // down output rows per wave
 
 __host__ __device__ inline bool fast_shape(int d, int F, int k) {
-  return d > 1792 && d <= 2048 && F == 512 && k <= 8;
+  return d > 1792 && d <= 2048 && F == FAST_F && k <= 8;
 }
 
 // Batched path (2 <= B <= 16) on MFMA matrix cores.
