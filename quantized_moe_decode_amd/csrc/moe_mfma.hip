@@ -518,7 +518,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   trace_point(ws.trace, TK_GATEUP, 1);
 
   // 2. this workgroup's items: a contiguous run of (group, 16-row tile)
-  const int tiles = F / MM_ROWS;                 // 32
+  constexpr int tiles = FAST_F / MM_ROWS;        // 32 (F == FAST_F on this path)
   const int items = G.U * tiles;
   const int per = (items + gridDim.x - 1) / gridDim.x;
   const int i0 = blockIdx.x * per;
