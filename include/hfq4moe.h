@@ -115,7 +115,8 @@ int hfq4_pack(const float* w, int64_t rows, int64_t K, int64_t ldw,
  *   y[b][r] = residual[b][r] + sum_{i<K} (zero + scale*q)[r][i] * x[b][i]
  * for b < batch (1..HFQ4_MAX_BATCH), r < rows.  W: HFQ4 rows (device or
  * mapped host), x: f32 [batch][ldx], residual: f32 [batch][ldr] or NULL,
- * y: f32 [batch][ldy].  y must not overlap x or W.  Products are taken
+ * y: f32 [batch][ldy].  y must not overlap x or W; residual may be y itself
+ * (in place) but must not partially overlap it.  Products are taken
  * with x scaled by a power of two per 32-element segment and rounded to
  * f16, accumulated in f32 (error well inside 1e-3 relative L2 for K <=
  * 16384, at any activation scale).  K <= 16384; batch*K <= 32768. */
