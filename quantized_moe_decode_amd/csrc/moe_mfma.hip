@@ -465,32 +465,36 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   int8_t* he = reinterpret_cast<int8_t*>(hq + (size_t)P * F * 2);   // [P][F / 16] exponents
   trace_point(ws.trace, TK_GATEUP, 0);
 
-  // 1. one wave per token: routing loads first, then the activations
-  //    (their loads overlap the routing loads), then top-k
-  if (wv < B) {
+  // 1. one wave per token routes it; the activations are staged by the
+  //    idle waves B..2B-1 when there are enough of them (B <= 8), otherwise
+  //    by the routing wave, its loads overlapping the routing loads
+  const bool split_stage = FROM_LOGITS && 2 * B <= (int)(blockDim.x >> 6);
+  if (FROM_LOGITS && wv < B) {
+    const bool pub = blockIdx.x == 0;
     const float* xb = a.x + (int64_t)wv * a.ldx;
     uint8_t* xe = xt + wv * XT_STRIDE;
-    if (FROM_LOGITS) {
-      const bool pub = blockIdx.x == 0;
-      if (E <= 256) {
-        RouteLoads<4> L;
-        route_load<4>(r, wv, L);
-        stage_token(xb, a.L.d, xe, &s_xs[wv]);
-        route_token<4>(r, wv, L, s_idx, s_wt, pub);
-      } else if (E <= 512) {
-        RouteLoads<8> L;
-        route_load<8>(r, wv, L);
-        stage_token(xb, a.L.d, xe, &s_xs[wv]);
-        route_token<8>(r, wv, L, s_idx, s_wt, pub);
-      } else {   // 16 loads per lane: route first, then stage
-        RouteLoads<16> L;
-        route_load<16>(r, wv, L);
-        route_token<16>(r, wv, L, s_idx, s_wt, pub);
-        stage_token(xb, a.L.d, xe, &s_xs[wv]);
-      }
-    } else {
-      stage_token(xb, a.L.d, xe, &s_xs[wv]);
+    if (E <= 256) {
+      RouteLoads<4> L;
+      route_load<4>(r, wv, L);
+      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
+      route_token<4>(r, wv, L, s_idx, s_wt, pub);
+    } else if (E <= 512) {
+      RouteLoads<8> L;
+      route_load<8>(r, wv, L);
+      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
+      route_token<8>(r, wv, L, s_idx, s_wt, pub);
+    } else {   // 16 loads per lane: route first, then stage
+      RouteLoads<16> L;
+      route_load<16>(r, wv, L);
+      route_token<16>(r, wv, L, s_idx, s_wt, pub);
+      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
     }
+  }
+  {
+    // the staging wave of token b: wave B + b (split) or wave b
+    const int b = split_stage ? wv - B : wv;
+    if ((split_stage || !FROM_LOGITS) && b >= 0 && b < B)
+      stage_token(a.x + (int64_t)b * a.ldx, a.L.d, xt + b * XT_STRIDE, &s_xs[b]);
   }
   if (!FROM_LOGITS && (int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();

@@ -139,6 +139,21 @@ def test_gemv_long_matrix(q):
         assert rel_l2(y[b][sample], ref) <= REL_L2_TOL, b
 
 
+@pytest.mark.parametrize("rows,K", [(2048, 2048), (300, 1000)])
+def test_gemv_residual_in_place(q, rows, K):
+    """residual and y the same buffer: y = y + W x."""
+    say("hfq4_gemv in place", rows, K)
+    rng = np.random.default_rng(rows + K)
+    W = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    P = hfq4.quantize_rows(W)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    r = rng.standard_normal((1, rows)).astype(np.float32)
+    yr = torch.from_numpy(r.copy()).cuda()
+    q.hfq4_gemv(torch.from_numpy(P).cuda(), rows, K, torch.from_numpy(x).cuda(), residual=yr, y=yr)
+    ref = hfq4.matvec(P, rows, K, x) + r
+    assert rel_l2(yr.cpu().numpy()[0], ref[0]) <= REL_L2_TOL
+
+
 def test_gemv_exact_grid_block(q):
     # block C dequantizes exactly; with x = ones the sum is exactly -34
     say("hfq4_gemv exact")
