@@ -42,31 +42,30 @@ namespace hq {
 
 // ====================================================================== routing
 
-// Router logits of one token, one workgroup per expert row: the four waves
-// split the row into quarters, each lane keeps up to 8 float4 loads of the
-// row and 8 of x in flight (buffer loads, so lanes past a quarter's end read
-// zeros without a branch), and the wave sums meet in LDS and are added in a
-// fixed order.  (Two or more tokens use the batched router.)
-__global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restrict__ logits,
-                                                     uint64_t* trace) {
-  __shared__ float part[4];
+// Router logits of one token, one single-wave workgroup per expert row:
+// each lane keeps up to 8 float4 loads of the row and 8 of x in flight
+// (buffer loads, so lanes past the end read zeros without a branch), the
+// bias word goes out with them, and one wave sum finishes the row -- no LDS
+// and no barrier.  (Two or more tokens use the batched router.)
+__global__ void __launch_bounds__(64) logits_kernel(RouteArgs a, float* __restrict__ logits,
+                                                    uint64_t* trace) {
   trace_point(trace, TK_LOGITS, 0);
   const int e = blockIdx.x;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int nq = a.d >> 2;
-  const int qw = (nq + 3) >> 2;
-  const int q_lo = wv * qw;
-  const int q_hi = q_lo + qw < nq ? q_lo + qw : nq;
   const uint32_t rowb = 4u * (uint32_t)a.d;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr + (int64_t)e * a.d, rowb);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, rowb);
+  // a null bias is a descriptor of 0 bytes: the load reads 0
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias ? 4u * (uint32_t)a.E : 0u);
+  const float bias = as_f32(bload4(rb, 4u * (uint32_t)e));
   float acc = 0.f;
-  for (int q0 = q_lo; q0 < q_hi; q0 += 64 * 8) {
+  for (int q0 = 0; q0 < nq; q0 += 64 * 8) {
     u32x4 w[8], xv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int q = q0 + u * 64 + lane;
-      const uint32_t off = q < q_hi ? 16u * (uint32_t)q : rowb;
+      const uint32_t off = q < nq ? 16u * (uint32_t)q : rowb;
       w[u] = bload16(rw, off);
       xv[u] = bload16(rx, off);
     }
@@ -79,11 +78,8 @@ __global__ void __launch_bounds__(256) logits_kernel(RouteArgs a, float* __restr
       acc = __builtin_fmaf(as_f32(w[u].w), as_f32(xv[u].w), acc);
     }
   }
-  const float t = wave_sum(acc);
-  if (lane == 0) part[wv] = t;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float l = ((part[0] + part[1]) + (part[2] + part[3])) + (a.bias ? a.bias[e] : 0.f);
+  const float l = wave_sum(acc) + bias;
+  if (lane == 0) {
     logits[e] = l;
     if (a.logits_out) a.logits_out[e] = l;
   }
@@ -688,7 +684,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
     if (int e = launch_logits_batched(a, ws.logits, s)) return e;
     return launch_route_batched(a, ws.logits, ws.err, s);
   }
-  hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(256), 0, s, a, ws.logits, ws.trace);
+  hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(64), 0, s, a, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
   if (err) return err;
   hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(256), 0, s, (const float*)ws.logits, E, B, k, idx,
@@ -785,7 +781,7 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
     if (int e = launch_route_batched(ra, ws.logits, ws.err, s)) return e;
     return launch_generic_experts(a, ws, s);
   }
-  hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(256), 0, s, ra, ws.logits, ws.trace);
+  hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(64), 0, s, ra, ws.logits, ws.trace);
   int err = (int)hipGetLastError();
   if (err) return err;
   if (fast) {
