@@ -405,8 +405,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle's CPU baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
-    ap.add_argument("--kernel-samples", type=int, default=40,
-                    help="single synchronised steps timed with HIP events for the roofline")
+    ap.add_argument("--kernel-samples", type=int, default=200,
+                    help="eager steps (back to back) timed with HIP events for the roofline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one device copy of 1 GiB (counter calibration)")
     ap.add_argument("--batches", default="1,4,16",
@@ -549,22 +549,31 @@ def main():
     if args.path == "fused":
         import ctypes
         hip = ctypes.CDLL("libamdhip64.so")
-        e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
-            raise SystemExit("hipEventCreate failed")
-        q.lib.hfq4_debug_set_events(e0, e1)
-        vals = []
-        for i in range(args.kernel_samples + 10):
+        # one event pair per step: the steps go back to back on the stream
+        # (no synchronisation between them, as in decode), and the pairs
+        # are read once at the end
+        n = args.kernel_samples + 10
+        evs = []
+        for _ in range(n):
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
+                raise SystemExit("hipEventCreate failed")
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(evs):
+            q.lib.hfq4_debug_set_events(e0, e1)
             step(i * 7919)
-            torch.cuda.synchronize()
+        q.lib.hfq4_debug_set_events(None, None)
+        torch.cuda.synchronize()
+        vals = []
+        for i, (e0, e1) in enumerate(evs):
             ms = ctypes.c_float()
             if hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1):
                 raise SystemExit("hipEventElapsedTime failed")
             if i >= 10:
                 vals.append(ms.value * 1e3)
-        q.lib.hfq4_debug_set_events(None, None)
-        hip.hipEventDestroy(e0)
-        hip.hipEventDestroy(e1)
+            hip.hipEventDestroy(e0)
+            hip.hipEventDestroy(e1)
         ev_us = (sum(vals) / len(vals), sorted(vals)[len(vals) // 2])
 
     if args.calib_copy:
@@ -609,7 +618,7 @@ def main():
                       "algorithmic_bytes_per_launch": gu_bytes,
                       "avg_launch_us": round(ev_us[0], 3),
                       "median_launch_us": round(ev_us[1], 3),
-                      "launch_timing": "HIP events around the launch, single synchronised steps",
+                      "launch_timing": "HIP events around the launch, eager steps back to back",
                       "samples": args.kernel_samples,
                       "in_kernel_span_us": ({k: round(v[0], 3) for k, v in kern.items()}
                                             if kern else None),
