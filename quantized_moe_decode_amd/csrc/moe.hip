@@ -378,8 +378,8 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
       // and its weight loads go out sooner; workgroup 0 runs all k rounds
       // and publishes the routing, and a host-mapped layer (every workgroup
       // copies every slot's down matrix) needs them all too.
-      // (with at most one item per wave, the usual case, the workgroup's
-      // last item is its last wave's; otherwise all k rounds)
+      // With at most one item per wave (the usual case) the workgroup's
+      // last item is its last wave's; otherwise it runs all k rounds.
       int need = k;
       if (blockIdx.x != 0 && !ws.dstage && items <= nw) {
         const int g0 = blockIdx.x * 4;
@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
       if (lane < k) {
         s_idx[lane] = e;
         s_w[lane] = w;
-        s_exp[lane] = e;   // a selection is always in range
+        s_exp[lane] = e;   // in range; -1 past the rounds this workgroup ran
       }
       if (nan_seen && lane == 0 && blockIdx.x == 0)
         __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
