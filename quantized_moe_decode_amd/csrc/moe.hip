@@ -14,8 +14,9 @@
 // output = sum_j w_j y_{e_j} (+ optional residual).
 //
 // Kernels
-//   logits_kernel  router GEMV of one token, one workgroup per expert row
-//                  (every shape; two or more tokens use the batched router).
+//   logits_kernel  router GEMV of 1..4 tokens, one single-wave workgroup
+//                  per expert row (every shape; more tokens use the MFMA
+//                  router of moe_mfma.hip).
 //   topk_kernel    standalone top-k, one wave per token (moe_route_topk for
 //                  one token, and the generic shapes).
 //   gateup_kernel  grouped gate/up dequant-GEMV: tokens that picked the same
@@ -42,48 +43,83 @@ namespace hq {
 
 // ====================================================================== routing
 
-// Router logits of one token, one single-wave workgroup per expert row:
-// each lane keeps up to 8 float4 loads of the row and 8 of x in flight
-// (buffer loads, so lanes past the end read zeros without a branch), the
-// bias word goes out with them, and one wave sum finishes the row -- no LDS
-// and no barrier.  (Two or more tokens use the batched router.)
+// Router logits of 1..LG_VALU_MAXB tokens, one single-wave workgroup per
+// expert row: each lane keeps up to 8 float4 loads of the row and 8 of each
+// token's x in flight (buffer loads, so lanes past the end and absent tokens
+// read zeros without a branch), the bias word goes out with them, and one
+// wave sum per token finishes the row -- no LDS and no barrier.  Token b's
+// logit goes to logits[b * ldl + e].  One token: the bias is added here and
+// the logit also goes to the caller's logits_out.  More tokens: the sums go
+// out without the bias, which the batched routing adds to every partial
+// layout alike (and it writes logits_out).
+// NT (1, 2 or 4) is the token count rounded up: one token keeps a single
+// stream of x loads.
+template <int NT>
 __global__ void __launch_bounds__(64) logits_kernel(RouteArgs a, float* __restrict__ logits,
-                                                    uint64_t* trace) {
+                                                    int ldl, uint64_t* trace) {
   trace_point(trace, TK_LOGITS, 0);
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int nq = a.d >> 2;
   const uint32_t rowb = 4u * (uint32_t)a.d;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr + (int64_t)e * a.d, rowb);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, rowb);
-  // a null bias is a descriptor of 0 bytes: the load reads 0
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias ? 4u * (uint32_t)a.E : 0u);
+  // tokens b < B at b * ldx: one descriptor over them
+  const uint32_t xbytes = NT == 1 ? rowb : (uint32_t)(4 * ((int64_t)(a.B - 1) * a.ldx + a.d));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, xbytes);
+  // a null bias (or more than one token) is a descriptor of 0 bytes: the load reads 0
+  const __amdgpu_buffer_rsrc_t rb =
+      make_rsrc(a.bias, (a.bias && NT == 1) ? 4u * (uint32_t)a.E : 0u);
   const float bias = as_f32(bload4(rb, 4u * (uint32_t)e));
-  float acc = 0.f;
+  float acc[NT];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) acc[b] = 0.f;
   for (int q0 = 0; q0 < nq; q0 += 64 * 8) {
-    u32x4 w[8], xv[8];
+    u32x4 w[8], xv[NT][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int q = q0 + u * 64 + lane;
-      const uint32_t off = q < nq ? 16u * (uint32_t)q : rowb;
-      w[u] = bload16(rw, off);
-      xv[u] = bload16(rx, off);
+      w[u] = bload16(rw, q < nq ? 16u * (uint32_t)q : rowb);
+#pragma unroll
+      for (int b = 0; b < NT; ++b)
+        xv[b][u] = bload16(rx, (q < nq && (b == 0 || b < a.B))
+                                   ? (uint32_t)(4 * ((int64_t)b * a.ldx + 4 * q))
+                                   : xbytes);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc = __builtin_fmaf(as_f32(w[u].x), as_f32(xv[u].x), acc);
-      acc = __builtin_fmaf(as_f32(w[u].y), as_f32(xv[u].y), acc);
-      acc = __builtin_fmaf(as_f32(w[u].z), as_f32(xv[u].z), acc);
-      acc = __builtin_fmaf(as_f32(w[u].w), as_f32(xv[u].w), acc);
+    for (int b = 0; b < NT; ++b) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[b] = __builtin_fmaf(as_f32(w[u].x), as_f32(xv[b][u].x), acc[b]);
+        acc[b] = __builtin_fmaf(as_f32(w[u].y), as_f32(xv[b][u].y), acc[b]);
+        acc[b] = __builtin_fmaf(as_f32(w[u].z), as_f32(xv[b][u].z), acc[b]);
+        acc[b] = __builtin_fmaf(as_f32(w[u].w), as_f32(xv[b][u].w), acc[b]);
+      }
     }
   }
-  const float l = wave_sum(acc) + bias;
-  if (lane == 0) {
-    logits[e] = l;
-    if (a.logits_out) a.logits_out[e] = l;
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    if (b == 0 || b < a.B) {
+      const float l = wave_sum(acc[b]) + bias;
+      if (lane == 0) {
+        logits[(int64_t)b * ldl + e] = l;
+        if (NT == 1 && a.logits_out) a.logits_out[e] = l;
+      }
+    }
   }
   trace_point(trace, TK_LOGITS, 1);
+}
+
+int launch_logits_valu(const RouteArgs& ra, float* out, int ldl, hipStream_t s) {
+  if (ra.B < 1 || ra.B > LG_VALU_MAXB) return (int)hipErrorInvalidValue;
+  static_assert(LG_VALU_MAXB == 4, "the instantiations cover 1, 2 and 4 tokens");
+  if (ra.B == 1)
+    hipLaunchKernelGGL(logits_kernel<1>, dim3(ra.E), dim3(64), 0, s, ra, out, ldl, get_trace());
+  else if (ra.B == 2)
+    hipLaunchKernelGGL(logits_kernel<2>, dim3(ra.E), dim3(64), 0, s, ra, out, ldl, get_trace());
+  else
+    hipLaunchKernelGGL(logits_kernel<4>, dim3(ra.E), dim3(64), 0, s, ra, out, ldl, get_trace());
+  return (int)hipGetLastError();
 }
 
 // Standalone top-k: one wave per token.
@@ -684,8 +720,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
     if (int e = launch_logits_batched(a, ws.logits, s)) return e;
     return launch_route_batched(a, ws.logits, ws.err, s);
   }
-  hipLaunchKernelGGL(logits_kernel, dim3(E), dim3(64), 0, s, a, ws.logits, ws.trace);
-  int err = (int)hipGetLastError();
+  int err = launch_logits_valu(a, ws.logits, E, s);
   if (err) return err;
   hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(256), 0, s, (const float*)ws.logits, E, B, k, idx,
                      wts, ws.err);
@@ -781,8 +816,7 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
     if (int e = launch_route_batched(ra, ws.logits, ws.err, s)) return e;
     return launch_generic_experts(a, ws, s);
   }
-  hipLaunchKernelGGL(logits_kernel, dim3(L.E), dim3(64), 0, s, ra, ws.logits, ws.trace);
-  int err = (int)hipGetLastError();
+  int err = launch_logits_valu(ra, ws.logits, L.E, s);
   if (err) return err;
   if (fast) {
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};

@@ -49,6 +49,14 @@ __host__ __device__ inline bool fast_shape(int d, int F, int k) {
 constexpr int LG_KS = 4;   // K splits of the batched router GEMV (partial logit sets)
 // Row stride of a partial logit set: E rounded up to 4 experts.
 __host__ __device__ inline int lg_stride(int E) { return (E + 3) & ~3; }
+// Up to LG_VALU_MAXB tokens the router is the VALU one-row-per-wave kernel,
+// which writes whole sums (without the bias) into set 0: the routing then
+// reads one set and adds the bias as it does to LG_KS partial sets.
+constexpr int LG_VALU_MAXB = 4;
+__host__ __device__ inline int lg_sets(int B) { return B <= LG_VALU_MAXB ? 1 : LG_KS; }
+// The VALU router for 1..LG_VALU_MAXB tokens: logits of token b at
+// out[b * ldl + e] (ldl = E for one token, lg_stride(E) for partial set 0).
+int launch_logits_valu(const RouteArgs& ra, float* out, int ldl, hipStream_t s);
 int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
 // Top-k and weights from the partial logits, one wave per token (routing
 // only).

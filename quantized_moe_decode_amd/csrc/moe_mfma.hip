@@ -27,9 +27,12 @@
 //
 // Kernels (one HIP graph node each; kernel boundaries are the only
 // grid-wide synchronisation, so no workgroup ever waits on another):
-//   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32):
-//                        16 experts x 16 tokens per tile, K split over 4
-//                        workgroups x 4 waves; writes 4 partial logit sets.
+//   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32)
+//                        for more than LG_VALU_MAXB tokens: 16 experts x 16
+//                        tokens per tile, K split over 4 workgroups x 4
+//                        waves; writes 4 partial logit sets.  Fewer tokens
+//                        take the VALU router of moe.hip, which writes whole
+//                        logits into set 0 (lg_sets).
 //   gateup_mfma_kernel   one wave per token routes it from the partial
 //                        logits (sums + bias, top-k, weights) and stages its
 //                        activations in LDS in the MFMA operand format; the
@@ -319,6 +322,7 @@ template <int PER>
 __device__ __forceinline__ void route_load(const BatchRouteArgs& r, int b, RouteLoads<PER>& L) {
   const int lane = threadIdx.x & 63;
   const int stride = lg_stride(r.E);
+  const int nsets = lg_sets(r.B);
   const uint32_t pbytes = (uint32_t)((int64_t)LG_KS * r.B * stride * 4);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(r.part, pbytes);
   const __amdgpu_buffer_rsrc_t rbias = make_rsrc(r.bias, r.bias ? (uint32_t)r.E * 4u : 0u);
@@ -326,9 +330,10 @@ __device__ __forceinline__ void route_load(const BatchRouteArgs& r, int b, Route
   for (int c = 0; c < PER / 4; ++c) {
     const int e0 = lane * PER + 4 * c;
 #pragma unroll
-    for (int p = 0; p < LG_KS; ++p)
-      L.raw[p][c] = bload16(rp, e0 < r.E ? (uint32_t)((((int64_t)p * r.B + b) * stride + e0) * 4)
-                                         : pbytes);
+    for (int p = 0; p < LG_KS; ++p)   // sets past lg_sets(B) read zeros
+      L.raw[p][c] = bload16(rp, (e0 < r.E && p < nsets)
+                                    ? (uint32_t)((((int64_t)p * r.B + b) * stride + e0) * 4)
+                                    : pbytes);
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i)   // zero without a bias or past E
@@ -848,6 +853,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
 // ====================================================================== host
 
 int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
+  if (lg_sets(ra.B) == 1) return launch_logits_valu(ra, part, lg_stride(ra.E), s);
   hipLaunchKernelGGL(logits_mfma_kernel, dim3((ra.E + 15) / 16, LG_KS), dim3(256), 0, s, ra, part,
                      get_trace());
   return (int)hipGetLastError();
