@@ -125,7 +125,10 @@ int launch_logits_valu(const RouteArgs& ra, float* out, int ldl, hipStream_t s) 
 // Standalone top-k: one wave per token.
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int E, int B,
                                                    int k, int32_t* idx, float* wts, uint32_t* err) {
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index through readfirstlane: the compiler then knows it (and
+  // the token, and the logits descriptor built from it) to be wave-uniform
+  // and issues the loads without a per-lane waterfall loop
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   for (int b = wv; b < B; b += (blockDim.x >> 6)) {
     int e;
     float w;

@@ -463,7 +463,10 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
   __shared__ float s_xs[HFQ4_MAXB_DEV];
   __shared__ f32x4 red[4][3][64];                    // partial tiles of roles 1..3
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index through readfirstlane: the role, and the gate or up
+  // descriptor chosen by it, are then known to be wave-uniform, and the
+  // weight loads go out without a per-lane waterfall loop
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int quad = wv >> 2, role = wv & 3;
   const int B = a.B, k = a.k, P = B * k, F = a.L.F, E = a.L.E;
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws.h);   // [P][F] f16 operand entries
