@@ -400,7 +400,9 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   __shared__ int s_idx[MAXK];
   __shared__ float s_w[MAXK];
   __shared__ int s_exp[MAXK];       // expert of slot j, -1 if out of range
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform wave index: the item, its slot and expert and the weight
+  // offsets are then scalar values
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int k = a.k, E = a.L.E, F = a.L.F;
   const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
