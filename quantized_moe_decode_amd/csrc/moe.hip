@@ -551,7 +551,9 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
 // Slots past k or out of range add nothing (selected out, whatever h holds).
 __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform wave index: the wave's first row and its part of the
+  // weight offsets are scalar values
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int k = a.k, d = a.L.d, F = a.L.F;
   const int g = lane >> 4, s = lane & 15;
   constexpr int64_t ROWB = 2 * BLK_BYTES;
