@@ -34,6 +34,8 @@ __global__ void __launch_bounds__(256) gemv_narrow_kernel(const uint8_t* __restr
   const int nb = (K + BLK - 1) / BLK;
   const int64_t ROWB = (int64_t)nb * BLK_BYTES;
   extern __shared__ __align__(16) uint8_t lds[];
+  // the wave index stays a per-lane value here: through wave_id() the
+  // streaming loop measured slower
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane / SEGS, s = lane % SEGS;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;

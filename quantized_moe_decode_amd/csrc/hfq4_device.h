@@ -204,6 +204,15 @@ __device__ __forceinline__ void stage_vector(const float* __restrict__ v, int n,
 // ---------------------------------------------------------------- reductions
 
 
+// Index of the calling wave in its workgroup, through readfirstlane: the
+// compiler then knows it to be wave-uniform, so what follows from it (rows,
+// items, buffer descriptors, offsets) is computed once per wave in scalar
+// registers, and loads through a descriptor chosen by it need no per-lane
+// waterfall loop.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---- DPP / permlane reductions (VALU only, fixed order, no LDS traffic)
 template <int CTL>
 __device__ __forceinline__ float dpp(float v) {

@@ -125,10 +125,7 @@ int launch_logits_valu(const RouteArgs& ra, float* out, int ldl, hipStream_t s) 
 // Standalone top-k: one wave per token.
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int E, int B,
                                                    int k, int32_t* idx, float* wts, uint32_t* err) {
-  // the wave index through readfirstlane: the compiler then knows it (and
-  // the token, and the logits descriptor built from it) to be wave-uniform
-  // and issues the loads without a per-lane waterfall loop
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;
   for (int b = wv; b < B; b += (blockDim.x >> 6)) {
     int e;
     float w;
@@ -361,7 +358,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a, Ws ws) {
   const int nchunk = (a.L.F + ROWS - 1) / ROWS;
   const int items = G.U * nchunk;
   const int nw = gridDim.x * (blockDim.x >> 6);
-  for (int it = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items; it += nw)
+  for (int it = blockIdx.x * (blockDim.x >> 6) + wave_id(); it < items; it += nw)
     gateup_item<NBD, RPW>(a, ws, G, xfr, it);
 }
 
@@ -375,7 +372,7 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a, Ws ws) {
     pexp[t] = (e >= 0 && e < a.L.E) ? e : -1;
   }
   const int nw = gridDim.x * (blockDim.x >> 6);
-  const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * (blockDim.x >> 6) + wave_id();
   for (int b = 0; b < a.B; ++b) {
     __syncthreads();
     stage_h<NBF>(a, ws, b, hfr);
@@ -400,9 +397,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   __shared__ int s_idx[MAXK];
   __shared__ float s_w[MAXK];
   __shared__ int s_exp[MAXK];       // expert of slot j, -1 if out of range
-  // wave-uniform wave index: the item, its slot and expert and the weight
-  // offsets are then scalar values
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;   // item, slot, expert, offsets: scalar
   const int k = a.k, E = a.L.E, F = a.L.F;
   const int nw = gridDim.x * (blockDim.x >> 6);
   const int gw = blockIdx.x * (blockDim.x >> 6) + wv;
@@ -551,9 +546,7 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
 // Slots past k or out of range add nothing (selected out, whatever h holds).
 __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
-  // wave-uniform wave index: the wave's first row and its part of the
-  // weight offsets are scalar values
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;   // the row part of the offsets: scalar
   const int k = a.k, d = a.L.d, F = a.L.F;
   const int g = lane >> 4, s = lane & 15;
   constexpr int64_t ROWB = 2 * BLK_BYTES;

@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __
   __shared__ f32x4 red[4][64];
   const int wg = blockIdx.x + gridDim.x * blockIdx.y;
   trace_point_at(trace, TK_LOGITS, wg, 0);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;
   const int n16 = lane & 15, c = lane >> 4;
   const int rt = blockIdx.x, ks = blockIdx.y;
   const int Kq = ((a.d + LG_KS * 64 - 1) / (LG_KS * 64)) * 64;   // per split, multiple of 64
@@ -463,10 +463,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   __shared__ float2 s_blk[HFQ4_MAXB_DEV][8];         // per token, block: (off, sx)
   __shared__ float s_xs[HFQ4_MAXB_DEV];
   __shared__ f32x4 red[4][3][64];                    // partial tiles of roles 1..3
-  // the wave index through readfirstlane: the role, and the gate or up
-  // descriptor chosen by it, are then known to be wave-uniform, and the
-  // weight loads go out without a per-lane waterfall loop
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;   // role and its gate/up descriptor: uniform
   const int quad = wv >> 2, role = wv & 3;
   const int B = a.B, k = a.k, P = B * k, F = a.L.F, E = a.L.E;
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws.h);   // [P][F] f16 operand entries
@@ -676,7 +673,7 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   __shared__ uint32_t s_he[MAXP * 8];                      // per pair: 32 tile exponents
   __shared__ float s_w[MAXP];
   __shared__ GroupTab G;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = wave_id(), lane = threadIdx.x & 63;
   const int B = a.B, k = a.k, P = B * k, d = a.L.d, F = a.L.F;
   const int r0 = blockIdx.x * DR_ROWS;
   const int n16 = lane & 15, c = lane >> 4;

@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ w, 
   const int lane = threadIdx.x & 63;
   const int64_t nb = (K + BLK - 1) / BLK;
   const int64_t total = rows * nb;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   for (int64_t blk = wave; blk < total; blk += nwaves) {
     const int64_t r = blk / nb, b = blk - r * nb;
