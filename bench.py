@@ -542,9 +542,12 @@ def main():
 
     # Launch duration of the gate/up kernel by HIP events on the stream the
     # library launches on (the library records a start and a stop event
-    # around that launch, hipExtLaunchKernel), over single steps of the same
-    # workload, each after a synchronisation: the duration rocprofv3's kernel
-    # trace reports (dispatch to completion), not the in-kernel span above.
+    # around that launch, hipExtLaunchKernel), over eager steps of the same
+    # workload issued back to back (the first 10 are not counted): the
+    # duration rocprofv3's kernel trace reports (dispatch to completion),
+    # not the in-kernel span above.  Eager steps leave host-side gaps between
+    # launches, so single durations vary; the average is reported, with the
+    # median beside it.
     ev_us = None
     if args.path == "fused":
         import ctypes
