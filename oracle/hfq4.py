@@ -15,6 +15,11 @@ Readings taken where the page is silent:
   subtract, then f32 divide), q = clamp(rint((w - zero) / scale), 0, 15)
   with f32 subtract and f32 divide and round-half-to-even; a block with
   max == min stores scale 0 and all codes 0;
+* signed zeros: -0.0 and +0.0 compare equal, so a block whose minimum is a
+  zero has no single "smallest" element; the zero field then holds +0.0
+  (the minimum plus +0.0 in f32, which maps -0.0 to +0.0 and leaves every
+  other value unchanged), so the stored bytes never depend on which of the
+  equal zeros a min() happens to return;
 * blocks run along K inside one row; a row whose K is not a multiple of 256
   ends in a padded block (min/max over the valid elements only, padded codes
   0, padded positions contribute nothing);
@@ -61,7 +66,7 @@ def quantize_block(w):
     if not np.isfinite(rng):
         raise ValueError("block range overflows f32")
     scale = np.float32(rng / np.float32(15.0))     # f32 divide
-    zero = mn
+    zero = np.float32(mn + np.float32(0.0))        # -0.0 -> +0.0 (signed-zero reading)
     codes = np.zeros(BLOCK, dtype=np.uint8)
     if scale != 0:
         t = np.float32(w - zero) / scale           # f32 subtract, f32 divide
@@ -112,7 +117,7 @@ def quantize_rows(W):
     if not np.all(np.isfinite(rng)):
         raise ValueError("block range overflows f32")
     scale = (rng / np.float32(15.0)).astype(np.float32)
-    zero = mn
+    zero = (mn + np.float32(0.0)).astype(np.float32)   # -0.0 -> +0.0 (signed-zero reading)
     safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
     t = ((Wb - zero[:, :, None]).astype(np.float32) / safe[:, :, None]).astype(np.float32)
     q = np.clip(np.rint(t), 0, 15).astype(np.uint8)

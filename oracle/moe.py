@@ -142,7 +142,8 @@ def moe_layer(x, Wr, experts, k, bias=None, logit_dtype=np.float64, idx=None):
     experts: a mapping/callable e -> PackedExpert (only the selected experts
     are ever requested).  If idx is given ([B, k]) it replaces the selection
     (used to re-evaluate an alternative, equally valid selection); the
-    weights are still the renormalised softmax of the float64 logits.
+    weights are then recomputed for that selection, in its order: the
+    renormalised softmax of the float64 logits of the given experts.
     Returns (idx int32 [B, k], wts float64 [B, k], y float64 [B, d], logits).
     """
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))

@@ -49,10 +49,15 @@ def _weights(name, K):
         w = np.zeros(K, np.float32)
         w[:4] = [0, 15, 2.5, 3.5]
         return w
+    if name in ("F", "G"):
+        w = (i % 16).astype(np.float32)
+        neg = (i % 32 == 0) if name == "F" else (i % 16 == 0)
+        w[neg] = np.float32(-0.0)
+        return w
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["A", "B", "C", "D", "E"])
+@pytest.mark.parametrize("name", ["A", "B", "C", "D", "E", "F", "G"])
 def test_golden_block_bytes(name):
     rec = _golden_records()[name]
     K = rec["K"]
@@ -99,6 +104,20 @@ def test_golden_D_ties_to_even_and_bound():
     assert abs(back[2] - 2.5) == 0.5  # exactly scale/2, so the bound is inclusive
 
 
+def test_golden_FG_signed_zero_minimum():
+    # the weights hold -0.0 (F: mixed with +0.0; G: the only zeros), and the
+    # zero field is +0.0 whichever zero a min() returns, in either scan order
+    for name in "FG":
+        w = _weights(name, 256)
+        assert np.signbit(w).sum() == (8 if name == "F" else 16)
+        for order in (w, w[::-1].copy()):
+            s, z, _ = hfq4.quantize_block(order)
+            assert struct.pack("<f", z) == b"\x00\x00\x00\x00"
+        P = hfq4.quantize_rows(w[None, :])
+        assert P.tobytes() == hfq4.quantize_rows(_weights("A", 256)[None, :]).tobytes()
+        assert np.array_equal(hfq4.dequantize(P, 1, 256)[0], np.abs(w).astype(np.float64))
+
+
 def test_golden_E_padding_does_not_contribute():
     P = hfq4.quantize_rows(_weights("E", 128)[None, :])
     assert P.size == 136
@@ -107,7 +126,7 @@ def test_golden_E_padding_does_not_contribute():
 
 def test_scalar_block_encoder_matches_golden():
     # the one-block scalar quantizer and encoder give the same golden bytes
-    for name in "ABCDE":
+    for name in "ABCDEFG":
         rec = _golden_records()[name]
         w = _weights(name, rec["K"])
         s, z, q = hfq4.quantize_block(w)
@@ -242,6 +261,55 @@ def test_topk_closed_forms():
     assert moe.topk_lower_index(l, 3) == [2, 1, 0]
     assert np.allclose(moe.softmax_renorm(l, [2, 1, 0]), [4 / 7, 2 / 7, 1 / 7], atol=1e-15)
     assert np.allclose(moe.softmax_renorm(l, [2, 1]), [2 / 3, 1 / 3], atol=1e-15)
+
+
+def test_router_bias_enters_with_its_sign():
+    # Wr = 0, so the logits are the bias alone: [0, ln 3] selects expert 1
+    # first with weight 3/(1+3) -- a bias subtracted instead of added would
+    # select expert 0 first
+    d = 16
+    Wr = np.zeros((2, d), np.float32)
+    x = np.random.default_rng(3).standard_normal((1, d))
+    bias = np.array([0.0, math.log(3.0)])
+    assert np.array_equal(moe.router_logits(Wr, x, bias), [[0.0, math.log(3.0)]])
+    idx, wts, _ = moe.route(Wr, x, 2, bias)
+    assert idx.tolist() == [[1, 0]]
+    assert np.allclose(wts, [[0.75, 0.25]], rtol=0, atol=1e-15)
+    # and in the layer: y = 3/4 y_1 + 1/4 y_0 with closed-form constant experts
+    D, F = 256, 128
+    xl = np.full((1, D), 1.0 / 256)
+    exps = {0: _const_expert(0.5, 0.25, 1.0, D, F), 1: _const_expert(1.0, 1.0, 2.0, D, F)}
+    idx, wts, y, _ = moe.moe_layer(xl, np.zeros((2, D), np.float32), exps, 2, bias=bias)
+    y0 = F * (0.5 / (1 + math.exp(-0.5)) * 0.25) * 1.0
+    y1 = F * (1.0 / (1 + math.exp(-1.0)) * 1.0) * 2.0
+    assert idx.tolist() == [[1, 0]]
+    assert np.allclose(y[0], 0.75 * y1 + 0.25 * y0, rtol=1e-13, atol=0)
+
+
+def test_idx_override_recomputes_weights():
+    # logits [0, ln 2, ln 4]: the oracle's own selection is [2, 1, 0] with
+    # weights [4/7, 2/7, 1/7]; a caller-given order or subset gets the
+    # weights of that selection, not the oracle's
+    d, F = 256, 128
+    x = np.full((1, d), 1.0 / 256)
+    Wr = np.zeros((3, d), np.float32)
+    Wr[1, :] = math.log(2.0)
+    Wr[2, :] = math.log(4.0)
+    c = [1.0, 2.0, 4.0]
+    exps = {e: _const_expert(0.5, 0.25, c[e], d, F) for e in range(3)}
+    yu = F * (0.5 / (1 + math.exp(-0.5)) * 0.25)      # expert e gives c[e] * yu
+    l = [0.0, float(np.float32(math.log(2.0))), float(np.float32(math.log(4.0)))]
+    p = np.exp(l)
+    idx, wts, y, _ = moe.moe_layer(x, Wr, exps, 3)
+    assert idx.tolist() == [[2, 1, 0]]
+    assert np.allclose(wts[0], p[[2, 1, 0]] / p.sum(), rtol=1e-14, atol=0)
+    idx, wts, y, _ = moe.moe_layer(x, Wr, exps, 3, idx=[[0, 1, 2]])
+    assert idx.tolist() == [[0, 1, 2]]
+    assert np.allclose(wts[0], p / p.sum(), rtol=1e-14, atol=0)
+    assert np.allclose(y[0], yu * float(np.dot(p / p.sum(), c)), rtol=1e-13, atol=0)
+    idx, wts, y, _ = moe.moe_layer(x, Wr, exps, 2, idx=[[0, 1]])
+    assert np.allclose(wts[0], p[:2] / p[:2].sum(), rtol=1e-14, atol=0)
+    assert np.allclose(y[0], yu * (p[0] * c[0] + p[1] * c[1]) / (p[0] + p[1]), rtol=1e-13, atol=0)
 
 
 def test_topk_matches_lexsort_and_k_term_softmax():
