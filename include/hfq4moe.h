@@ -173,7 +173,11 @@ int moe_workspace_bytes(const moe_layer* L, int batch, int k, size_t* out);
 /* Zero a workspace with a fill kernel (safe inside HIP graph capture). */
 int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Expert half of the layer, given the routing:
+/* Expert half of the layer, given the routing [EXPERTS] [TOPK] [HFQ]: each
+ * token runs the k experts its router chose (top-8 in [TOPK]), each expert
+ * its own gate, up and down HFQ4 tensors ([EXPERTS]: the per-expert
+ * ffn_gate / ffn_up / ffn_down weights of an MoE layer), and the outputs are
+ * mixed by the routing weights:
  *   y[b] = residual[b] + sum_{j<k} wts[b][j] * down_e( SiLU(gate_e x[b]) * (up_e x[b]) ),
  *   e = idx[b][j].
  * Tokens that share an expert read its weights once (grouping); an index
@@ -191,8 +195,14 @@ int moe_expert_decode(const moe_layer* L, const float* x, int64_t ldx, int batch
                       const float* residual, float* y, int64_t ldy,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Whole layer in one enqueue: moe_route_topk followed by
- * moe_expert_decode, same results bit for bit (idx, wts, y). */
+/* Whole layer in one enqueue [TOPK] [EXPERTS]: the decode step of one
+ * routed-expert layer -- router logits, top-k selection of that layer's
+ * experts for each token (top-8 in [TOPK]) and the selected experts' gate /
+ * up / down computation and weighted mix ([EXPERTS]) -- equal to
+ * moe_route_topk followed by moe_expert_decode, same results bit for bit
+ * (idx, wts, y).  Arguments as in those two calls; Wr: f32 [E][d], bias:
+ * f32 [E] or NULL.  Errors: as the two calls (nothing is enqueued on a
+ * refusal). */
 int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias,
                      const float* x, int64_t ldx, int batch, int k,
                      int32_t* idx, float* wts, const float* residual,

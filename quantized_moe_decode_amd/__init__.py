@@ -55,8 +55,9 @@ class MoeLayerC(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libhfq4moe.so not built at %s -- run quantized_moe_decode_amd.build "
-                          "(no CPU fallback exists)" % LIB_PATH)
+        raise ImportError("libhfq4moe.so not built at %s -- build it with "
+                          "'python quantized_moe_decode_amd/build.py' (no CPU fallback exists)"
+                          % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
@@ -101,6 +102,26 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(cond, msg):
+    """Argument checks the C ABI cannot make (it sees pointers, not tensor
+    sizes or dtypes): refuse before anything is enqueued."""
+    if not cond:
+        raise Hfq4Error(HFQ4_E_INVALID, msg)
+
+
+def _f32(t, name):
+    import torch
+    _need(t.dtype == torch.float32, "%s must be float32, got %s" % (name, t.dtype))
+    _need(t.dim() <= 1 or t.stride(-1) == 1, "%s must have unit stride along its rows" % name)
+
+
+def _rows(t, name, n, width):
+    """t holds n rows of at least `width` elements at its row stride."""
+    t2 = t if t.dim() == 2 else t.view(1, -1)
+    _need(t2.shape[0] == n, "%s has %d rows, expected %d" % (name, t2.shape[0], n))
+    _need(t2.shape[1] >= width, "%s rows hold %d elements, need %d" % (name, t2.shape[1], width))
+
+
 def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(stream)
@@ -143,8 +164,19 @@ def hfq4_gemv(W, rows, K, x, residual=None, y=None, stream=None):
     import torch
     x2 = x if x.dim() == 2 else x.view(1, -1)
     batch = x2.shape[0]
+    _f32(x2, "x")
+    _need(x2.shape[1] >= K, "x rows hold %d elements, need K = %d" % (x2.shape[1], K))
+    _need(W.dtype == torch.uint8 and W.is_contiguous(), "W must be a contiguous uint8 tensor")
+    _need(W.numel() >= hfq4_packed_bytes(rows, K),
+          "W holds %d bytes, a %d x %d HFQ4 matrix needs %d" % (W.numel(), rows, K,
+                                                               hfq4_packed_bytes(rows, K)))
     if y is None:
         y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
+    _f32(y, "y")
+    _rows(y, "y", batch, rows)
+    if residual is not None:
+        _f32(residual, "residual")
+        _rows(residual, "residual", batch, rows)
     ldr = residual.stride(0) if (residual is not None and residual.dim() == 2) else rows
     wp = _ptr(W) if W.is_cuda else ctypes.c_void_p(host_device_pointer(W))
     _check(lib.hfq4_gemv(wp, rows, K, _ptr(x2), x2.stride(0), batch, _ptr(residual), ldr,
@@ -166,15 +198,54 @@ def moe_route_topk(Wr, x, k, bias=None, ws=None, logits=None, idx=None, wts=None
     E, d = Wr.shape
     x2 = x if x.dim() == 2 else x.view(1, -1)
     B = x2.shape[0]
+    _f32(Wr, "Wr")
+    _need(Wr.is_contiguous(), "Wr must be contiguous [E, d]")
+    _f32(x2, "x")
+    _need(x2.shape[1] >= d, "x rows hold %d elements, need d = %d" % (x2.shape[1], d))
+    if bias is not None:
+        _f32(bias, "bias")
+        _need(bias.numel() >= E, "bias holds %d values, need E = %d" % (bias.numel(), E))
     if ws is None:
         ws = torch.zeros(moe_route_workspace_bytes(E, B), dtype=torch.uint8, device=x.device)
     if idx is None:
         idx = torch.empty((B, k), dtype=torch.int32, device=x.device)
     if wts is None:
         wts = torch.empty((B, k), dtype=torch.float32, device=x.device)
+    _check_routing_out(idx, wts, B, k)
+    if logits is not None:
+        _f32(logits, "logits")
+        _need(logits.is_contiguous() and logits.numel() >= B * E,
+              "logits must be a contiguous [B, E] float32 tensor")
+    _need(ws.dtype == torch.uint8, "ws must be a uint8 tensor")
     _check(lib.moe_route_topk(_ptr(Wr), _ptr(bias), E, d, _ptr(x2), x2.stride(0), B, k, _ptr(idx),
                               _ptr(wts), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)))
     return idx, wts
+
+
+def _check_routing_out(idx, wts, B, k):
+    import torch
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() == B * k,
+          "idx must be a contiguous [B, k] int32 tensor")
+    _need(wts.dtype == torch.float32 and wts.is_contiguous() and wts.numel() == B * k,
+          "wts must be a contiguous [B, k] float32 tensor")
+
+
+def _check_io(layer, x2, y, residual, ws):
+    """Shapes, dtypes and strides of a layer call's activations."""
+    import torch
+    B = x2.shape[0]
+    _f32(x2, "x")
+    _need(x2.shape[1] >= layer.d, "x rows hold %d elements, need d = %d" % (x2.shape[1], layer.d))
+    _f32(y, "y")
+    _rows(y, "y", B, layer.d)
+    if residual is not None:
+        r2 = residual if residual.dim() == 2 else residual.view(1, -1)
+        _f32(r2, "residual")
+        _rows(r2, "residual", B, layer.d)
+        # the C ABI reads the residual at y's row stride
+        _need(B == 1 or r2.stride(0) == y.stride(0),
+              "residual row stride %d differs from y's %d" % (r2.stride(0), y.stride(0)))
+    _need(ws.dtype == torch.uint8, "ws must be a uint8 tensor")
 
 
 def host_device_pointer(t):
@@ -195,11 +266,25 @@ class MoeLayer:
 
     def __init__(self, gate, up, down, E, d, F, Wr=None, bias=None, host_mapped=False,
                  stride_gate=None, stride_up=None, stride_down=None):
+        import torch
         self.gate, self.up, self.down = gate, up, down
         self.E, self.d, self.F = E, d, F
         self.Wr, self.bias = Wr, bias
         gb = hfq4_packed_bytes(F, d)
         db = hfq4_packed_bytes(d, F)
+        # the kernels address E * stride bytes of each tensor
+        for t, name, st in ((gate, "gate", stride_gate or gb), (up, "up", stride_up or gb),
+                            (down, "down", stride_down or db)):
+            _need(t.dtype == torch.uint8 and t.is_contiguous(),
+                  "%s must be a contiguous uint8 tensor" % name)
+            _need(t.numel() >= E * st, "%s holds %d bytes, %d experts at stride %d need %d"
+                  % (name, t.numel(), E, st, E * st))
+        if Wr is not None:
+            _f32(Wr, "Wr")
+            _need(Wr.is_contiguous() and tuple(Wr.shape) == (E, d), "Wr must be contiguous [E, d]")
+        if bias is not None:
+            _f32(bias, "bias")
+            _need(bias.numel() == E, "bias must hold E = %d values" % E)
         if host_mapped:
             ptrs = [host_device_pointer(t) for t in (gate, up, down)]
         else:
@@ -238,6 +323,8 @@ def moe_expert_decode(layer, x, idx, wts, ws, residual=None, y=None, stream=None
     k = idx.shape[-1]
     if y is None:
         y = torch.empty((B, layer.d), dtype=torch.float32, device=x.device)
+    _check_io(layer, x2, y, residual, ws)
+    _check_routing_out(idx, wts, B, k)
     _check(lib.moe_expert_decode(ctypes.byref(layer.c), _ptr(x2), x2.stride(0), B, _ptr(idx),
                                  _ptr(wts), k, _ptr(residual), _ptr(y), y.stride(0), _ptr(ws),
                                  ws.numel(), _stream(stream)))
@@ -255,6 +342,9 @@ def moe_layer_decode(layer, x, k, ws, residual=None, y=None, idx=None, wts=None,
         idx = torch.empty((B, k), dtype=torch.int32, device=x.device)
     if wts is None:
         wts = torch.empty((B, k), dtype=torch.float32, device=x.device)
+    _need(layer.Wr is not None, "the layer has no router (Wr)")
+    _check_io(layer, x2, y, residual, ws)
+    _check_routing_out(idx, wts, B, k)
     _check(lib.moe_layer_decode(ctypes.byref(layer.c), _ptr(layer.Wr), _ptr(layer.bias), _ptr(x2),
                                 x2.stride(0), B, k, _ptr(idx), _ptr(wts), _ptr(residual), _ptr(y),
                                 y.stride(0), _ptr(ws), ws.numel(), _stream(stream)))

@@ -5,6 +5,10 @@
 // 128 code bytes).  Quantizer (a reading; the page gives only the fields):
 // zero = block min, scale = f32(f32(max - min) / 15), q = clamp(rint(f32(
 // f32(w - zero) / scale)), 0, 15), ties to even; scale 0 => all codes 0.
+// -0.0 and +0.0 compare equal, so which zero a min reduction returns depends
+// on its order; the zero field is the minimum plus +0.0, which is +0.0 for
+// either zero and the minimum itself otherwise, so the bytes never depend
+// on the reduction order.
 // The f32 subtract and the correctly rounded f32 divide make every code
 // decision identical to a host f32 implementation of the same definition.
 #include "hfq4_device.h"
@@ -65,11 +69,12 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ w, 
       continue;
     }
     const float scale = range / 15.0f;   // correctly rounded f32 divide
+    const float zero = mn + 0.0f;        // -0.0 -> +0.0 (not folded: IEEE signed zeros)
     uint32_t q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float t = 0.f;
-      if (valid[i] && scale != 0.f) t = rintf((v[i] - mn) / scale);
+      if (valid[i] && scale != 0.f) t = rintf((v[i] - zero) / scale);
       t = fminf(fmaxf(t, 0.f), 15.f);
       q[i] = valid[i] ? (uint32_t)t : 0u;
     }
@@ -77,7 +82,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ w, 
     reinterpret_cast<uint16_t*>(dst + 8)[lane] = (uint16_t)two;
     if (lane == 0) {
       reinterpret_cast<float*>(dst)[0] = scale;
-      reinterpret_cast<float*>(dst)[1] = mn;
+      reinterpret_cast<float*>(dst)[1] = zero;
     }
   }
 }

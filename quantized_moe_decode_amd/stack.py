@@ -37,7 +37,8 @@ class Stack:
     def step(self, x, capture=None):
         """One decode step of the token batch x [batch, d]; returns the tensor
         holding the output.  With capture (a list), every layer appends
-        (output, idx, wts) copies (for checks; not for timing)."""
+        (input to the MoE layer, output, idx, wts) copies (for checks; not
+        for timing)."""
         cur = x
         flip = 0
         for li, L in enumerate(self.layers):
@@ -53,7 +54,7 @@ class Stack:
             flip ^= 1
             cur = out
             if capture is not None:
-                capture.append((out.clone(), self.idx.clone(), self.wts.clone()))
+                capture.append((t.clone(), out.clone(), self.idx.clone(), self.wts.clone()))
         return cur
 
 

@@ -68,7 +68,7 @@ def test_batched_layer_vs_oracle(q, B, k, d, E, fused):
                                   idx.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy(),
                                   residual=res.cpu().numpy())
     say("max rel-L2 %.3g, tie-ambiguous tokens %d" % (err, amb))
-    assert err <= REL_L2_TOL
+    assert amb == 0 and err <= REL_L2_TOL
 
 
 @pytest.mark.parametrize("E,k", [(100, 8), (1024, 8), (1024, 1), (64, 5)])
@@ -85,10 +85,10 @@ def test_single_token_expert_counts(q, E, k):
     idx, wts, y = q.moe_layer_decode(L, x, k, ws, residual=res)
     torch.cuda.synchronize()
     assert q.workspace_error(ws) == 0
-    err, _ = oracle_layer_check(x.cpu().numpy(), L.Wr.cpu().numpy(), None, cache, k,
-                                idx.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy(),
-                                residual=res.cpu().numpy())
-    assert err <= REL_L2_TOL
+    err, amb = oracle_layer_check(x.cpu().numpy(), L.Wr.cpu().numpy(), None, cache, k,
+                                  idx.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy(),
+                                  residual=res.cpu().numpy())
+    assert amb == 0 and err <= REL_L2_TOL
     # the two-call form gives the same bits
     i2, w2 = q.moe_route_topk(L.Wr, x, k, ws=ws)
     y2 = q.moe_expert_decode(L, x, i2, w2, ws, residual=res)

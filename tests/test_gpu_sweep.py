@@ -15,7 +15,7 @@ import pytest
 from oracle import moe
 import synth
 
-from _parity import REL_L2_TOL, ExpertCache, check_routing, oracle_layer_check
+from _parity import REL_L2_TOL, ExpertCache, check_routing, logit_tol, oracle_layer_check
 
 pytestmark = pytest.mark.gpu
 
@@ -94,11 +94,12 @@ def test_sweep_case(q, c):
     Wr = L.Wr.cpu().numpy()
     bnp = None if bias is None else np.asarray(bias, dtype=np.float64)
     logits = moe.router_logits(Wr, xs.astype(np.float64), bnp)
-    check_routing(idx.cpu().numpy(), wts.cpu().numpy(), logits, k)
+    amb = check_routing(idx.cpu().numpy(), wts.cpu().numpy(), logits, k, logit_tol(Wr, xs, bnp))
+    assert amb == 0
     sel = sorted(set([0, B // 2, B - 1]))
     cache = ExpertCache(torch, "cuda", seed, 0, d, F)
     err, amb = oracle_layer_check(xs[sel], Wr, bnp, cache, k, idx.cpu().numpy()[sel],
                                   wts.cpu().numpy()[sel], y.cpu().numpy()[sel],
                                   residual=None if res is None else res.cpu().numpy()[sel])
     say("max rel-L2 %.3g over tokens %s, tie-ambiguous %d" % (err, sel, amb))
-    assert err <= REL_L2_TOL
+    assert amb == 0 and err <= REL_L2_TOL
