@@ -411,11 +411,12 @@ def main():
                     help="also run one device copy of 1 GiB (counter calibration)")
     ap.add_argument("--batches", default="1,4,16",
                     help="token batch sizes of the skewed workload")
-    ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed"],
+    ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed", "floor"],
                     default="layer",
                     help="layer: one MoE layer (the headline line); stack: 40 layers with a dense "
                          "GEMV each; hostmapped: 48 layers, experts of 24 in pinned host memory; "
-                         "skewed: 512 experts, Zipf-biased routing, token batches 1/4/16")
+                         "skewed: 512 experts, Zipf-biased routing, token batches 1/4/16; "
+                         "floor: the latency and bandwidth probes of the one-token floor model")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -432,6 +433,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.workload == "floor":
+        from quantized_moe_decode_amd import probes
+        out = {"workload": "latency and bandwidth probes (floor model of the one-token layer)",
+               "probes": probes.run_all(torch, log=log)}
+        print(json.dumps(out), flush=True)
+        return
     if args.workload != "layer":
         out = {"stack": bench_stack, "hostmapped": bench_hostmapped,
                "skewed": bench_skewed}[args.workload](args, torch, q)

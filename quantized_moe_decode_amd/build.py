@@ -5,7 +5,9 @@
 (Run it as a script: importing the package would load the library first.)
 
 Every source under csrc/ is compiled into one shared library next to this
-file.  All HIP code is built with packed-FP32 instructions disabled.
+file (libhfq4moe.so, the decode library); the latency probes under probes/
+into a second one (libhfq4probe.so, measurement only).  All HIP code is
+built with packed-FP32 instructions disabled.
 """
 import os
 import subprocess
@@ -15,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhfq4moe.so")
 SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "moe.hip", "moe_mfma.hip"]
+PROBE_LIB = os.path.join(HERE, "libhfq4probe.so")
+PROBE_SOURCES = [os.path.join(HERE, "probes", "probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -24,17 +28,21 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _hipcc(srcs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC] + FLAGS + ["-x", "hip"] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libhfq4moe.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed building %s" % os.path.basename(lib))
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,193 @@
+"""Latency and bandwidth probes behind the one-token floor model.
+
+Runs the kernels of probes/probe.hip (libhfq4probe.so) and returns plain
+numbers; `python bench.py --workload floor` prints them as one JSON line.
+Measurement only: nothing here is on the decode path.
+
+* chase      dependent-load latency (one lane following a random cyclic
+             chain of 128-byte lines) for a footprint that sits in L2, in
+             the Infinity Cache, or in HBM;
+* boundary   a kernel writing one value per workgroup followed on the
+             stream by one reading all of them: the gap between the last
+             producer's end and the first consumer's start, and how long
+             the consumer's first read takes (data written on other dies);
+* empty      back-to-back empty kernels, eager and inside a HIP graph;
+* pingpong   a flag bounced between two workgroups with agent-scope
+             atomics (one-way latency), on the same die and across dies,
+             relaxed and as release/acquire with a payload;
+* read       a plain streaming read of a large buffer (GB/s).
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB_PATH = os.path.join(HERE, "libhfq4probe.so")
+TICK_NS = 10.0   # s_memrealtime runs at 100 MHz
+
+
+def _lib():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libhfq4probe.so not built at %s -- run "
+                          "'python quantized_moe_decode_amd/build.py'" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, U32, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
+    for name, args in {"probe_chase": [P, U32, I, P, P], "probe_empty": [I, I, P],
+                       "probe_pingpong": [P, P, I, I, I, I, P, P],
+                       "probe_produce": [P, I, P, P], "probe_consume": [P, I, P, P, P],
+                       "probe_read": [P, SZ, I, P, P]}.items():
+        f = getattr(lib, name)
+        f.restype = I
+        f.argtypes = args
+    return lib
+
+
+def _s(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ok(rc, what):
+    if rc != 0:
+        raise RuntimeError("%s: HIP error %d" % (what, rc))
+
+
+def chase(torch, footprint, hops=20000, seed=0):
+    """ns per dependent load over a random cycle of 128-byte lines spanning
+    `footprint` bytes."""
+    lib = _lib()
+    lines = footprint // 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    perm = torch.randperm(lines, generator=g, device="cuda", dtype=torch.int64)
+    nxt = torch.zeros(lines * 32, dtype=torch.int32, device="cuda")
+    # line perm[i] points at line perm[i+1] (one cycle through every line)
+    nxt[perm * 32] = (torch.roll(perm, -1) * 32).to(torch.int32)
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    start = int(perm[0].item()) * 32
+    _ok(lib.probe_chase(_p(nxt), start, hops, _p(out), _s(torch)), "probe_chase")
+    torch.cuda.synchronize()
+    ticks = int(out[0].item())
+    del nxt, perm
+    return ticks * TICK_NS / hops
+
+
+def boundary(torch, n=256, reps=50):
+    """Producer -> consumer launch pair on one stream, inside a HIP graph:
+    (median gap between the last producer store and the first consumer
+    start, median time of the consumer's read of the n values, fraction of
+    consumer workgroups that ran on another die than value 0's producer)."""
+    import numpy as np
+    lib = _lib()
+    vals = torch.zeros(n, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(4 * n, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    gaps, reads = [], []
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            _ok(lib.probe_produce(_p(vals), n, _p(stamps), _s(torch)), "probe_produce")
+            _ok(lib.probe_consume(_p(vals), n, _p(stamps), _p(sink), _s(torch)), "probe_consume")
+    for _ in range(reps):
+        g.replay()
+        torch.cuda.synchronize()
+        st = stamps.cpu().numpy()
+        prod_end = st[:n].max()
+        cons_start = st[n:2 * n]
+        gaps.append((cons_start.min() - prod_end) * TICK_NS)
+        reads.append(np.median(st[2 * n:3 * n] - cons_start) * TICK_NS)
+    return float(np.median(gaps)), float(np.median(reads))
+
+
+def empty(torch, n=2000, grid=256, block=256):
+    """us per empty kernel: (eager back to back, inside one HIP graph)."""
+    lib = _lib()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(100):
+        _ok(lib.probe_empty(grid, block, _s(torch)), "probe_empty")
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(n):
+        lib.probe_empty(grid, block, _s(torch))
+    ev1.record()
+    torch.cuda.synchronize()
+    eager = ev0.elapsed_time(ev1) * 1e3 / n
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(n):
+                lib.probe_empty(grid, block, _s(torch))
+    g.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return eager, ev0.elapsed_time(ev1) * 1e3 / n
+
+
+def pingpong(torch, partner, rounds=2000, release=False, payload_words=0):
+    """One-way flag latency in ns between workgroup 0 and `partner` (half a
+    round trip), and the two workgroups' die ids."""
+    lib = _lib()
+    flags = torch.zeros(64, dtype=torch.int32, device="cuda")
+    payload = torch.zeros(max(payload_words, 1), dtype=torch.int32, device="cuda")
+    out = torch.zeros(8, dtype=torch.int64, device="cuda")
+    _ok(lib.probe_pingpong(_p(flags), _p(payload), payload_words, rounds, partner,
+                           1 if release else 0, _p(out), _s(torch)), "probe_pingpong")
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    if o[4]:
+        return None, int(o[2]), int(o[3])
+    return float(o[0]) * TICK_NS / rounds / 2.0, int(o[2]), int(o[3])
+
+
+def read(torch, nbytes=1 << 32, reps=5):
+    """Best GB/s of a plain streaming read of nbytes in HBM."""
+    lib = _lib()
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    grid = 4 * torch.cuda.get_device_properties(0).multi_processor_count * 4
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _ok(lib.probe_read(_p(buf), nbytes, grid, _p(sink), _s(torch)), "probe_read")
+    best = 0.0
+    for _ in range(reps):
+        ev0.record()
+        lib.probe_read(_p(buf), nbytes, grid, _p(sink), _s(torch))
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+    del buf
+    return best
+
+
+def run_all(torch, log=print):
+    """Every probe once; returns a dict of the numbers."""
+    res = {}
+    for name, fp in (("l2", 1 << 20), ("infinity_cache", 64 << 20), ("hbm", 4 << 30)):
+        res["chase_ns_" + name] = round(chase(torch, fp), 1)
+        log("chase %s (%d B footprint): %.1f ns per dependent load" % (name, fp, res["chase_ns_" + name]))
+    gap, rd = boundary(torch)
+    res["boundary_gap_ns"], res["boundary_first_read_ns"] = round(gap, 1), round(rd, 1)
+    log("graph boundary: %.0f ns from last producer store to first consumer start; "
+        "consumer read of 256 values written on other dies %.0f ns" % (gap, rd))
+    eager, graph = empty(torch)
+    res["empty_kernel_us_eager"], res["empty_kernel_us_graph"] = round(eager, 3), round(graph, 3)
+    log("empty 256x256 kernel: %.2f us eager, %.2f us in a graph" % (eager, graph))
+    pp = {}
+    for partner in (8, 1, 2, 3, 4, 5, 6, 7):
+        ns, a, b = pingpong(torch, partner)
+        pp["wg0-wg%d" % partner] = {"ns": None if ns is None else round(ns, 1), "dies": [a, b]}
+        log("flag one-way wg0 -> wg%d (dies %d, %d): %s ns" % (partner, a, b, ns))
+    res["flag_relaxed_agent"] = pp
+    ns, a, b = pingpong(torch, 1, rounds=1000, release=True, payload_words=256)
+    res["flag_release_acquire_1KiB_ns"] = None if ns is None else round(ns, 1)
+    log("release/acquire message of 1 KiB, one way (dies %d, %d): %s ns" % (a, b, ns))
+    res["read_gbs"] = round(read(torch), 1)
+    log("streaming read of 4 GiB: %.1f GB/s" % res["read_gbs"])
+    return res
