@@ -209,6 +209,29 @@ int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias,
                      float* y, int64_t ldy,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: moe_layer_decode without
+ * a caller workspace.  The scratch it needs (the workspace's contents) is a
+ * fixed device array of this library, HFQ4_NOALLOC_SCRATCH_BYTES per GPU,
+ * held by each GPU the library runs on until the process ends; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Arguments and results are those of moe_layer_decode, bit for bit, except:
+ *  - no ws / ws_bytes; a call whose workspace (moe_workspace_bytes) would
+ *    exceed HFQ4_NOALLOC_SCRATCH_BYTES is refused with HFQ4_E_WORKSPACE
+ *    (every shape of d <= 2048, F = 512, E <= 1024, k <= 8 fits, host-mapped
+ *    one-token layers included);
+ *  - err: device uint32 that receives the sticky HFQ4_DEV_ERR_* bits (OR-ed;
+ *    the caller zeroes it), or NULL to drop them.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads without ordering) race and give
+ * undefined results; order them on one stream.  No part of the array needs
+ * to be zero at the start of a call. */
+#define HFQ4_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_layer_decode_noalloc(const moe_layer* L, const float* Wr, const float* bias,
+                             const float* x, int64_t ldx, int batch, int k,
+                             int32_t* idx, float* wts, const float* residual,
+                             float* y, int64_t ldy, uint32_t* err, hipStream_t stream);
+
 /* Testing hook: make the device check see `arch` instead of the real
  * device ("" or NULL restores the real query).  Lets the refusal on a
  * non-gfx950 device be exercised without such a device. */

@@ -35,8 +35,9 @@ EXPORTS = [
     "hfq4_last_error", "hfq4_version", "hfq4_debug_set_arch", "hfq4_packed_bytes", "hfq4_pack",
     "hfq4_gemv", "moe_route_workspace_bytes", "moe_route_topk", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_decode", "moe_layer_decode", "hfq4_host_device_pointer",
-    "hfq4_debug_set_trace", "hfq4_debug_set_events",
+    "hfq4_debug_set_trace", "hfq4_debug_set_events", "moe_layer_decode_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class Hfq4Error(RuntimeError):
@@ -76,6 +77,8 @@ def _load():
         "moe_layer_decode": (I32, [ctypes.POINTER(MoeLayerC), P, P, P, I64, I32, I32, P, P, P, P,
                                    I64, P, SZ, P]),
         "hfq4_host_device_pointer": (I32, [P, ctypes.POINTER(P)]),
+        "moe_layer_decode_noalloc": (I32, [ctypes.POINTER(MoeLayerC), P, P, P, I64, I32, I32, P, P,
+                                           P, P, I64, P, P]),
         "hfq4_debug_set_trace": (I32, [P, SZ]),
         "hfq4_debug_set_events": (I32, [P, P]),
     }
@@ -348,6 +351,32 @@ def moe_layer_decode(layer, x, k, ws, residual=None, y=None, idx=None, wts=None,
     _check(lib.moe_layer_decode(ctypes.byref(layer.c), _ptr(layer.Wr), _ptr(layer.bias), _ptr(x2),
                                 x2.stride(0), B, k, _ptr(idx), _ptr(wts), _ptr(residual), _ptr(y),
                                 y.stride(0), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, wts, y
+
+
+def moe_layer_decode_noalloc(layer, x, k, idx, wts, y, residual=None, err=None, stream=None):
+    """moe_layer_decode on the library's fixed scratch (no workspace): for
+    callers that cannot allocate.  Every output is the caller's (nothing is
+    allocated here or in the library); err is an optional device int32 [1]
+    that receives the sticky device error bits."""
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    B = x2.shape[0]
+    _need(layer.Wr is not None, "the layer has no router (Wr)")
+    _f32(x2, "x")
+    _need(x2.shape[1] >= layer.d, "x rows hold %d elements, need d = %d" % (x2.shape[1], layer.d))
+    _f32(y, "y")
+    _rows(y, "y", B, layer.d)
+    if residual is not None:
+        r2 = residual if residual.dim() == 2 else residual.view(1, -1)
+        _f32(r2, "residual")
+        _rows(r2, "residual", B, layer.d)
+        _need(B == 1 or r2.stride(0) == y.stride(0),
+              "residual row stride %d differs from y's %d" % (r2.stride(0), y.stride(0)))
+    _check_routing_out(idx, wts, B, k)
+    _check(lib.moe_layer_decode_noalloc(ctypes.byref(layer.c), _ptr(layer.Wr), _ptr(layer.bias),
+                                        _ptr(x2), x2.stride(0), B, k, _ptr(idx), _ptr(wts),
+                                        _ptr(residual), _ptr(y), y.stride(0), _ptr(err),
+                                        _stream(stream)))
     return idx, wts, y
 
 

@@ -323,6 +323,78 @@ int moe_layer_decode(const moe_layer* L, const float* Wr, const float* bias, con
                     "moe_layer_decode launch");
 }
 
+// ---------------------------------------------------------------- no-alloc variant
+//
+// moe_layer_decode for callers that cannot allocate: the scratch memory the
+// kernels need (logits, routing copy, h, token groups, staged down
+// matrices) lives in a fixed device array of this library instead of a
+// caller workspace.  Each GPU holds its own copy of the array, at its own
+// address; host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol) but the address looked up per device.
+
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[HFQ4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {nullptr};   // per device: address of `scratch`
+
+// The array's device address on the current device, looked up once per
+// device with that device current.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HFQ4_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(HFQ4_E_UNSUPPORTED, "device ordinal %d above 63", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HFQ4_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return HFQ4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_decode_noalloc(const moe_layer* L, const float* Wr, const float* bias,
+                             const float* x, int64_t ldx, int batch, int k, int32_t* idx,
+                             float* wts, const float* residual, float* y, int64_t ldy,
+                             uint32_t* err, hipStream_t stream) {
+  int r = check_layer(L);
+  if (r) return r;
+  if (!Wr) return fail(HFQ4_E_INVALID, "Wr is NULL");
+  if (!aligned16(Wr)) return fail(HFQ4_E_ALIGN, "Wr must be 16-byte aligned");
+  r = check_expert_io(L, x, ldx, batch, idx, wts, k, residual, y, ldy);
+  if (r) return r;
+  if (err && (reinterpret_cast<uintptr_t>(err) & 3u)) return fail(HFQ4_E_ALIGN, "err must be 4-byte aligned");
+  const size_t need = ws_bytes_for(L->E, batch, k, L->d, L->F, L->flags);
+  if (need > HFQ4_NOALLOC_SCRATCH_BYTES)
+    return fail(HFQ4_E_WORKSPACE,
+                "this call needs %zu bytes of scratch, the fixed no-alloc scratch holds %zu "
+                "(use moe_layer_decode with a caller workspace)",
+                need, (size_t)HFQ4_NOALLOC_SCRATCH_BYTES);
+  r = check_device();
+  if (r) return r;
+  void* base = nullptr;
+  r = scratch_for_current_device(&base);
+  if (r) return r;
+  hq::Ws w = hq::ws_carve(base, L->E, batch, k, L->d, L->F, L->flags);
+  // Device errors go to the caller's word when given; otherwise to the
+  // array's own header word, which nothing reads.  Every other part of the
+  // scratch is written before it is read within a call, so no part of it
+  // needs clearing between calls.
+  if (err) w.err = err;
+  return hip_status(hq::launch_layer(to_dev(L), Wr, bias, x, ldx, batch, k, idx, wts, residual, y, ldy, w, stream),
+                    "moe_layer_decode_noalloc launch");
+}
+
 int hfq4_host_device_pointer(void* host, void** dev) {
   if (!host || !dev) return fail(HFQ4_E_INVALID, "host and dev must be non-NULL");
   int r = check_device();

@@ -166,3 +166,23 @@ def test_device_refusal_names_arch(q):
     r = q.lib.moe_workspace_init(P(A), 1024, None)
     assert r == q.HFQ4_E_DEVICE and "gfx90a" in q.last_error()
     q.lib.hfq4_debug_set_arch(b"gfx942")
+
+
+def test_noalloc_refuses_beyond_its_scratch(q):
+    # a host-mapped one-token layer with F = 2048 and k = 16 stages 16 down
+    # matrices of 2048 x 2048 (35.7 MB): beyond the fixed scratch, refused on
+    # the host before any device work
+    E, d, F, k = 64, 2048, 2048, 16
+    gb = 2048 * 8 * 136
+    L = q.MoeLayerC(16, 16, 16, E, d, F, gb, gb, gb, q.HFQ4_LAYER_HOST_MAPPED, 0)
+    P = ctypes.c_void_p
+    rc = q.lib.moe_layer_decode_noalloc(ctypes.byref(L), P(16), None, P(4096), d, 1, k,
+                                        P(1 << 20), P(1 << 21), None, P(1 << 22), d, None, None)
+    assert rc == q.HFQ4_E_WORKSPACE
+    msg = q.last_error()
+    assert "scratch" in msg and str(q.NOALLOC_SCRATCH_BYTES) in msg
+    # within the scratch, validation passes and the (forced) device check refuses
+    L = q.MoeLayerC(16, 16, 16, 256, 2048, 512, 557056, 557056, 557056, 0, 0)
+    rc = q.lib.moe_layer_decode_noalloc(ctypes.byref(L), P(16), None, P(4096), 2048, 16, 8,
+                                        P(1 << 20), P(1 << 21), None, P(1 << 22), 2048, None, None)
+    assert rc == q.HFQ4_E_DEVICE
