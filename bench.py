@@ -59,43 +59,85 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, layers_f32_seed, xs_host, routers_host, budget_s):
     """The oracle (numpy float64) on the first tokens of the same workload,
-    timed on the host cores; experts are quantized by the oracle before
-    timing starts, as the GPU path gets pre-packed weights."""
-    import numpy as np
+    timed on the host cores: once with the BLAS pool at the cores this
+    process may run on (capped by OMP_NUM_THREADS when set, the machine's CPU
+    share), once single-threaded on a shorter sample.  Experts are quantized
+    by the oracle before timing starts, as the GPU path gets pre-packed
+    weights."""
     from oracle import moe
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    spent, n, t_total = 0.0, 0, 0.0
+    from threadpoolctl import threadpool_limits
+    avail = len(os.sched_getaffinity(0))
+    want = int(os.environ.get("OMP_NUM_THREADS") or avail)
+    threads = max(1, min(avail, want))
     seed = layers_f32_seed
-    while spent < budget_s and n < len(xs_host):
-        r = n % len(routers_host)
-        x = xs_host[n:n + 1]
-        Wr = routers_host[r]
-        idx, _, _ = moe.route(Wr, x, K_TOP)
+    exps_cache = {}
+
+    def experts_of(r, idx):
         exps = {}
-        for e in idx[0]:
-            g, u, dn = synth.expert_f32(torch, "cuda", seed, r, int(e), D, F)
-            exps[int(e)] = moe.PackedExpert.from_f32(g.cpu().numpy(), u.cpu().numpy(),
-                                                     dn.cpu().numpy())
-        t0 = time.perf_counter()
-        moe.moe_layer(x, Wr, exps, K_TOP)
-        dt = time.perf_counter() - t0
-        t_total += dt
-        spent += dt
-        n += 1
+        for e in idx:
+            key = (r, int(e))
+            if key not in exps_cache:
+                g, u, dn = synth.expert_f32(torch, "cuda", seed, r, int(e), D, F)
+                exps_cache[key] = moe.PackedExpert.from_f32(g.cpu().numpy(), u.cpu().numpy(),
+                                                            dn.cpu().numpy())
+            exps[int(e)] = exps_cache[key]
+        return exps
+
+    def run(nthreads, budget, max_tokens):
+        spent, n = 0.0, 0
+        with threadpool_limits(limits=nthreads):
+            while spent < budget and n < min(len(xs_host), max_tokens):
+                r = n % len(routers_host)
+                x = xs_host[n:n + 1]
+                Wr = routers_host[r]
+                idx, _, _ = moe.route(Wr, x, K_TOP)
+                exps = experts_of(r, idx[0])
+                t0 = time.perf_counter()
+                moe.moe_layer(x, Wr, exps, K_TOP)
+                spent += time.perf_counter() - t0
+                n += 1
+        return n, spent
+
+    n, t_total = run(threads, budget_s, len(xs_host))
     per_tok = t_total / n
+    n1, t1 = run(1, budget_s / 4, n)
+    per_tok1 = t1 / n1
     return {"value": round(K_TOP * 1671168 / per_tok / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "%d single-token layer calls of the same workload (replica r = token mod 32), "
                       "%.1f s of oracle time, %.3f s per token-layer; quantization untimed" %
                       (n, t_total, per_tok),
-            "tokens_per_s": round(1.0 / per_tok, 4)}
+            "tokens_per_s": round(1.0 / per_tok, 4),
+            "cores_available": avail, "cpu_model": _cpu_model(),
+            "single_thread": {"value": round(K_TOP * 1671168 / per_tok1 / 1e9, 4), "unit": "GB/s",
+                              "tokens_per_s": round(1.0 / per_tok1, 4),
+                              "sample": "%d of the same calls, %.1f s" % (n1, t1)}}
+
+
+def _graph_upload(torch, g):
+    """Upload an instantiated graph to the device (hipGraphUpload) so that
+    its first timed replay carries no upload cost."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    ex = g.raw_cuda_graph_exec()
+    rc = hip.hipGraphUpload(ctypes.c_void_p(ex), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise SystemExit("hipGraphUpload failed: %d" % rc)
 
 
 def _calib_copy(torch):
@@ -392,7 +434,7 @@ def main():
     ap = argparse.ArgumentParser(description="Throughput of the HFQ4 MoE decode path on one MI355X; "
                                              "prints one JSON line.")
     ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1 is supported)")
-    ap.add_argument("--steps", type=int, default=20000, help="timed steps (rounded to whole graphs)")
+    ap.add_argument("--steps", type=int, default=20000, help="timed steps (exactly this many)")
     ap.add_argument("--warmup", type=int, default=2000, help="untimed steps before timing")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="steps as HIP-graph replays or as eager launches")
@@ -401,7 +443,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=32,
                     help="distinct layer copies cycled through (so caches cannot serve repeats)")
     ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
-    ap.add_argument("--graph-steps", type=int, default=512, help="steps captured per HIP graph")
+    ap.add_argument("--graph-steps", type=int, default=512,
+                    help="most steps captured in one HIP graph (the graph holds the largest "
+                         "divisor of --steps not above this)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle's CPU baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
@@ -470,7 +514,12 @@ def main():
 
     stream = torch.cuda.current_stream()
     if args.mode == "graph":
-        G = args.graph_steps
+        # exactly K timed steps: one graph of G steps (G the largest divisor
+        # of K not above --graph-steps) replayed K / G times, uploaded to the
+        # device before timing; the W warmup steps run eagerly (the same
+        # calls) on other activations of the pool
+        K = args.steps
+        G = max(g for g in range(1, min(K, args.graph_steps) + 1) if K % g == 0)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(stream)
@@ -483,16 +532,16 @@ def main():
             for i in range(G):
                 step(i)
         torch.cuda.synchronize()
-        reps_w = max(1, args.warmup // G)
-        reps = max(1, args.steps // G)
-        steps = reps * G
-        warm = reps_w * G
+        _graph_upload(torch, g)
+        reps = K // G
+        steps, warm = K, args.warmup
         run = lambda: [g.replay() for _ in range(reps)]
-        run_w = lambda: [g.replay() for _ in range(reps_w)]
+        run_w = lambda: [step(G + i) for i in range(warm)]
     else:
+        G = 0
         steps, warm = args.steps, args.warmup
         run = lambda: [step(i) for i in range(steps)]
-        run_w = lambda: [step(i) for i in range(warm)]
+        run_w = lambda: [step(steps + i) for i in range(warm)]
 
     run_w()
     torch.cuda.synchronize()
