@@ -18,6 +18,7 @@ dominant kernel's roofline and the CPU oracle timed on a bounded sample.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -347,6 +348,170 @@ def bench_hostmapped(args, torch, q):
     return out
 
 
+def bench_offload(args, torch, q):
+    """One host-resident layer of the host-mapped workload's shape (d=2048,
+    F=512, E=512, top-8, Zipf-biased router): one decode step timed with the
+    experts read over PCIe by the GPU kernels and with the experts computed
+    on the host CPU (router on the GPU), and the route the 15% rule picks."""
+    import synth
+    from quantized_moe_decode_amd.offload import measure_routes
+    EH, N = 512, 64
+    zc, dma = _zero_copy_rate(torch, q, 1 << 32)
+    L = q.synthetic.build_layer(torch, 0, 30, EH, D, F, bias=synth.zipf_bias(0, EH),
+                                host_mapped=True)
+    xs = synth.activations(torch, "cuda", 6, N, D)
+    m = measure_routes(torch, L, xs, K_TOP)
+    best = min(m["pcie_s_per_step"], m["cpu_s_per_step"])
+    out = _base(args, N, 3, best, m["expert_bytes_per_step"] / best / 1e9,
+                "host-resident expert layer (d=2048, FFN 512, 512 experts, top-8, Zipf router), "
+                "experts in pinned host memory; PCIe zero-copy route vs CPU route; 1 token; %d "
+                "fresh tokens" % N)
+    out["offload"] = {k: (round(v, 8) if isinstance(v, float) else v) for k, v in m.items()}
+    out["offload"]["rule"] = "CPU only when at least 15% faster than PCIe"
+    out["offload"]["cpu_threads"] = len(os.sched_getaffinity(0))
+    out["offload"]["cpu_model"] = _cpu_model()
+    out["roofline"] = {"bound": "pcie", "achieved": round(m["pcie_expert_gbs"], 2),
+                       "peak": round(max(zc, dma), 2), "unit": "GB/s",
+                       "frac": round(m["pcie_expert_gbs"] / max(zc, dma), 4), "traffic": None,
+                       "kernel": "PCIe route: whole layer step (router, top-k + gate/up, down)",
+                       "pcie_zero_copy_gbs": round(zc, 2), "pcie_dma_gbs": round(dma, 2)}
+    return out
+
+
+def bench_cache(args, torch, q):
+    """An HBM expert cache over host-resident experts: 8 layers of the
+    host-mapped workload's shape (d=2048, F=512, E=512, top-8) with a
+    Zipf(1.1)-biased router, every expert in pinned host memory; the HBM
+    budget holds a quarter of the expert bytes (plus the routers); hot-set
+    placement from each layer's routing of 256 calibration tokens, and, for
+    comparison, whole-layer placement at the same budget.  Decode steps
+    x' = x + MoE(x) through the 8 layers, one token at a time."""
+    import numpy as np
+    import synth
+    import quantized_moe_decode_amd.cache as cache
+    NL, EH, POOL = 8, 512, 64
+    zc, dma = _zero_copy_rate(torch, q, 1 << 32)
+    pcie = max(zc, dma)
+    bias = synth.zipf_bias(0, EH)
+    t0 = time.time()
+    layers = [q.synthetic.build_layer(torch, 0, l, EH, D, F, bias=bias, host_mapped=True)
+              for l in range(NL)]
+    log("built %d host-resident layers in %.1f s" % (NL, time.time() - t0))
+    eb = layers[0].expert_bytes()
+    fixed = NL * EH * D * 4                       # the routers stay in HBM
+    budget = fixed + NL * EH * eb // 4
+    calib = synth.activations(torch, "cuda", 21, 256, D)
+    heat = cache.routing_heat(torch, layers, calib, K_TOP)
+    xs = synth.activations(torch, "cuda", 22, POOL, D)
+    ws = q.new_workspace(layers[0], 1, K_TOP)
+    res = {}
+    for mode, name in ((q.HFQ4_PLACE_HOTSET, "hotset"), (q.HFQ4_PLACE_LAYERS, "layers")):
+        tables, pool, resident, placed = cache.place_and_build(torch, layers, heat, budget, fixed,
+                                                               mode=mode)
+        hits = torch.zeros(2, dtype=torch.int64, device="cuda")
+        bufs = [torch.empty((1, D), dtype=torch.float32, device="cuda") for _ in range(2)]
+        outs = torch.empty((POOL, D), dtype=torch.float32, device="cuda")
+
+        def step(i):
+            cur = xs[i:i + 1]
+            for li, T in enumerate(tables):
+                out = bufs[li & 1]
+                q.moe_layer_decode_table(T, cur, K_TOP, ws, residual=cur, y=out, hits=hits)
+                cur = out
+            outs[i:i + 1].copy_(cur)
+
+        gs = _graphs(torch, step, POOL, POOL)
+        for g in gs:                       # upload and warm
+            g.replay()
+        torch.cuda.synchronize()
+        hits.zero_()
+        secs = _time_graphs(torch, gs, 0, 1)
+        h = hits.cpu().numpy().astype(np.float64)
+        per = secs / POOL
+        sel = h.sum() / POOL                        # expert selections per step (= NL * k)
+        hit = h[0] / h.sum()
+        hbm_b = hit * sel * eb + NL * EH * D * 4
+        host_b = (1 - hit) * sel * eb
+        t_bound = hbm_b / (HBM_PEAK_GBS * 1e9) + host_b / (pcie * 1e9)
+        res[name] = {"ms_per_step": round(per * 1e3, 4), "tokens_per_s": round(1 / per, 1),
+                     "hit_rate": round(hit, 4), "resident_experts": int(resident.sum()),
+                     "resident_fraction": round(float(resident.mean()), 4),
+                     "hbm_bytes_per_step": int(hbm_b), "pcie_bytes_per_step": int(host_b),
+                     "expert_gbs": round(sel * eb / per / 1e9, 2),
+                     "bound_ms_per_step": round(t_bound * 1e3, 4),
+                     "frac_of_split_bound": round(t_bound / per, 4)}
+        log("%s placement: hit rate %.3f, %.3f ms per step (bound %.3f ms)"
+            % (name, hit, per * 1e3, t_bound * 1e3))
+        del tables, pool, gs
+        torch.cuda.empty_cache()
+    hs = res["hotset"]
+    out = _base(args, POOL, 1, hs["ms_per_step"] / 1e3, hs["expert_gbs"],
+                "HBM expert cache over host-resident experts: 8 layers (d=2048, FFN 512, 512 "
+                "experts, top-8, Zipf(1.1) router), HBM budget = routers + 1/4 of the expert "
+                "bytes, hot-set placement from 256 calibration tokens; 1 token; %d fresh tokens"
+                % POOL)
+    out["cache"] = res
+    out["cache"]["budget_bytes"] = int(budget)
+    out["tokens_per_s"] = hs["tokens_per_s"]
+    out["roofline"] = {"bound": "hbm+pcie", "achieved": hs["expert_gbs"],
+                       "peak": round(sel * eb / (hs["bound_ms_per_step"] / 1e3) / 1e9, 2),
+                       "unit": "GB/s", "frac": hs["frac_of_split_bound"], "traffic": None,
+                       "kernel": "whole step: 8 table layers (single launch each)",
+                       "pcie_zero_copy_gbs": round(zc, 2), "pcie_dma_gbs": round(dma, 2)}
+    return out
+
+
+def bench_turbo(args, torch, q):
+    """TurboQuant KV codec: encode and decode of 2^21 vectors of 128 f32
+    values (1 GiB) at 2, 3, 4 and 8 bits; both kernels are HBM streams, so
+    the roofline is HBM bandwidth over the bytes read plus written."""
+    N, n = 1 << 21, 128
+    V = torch.randn((N, n), dtype=torch.float32, device="cuda")
+    res = {}
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    for bits in (4, 3, 2, 8):
+        rec = q.turbo_record_bytes(n, bits)
+        out = torch.empty((N, rec), dtype=torch.uint8, device="cuda")
+        dec = torch.empty((N, n), dtype=torch.float32, device="cuda")
+        q.turbo_encode(V, bits, out=out)
+        q.turbo_decode(out, n, bits, v=dec)
+        torch.cuda.synchronize()
+        t = {}
+        for name, fn in (("encode", lambda: q.turbo_encode(V, bits, out=out)),
+                         ("decode", lambda: q.turbo_decode(out, n, bits, v=dec))):
+            best = 1e9
+            for _ in range(5):
+                ev0.record()
+                fn()
+                ev1.record()
+                torch.cuda.synchronize()
+                best = min(best, ev0.elapsed_time(ev1) / 1e3)
+            t[name] = best
+        moved = N * (4 * n + rec)
+        res[str(bits)] = {"record_bytes": rec, "ratio_vs_f32": round(4 * n / rec, 3),
+                          "encode_ms": round(t["encode"] * 1e3, 4),
+                          "decode_ms": round(t["decode"] * 1e3, 4),
+                          "encode_gbs": round(moved / t["encode"] / 1e9, 1),
+                          "decode_gbs": round(moved / t["decode"] / 1e9, 1),
+                          "encode_frac": round(moved / t["encode"] / 1e9 / HBM_PEAK_GBS, 4),
+                          "decode_frac": round(moved / t["decode"] / 1e9 / HBM_PEAK_GBS, 4),
+                          "vectors_per_s_decode": round(N / t["decode"], 0)}
+        log("turbo%d: encode %.1f GB/s, decode %.1f GB/s" % (bits, res[str(bits)]["encode_gbs"],
+                                                             res[str(bits)]["decode_gbs"]))
+        del out, dec
+    r4 = res["4"]
+    out = _base(args, 5, 1, r4["decode_ms"] / 1e3, r4["decode_gbs"],
+                "TurboQuant KV codec: 2^21 vectors of 128 f32 (1 GiB), 4-bit records of 68 bytes; "
+                "value = decode GB/s (record bytes read + f32 written)")
+    out["unit"] = "GB/s"
+    out["turbo"] = res
+    out["roofline"] = {"bound": "hbm", "achieved": r4["decode_gbs"], "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": r4["decode_frac"], "traffic": None,
+                       "kernel": "turbo_decode_kernel<2, 4>"}
+    return out
+
+
 def bench_skewed(args, torch, q):
     """One layer shape (d=2048, F=512, E=512, top-8) with Zipf(1.1)-biased
     router logits; token batches of 1, 4 and 16.  16 replicas of the layer
@@ -440,6 +605,10 @@ def main():
                     help="steps as HIP-graph replays or as eager launches")
     ap.add_argument("--path", choices=["fused", "split"], default="fused",
                     help="moe_layer_decode, or moe_route_topk + moe_expert_decode")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="run one-token layers as one launch whose workgroups exchange logits "
+                         "and h through tagged words, instead of the router -> gate/up -> down "
+                         "launch chain (same results)")
     ap.add_argument("--replicas", type=int, default=32,
                     help="distinct layer copies cycled through (so caches cannot serve repeats)")
     ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
@@ -455,12 +624,15 @@ def main():
                     help="also run one device copy of 1 GiB (counter calibration)")
     ap.add_argument("--batches", default="1,4,16",
                     help="token batch sizes of the skewed workload")
-    ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed", "floor"],
+    ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed", "floor",
+                                           "offload", "cache", "turbo"],
                     default="layer",
                     help="layer: one MoE layer (the headline line); stack: 40 layers with a dense "
                          "GEMV each; hostmapped: 48 layers, experts of 24 in pinned host memory; "
                          "skewed: 512 experts, Zipf-biased routing, token batches 1/4/16; "
-                         "floor: the latency and bandwidth probes of the one-token floor model")
+                         "floor: the latency and bandwidth probes of the one-token floor model; "
+                         "offload: PCIe vs CPU route for host-resident experts; cache: HBM expert "
+                         "cache over host-resident experts; turbo: TurboQuant KV codec")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -477,6 +649,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
+    q.lib.hfq4_debug_set_single_launch(1 if args.single_launch else 0)
     if args.workload == "floor":
         from quantized_moe_decode_amd import probes
         out = {"workload": "latency and bandwidth probes (floor model of the one-token layer)",
@@ -484,8 +657,9 @@ def main():
         print(json.dumps(out), flush=True)
         return
     if args.workload != "layer":
-        out = {"stack": bench_stack, "hostmapped": bench_hostmapped,
-               "skewed": bench_skewed}[args.workload](args, torch, q)
+        out = {"stack": bench_stack, "hostmapped": bench_hostmapped, "skewed": bench_skewed,
+               "offload": bench_offload, "cache": bench_cache,
+               "turbo": bench_turbo}[args.workload](args, torch, q)
         print(json.dumps(out), flush=True)
         return
 
@@ -552,13 +726,17 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    from quantized_moe_decode_amd import probes
     wall0 = time.perf_counter()
+    probes.spin(torch, 200)
     ev0.record(stream)
     run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = ev0.elapsed_time(ev1)
+    timing = ("HIP events around the replays; a 200 us single-wave spin ahead of the first "
+              "event keeps the device busy while the host enqueues them")
     err = q.workspace_error(ws)
     if err:
         raise SystemExit("device error word %d after timed run" % err)
@@ -570,7 +748,7 @@ def main():
     # last-workgroup-end.  The stamps cost a few stores per workgroup.
     kern = None
     if args.mode == "graph" and args.path == "fused":
-        import ctypes
+
         tr = torch.zeros(4 * 1024 * 8, dtype=torch.int64, device=dev)
         q.lib.hfq4_debug_set_trace(ctypes.c_void_p(tr.data_ptr()), tr.numel() * 8)
         gt = torch.cuda.CUDAGraph()
@@ -579,11 +757,19 @@ def main():
                 step(i)
         q.lib.hfq4_debug_set_trace(None, 0)
         samples = {"logits": [], "gateup": [], "down": [], "step": []}
-        nwg = {0: E, 1: torch.cuda.get_device_properties(0).multi_processor_count, 2: D // 8}
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        nwg = {0: E, 1: ncu, 2: D // 8}
         for rep in range(args.kernel_samples):
             gt.replay()
             torch.cuda.synchronize()
             t = tr.view(4, 1024, 8).cpu().numpy()
+            if int(t[0, :E, 0].max()) == 0:
+                # one launch per step (the single-launch layer): stamps 0..6
+                n = min(ncu, 1024)
+                span = (int(t[1, :n, 6].max()) - int(t[1, :n, 0].min())) / 100.0
+                samples["gateup"].append(span)
+                samples["step"].append(span)
+                continue
             st, en = {}, {}
             for kk, last in ((0, 1), (1, 5), (2, 3)):
                 n = min(nwg[kk], 1024)
@@ -593,7 +779,7 @@ def main():
             samples["gateup"].append((en[1] - st[1]) / 100.0)
             samples["down"].append((en[2] - st[2]) / 100.0)
             samples["step"].append((en[2] - st[0]) / 100.0)
-        kern = {k: (sum(v) / len(v), sorted(v)[len(v) // 2]) for k, v in samples.items()}
+        kern = {k: (sum(v) / len(v), sorted(v)[len(v) // 2]) for k, v in samples.items() if v}
         del gt
 
     # Launch duration of the gate/up kernel by HIP events on the stream the
@@ -606,7 +792,7 @@ def main():
     # median beside it.
     ev_us = None
     if args.path == "fused":
-        import ctypes
+
         hip = ctypes.CDLL("libamdhip64.so")
         # one event pair per step: the steps go back to back on the stream
         # (no synchronisation between them, as in decode), and the pairs
@@ -668,6 +854,7 @@ def main():
         "tokens_per_s": round(1.0 / per_step_s, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed": round(wall, 4),
+        "step_timing": timing,
         "roofline": ({"bound": "hbm",
                       "achieved": round(gu_bytes / (ev_us[0] * 1e-6) / 1e9, 2),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -16,6 +16,25 @@
  *            fit is refused loudly, naming what is short and by how much.
  *  [EXPERTS] Strata user report (lcz.me), section "3. 模型与引擎": each
  *            expert of a layer has its own gate, up and down tensors.
+ *  [PLACE]   same page, section "放置算法：auto 自动放置…": fixed weights
+ *            first, then routed experts fill the device budget layer by
+ *            layer; a decode-heat ranking (hot set) lets the device keep
+ *            the most often selected experts; a configuration that does
+ *            not fit is refused, naming the bytes short.  Strata user
+ *            report, sections "1. Strata 是什么" and "5. 实测速度": the most
+ *            routed experts cached on the device, the cache's hit rate.
+ *  [TURBO]   page "hipfire：为AMD RDNA GPU打造的Rust原生LLM推理引擎", section
+ *            "3. TurboQuant KV缓存压缩": KV vectors normalised to unit norm,
+ *            rotated by a fast Walsh-Hadamard transform, quantised to
+ *            Lloyd-Max centroids, stored with the ratio of the original to
+ *            the reconstructed norm (exact norm on decode); 3.88x / 7.5x /
+ *            9.85x / 14.2x against f32 for 8 / 4 / 3 / 2 bits.
+ *  [CPUEXEC] hipfire explainer, section "PCIe 直通": host-resident experts
+ *            can instead be computed by a CPU GEMV; at load the PCIe path
+ *            and the CPU path are timed and the CPU is used only when it
+ *            is at least 15% faster.  Strata user report, sections "1.
+ *            Strata 是什么" and "2. 硬件配置": experts that miss the VRAM
+ *            cache run on the CPU (AVX-2 kernels).
  *
  * Readings taken where the pages are silent (stated once here, used by
  * every entry point): w = zero + scale*q; scale at byte 0 and zero at byte
@@ -66,6 +85,7 @@ extern "C" {
 #define HFQ4_E_DEVICE     (-4)  /* current device is not gfx950 */
 #define HFQ4_E_HIP        (-5)  /* a HIP runtime call or kernel launch failed */
 #define HFQ4_E_UNSUPPORTED (-6) /* valid request outside the sizes built here */
+#define HFQ4_E_NOFIT      (-7)  /* a placement does not fit its budget (detail: bytes short) */
 
 /* Sticky device-side error bits, OR-ed into the first 4 bytes of a MoE
  * workspace (see moe_workspace_bytes) or into hfq4_pack's `bad` counter. */
@@ -232,6 +252,115 @@ int moe_layer_decode_noalloc(const moe_layer* L, const float* Wr, const float* b
                              int32_t* idx, float* wts, const float* residual,
                              float* y, int64_t ldy, uint32_t* err, hipStream_t stream);
 
+/* ------------------------------------------------------------ expert cache [PLACE] */
+
+#define HFQ4_PLACE_LAYERS 0   /* whole layers, first to last, while the budget lasts */
+#define HFQ4_PLACE_HOTSET 1   /* single experts by decode heat, hottest first */
+
+/* Placement of `layers` x E routed experts (expert_bytes each) into an HBM
+ * budget [PLACE].  The fixed weights (router, dense, everything that is
+ * not a routed expert: fixed_bytes) are placed first; if they alone exceed
+ * budget_bytes the call fails with HFQ4_E_NOFIT and a detail naming the
+ * bytes short.  Then experts are placed while they fit:
+ *  HFQ4_PLACE_LAYERS  whole layers in order (heat may be NULL);
+ *  HFQ4_PLACE_HOTSET  single experts by heat[l*E + e] (selection counts of
+ *                     a calibration decode), the hottest first, equal heat
+ *                     to the lower (layer, expert) index.
+ * resident[l*E + e] (host, layers*E bytes) receives 1 for experts placed
+ * in HBM, 0 for the rest (pinned host memory); *placed_bytes (may be NULL)
+ * the expert bytes placed.  Host only, deterministic. */
+int moe_place_experts(int mode, int64_t layers, int64_t E, const uint64_t* heat,
+                      uint64_t expert_bytes, uint64_t fixed_bytes, uint64_t budget_bytes,
+                      uint8_t* resident, uint64_t* placed_bytes);
+
+/* A layer whose experts are reached through a pointer table [PLACE]
+ * [PCIE]: ptr[3e + 0/1/2] (device memory, E*3 entries) hold device-visible
+ * addresses of expert e's gate [F][d], up [F][d] and down [d][F] HFQ4
+ * matrices -- an HBM slot of an expert cache, or pinned host memory mapped
+ * for the device (hfq4_host_device_pointer) -- each 16-byte aligned and
+ * valid for the whole call.  resident (device, E bytes, or NULL) marks the
+ * experts whose matrices are in HBM. */
+typedef struct moe_layer_table {
+    const uint64_t* ptr;
+    const uint8_t* resident;
+    int64_t E, d, F;
+} moe_layer_table;
+
+/* moe_layer_decode for one token of a table layer: the same results, bit
+ * for bit, as a layer holding the same bytes in one tensor each.  hits
+ * (device uint64 [2], or NULL) accumulates the selections of experts
+ * marked resident ([0]) and of the others ([1]) -- the cache's hit count.
+ * Supported: batch 1 and the tuned shape (1792 < d <= 2048, F = 512,
+ * k <= 8, E <= 1024); other requests fail with HFQ4_E_UNSUPPORTED.  ws as
+ * for moe_layer_decode with an HBM layer of the same E, d, F, batch 1. */
+int moe_layer_decode_table(const moe_layer_table* L, const float* Wr, const float* bias,
+                           const float* x, int batch, int k, int32_t* idx, float* wts,
+                           const float* residual, float* y, uint64_t* hits,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ TurboQuant KV codec [TURBO] */
+
+/* Readings (the page gives the steps, not these details): rotation by the
+ * orthonormal Walsh-Hadamard matrix H_n / sqrt(n) in natural order, no
+ * random signs; levels = the Lloyd-Max quantiser of the standard normal
+ * with 2^bits levels scaled by 1/sqrt(n), each rotated coordinate taking
+ * the nearest level (ties to the lower); record of one vector = the n codes
+ * packed LSB-first (code j at bits [j*bits, j*bits + bits) of a
+ * little-endian bit stream), then s = |v| / |c| as an f32 (c the chosen
+ * levels), n*bits/8 + 4 bytes; a zero vector stores codes 0 and s = 0.
+ * Decode: v' = s * H c / sqrt(n), whose norm is |v| up to the f32 of s.
+ * Supported: n in {64, 128, 256}, bits in {2, 3, 4, 8}. */
+
+/* Bytes of one encoded vector. */
+int turbo_record_bytes(int n, int bits, size_t* out);
+
+/* The level table the kernels use (host floats, 2^bits entries,
+ * ascending), for inspection. */
+int turbo_levels(int n, int bits, float* levels);
+
+/* Encode count vectors v[i][0..n) (device f32, row stride ldv >= n
+ * elements) into out (device, count * turbo_record_bytes bytes, 4-byte
+ * aligned).  One wave per vector; enqueued on stream. */
+int turbo_encode(const float* v, int64_t count, int n, int64_t ldv, int bits, void* out,
+                 size_t out_bytes, hipStream_t stream);
+
+/* Decode count records (device) into v[i][0..n) (device f32, row stride
+ * ldv >= n). */
+int turbo_decode(const void* in, size_t in_bytes, int64_t count, int n, int bits, float* v,
+                 int64_t ldv, hipStream_t stream);
+
+/* ------------------------------------------------------------ host CPU execution */
+
+/* Dequantizing GEMV on the host CPU [CPUEXEC] [HFQ]: the same result as
+ * hfq4_gemv (y[b] = residual[b] + W x[b]), computed in f32 with FMA (AVX2
+ * where the CPU has it) on `nthreads` host threads (0 = one per hardware
+ * thread; a pool created on first use serves every later call).  Every
+ * pointer is host memory (pinned or pageable); nothing touches a GPU and
+ * the call returns when y is written.  Each output is summed by one thread
+ * in a fixed order, so results do not depend on nthreads.  batch 1..16,
+ * K >= 1; y must not overlap x or W, residual may be y. */
+int hfq4_gemv_host(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx,
+                   int batch, const float* residual, int64_t ldr, float* y, int64_t ldy,
+                   int nthreads);
+
+/* The expert half of a layer on the host CPU [CPUEXEC] [EXPERTS]: the same
+ * result as moe_expert_decode, with L's gate/up/down pointers, x, idx, wts,
+ * residual and y all host memory.  An index outside [0, E) adds nothing and
+ * sets HFQ4_DEV_ERR_INDEX in *err (host uint32, may be NULL).  Layer limits
+ * as for moe_expert_decode. */
+int moe_expert_decode_host(const moe_layer* L, const float* x, int64_t ldx, int batch,
+                           const int32_t* idx, const float* wts, int k,
+                           const float* residual, float* y, int64_t ldy, int nthreads,
+                           uint32_t* err);
+
+/* The measured route choice for host-resident experts [CPUEXEC]: given the
+ * time one decode step of such a layer takes when the GPU reads the experts
+ * over PCIe and when the CPU computes them (both measured by the caller on
+ * this machine), *use_cpu = 1 only if the CPU is at least 15% faster
+ * (cpu_seconds * 1.15 <= pcie_seconds), else 0: the decision leans to the
+ * PCIe path.  Times must be positive and finite. */
+int hfq4_offload_choice(double pcie_seconds, double cpu_seconds, int* use_cpu);
+
 /* Testing hook: make the device check see `arch` instead of the real
  * device ("" or NULL restores the real query).  Lets the refusal on a
  * non-gfx950 device be exercised without such a device. */
@@ -241,6 +370,14 @@ int hfq4_debug_set_arch(const char* arch);
  * launches fill with per-workgroup phase timestamps (s_memrealtime, 100
  * MHz), slot [(kernel*1024 + workgroup)*8 + point]; NULL turns it off. */
 int hfq4_debug_set_trace(void* dev, size_t bytes);
+
+/* Diagnostics: one-token layers of the tuned shape (moe_layer_decode)
+ * run as the three-launch chain router -> gate/up -> down (on = 0, the
+ * default) or as one launch whose workgroups exchange the logits and h
+ * through tagged words (on != 0; measured slower on the MI355X, see the
+ * design notes).  Both give the same bits; the switch exists to compare
+ * them and is process-wide. */
+int hfq4_debug_set_single_launch(int on);
 
 /* Diagnostics: hipEvent_t handles (cast to void*) recorded when each
  * later launch of the expert gate/up kernel starts and ends, so a caller

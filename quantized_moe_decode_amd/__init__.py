@@ -23,6 +23,9 @@ HFQ4_E_WORKSPACE = -3
 HFQ4_E_DEVICE = -4
 HFQ4_E_HIP = -5
 HFQ4_E_UNSUPPORTED = -6
+HFQ4_E_NOFIT = -7
+HFQ4_PLACE_LAYERS = 0
+HFQ4_PLACE_HOTSET = 1
 HFQ4_DEV_ERR_INDEX = 1
 HFQ4_DEV_ERR_TIMEOUT = 2
 HFQ4_DEV_ERR_NONFINITE = 4
@@ -36,6 +39,9 @@ EXPORTS = [
     "hfq4_gemv", "moe_route_workspace_bytes", "moe_route_topk", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_decode", "moe_layer_decode", "hfq4_host_device_pointer",
     "hfq4_debug_set_trace", "hfq4_debug_set_events", "moe_layer_decode_noalloc",
+    "hfq4_gemv_host", "moe_expert_decode_host", "hfq4_offload_choice",
+    "hfq4_debug_set_single_launch", "moe_place_experts", "moe_layer_decode_table",
+    "turbo_record_bytes", "turbo_levels", "turbo_encode", "turbo_decode",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -44,6 +50,11 @@ class Hfq4Error(RuntimeError):
     def __init__(self, code, msg):
         super().__init__("hfq4 status %d: %s" % (code, msg))
         self.code = code
+
+
+class MoeLayerTableC(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("resident", ctypes.c_void_p), ("E", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("F", ctypes.c_int64)]
 
 
 class MoeLayerC(ctypes.Structure):
@@ -79,6 +90,19 @@ def _load():
         "hfq4_host_device_pointer": (I32, [P, ctypes.POINTER(P)]),
         "moe_layer_decode_noalloc": (I32, [ctypes.POINTER(MoeLayerC), P, P, P, I64, I32, I32, P, P,
                                            P, P, I64, P, P]),
+        "hfq4_gemv_host": (I32, [P, I64, I64, P, I64, I32, P, I64, P, I64, I32]),
+        "moe_expert_decode_host": (I32, [ctypes.POINTER(MoeLayerC), P, I64, I32, P, P, I32, P, P,
+                                         I64, I32, ctypes.POINTER(ctypes.c_uint32)]),
+        "hfq4_offload_choice": (I32, [ctypes.c_double, ctypes.c_double, ctypes.POINTER(I32)]),
+        "hfq4_debug_set_single_launch": (I32, [I32]),
+        "moe_place_experts": (I32, [I32, I64, I64, P, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_uint64, P, ctypes.POINTER(ctypes.c_uint64)]),
+        "moe_layer_decode_table": (I32, [ctypes.POINTER(MoeLayerTableC), P, P, P, I32, I32, P, P, P,
+                                         P, P, P, SZ, P]),
+        "turbo_record_bytes": (I32, [I32, I32, ctypes.POINTER(SZ)]),
+        "turbo_levels": (I32, [I32, I32, P]),
+        "turbo_encode": (I32, [P, I64, I32, I64, I32, P, SZ, P]),
+        "turbo_decode": (I32, [P, SZ, I64, I32, I32, P, I64, P]),
         "hfq4_debug_set_trace": (I32, [P, SZ]),
         "hfq4_debug_set_events": (I32, [P, P]),
     }
@@ -378,6 +402,195 @@ def moe_layer_decode_noalloc(layer, x, k, idx, wts, y, residual=None, err=None, 
                                         _ptr(residual), _ptr(y), y.stride(0), _ptr(err),
                                         _stream(stream)))
     return idx, wts, y
+
+
+# ------------------------------------------------------------------ host CPU execution
+
+def _host_array(a, name, dtype):
+    """(pointer, numpy view) of a host buffer: a numpy array or a CPU torch
+    tensor (pinned or not), C-contiguous along its rows."""
+    import numpy as np
+    if hasattr(a, "is_cuda"):
+        _need(not a.is_cuda, "%s must be host memory" % name)
+        arr = a.numpy()
+    else:
+        arr = np.asarray(a)
+    _need(arr.dtype == dtype, "%s must be %s, got %s" % (name, np.dtype(dtype), arr.dtype))
+    _need(arr.ndim <= 1 or arr.strides[-1] == arr.itemsize, "%s must have unit stride" % name)
+    return ctypes.c_void_p(arr.ctypes.data), arr
+
+
+def hfq4_gemv_host(W, rows, K, x, residual=None, y=None, nthreads=0):
+    """y[b] = residual[b] + W x[b] on the host CPU (every buffer host memory;
+    numpy arrays or CPU torch tensors).  Returns y (numpy, float32)."""
+    import numpy as np
+    wp, Wa = _host_array(W, "W", np.uint8)
+    _need(Wa.size >= hfq4_packed_bytes(rows, K), "W holds %d bytes, need %d"
+          % (Wa.size, hfq4_packed_bytes(rows, K)))
+    xp, xa = _host_array(x, "x", np.float32)
+    xa2 = xa.reshape(1, -1) if xa.ndim == 1 else xa
+    batch = xa2.shape[0]
+    _need(xa2.shape[1] >= K, "x rows hold %d elements, need K = %d" % (xa2.shape[1], K))
+    if y is None:
+        y = np.empty((batch, rows), dtype=np.float32)
+    yp, ya = _host_array(y, "y", np.float32)
+    ya2 = ya.reshape(1, -1) if ya.ndim == 1 else ya
+    rp, ldr = None, rows
+    if residual is not None:
+        rp, ra = _host_array(residual, "residual", np.float32)
+        ra2 = ra.reshape(1, -1) if ra.ndim == 1 else ra
+        ldr = ra2.strides[0] // 4
+    _check(lib.hfq4_gemv_host(wp, rows, K, xp, xa2.strides[0] // 4, batch, rp, ldr, yp,
+                              ya2.strides[0] // 4, int(nthreads)))
+    return y
+
+
+class HostMoeLayer:
+    """One MoE layer's experts in host memory for moe_expert_decode_host:
+    gate/up [E * packed(F, d)] and down [E * packed(d, F)] uint8 buffers
+    (numpy arrays or CPU torch tensors, pinned or not)."""
+
+    def __init__(self, gate, up, down, E, d, F):
+        import numpy as np
+        self.E, self.d, self.F = E, d, F
+        gb, db = hfq4_packed_bytes(F, d), hfq4_packed_bytes(d, F)
+        ptrs = []
+        self._keep = []
+        for t, name, need in ((gate, "gate", E * gb), (up, "up", E * gb), (down, "down", E * db)):
+            p, a = _host_array(t, name, np.uint8)
+            _need(a.size >= need, "%s holds %d bytes, need %d" % (name, a.size, need))
+            ptrs.append(p.value)
+            self._keep.append(t)
+        self.c = MoeLayerC(ptrs[0], ptrs[1], ptrs[2], E, d, F, gb, gb, db, 0, 0)
+
+
+def moe_expert_decode_host(layer, x, idx, wts, residual=None, y=None, nthreads=0):
+    """The expert half of a layer on the host CPU.  Returns (y, error bits)."""
+    import numpy as np
+    xp, xa = _host_array(x, "x", np.float32)
+    xa2 = xa.reshape(1, -1) if xa.ndim == 1 else xa
+    B = xa2.shape[0]
+    ip, ia = _host_array(idx, "idx", np.int32)
+    wp, wa = _host_array(wts, "wts", np.float32)
+    k = ia.shape[-1]
+    _need(ia.size == B * k and wa.size == B * k, "idx and wts must be [B, k]")
+    if y is None:
+        y = np.empty((B, layer.d), dtype=np.float32)
+    yp, ya = _host_array(y, "y", np.float32)
+    ya2 = ya.reshape(1, -1) if ya.ndim == 1 else ya
+    rp = None
+    if residual is not None:
+        rp, ra = _host_array(residual, "residual", np.float32)
+        ra2 = ra.reshape(1, -1) if ra.ndim == 1 else ra
+        _need(B == 1 or ra2.strides[0] == ya2.strides[0], "residual row stride differs from y's")
+    err = ctypes.c_uint32(0)
+    _check(lib.moe_expert_decode_host(ctypes.byref(layer.c), xp, xa2.strides[0] // 4, B, ip, wp, k,
+                                      rp, yp, ya2.strides[0] // 4, int(nthreads),
+                                      ctypes.byref(err)))
+    return y, err.value
+
+
+def hfq4_offload_choice(pcie_seconds, cpu_seconds):
+    """True when the CPU path is at least 15% faster than the PCIe path."""
+    out = ctypes.c_int()
+    _check(lib.hfq4_offload_choice(float(pcie_seconds), float(cpu_seconds), ctypes.byref(out)))
+    return bool(out.value)
+
+
+# ------------------------------------------------------------------ expert cache
+
+def moe_place_experts(mode, layers, E, expert_bytes, fixed_bytes, budget_bytes, heat=None):
+    """Placement of layers x E experts into an HBM budget (see the C ABI).
+    Returns (resident uint8 [layers, E] numpy, placed bytes); raises
+    Hfq4Error(HFQ4_E_NOFIT) naming the bytes short when it does not fit."""
+    import numpy as np
+    res = np.zeros((layers, E), dtype=np.uint8)
+    hp = None
+    if heat is not None:
+        heat = np.ascontiguousarray(heat, dtype=np.uint64)
+        _need(heat.shape == (layers, E), "heat must be [layers, E]")
+        hp = ctypes.c_void_p(heat.ctypes.data)
+    placed = ctypes.c_uint64()
+    _check(lib.moe_place_experts(int(mode), layers, E, hp, int(expert_bytes), int(fixed_bytes),
+                                 int(budget_bytes), ctypes.c_void_p(res.ctypes.data),
+                                 ctypes.byref(placed)))
+    return res, placed.value
+
+
+def moe_layer_decode_table(tlayer, x, k, ws, residual=None, y=None, idx=None, wts=None, hits=None,
+                           stream=None):
+    """One token through a table layer (cache.TableLayer).  Returns (idx, wts, y)."""
+    import torch
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    _need(x2.shape[0] == 1, "table layers take one token per call")
+    _f32(x2, "x")
+    _need(x2.is_contiguous() and x2.shape[1] == tlayer.d, "x must be a contiguous [1, d] tensor")
+    if y is None:
+        y = torch.empty((1, tlayer.d), dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty((1, k), dtype=torch.int32, device=x.device)
+    if wts is None:
+        wts = torch.empty((1, k), dtype=torch.float32, device=x.device)
+    _f32(y, "y")
+    _need(y.is_contiguous() and y.numel() == tlayer.d, "y must be a contiguous [1, d] tensor")
+    if residual is not None:
+        _need(residual.is_contiguous() and residual.numel() == tlayer.d and
+              residual.dtype == torch.float32, "residual must be a contiguous [1, d] float32 tensor")
+    _check_routing_out(idx, wts, 1, k)
+    if hits is not None:
+        _need(hits.dtype == torch.int64 and hits.numel() >= 2, "hits must be an int64 [2] tensor")
+    _need(ws.dtype == torch.uint8, "ws must be a uint8 tensor")
+    _check(lib.moe_layer_decode_table(ctypes.byref(tlayer.c), _ptr(tlayer.Wr), _ptr(tlayer.bias),
+                                      _ptr(x2), 1, k, _ptr(idx), _ptr(wts), _ptr(residual), _ptr(y),
+                                      _ptr(hits), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, wts, y
+
+
+# ------------------------------------------------------------------ TurboQuant KV codec
+
+def turbo_record_bytes(n, bits):
+    out = ctypes.c_size_t()
+    _check(lib.turbo_record_bytes(n, bits, ctypes.byref(out)))
+    return out.value
+
+
+def turbo_levels(n, bits):
+    """The library's level table (numpy float32, 2^bits ascending)."""
+    import numpy as np
+    out = np.zeros(1 << bits, dtype=np.float32)
+    _check(lib.turbo_levels(n, bits, ctypes.c_void_p(out.ctypes.data)))
+    return out
+
+
+def turbo_encode(v, bits, out=None, stream=None):
+    """Encode f32 vectors v [count, n] (device) into records (uint8 [count,
+    record bytes])."""
+    import torch
+    _f32(v, "v")
+    count, n = v.shape
+    rec = turbo_record_bytes(n, bits)
+    if out is None:
+        out = torch.empty((count, rec), dtype=torch.uint8, device=v.device)
+    _need(out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= count * rec,
+          "out must be a contiguous uint8 tensor of %d bytes" % (count * rec))
+    _check(lib.turbo_encode(_ptr(v), count, n, v.stride(0), bits, _ptr(out), out.numel(),
+                            _stream(stream)))
+    return out
+
+
+def turbo_decode(records, n, bits, v=None, stream=None):
+    """Decode records (uint8 [count, record bytes], device) into f32 [count, n]."""
+    import torch
+    rec = turbo_record_bytes(n, bits)
+    _need(records.dtype == torch.uint8 and records.is_contiguous(), "records must be contiguous uint8")
+    count = records.numel() // rec
+    if v is None:
+        v = torch.empty((count, n), dtype=torch.float32, device=records.device)
+    _f32(v, "v")
+    _need(v.shape[0] >= count and v.shape[1] >= n, "v must be [count, n]")
+    _check(lib.turbo_decode(_ptr(records), records.numel(), count, n, bits, _ptr(v), v.stride(0),
+                            _stream(stream)))
+    return v
 
 
 def workspace_error(ws):

@@ -16,7 +16,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhfq4moe.so")
-SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "moe.hip", "moe_mfma.hip"]
+SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "moe.hip", "moe_mfma.hip", "turbo.hip"]
+HOST_SOURCES = ["host_cpu.cpp", "placement.cpp", "turbo_tables.cpp"]   # host-only C++
 PROBE_LIB = os.path.join(HERE, "libhfq4probe.so")
 PROBE_SOURCES = [os.path.join(HERE, "probes", "probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,9 +29,27 @@ FLAGS = [
 ]
 
 
-def _hipcc(srcs, lib, verbose):
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
+
+
+def _host_objects(verbose):
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(HERE, os.path.splitext(src)[0] + ".host.o")
+        cmd = [HIPCC] + HOST_FLAGS + ["-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("compiling %s failed" % src)
+        objs.append(obj)
+    return objs
+
+
+def _hipcc(srcs, lib, verbose, objs=()):
     tmp = lib + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-x", "hip"] + srcs + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + ["-x", "hip"] + srcs + ["-x", "none"] + list(objs) + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,7 +60,10 @@ def _hipcc(srcs, lib, verbose):
 
 
 def build(verbose=False):
-    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    objs = _host_objects(verbose)
+    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose, objs)
+    for o in objs:
+        os.remove(o)
     _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 

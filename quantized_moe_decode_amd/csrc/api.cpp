@@ -7,6 +7,7 @@
 // short and by how much instead of failing later).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -14,7 +15,10 @@
 #include <string>
 
 #include "../../include/hfq4moe.h"
+#include "host_cpu.h"
 #include "launch.h"
+#include "placement.h"
+#include "turbo.h"
 
 namespace {
 
@@ -163,6 +167,13 @@ int hfq4_debug_set_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
     return fail(HFQ4_E_INVALID, "give both events or neither");
   hq::set_timing_events(start, stop);
+  return ok();
+}
+
+// Diagnostics: one-token layers of the tuned shape as the three-launch
+// chain (0, the default) or as one launch (1); results are the same bits.
+int hfq4_debug_set_single_launch(int on) {
+  hq::set_single_launch(on != 0);
   return ok();
 }
 
@@ -393,6 +404,198 @@ int moe_layer_decode_noalloc(const moe_layer* L, const float* Wr, const float* b
   if (err) w.err = err;
   return hip_status(hq::launch_layer(to_dev(L), Wr, bias, x, ldx, batch, k, idx, wts, residual, y, ldy, w, stream),
                     "moe_layer_decode_noalloc launch");
+}
+
+int hfq4_gemv_host(const void* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,
+                   const float* residual, int64_t ldr, float* y, int64_t ldy, int nthreads) {
+  if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);
+  if (K < 1) return fail(HFQ4_E_INVALID, "K = %lld < 1", (long long)K);
+  if (batch < 1 || batch > HFQ4_MAX_BATCH)
+    return fail(HFQ4_E_INVALID, "batch = %d outside [1, %d]", batch, HFQ4_MAX_BATCH);
+  if (nthreads < 0) return fail(HFQ4_E_INVALID, "nthreads = %d < 0", nthreads);
+  if (rows == 0) return ok();
+  if (!W || !x || !y) return fail(HFQ4_E_INVALID, "W, x and y must be non-NULL");
+  if (ldx < K) return fail(HFQ4_E_INVALID, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldy < rows) return fail(HFQ4_E_INVALID, "ldy = %lld < rows = %lld", (long long)ldy, (long long)rows);
+  if (residual && ldr < rows) return fail(HFQ4_E_INVALID, "ldr = %lld < rows = %lld", (long long)ldr, (long long)rows);
+  const size_t yb = sizeof(float) * ((size_t)(batch - 1) * ldy + rows);
+  if (overlap(x, sizeof(float) * ((size_t)(batch - 1) * ldx + K), y, yb))
+    return fail(HFQ4_E_INVALID, "y overlaps x");
+  if (overlap(W, packed(rows, K), y, yb)) return fail(HFQ4_E_INVALID, "y overlaps W");
+  if (residual && residual != y && overlap(residual, sizeof(float) * ((size_t)(batch - 1) * ldr + rows), y, yb))
+    return fail(HFQ4_E_INVALID, "residual partially overlaps y");
+  hq::gemv_host(static_cast<const uint8_t*>(W), rows, K, x, ldx, batch, residual, ldr, y, ldy,
+                nthreads ? nthreads : hq::host_threads_default());
+  return ok();
+}
+
+int moe_expert_decode_host(const moe_layer* L, const float* x, int64_t ldx, int batch,
+                           const int32_t* idx, const float* wts, int k, const float* residual,
+                           float* y, int64_t ldy, int nthreads, uint32_t* err) {
+  int r = check_layer(L);
+  if (r) return r;
+  r = check_expert_io(L, x, ldx, batch, idx, wts, k, residual, y, ldy);
+  if (r) return r;
+  if (nthreads < 0) return fail(HFQ4_E_INVALID, "nthreads = %d < 0", nthreads);
+  hq::HostLayer H{static_cast<const uint8_t*>(L->gate), static_cast<const uint8_t*>(L->up),
+                  static_cast<const uint8_t*>(L->down), L->E, L->d, L->F,
+                  L->stride_gate, L->stride_up, L->stride_down};
+  hq::expert_decode_host(H, x, ldx, batch, idx, wts, k, residual, y, ldy,
+                         nthreads ? nthreads : hq::host_threads_default(), err);
+  return ok();
+}
+
+int moe_place_experts(int mode, int64_t layers, int64_t E, const uint64_t* heat,
+                      uint64_t expert_bytes, uint64_t fixed_bytes, uint64_t budget_bytes,
+                      uint8_t* resident, uint64_t* placed_bytes) {
+  if (mode != HFQ4_PLACE_LAYERS && mode != HFQ4_PLACE_HOTSET)
+    return fail(HFQ4_E_INVALID, "placement mode %d is neither HFQ4_PLACE_LAYERS nor HFQ4_PLACE_HOTSET", mode);
+  if (layers < 1 || E < 1) return fail(HFQ4_E_INVALID, "layers = %lld, E = %lld: need >= 1", (long long)layers, (long long)E);
+  if (!resident) return fail(HFQ4_E_INVALID, "resident is NULL");
+  if (mode == HFQ4_PLACE_HOTSET && !heat) return fail(HFQ4_E_INVALID, "hot-set placement needs the heat counts");
+  if (expert_bytes == 0) return fail(HFQ4_E_INVALID, "expert_bytes is 0");
+  uint64_t placed = 0, shortb = 0;
+  const int nofit = hq::place_experts(mode, layers, E, heat, expert_bytes, fixed_bytes, budget_bytes,
+                                      resident, &placed, &shortb);
+  if (placed_bytes) *placed_bytes = placed;
+  if (nofit)
+    return fail(HFQ4_E_NOFIT,
+                "DOES NOT FIT: the fixed weights need %llu bytes, the HBM budget is %llu: short by "
+                "%llu bytes (raise the budget by at least that)",
+                (unsigned long long)fixed_bytes, (unsigned long long)budget_bytes,
+                (unsigned long long)shortb);
+  return ok();
+}
+
+int moe_layer_decode_table(const moe_layer_table* T, const float* Wr, const float* bias,
+                           const float* x, int batch, int k, int32_t* idx, float* wts,
+                           const float* residual, float* y, uint64_t* hits, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!T) return fail(HFQ4_E_INVALID, "table layer descriptor is NULL");
+  if (!T->ptr) return fail(HFQ4_E_INVALID, "table layer ptr is NULL");
+  if (reinterpret_cast<uintptr_t>(T->ptr) & 7u) return fail(HFQ4_E_ALIGN, "ptr must be 8-byte aligned");
+  if (hits && (reinterpret_cast<uintptr_t>(hits) & 7u)) return fail(HFQ4_E_ALIGN, "hits must be 8-byte aligned");
+  if (T->E < 1 || T->E > HFQ4_MAX_EXPERTS)
+    return fail(HFQ4_E_INVALID, "E = %lld outside [1, %d]", (long long)T->E, HFQ4_MAX_EXPERTS);
+  if (batch != 1) return fail(HFQ4_E_UNSUPPORTED, "table layers take one token per call, got batch = %d", batch);
+  if (k < 1 || k > HFQ4_MAX_TOPK || k > T->E)
+    return fail(HFQ4_E_INVALID, "k = %d: need 1 <= k <= min(E = %lld, %d)", k, (long long)T->E, HFQ4_MAX_TOPK);
+  if (!(T->d > 1792 && T->d <= 2048 && (T->d & 3) == 0 && T->F == 512 && k <= 8))
+    return fail(HFQ4_E_UNSUPPORTED, "table layers need 1792 < d <= 2048 (d %% 4 == 0), F = 512, k <= 8; "
+                "got d = %lld, F = %lld, k = %d", (long long)T->d, (long long)T->F, k);
+  if (!Wr || !aligned16(Wr)) return fail(HFQ4_E_ALIGN, "Wr must be non-NULL and 16-byte aligned");
+  // reuse the HBM-layer checks for the activations and workspace
+  moe_layer L{reinterpret_cast<const void*>(16), reinterpret_cast<const void*>(16),
+              reinterpret_cast<const void*>(16), T->E, T->d, T->F,
+              (int64_t)packed(T->F, T->d), (int64_t)packed(T->F, T->d), (int64_t)packed(T->d, T->F), 0u, 0u};
+  int r = check_expert_io(&L, x, T->d, 1, idx, wts, k, residual, y, T->d);
+  if (r) return r;
+  if (!ws) return fail(HFQ4_E_INVALID, "ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(HFQ4_E_ALIGN, "ws must be 256-byte aligned");
+  const size_t need = ws_bytes_for(T->E, 1, k, T->d, T->F, 0);
+  if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  r = check_device();
+  if (r) return r;
+  if (hq::num_cus() > hq::XG_MAX)
+    return fail(HFQ4_E_UNSUPPORTED, "%d compute units: table layers support at most %d", hq::num_cus(), hq::XG_MAX);
+  hq::LayerDev D{};
+  D.E = (int)T->E;
+  D.d = (int)T->d;
+  D.F = (int)T->F;
+  hq::Ws w = hq::ws_carve(ws, T->E, 1, k, T->d, T->F, 0);
+  return hip_status(hq::launch_layer_table(D, T->ptr, T->resident, reinterpret_cast<unsigned long long*>(hits),
+                                           Wr, bias, x, k, idx, wts, residual, y, w, stream),
+                    "moe_layer_decode_table launch");
+}
+
+static int check_turbo(int n, int bits) {
+  if (n != 64 && n != 128 && n != 256) return fail(HFQ4_E_UNSUPPORTED, "n = %d: need 64, 128 or 256", n);
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(HFQ4_E_UNSUPPORTED, "bits = %d: need 2, 3, 4 or 8", bits);
+  return HFQ4_OK;
+}
+
+// Level tables, computed on first use per (n, bits) and kept.
+static const hq::TurboTable& turbo_table_for(int n, int bits) {
+  static std::mutex mu;
+  static hq::TurboTable* tabs[3][9] = {{nullptr}};
+  const int ni = n == 64 ? 0 : n == 128 ? 1 : 2;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!tabs[ni][bits]) {
+    tabs[ni][bits] = new hq::TurboTable();
+    hq::turbo_table(n, bits, tabs[ni][bits]);
+  }
+  return *tabs[ni][bits];
+}
+
+int turbo_record_bytes(int n, int bits, size_t* out) {
+  if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
+  int r = check_turbo(n, bits);
+  if (r) return r;
+  *out = (size_t)n * bits / 8 + 4;
+  return ok();
+}
+
+int turbo_levels(int n, int bits, float* levels) {
+  if (!levels) return fail(HFQ4_E_INVALID, "levels is NULL");
+  int r = check_turbo(n, bits);
+  if (r) return r;
+  const hq::TurboTable& t = turbo_table_for(n, bits);
+  for (int j = 0; j < (1 << bits); ++j) levels[j] = t.cent[j];
+  return ok();
+}
+
+int turbo_encode(const float* v, int64_t count, int n, int64_t ldv, int bits, void* out,
+                 size_t out_bytes, hipStream_t stream) {
+  int r = check_turbo(n, bits);
+  if (r) return r;
+  if (count < 0) return fail(HFQ4_E_INVALID, "count = %lld < 0", (long long)count);
+  if (count == 0) return ok();
+  if (!v || !out) return fail(HFQ4_E_INVALID, "v and out must be non-NULL");
+  if (ldv < n) return fail(HFQ4_E_INVALID, "ldv = %lld < n = %d", (long long)ldv, n);
+  const size_t rec = (size_t)n * bits / 8 + 4;
+  if (out_bytes < rec * (size_t)count)
+    return fail(HFQ4_E_INVALID, "out needs %zu bytes, got %zu", rec * (size_t)count, out_bytes);
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) || (reinterpret_cast<uintptr_t>(v) & 3u))
+    return fail(HFQ4_E_ALIGN, "v and out must be 4-byte aligned");
+  if (overlap(v, sizeof(float) * ((size_t)(count - 1) * ldv + n), out, rec * (size_t)count))
+    return fail(HFQ4_E_INVALID, "out overlaps v");
+  r = check_device();
+  if (r) return r;
+  return hip_status(hq::launch_turbo(true, v, count, n, ldv, out, bits, turbo_table_for(n, bits), stream),
+                    "turbo_encode launch");
+}
+
+int turbo_decode(const void* in, size_t in_bytes, int64_t count, int n, int bits, float* v,
+                 int64_t ldv, hipStream_t stream) {
+  int r = check_turbo(n, bits);
+  if (r) return r;
+  if (count < 0) return fail(HFQ4_E_INVALID, "count = %lld < 0", (long long)count);
+  if (count == 0) return ok();
+  if (!v || !in) return fail(HFQ4_E_INVALID, "in and v must be non-NULL");
+  if (ldv < n) return fail(HFQ4_E_INVALID, "ldv = %lld < n = %d", (long long)ldv, n);
+  const size_t rec = (size_t)n * bits / 8 + 4;
+  if (in_bytes < rec * (size_t)count)
+    return fail(HFQ4_E_INVALID, "in holds %zu bytes, %lld records need %zu", in_bytes, (long long)count,
+                rec * (size_t)count);
+  if ((reinterpret_cast<uintptr_t>(in) & 3u) || (reinterpret_cast<uintptr_t>(v) & 3u))
+    return fail(HFQ4_E_ALIGN, "in and v must be 4-byte aligned");
+  if (overlap(v, sizeof(float) * ((size_t)(count - 1) * ldv + n), in, rec * (size_t)count))
+    return fail(HFQ4_E_INVALID, "v overlaps in");
+  r = check_device();
+  if (r) return r;
+  return hip_status(hq::launch_turbo(false, in, count, n, ldv, v, bits, turbo_table_for(n, bits), stream),
+                    "turbo_decode launch");
+}
+
+int hfq4_offload_choice(double pcie_seconds, double cpu_seconds, int* use_cpu) {
+  if (!use_cpu) return fail(HFQ4_E_INVALID, "use_cpu is NULL");
+  if (!(pcie_seconds > 0.0) || !(cpu_seconds > 0.0) || pcie_seconds == HUGE_VAL ||
+      cpu_seconds == HUGE_VAL)
+    return fail(HFQ4_E_INVALID, "times must be positive and finite (pcie %g s, cpu %g s)",
+                pcie_seconds, cpu_seconds);
+  *use_cpu = cpu_seconds * 1.15 <= pcie_seconds ? 1 : 0;
+  return ok();
 }
 
 int hfq4_host_device_pointer(void* host, void** dev) {

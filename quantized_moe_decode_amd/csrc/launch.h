@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "turbo.h"
+
 namespace hq {
 
 // Kernel-side view of one MoE layer's expert weights.
@@ -45,7 +47,20 @@ struct Ws {
   uint32_t dslot;     // bytes per staged down matrix
   GroupTab* gtab;     // batched: the token groups, published by the gate/up kernel
   uint64_t* trace;    // optional phase timestamps (null unless tracing is on)
+  // one token, single-launch layer: words exchanged between its workgroups,
+  // each (generation << 32 | value bits), and the call counter.  They sit
+  // at the same place in every layout, right after the header, and no other
+  // kernel writes there, so a workspace used for calls of other shapes in
+  // between never leaves data that looks like a current word.
+  uint64_t* xlog;     // [XL_MAX] router logits
+  uint64_t* xh;       // [XH_MAX] SiLU(gate) * up, [k][F]
+  uint32_t* xflag;    // [XG_MAX] generation of the last h a workgroup published
+  uint32_t* gen;      // [1] single-launch calls run on this workspace
 };
+constexpr int XG_MAX = 1024;       // workgroups of the single-launch layer
+constexpr int XL_MAX = 1024;       // experts (HFQ4_MAX_EXPERTS)
+constexpr int XH_MAX = 8 * 512;    // k * F of the tuned shape
+constexpr int XREG_BYTES = 8 * XL_MAX + 8 * XH_MAX + 4 * XG_MAX + 256;
 constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
 constexpr int WS_COUNTERS = 240;
 
@@ -56,12 +71,15 @@ enum TraceKernel { TK_LOGITS = 0, TK_GATEUP = 1, TK_DOWN = 2, TK_TOPK = 3 };
 void set_trace(uint64_t* p);
 uint64_t* get_trace();
 void set_timing_events(void* start, void* stop);
+// Diagnostics: whether one-token layers of the tuned shape run as one
+// launch (the default) or as the three-launch chain.
+void set_single_launch(bool on);
 
 // Byte layout of a workspace for (E, B, k, d, F, layer flags) (k = 0:
 // routing only).
 constexpr uint32_t LAYER_HOST_MAPPED = 1u;
 struct WsLayout {
-  size_t logits, idx, wts, h, gtab, dstage, dslot, total;
+  size_t logits, idx, wts, h, gtab, dstage, dslot, xlog, xh, xflag, gen, total;
 };
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
 Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
@@ -79,6 +97,15 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// TurboQuant: encode (f32 [count][ld] -> records) or decode (records -> f32).
+int launch_turbo(bool encode, const void* src, int64_t count, int n, int64_t ld, void* dst,
+                 int bits, const TurboTable& tab, hipStream_t s);
+// One token of the tuned shape with expert weights through a pointer table
+// (ptr [E][3] device addresses of gate, up, down), hit counts into hits[2].
+int launch_layer_table(const LayerDev& L, const uint64_t* ptr, const uint8_t* resident,
+                       unsigned long long* hits, const float* Wr, const float* bias,
+                       const float* x, int k, int32_t* idx, float* wts, const float* residual,
+                       float* y, Ws ws, hipStream_t s);
 // Compute units of the current device (cached per device).
 int num_cus();
 

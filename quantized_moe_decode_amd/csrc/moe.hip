@@ -43,6 +43,39 @@ namespace hq {
 
 // ====================================================================== routing
 
+// Router logit of expert row e for one token, by one wave: each lane keeps
+// up to 8 float4 loads of the row and 8 of x in flight (buffer loads, so
+// lanes past the end read zeros without a branch), the bias word goes out
+// with them, and one wave sum finishes the row.  Every kernel that computes
+// a one-token logit calls this, so they all get the same bits.
+__device__ __forceinline__ float router_row1(const RouteArgs& a, int e, int lane) {
+  const int nq = a.d >> 2;
+  const uint32_t rowb = 4u * (uint32_t)a.d;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr + (int64_t)e * a.d, rowb);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, rowb);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias ? 4u * (uint32_t)a.E : 0u);
+  const float bias = as_f32(bload4(rb, 4u * (uint32_t)e));
+  float acc = 0.f;
+  for (int q0 = 0; q0 < nq; q0 += 64 * 8) {
+    u32x4 w[8], xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u * 64 + lane;
+      w[u] = bload16(rw, q < nq ? 16u * (uint32_t)q : rowb);
+      xv[u] = bload16(rx, q < nq ? 16u * (uint32_t)q : rowb);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc = __builtin_fmaf(as_f32(w[u].x), as_f32(xv[u].x), acc);
+      acc = __builtin_fmaf(as_f32(w[u].y), as_f32(xv[u].y), acc);
+      acc = __builtin_fmaf(as_f32(w[u].z), as_f32(xv[u].z), acc);
+      acc = __builtin_fmaf(as_f32(w[u].w), as_f32(xv[u].w), acc);
+    }
+  }
+  return wave_sum(acc) + bias;
+}
+
 // Router logits of 1..LG_VALU_MAXB tokens, one single-wave workgroup per
 // expert row: each lane keeps up to 8 float4 loads of the row and 8 of each
 // token's x in flight (buffer loads, so lanes past the end and absent tokens
@@ -60,6 +93,15 @@ __global__ void __launch_bounds__(64) logits_kernel(RouteArgs a, float* __restri
   trace_point(trace, TK_LOGITS, 0);
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63;
+  if (NT == 1) {
+    const float l = router_row1(a, e, lane);
+    if (lane == 0) {
+      logits[e] = l;
+      if (a.logits_out) a.logits_out[e] = l;
+    }
+    trace_point(trace, TK_LOGITS, 1);
+    return;
+  }
   const int nq = a.d >> 2;
   const uint32_t rowb = 4u * (uint32_t)a.d;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.Wr + (int64_t)e * a.d, rowb);
@@ -638,6 +680,382 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   trace_point(ws.trace, TK_DOWN, 3);
 }
 
+
+// ====================================================================== single-launch layer, one token
+
+// The one-token layer of the tuned shape in one launch: the workgroups
+// exchange the router logits and h between the layer's phases through
+// tagged words -- the value's bits with the call's generation in the high
+// half, written and read with relaxed atomics at agent scope (coherent
+// across the chip's dies) -- instead of through kernel boundaries.  A word
+// carries its own validity, so no fence orders the exchange: a reader
+// polls until every word it needs holds this call's generation.  Measured
+// on the MI355X, such a word is seen on another die about 0.5 us after it
+// is written, against about 2.3 us for a kernel boundary followed by the
+// first read of data written on other dies.
+//
+// Every workgroup must be resident at once (the grid is one workgroup per
+// compute unit and a workgroup needs a fraction of one), and every wait is
+// bounded: after XWAIT_TICKS a workgroup stops waiting, sets
+// HFQ4_DEV_ERR_TIMEOUT and finishes with what it has.
+//
+// Generations: the workspace counts the single-launch calls run on it; the
+// current call's generation is g = count + 1.  Every workgroup reads the
+// count first and then raises its start flag to g; workgroup 0 advances the
+// count only at its very end and only after it has seen every start flag at
+// g, so every workgroup of a call has read the same count: all agree on g.
+// A zeroed workspace starts at count 0 with every word at generation 0,
+// never a call's.
+//
+// Per workgroup (four waves):
+//  R  the waves that own a router row (rows wg, wg + nwg, ... ; one wave
+//     each, the same arithmetic as the router kernel) compute and publish
+//     its logit; the others stage x in LDS;
+//  T  wave 0 polls the E logits and runs the top-k (as the gate/up kernel
+//     of the three-launch path does);
+//  G  every wave issues the loads of its gate/up item and, at once, of its
+//     two down rows of every selected expert; computes the item and
+//     publishes its four h values;
+//  D  the workgroup polls all k*F h words until every one holds this
+//     call's generation, stages them as fragments, and every wave finishes
+//     its down rows (weights already in registers) with the
+//     routing-weighted slot sum.
+// Every dot product, reduction and fragment is the one the three-launch
+// kernels compute, so idx, wts and y are bit-identical to that path.
+constexpr uint64_t XWAIT_TICKS = 200000;   // 2 ms at 100 MHz
+
+__device__ __forceinline__ void put_word(uint64_t* p, uint32_t bits, uint32_t g) {
+  __hip_atomic_store(p, ((uint64_t)g << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Expert weights through a per-expert pointer table (the HBM expert cache):
+// entry e holds the device-visible addresses of expert e's gate, up and
+// down matrices -- an HBM slot or mapped pinned host memory -- and
+// resident[e] says which (for the hit counts).  Global loads at 8-byte
+// alignment (a block's code bytes start 8 bytes into it).
+struct TableArgs {
+  const uint64_t* ptr;          // [E][3]
+  const uint8_t* resident;      // [E] or null
+  unsigned long long* hits;     // [2]: selections of resident / other experts, or null
+};
+typedef uint32_t u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
+__device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
+  const u32x4a8 v = *reinterpret_cast<const u32x4a8*>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ u32x2 gload8(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+template <int PER, bool TABLE>
+__global__ void __launch_bounds__(256) layer1_kernel(ExpertArgs a, Ws ws, RouteArgs ra,
+                                                     int32_t* idx_out, float* wts_out,
+                                                     TableArgs tb) {
+  __shared__ uint64_t s_ptr[MAXK][3];
+  __shared__ __align__(16) uint8_t xfr[frag_bytes(FAST_SEGS_D)];
+  __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
+  __shared__ __align__(16) float hval[8 * FAST_F];
+  __shared__ int s_exp[MAXK];
+  __shared__ float s_w[MAXK];
+  __shared__ uint32_t s_gen;
+  const int wv = wave_id(), lane = threadIdx.x & 63;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int k = a.k, E = a.L.E, F = a.L.F, d = a.L.d;
+  __shared__ int s_started;
+  trace_point(ws.trace, TK_GATEUP, 0);
+  if (threadIdx.x == 0) {
+    s_gen = ws.gen[0] + 1u;
+    s_started = 0;
+    __hip_atomic_store(ws.xflag + wg, s_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // R: router rows, x staging
+  const int nrows = E > wg ? min(4, (E - wg + nwg - 1) / nwg) : 0;
+  if (wv < nrows) {
+    const int e = wg + nwg * wv;
+    const float l = router_row1(ra, e, lane);
+    const uint32_t g = __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u;
+    if (lane == 0) put_word(ws.xlog + e, __float_as_uint(l), g);
+  }
+  if (nrows < 4) {
+    if (wv >= nrows)
+      stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x - 64 * nrows, 256 - 64 * nrows);
+  } else {
+    stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x, 256);
+  }
+  __syncthreads();
+  const uint32_t g = s_gen;
+  trace_point(ws.trace, TK_GATEUP, 1);
+
+  // T: wave 0 gathers the logits and selects
+  if (wv == 0) {
+    uint32_t key[PER];
+    int nan_seen = 0;
+    bool ok = false;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      bool mine = true;
+      nan_seen = 0;
+      uint64_t wd[PER];
+      // addresses clamped into the array, so the loads need no branch and
+      // all go out before the first is used
+#pragma unroll
+      for (int i = 0; i < PER; ++i) wd[i] = get_word(ws.xlog + min(lane * PER + i, E - 1));
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane * PER + i;
+        const float f = __uint_as_float((uint32_t)wd[i]);
+        mine &= (uint32_t)(wd[i] >> 32) == g || e >= E;
+        key[i] = e < E ? okey(f) : 0u;
+        nan_seen |= (e < E) & __builtin_isnan(f);
+      }
+      ok = __all(mine);
+      if (ok || __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS) break;
+    }
+    if (!ok && lane == 0)
+      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int e;
+    float w;
+    topk_keys<PER>(key, E, k, k, e, w, ws.trace);
+    if (lane < k) {
+      s_exp[lane] = e;
+      s_w[lane] = w;
+    }
+    if (TABLE) {
+      if (lane < k) {
+        s_ptr[lane][0] = tb.ptr[3 * e];
+        s_ptr[lane][1] = tb.ptr[3 * e + 1];
+        s_ptr[lane][2] = tb.ptr[3 * e + 2];
+      }
+      if (wg == 0 && tb.hits) {   // hit accounting, once per call
+        const bool res = lane < k && tb.resident && tb.resident[lane < k ? e : 0];
+        const unsigned long long nres = __popcll(__ballot(res));
+        if (lane == 0) {
+          atomicAdd(tb.hits, nres);
+          atomicAdd(tb.hits + 1, (unsigned long long)k - nres);
+        }
+      }
+    }
+    if (__any(nan_seen) && lane == 0 && wg == 0)
+      __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (wv == 1 && wg == 0) {
+    // every workgroup's start flag at g: all have read the count
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      bool mine = true;
+      uint32_t fw[XG_MAX / 64];
+      const int nfl = (nwg + 63) >> 6;
+#pragma unroll
+      for (int i = 0; i < XG_MAX / 64; ++i)
+        if (i < nfl)
+          fw[i] = __hip_atomic_load(ws.xflag + min(lane + 64 * i, nwg - 1), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int i = 0; i < XG_MAX / 64; ++i)
+        if (i < nfl) mine &= fw[i] == g;
+      if (__all(mine)) {
+        if (lane == 0) s_started = 1;
+        break;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS) break;
+    }
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 2);
+  if (wg == 0 && threadIdx.x < k) {
+    idx_out[threadIdx.x] = s_exp[threadIdx.x];
+    wts_out[threadIdx.x] = s_w[threadIdx.x];
+  }
+
+  // G: gate/up item and down rows, all loads in flight together
+  const int nw = nwg * 4;
+  const int gw = wg * 4 + wv;
+  constexpr int nchunk = FAST_F / FAST_RP;
+  const int items = k * nchunk;
+  constexpr int64_t ROWB = 8 * BLK_BYTES;
+  const uint32_t hoff = (uint32_t)((lane >> 3) * BLK_BYTES);
+  const uint32_t coff = hoff + 8 + 16 * (lane & 7);
+  u32x4 cg[FAST_RP], cu[FAST_RP];
+  u32x2 hg[FAST_RP], hu[FAST_RP];
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate, a.L.gate_bytes);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up, a.L.up_bytes);
+  const uint32_t gmat = (uint32_t)((int64_t)F * ROWB);   // bytes of one gate (or up) matrix
+  auto issue = [&](int item) {
+    const int u = item / nchunk, c = item - u * nchunk;
+    const int e = s_exp[u];
+    uint32_t bg, bu;
+    __amdgpu_buffer_rsrc_t qg = rg, qu = ru;
+    if (TABLE) {   // the item's expert is wave-uniform: one descriptor per matrix
+      qg = make_rsrc(reinterpret_cast<const void*>(s_ptr[u][0]), gmat);
+      qu = make_rsrc(reinterpret_cast<const void*>(s_ptr[u][1]), gmat);
+      bg = bu = (uint32_t)((int64_t)c * FAST_RP * ROWB);
+    } else {
+      bg = (uint32_t)(e * a.L.sg + (int64_t)c * FAST_RP * ROWB);
+      bu = (uint32_t)(e * a.L.su + (int64_t)c * FAST_RP * ROWB);
+    }
+#pragma unroll
+    for (int r = 0; r < FAST_RP; ++r) {
+      hg[r] = bload8(qg, bg + r * ROWB + hoff);
+      cg[r] = bload16(qg, bg + r * ROWB + coff);
+    }
+#pragma unroll
+    for (int r = 0; r < FAST_RP; ++r) {
+      hu[r] = bload8(qu, bu + r * ROWB + hoff);
+      cu[r] = bload16(qu, bu + r * ROWB + coff);
+    }
+  };
+  // down: lane group dg (16 lanes) takes slots dg and dg + 4 of the wave's
+  // row pair, as the down kernel does
+  const int dg = lane >> 4, ds = lane & 15;
+  constexpr int64_t DROWB = 2 * BLK_BYTES;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  const uint32_t dhoff = (uint32_t)((ds >> 3) * BLK_BYTES);
+  const uint32_t dcoff = dhoff + 8 + 16 * (ds & 7);
+  u32x4 dc[2][FAST_ROWS];
+  u32x2 dh[2][FAST_ROWS];
+  bool dlive[2];
+  float dwt[2];
+  auto issue_down = [&](int r0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = dg + 4 * t;
+      const int e = j < k ? s_exp[j] : -1;
+      dlive[t] = e >= 0;
+      dwt[t] = j < k ? s_w[j] : 0.f;
+      if (TABLE) {
+        // the lane groups take different experts: per-lane addresses; a
+        // dead slot reads slot 0's first rows (selected out below)
+        const bool ok = dlive[t] && r0 < d;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(s_ptr[ok ? j : 0][2]) +
+                              (ok ? (int64_t)r0 * DROWB : 0);
+#pragma unroll
+        for (int r = 0; r < FAST_ROWS; ++r) {
+          const int rr = ok && r0 + r < d ? r : 0;
+          dh[t][r] = gload8(base + rr * DROWB + dhoff);
+          dc[t][r] = gload16(base + rr * DROWB + dcoff);
+        }
+      } else {
+        const uint32_t base = (dlive[t] && r0 < d) ? (uint32_t)(e * a.L.sd + (int64_t)r0 * DROWB)
+                                                   : a.L.down_bytes;
+#pragma unroll
+        for (int r = 0; r < FAST_ROWS; ++r) {
+          dh[t][r] = bload8(rd, base + r * DROWB + dhoff);
+          dc[t][r] = bload16(rd, base + r * DROWB + dcoff);
+        }
+      }
+    }
+  };
+  int it = gw;
+  if (it < items) issue(it);
+  issue_down(gw * FAST_ROWS);
+  trace_point(ws.trace, TK_GATEUP, 3);
+  const int row = lane >> 4;
+  {
+    Frag f;
+    frag_load(xfr, FAST_SEGS_D, lane, f);
+    while (it < items) {
+      const int u = it / nchunk, c = it - u * nchunk;
+      float gs[FAST_RP], us[FAST_RP];
+#pragma unroll
+      for (int r = 0; r < FAST_RP; ++r) {
+        gs[r] = dot_seg(cg[r], hg[r], f);
+        us[r] = dot_seg(cu[r], hu[r], f);
+      }
+      const float tg = row_sum16(fold16(fold32(gs[0], gs[2]), fold32(gs[1], gs[3])));
+      const float tu = row_sum16(fold16(fold32(us[0], us[2]), fold32(us[1], us[3])));
+      if ((lane & 15) == 0)
+        put_word(ws.xh + (int64_t)u * F + c * FAST_RP + row, __float_as_uint(silu_mul(tg, tu)), g);
+      it += nw;
+      if (it < items) issue(it);
+    }
+  }
+  trace_point(ws.trace, TK_GATEUP, 4);
+
+  // D: read every workgroup's h words until all hold this call's
+  // generation (all of a thread's loads in flight before the first is
+  // used; each workgroup starts at a different word, so the polls of the
+  // grid do not all hit the same lines at once), stage them
+  const int nh = k * F;
+  {
+    constexpr int HPT = 8 * FAST_F / 256;   // words per thread (k <= 8, F = 512)
+    const int rot = (wg * 64) % nh;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    int expired = 0;
+    while (true) {
+      uint64_t hw[HPT];
+      int at[HPT];
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        int j = (int)threadIdx.x + 256 * i + rot;
+        j = j >= nh ? j - nh : j;
+        at[i] = j;
+        hw[i] = get_word(ws.xh + min(j, nh - 1));
+      }
+      int stale = 0;
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const bool in = (int)threadIdx.x + 256 * i < nh;
+        stale |= in && (uint32_t)(hw[i] >> 32) != g;
+        if (in) hval[at[i]] = __uint_as_float((uint32_t)hw[i]);
+      }
+      const int any_stale = __syncthreads_or(stale);
+      expired = __syncthreads_or(threadIdx.x == 0 &&
+                                 __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS);
+      if (!any_stale || expired) break;
+    }
+    if (expired && threadIdx.x == 0)
+      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  constexpr int fbh = frag_bytes(FAST_SEGS_F);
+  {
+    const int j = threadIdx.x / FAST_SEGS_F, sg = threadIdx.x - j * FAST_SEGS_F;
+    if (j < k) {
+      float buf[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) buf[i] = hval[j * F + sg * SEG + i];
+      Frag fr;
+      make_frag(buf, fr);
+      frag_store(hfr + j * fbh, FAST_SEGS_F, sg, fr);
+    }
+  }
+  __syncthreads();
+  trace_point(ws.trace, TK_GATEUP, 5);
+
+  // the down rows of this wave, then any further row pairs
+  for (int r0 = gw * FAST_ROWS; r0 < d; r0 += nw * FAST_ROWS) {
+    if (r0 != gw * FAST_ROWS) issue_down(r0);
+    float acc[FAST_ROWS];
+#pragma unroll
+    for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = dg + 4 * t;
+      Frag f;
+      frag_load(hfr + (j < k ? j : 0) * fbh, FAST_SEGS_F, ds, f);
+#pragma unroll
+      for (int r = 0; r < FAST_ROWS; ++r) {
+        const float v = __builtin_fmaf(dwt[t], dot_seg(dc[t][r], dh[t][r], f), acc[r]);
+        acc[r] = dlive[t] ? v : acc[r];
+      }
+    }
+    const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
+    if ((lane == 0 || lane == 32)) {
+      const int rr = r0 + (lane >> 5);
+      if (rr < d) a.y[rr] = (a.res ? a.res[rr] : 0.f) + t;
+    }
+  }
+  if (wg == 0 && threadIdx.x == 0) {
+    // a workgroup that had not started by phase T would read the count
+    // after this store: never advance it then (the call reports a time-out)
+    if (s_started)
+      ws.gen[0] = g;
+    else
+      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  trace_point(ws.trace, TK_GATEUP, 6);
+}
+
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -663,6 +1081,12 @@ void set_timing_events(void* start, void* stop) {
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags) {
   WsLayout l{};
   size_t o = WS_HEADER;
+  // the single-launch layer's region, at the same place in every layout
+  l.xlog = o;
+  l.xh = l.xlog + 8 * XL_MAX;
+  l.xflag = l.xh + 8 * XH_MAX;
+  l.gen = l.xflag + 4 * XG_MAX;
+  o = al256(o + XREG_BYTES);
   l.logits = o;   // batched calls keep LG_KS partial logit sets
   o = al256(o + sizeof(float) * (B >= 2 ? (size_t)LG_KS : 1) * B * lg_stride((int)E));
   l.idx = o;
@@ -698,6 +1122,10 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t 
   w.gtab = l.gtab ? reinterpret_cast<GroupTab*>(p + l.gtab) : nullptr;
   w.dslot = (uint32_t)l.dslot;
   w.trace = get_trace();
+  w.xlog = reinterpret_cast<uint64_t*>(p + l.xlog);
+  w.xh = reinterpret_cast<uint64_t*>(p + l.xh);
+  w.xflag = reinterpret_cast<uint32_t*>(p + l.xflag);
+  w.gen = reinterpret_cast<uint32_t*>(p + l.gen);
   return w;
 }
 
@@ -801,11 +1229,45 @@ int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const 
   return launch_generic_experts(a, ws, s);
 }
 
+// One token, tuned shape, weights in device memory: the single-launch layer.
+template <bool TABLE>
+static int launch_layer1(const ExpertArgs& a, const RouteArgs& ra, Ws ws, TableArgs tb,
+                         hipStream_t s) {
+  const int nwg = num_cus();
+  const int E = a.L.E;
+#define HQ_L1(PER)                                                                            \
+  hipExtLaunchKernelGGL((layer1_kernel<PER, TABLE>), dim3(nwg), dim3(256), 0, s, g_ev_start, \
+                        g_ev_stop, 0, a, ws, ra, ra.idx_out, ra.wts_out, tb)
+  if (E <= 256)
+    HQ_L1(4);
+  else if (E <= 512)
+    HQ_L1(8);
+  else
+    HQ_L1(16);
+#undef HQ_L1
+  return (int)hipGetLastError();
+}
+
+// The single-launch layer serves one token of the tuned shape whose
+// weights are in device memory, when the grid (one workgroup per compute
+// unit) fits the workspace's per-workgroup state.
+static bool g_single_launch = false;
+void set_single_launch(bool on) { g_single_launch = on; }
+static bool use_layer1(const LayerDev& L, int B, int k, const Ws& ws) {
+  return g_single_launch && B == 1 && fast_shape(L.d, L.F, k) &&
+         !(L.flags & LAYER_HOST_MAPPED) && L.E <= XL_MAX && k * L.F <= XH_MAX &&
+         num_cus() <= XG_MAX;
+}
+
 int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const float* x,
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s) {
   RouteArgs ra{Wr, bias, L.E, L.d, x, ldx, B, k, idx, wts, nullptr};
   const bool fast = fast_shape(L.d, L.F, k);
+  if (use_layer1(L, B, k, ws)) {
+    ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
+    return launch_layer1<false>(a, ra, ws, TableArgs{nullptr, nullptr, nullptr}, s);
+  }
   if (B >= 2) {
     // the same router and routing functions as moe_route_topk, so the
     // two-call path gives the same bits; on the fast shape the gate/up
@@ -828,6 +1290,16 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
   if (err) return err;
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
   return launch_generic_experts(a, ws, s);
+}
+
+int launch_layer_table(const LayerDev& L, const uint64_t* ptr, const uint8_t* resident,
+                       unsigned long long* hits, const float* Wr, const float* bias,
+                       const float* x, int k, int32_t* idx, float* wts, const float* residual,
+                       float* y, Ws ws, hipStream_t s) {
+  if (!fast_shape(L.d, L.F, k) || L.E > XL_MAX || num_cus() > XG_MAX) return (int)hipErrorInvalidValue;
+  RouteArgs ra{Wr, bias, L.E, L.d, x, L.d, 1, k, idx, wts, nullptr};
+  ExpertArgs a{L, x, L.d, 1, k, idx, wts, residual, y, L.d};
+  return launch_layer1<true>(a, ra, ws, TableArgs{ptr, resident, hits}, s);
 }
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

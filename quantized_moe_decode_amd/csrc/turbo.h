@@ -1,0 +1,20 @@
+// TurboQuant codec: the level table the kernels take (host-side helpers;
+// the launcher is declared in launch.h).
+#pragma once
+#include <stdint.h>
+
+namespace hq {
+
+// Levels of one (n, bits) codec: cent[0 .. 2^bits) ascending (already
+// scaled by 1/sqrt(n)) and thr[m] = the midpoint of cent[m], cent[m+1].
+struct TurboTable {
+  float cent[256];
+  float thr[255];
+};
+
+// Lloyd-Max levels of the standard normal with 2^bits levels (host, f64).
+void lloyd_max_normal(int bits, double* levels);
+// The f32 table of an (n, bits) codec.
+void turbo_table(int n, int bits, TurboTable* t);
+
+}  // namespace hq

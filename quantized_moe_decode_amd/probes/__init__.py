@@ -35,7 +35,9 @@ def _lib():
     for name, args in {"probe_chase": [P, U32, I, P, P], "probe_empty": [I, I, P],
                        "probe_pingpong": [P, P, I, I, I, I, P, P],
                        "probe_produce": [P, I, P, P], "probe_consume": [P, I, P, P, P],
-                       "probe_read": [P, SZ, I, P, P]}.items():
+                       "probe_read": [P, SZ, I, P, P],
+                       "probe_exchange": [P, P, I, I, U32, I, P, I, I, P],
+                       "probe_spin": [ctypes.c_uint64, P]}.items():
         f = getattr(lib, name)
         f.restype = I
         f.argtypes = args
@@ -147,12 +149,43 @@ def pingpong(torch, partner, rounds=2000, release=False, payload_words=0):
     return float(o[0]) * TICK_NS / rounds / 2.0, int(o[2]), int(o[3])
 
 
+def exchange(torch, per_wg, flags=False, nwg=None, reps=20, replicas=1, stagger=False):
+    """All-to-all exchange inside one launch: every workgroup publishes
+    per_wg tagged words and polls all of them.  Returns (median over
+    launches of: last workgroup done - last publish, in ns; median poll
+    rounds; timeouts)."""
+    import numpy as np
+    lib = _lib()
+    nwg = nwg or torch.cuda.get_device_properties(0).multi_processor_count
+    words = torch.zeros(replicas * nwg * per_wg, dtype=torch.int64, device="cuda")
+    flagw = torch.zeros(nwg, dtype=torch.int32, device="cuda")
+    stamps = torch.zeros(4 * nwg, dtype=torch.int64, device="cuda")
+    spans, rounds, tos = [], [], 0
+    for r in range(reps):
+        _ok(lib.probe_exchange(_p(words), _p(flagw), nwg, per_wg, r + 1, 1 if flags else 0,
+                               _p(stamps), replicas, 1 if stagger else 0, _s(torch)),
+            "probe_exchange")
+        torch.cuda.synchronize()
+        st = stamps.cpu().numpy()
+        spans.append((st[nwg:2 * nwg].max() - st[:nwg].max()) * TICK_NS)
+        rounds.append(np.median(st[2 * nwg:3 * nwg]))
+        tos += int(st[3 * nwg:].sum())
+    return float(np.median(spans)), float(np.median(rounds)), tos
+
+
+def spin(torch, us):
+    """Keep the device busy for `us` microseconds (one wave) on the current
+    stream: put in front of a timed region so that the host has enqueued the
+    region's work before the device reaches it."""
+    _ok(_lib().probe_spin(int(us * 100), _s(torch)), "probe_spin")
+
+
 def read(torch, nbytes=1 << 32, reps=5):
     """Best GB/s of a plain streaming read of nbytes in HBM."""
     lib = _lib()
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
-    grid = 4 * torch.cuda.get_device_properties(0).multi_processor_count * 4
+    grid = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     _ok(lib.probe_read(_p(buf), nbytes, grid, _p(sink), _s(torch)), "probe_read")
     best = 0.0
@@ -188,6 +221,16 @@ def run_all(torch, log=print):
     ns, a, b = pingpong(torch, 1, rounds=1000, release=True, payload_words=256)
     res["flag_release_acquire_1KiB_ns"] = None if ns is None else round(ns, 1)
     log("release/acquire message of 1 KiB, one way (dies %d, %d): %s ns" % (a, b, ns))
+    for per_wg, fl, rep, stg in ((1, False, 1, False), (1, False, 8, False), (1, False, 32, False),
+                                 (16, False, 1, False), (16, False, 1, True), (16, False, 8, False),
+                                 (16, False, 8, True), (16, True, 8, True), (2, False, 8, True)):
+        ns, rnd, to = exchange(torch, per_wg, flags=fl, replicas=rep, stagger=stg)
+        key = "exchange_%dw_r%d%s%s" % (per_wg, rep, "_stagger" if stg else "", "_flags" if fl else "")
+        res[key] = {"ns": round(ns, 1), "median_rounds": rnd, "timeouts": to}
+        log("all-to-all exchange, %d tagged words per workgroup, %d copies%s%s: %.0f ns after the "
+            "last publish (median %.0f poll rounds, %d timeouts)"
+            % (per_wg, rep, ", staggered reads" if stg else "",
+               ", behind per-workgroup flags" if fl else "", ns, rnd, to))
     res["read_gbs"] = round(read(torch), 1)
     log("streaming read of 4 GiB: %.1f GB/s" % res["read_gbs"])
     return res

@@ -141,20 +141,101 @@ __global__ void consume_kernel(const float* vals, int n, uint64_t* stamps, float
   if (s == -1.f) sink[0] = s;   // never true for these values; keeps the loads
 }
 
+// ---------------------------------------------------------------- all-to-all exchange
+
+// Every workgroup publishes `per_wg` 64-bit words (value, tag) with relaxed
+// agent-scope atomic stores, then polls all nwg * per_wg words until every
+// tag is this run's, up to a bounded number of rounds -- the data exchange
+// a single-launch layer would need between its phases (router logits: one
+// word per workgroup; h: 16 per workgroup).  With `flags`, a workgroup also
+// raises a tagged per-workgroup flag after its words and the pollers first
+// wait for all flags, then read the words once (re-reading any stale one).
+// stamps[wg] = publish time, stamps[nwg + wg] = all data seen, stamps[2 nwg
+// + wg] = poll rounds, stamps[3 nwg + wg] = 1 on timeout.
+__global__ void __launch_bounds__(256) exchange_kernel(uint64_t* words, uint32_t* flagw, int per_wg,
+                                                       uint32_t tag, int flags, uint64_t* stamps,
+                                                       int replicas, int stagger) {
+  const int nwg = gridDim.x, wg = blockIdx.x, t = threadIdx.x;
+  const int total = nwg * per_wg;
+  // each word goes to `replicas` copies; a reader polls copy wg % replicas
+  // (with round-robin placement of workgroups on dies, copy = die for 8)
+  for (int i = t; i < per_wg * replicas; i += blockDim.x) {
+    const int r = i / per_wg, j = i - r * per_wg;
+    const uint64_t w = ((uint64_t)tag << 32) | (uint32_t)(wg * per_wg + j);
+    __hip_atomic_store(words + (size_t)r * total + wg * per_wg + j, w, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const uint64_t* mine = words + (size_t)(wg % replicas) * total;
+  const int rot = stagger ? (wg * 64) % total : 0;   // readers start at different words
+  __syncthreads();
+  if (flags && t == 0) __hip_atomic_store(flagw + wg, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t t0 = now();
+  int rounds = 0, missing = 0;
+  const int kMaxRounds = 100000;
+  if (flags) {
+    do {
+      int miss = 0;
+      for (int i = t; i < nwg; i += blockDim.x)
+        miss |= __hip_atomic_load(flagw + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
+      missing = __syncthreads_or(miss);
+      ++rounds;
+    } while (missing && rounds < kMaxRounds);
+  }
+  do {
+    int miss = 0;
+    uint64_t w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = t + u * 256;
+      int j = i + rot;
+      j = j >= total ? j - total : j;
+      w[u] = __hip_atomic_load(const_cast<uint64_t*>(mine) + (i < total ? j : 0), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) miss |= (t + u * 256 < total) && (uint32_t)(w[u] >> 32) != tag;
+    missing = __syncthreads_or(miss);
+    ++rounds;
+  } while (missing && rounds < kMaxRounds);
+  const uint64_t t1 = now();
+  if (t == 0) {
+    stamps[wg] = t0;
+    stamps[nwg + wg] = t1;
+    stamps[2 * nwg + wg] = rounds;
+    stamps[3 * nwg + wg] = missing ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- spin
+
+// One wave that keeps the device busy for `ticks` (100 MHz) and exits: put
+// in front of a timed region, it lets the host enqueue the region's work
+// before the device reaches it.
+__global__ void spin_kernel(uint64_t ticks) {
+  const uint64_t t0 = now();
+  while (now() - t0 < ticks) __builtin_amdgcn_s_sleep(2);
+}
+
 // ---------------------------------------------------------------- streaming read
 
-// Every lane reads 16-byte chunks, grid-strided, four in flight; one sum per
-// workgroup is written so the loads stay live.
+// Every lane reads 16-byte chunks, eight in flight; each workgroup walks a
+// contiguous slice of the buffer (chunks of 8 x 4 KiB per step), and one
+// value per workgroup is written so the loads stay live.
 __global__ void __launch_bounds__(256) read_kernel(const uint4* __restrict__ p, size_t n16,
                                                    uint32_t* sink) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
   }
-  for (; i < n16; i += stride) acc ^= p[i].x;
+  for (; i < hi; i += 256) acc ^= p[i].x;
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
@@ -188,6 +269,21 @@ int probe_produce(float* vals, int n, uint64_t* stamps, hipStream_t s) {
 
 int probe_consume(const float* vals, int n, uint64_t* stamps, float* sink, hipStream_t s) {
   hipLaunchKernelGGL(consume_kernel, dim3(n), dim3(64), 0, s, vals, n, stamps, sink);
+  return (int)hipGetLastError();
+}
+
+int probe_exchange(uint64_t* words, uint32_t* flagw, int nwg, int per_wg, uint32_t tag, int flags,
+                   uint64_t* stamps, int replicas, int stagger, hipStream_t s) {
+  if (nwg < 1 || nwg > 1024 || per_wg < 1 || nwg * per_wg > 4096 || replicas < 1 || replicas > 64)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(exchange_kernel, dim3(nwg), dim3(256), 0, s, words, flagw, per_wg, tag, flags,
+                     stamps, replicas, stagger);
+  return (int)hipGetLastError();
+}
+
+int probe_spin(uint64_t ticks, hipStream_t s) {
+  if (ticks > 10000000ull) return (int)hipErrorInvalidValue;   // at most 0.1 s
+  hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, s, ticks);
   return (int)hipGetLastError();
 }
 

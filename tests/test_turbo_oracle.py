@@ -123,3 +123,14 @@ def test_codes_minimise_distance_brute_force():
                    key=lambda c: float(np.sum((r - cents[list(c)]) ** 2)))
         assert list(best) == codes.tolist()
 
+
+@pytest.mark.parametrize("n", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_library_levels_match_oracle(n, bits):
+    # the library computes its level table on the host with its own
+    # Lloyd-Max iteration; it must agree with the oracle's to f32 rounding
+    import quantized_moe_decode_amd as q
+    got = q.turbo_levels(n, bits).astype(np.float64)
+    ref = turbo.centroids(n, bits)
+    assert np.max(np.abs(got - ref) / np.abs(ref)) < 1e-7
+    assert q.turbo_record_bytes(n, bits) == turbo.record_bytes(n, bits)
