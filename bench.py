@@ -605,10 +605,11 @@ def main():
                     help="steps as HIP-graph replays or as eager launches")
     ap.add_argument("--path", choices=["fused", "split"], default="fused",
                     help="moe_layer_decode, or moe_route_topk + moe_expert_decode")
-    ap.add_argument("--single-launch", action="store_true",
-                    help="run one-token layers as one launch whose workgroups exchange logits "
-                         "and h through tagged words, instead of the router -> gate/up -> down "
-                         "launch chain (same results)")
+    ap.add_argument("--launches", type=int, choices=[1, 2, 3], default=3,
+                    help="one-token layers as the router -> gate/up -> down launch chain (3), "
+                         "as one launch whose workgroups exchange the logits, h and the per-slot "
+                         "down sums through tagged words (1), or as that launch's routing and "
+                         "gate/up phases followed by the down kernel (2); same results")
     ap.add_argument("--replicas", type=int, default=32,
                     help="distinct layer copies cycled through (so caches cannot serve repeats)")
     ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
@@ -649,7 +650,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     torch.cuda.set_device(0)
-    q.lib.hfq4_debug_set_single_launch(1 if args.single_launch else 0)
+    q.lib.hfq4_debug_set_single_launch({3: 0, 1: 1, 2: 2}[args.launches])
     if args.workload == "floor":
         from quantized_moe_decode_amd import probes
         out = {"workload": "latency and bandwidth probes (floor model of the one-token layer)",
@@ -764,11 +765,19 @@ def main():
             torch.cuda.synchronize()
             t = tr.view(4, 1024, 8).cpu().numpy()
             if int(t[0, :E, 0].max()) == 0:
-                # one launch per step (the single-launch layer): stamps 0..6
                 n = min(ncu, 1024)
-                span = (int(t[1, :n, 6].max()) - int(t[1, :n, 0].min())) / 100.0
-                samples["gateup"].append(span)
-                samples["step"].append(span)
+                if int(t[2, :nwg[2], 0].max()) == 0:
+                    # one launch per step (the single-launch layer): stamps 0..6
+                    span = (int(t[1, :n, 6].max()) - int(t[1, :n, 0].min())) / 100.0
+                    samples["gateup"].append(span)
+                    samples["step"].append(span)
+                    continue
+                # two launches: routing + gate/up (stamps 0..4), then down
+                st1, en1 = int(t[1, :n, 0].min()), int(t[1, :n, 4].max())
+                st2, en2 = int(t[2, :nwg[2], 0].min()), int(t[2, :nwg[2], 3].max())
+                samples["gateup"].append((en1 - st1) / 100.0)
+                samples["down"].append((en2 - st2) / 100.0)
+                samples["step"].append((en2 - st1) / 100.0)
                 continue
             st, en = {}, {}
             for kk, last in ((0, 1), (1, 5), (2, 3)):
@@ -850,7 +859,7 @@ def main():
         "config": {"workload": "single MoE layer decode, d=2048, expert FFN 512, 256 experts, "
                                "top-8, 1 token, HFQ4 experts; %d replicas, %d-token x pool" %
                                (args.replicas, args.pool),
-                   "global_batch": 1, "mode": args.mode, "path": args.path},
+                   "global_batch": 1, "mode": args.mode, "path": args.path, "launches": args.launches},
         "tokens_per_s": round(1.0 / per_step_s, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed": round(wall, 4),

@@ -290,9 +290,11 @@ typedef struct moe_layer_table {
  * for bit, as a layer holding the same bytes in one tensor each.  hits
  * (device uint64 [2], or NULL) accumulates the selections of experts
  * marked resident ([0]) and of the others ([1]) -- the cache's hit count.
- * Supported: batch 1 and the tuned shape (1792 < d <= 2048, F = 512,
- * k <= 8, E <= 1024); other requests fail with HFQ4_E_UNSUPPORTED.  ws as
- * for moe_layer_decode with an HBM layer of the same E, d, F, batch 1. */
+ * It runs as the single-launch layer (one workgroup per compute unit).
+ * Supported: batch 1, the tuned shape (1792 < d <= 2048, F = 512,
+ * k in {2, 4, 8}, E <= 1024) and a device of 256 compute units; other
+ * requests fail with HFQ4_E_UNSUPPORTED.  ws as for moe_layer_decode with
+ * an HBM layer of the same E, d, F, batch 1. */
 int moe_layer_decode_table(const moe_layer_table* L, const float* Wr, const float* bias,
                            const float* x, int batch, int k, int32_t* idx, float* wts,
                            const float* residual, float* y, uint64_t* hits,
@@ -371,12 +373,13 @@ int hfq4_debug_set_arch(const char* arch);
  * MHz), slot [(kernel*1024 + workgroup)*8 + point]; NULL turns it off. */
 int hfq4_debug_set_trace(void* dev, size_t bytes);
 
-/* Diagnostics: one-token layers of the tuned shape (moe_layer_decode)
- * run as the three-launch chain router -> gate/up -> down (on = 0, the
- * default) or as one launch whose workgroups exchange the logits and h
- * through tagged words (on != 0; measured slower on the MI355X, see the
- * design notes).  Both give the same bits; the switch exists to compare
- * them and is process-wide. */
+/* Diagnostics: one-token layers of the tuned shape with k in {2, 4, 8}
+ * (moe_layer_decode, moe_expert_decode) run as the three-launch chain
+ * router -> gate/up -> down (on = 0, the default) or as one launch of one
+ * workgroup per compute unit whose workgroups exchange the logits, each
+ * slot's h and the per-slot down sums through tagged words (on != 0;
+ * 256-compute-unit devices only).  Both give the same bits; the switch
+ * exists to compare them and is process-wide. */
 int hfq4_debug_set_single_launch(int on);
 
 /* Diagnostics: hipEvent_t handles (cast to void*) recorded when each

@@ -173,7 +173,7 @@ int hfq4_debug_set_events(void* start, void* stop) {
 // Diagnostics: one-token layers of the tuned shape as the three-launch
 // chain (0, the default) or as one launch (1); results are the same bits.
 int hfq4_debug_set_single_launch(int on) {
-  hq::set_single_launch(on != 0);
+  hq::set_single_launch(on == 2 ? 2 : on != 0 ? 1 : 0);
   return ok();
 }
 
@@ -480,9 +480,11 @@ int moe_layer_decode_table(const moe_layer_table* T, const float* Wr, const floa
   if (batch != 1) return fail(HFQ4_E_UNSUPPORTED, "table layers take one token per call, got batch = %d", batch);
   if (k < 1 || k > HFQ4_MAX_TOPK || k > T->E)
     return fail(HFQ4_E_INVALID, "k = %d: need 1 <= k <= min(E = %lld, %d)", k, (long long)T->E, HFQ4_MAX_TOPK);
-  if (!(T->d > 1792 && T->d <= 2048 && (T->d & 3) == 0 && T->F == 512 && k <= 8))
-    return fail(HFQ4_E_UNSUPPORTED, "table layers need 1792 < d <= 2048 (d %% 4 == 0), F = 512, k <= 8; "
-                "got d = %lld, F = %lld, k = %d", (long long)T->d, (long long)T->F, k);
+  if (!(T->d > 1792 && T->d <= 2048 && (T->d & 3) == 0 && T->F == 512 && (k == 2 || k == 4 || k == 8) &&
+        T->E <= hq::XL_MAX))
+    return fail(HFQ4_E_UNSUPPORTED, "table layers need 1792 < d <= 2048 (d %% 4 == 0), F = 512, "
+                "k in {2, 4, 8}, E <= %d; got E = %lld, d = %lld, F = %lld, k = %d", hq::XL_MAX,
+                (long long)T->E, (long long)T->d, (long long)T->F, k);
   if (!Wr || !aligned16(Wr)) return fail(HFQ4_E_ALIGN, "Wr must be non-NULL and 16-byte aligned");
   // reuse the HBM-layer checks for the activations and workspace
   moe_layer L{reinterpret_cast<const void*>(16), reinterpret_cast<const void*>(16),
@@ -496,8 +498,9 @@ int moe_layer_decode_table(const moe_layer_table* T, const float* Wr, const floa
   if (ws_bytes < need) return fail(HFQ4_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   r = check_device();
   if (r) return r;
-  if (hq::num_cus() > hq::XG_MAX)
-    return fail(HFQ4_E_UNSUPPORTED, "%d compute units: table layers support at most %d", hq::num_cus(), hq::XG_MAX);
+  if (!hq::single_launch_shape((int)T->E, (int)T->d, (int)T->F, k))
+    return fail(HFQ4_E_UNSUPPORTED, "table layers run one workgroup per compute unit on a "
+                "256-compute-unit device; this one has %d", hq::num_cus());
   hq::LayerDev D{};
   D.E = (int)T->E;
   D.d = (int)T->d;

@@ -56,11 +56,13 @@ struct Ws {
   uint64_t* xh;       // [XH_MAX] SiLU(gate) * up, [k][F]
   uint32_t* xflag;    // [XG_MAX] generation of the last h a workgroup published
   uint32_t* gen;      // [1] single-launch calls run on this workspace
+  uint64_t* xs;       // [XS_MAX] slot sums of the down rows, [slot][2048]
 };
 constexpr int XG_MAX = 1024;       // workgroups of the single-launch layer
 constexpr int XL_MAX = 1024;       // experts (HFQ4_MAX_EXPERTS)
 constexpr int XH_MAX = 8 * 512;    // k * F of the tuned shape
-constexpr int XREG_BYTES = 8 * XL_MAX + 8 * XH_MAX + 4 * XG_MAX + 256;
+constexpr int XS_MAX = 8 * 2048;   // k * d of the tuned shape
+constexpr int XREG_BYTES = 8 * XL_MAX + 8 * XH_MAX + 4 * XG_MAX + 256 + 8 * XS_MAX;
 constexpr int WS_HEADER = 1024;    // err word at 0, counters from byte 64
 constexpr int WS_COUNTERS = 240;
 
@@ -73,13 +75,15 @@ uint64_t* get_trace();
 void set_timing_events(void* start, void* stop);
 // Diagnostics: whether one-token layers of the tuned shape run as one
 // launch (the default) or as the three-launch chain.
-void set_single_launch(bool on);
+void set_single_launch(int mode);   // 0: three launches, 1: one, 2: two
+// Shapes the single-launch layer (and so the pointer-table layers) serve.
+bool single_launch_shape(int E, int d, int F, int k);
 
 // Byte layout of a workspace for (E, B, k, d, F, layer flags) (k = 0:
 // routing only).
 constexpr uint32_t LAYER_HOST_MAPPED = 1u;
 struct WsLayout {
-  size_t logits, idx, wts, h, gtab, dstage, dslot, xlog, xh, xflag, gen, total;
+  size_t logits, idx, wts, h, gtab, dstage, dslot, xlog, xh, xflag, gen, xs, total;
 };
 WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);
 Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags);

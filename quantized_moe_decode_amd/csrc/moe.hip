@@ -581,11 +581,25 @@ __global__ void __launch_bounds__(256) gateup_fast_kernel(ExpertArgs a, Ws ws,
   trace_point(ws.trace, TK_GATEUP, 5);
 }
 
+// The slot combine of one output row, shared by every one-token down path so
+// that they give the same bits: s_j = the sum of slot j's 16 segment
+// partials by row_sum16, taken from the first lane of the 16-lane group that
+// holds them; y = res + (... (0 + w_0 s_0) + w_1 s_1 ...) as fmas in slot
+// order, dead slots (past k, or an index out of range) skipped.
+__device__ __forceinline__ float combine_slots(const float* sj, const float* wj, const bool* live,
+                                               int k, float res) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXK / 2; ++j)
+    if (j < k) acc = live[j] ? __builtin_fmaf(wj[j], sj[j], acc) : acc;
+  return res + acc;
+}
+
 // K3, one token: down dequant-GEMV + routing-weighted combine.  A wave owns
 // FAST_ROWS output rows; lane group g (16 lanes) takes slots g and g + 4
-// (k <= 8), so every lane sums w_j * partial over its two slots first and
-// one 64-lane reduction per row finishes the sum over segments and slots.
-// Slots past k or out of range add nothing (selected out, whatever h holds).
+// (k <= 8); each slot's 16 segment partials are summed within the group,
+// and the slot sums are combined in slot order (combine_slots).  Slots past
+// k or out of range add nothing (selected out, whatever h holds).
 __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
   const int wv = wave_id(), lane = threadIdx.x & 63;   // the row part of the offsets: scalar
@@ -657,25 +671,31 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
   }
   __syncthreads();
   trace_point(ws.trace, TK_DOWN, 2);
-  float acc[FAST_ROWS];
-#pragma unroll
-  for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
+  float ps[2][FAST_ROWS];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int j = g + 4 * t;
     Frag f;
     frag_load(hfr + (j < k ? j : 0) * fb, FAST_SEGS_F, s, f);
 #pragma unroll
-    for (int r = 0; r < FAST_ROWS; ++r) {
-      const float v = __builtin_fmaf(w[t], dot_seg(c[t][r], hd[t][r], f), acc[r]);
-      acc[r] = live[t] ? v : acc[r];
-    }
+    for (int r = 0; r < FAST_ROWS; ++r) ps[t][r] = row_sum16(dot_seg(c[t][r], hd[t][r], f));
   }
-  // rows 0 and 2 of t hold output rows r0 and r0+1
-  const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
-  if ((lane == 0 || lane == 32)) {
-    const int rr = r0 + (lane >> 5);
-    if (rr < d) a.y[rr] = (a.res ? a.res[rr] : 0.f) + t;
+  // slot j's sums sit in lane 16 (j % 4) of ps[j / 4]
+  float wj[MAXK / 2];
+  bool lj[MAXK / 2];
+#pragma unroll
+  for (int j = 0; j < MAXK / 2; ++j) {
+    wj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w[j >> 2]), 16 * (j & 3)));
+    lj[j] = __builtin_amdgcn_readlane((int)live[j >> 2], 16 * (j & 3)) != 0;
+  }
+#pragma unroll
+  for (int r = 0; r < FAST_ROWS; ++r) {
+    float sj[MAXK / 2];
+#pragma unroll
+    for (int j = 0; j < MAXK / 2; ++j)
+      sj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps[j >> 2][r]), 16 * (j & 3)));
+    const int rr = r0 + r;
+    if (lane == 0 && rr < d) a.y[rr] = combine_slots(sj, wj, lj, k, a.res ? a.res[rr] : 0.f);
   }
   trace_point(ws.trace, TK_DOWN, 3);
 }
@@ -683,46 +703,59 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
 
 // ====================================================================== single-launch layer, one token
 
-// The one-token layer of the tuned shape in one launch: the workgroups
-// exchange the router logits and h between the layer's phases through
-// tagged words -- the value's bits with the call's generation in the high
-// half, written and read with relaxed atomics at agent scope (coherent
-// across the chip's dies) -- instead of through kernel boundaries.  A word
-// carries its own validity, so no fence orders the exchange: a reader
-// polls until every word it needs holds this call's generation.  Measured
-// on the MI355X, such a word is seen on another die about 0.5 us after it
-// is written, against about 2.3 us for a kernel boundary followed by the
+// The one-token layer of the tuned shape in one launch.  Its workgroups
+// exchange data between the layer's phases through tagged words -- the
+// value's bits with the call's generation in the high half, written and
+// read with relaxed atomics at agent scope (coherent across the chip's
+// dies) -- instead of through kernel boundaries.  A word carries its own
+// validity, so no fence orders an exchange: a reader polls until every word
+// it needs holds this call's generation, with all of its loads in flight
+// before the first is used.
+//
+// Work split (256 workgroups, k in {2, 4, 8}; G = 256 / k workgroups per
+// slot): workgroup w serves slot j = w % k and block b = w / k.  Its first
+// k/2 waves compute k/2 chunks of 4 gate/up row pairs of slot j (rows 4c ..
+// 4c+3, c = b*k/2 + wave), and all four waves compute the down rows
+// [R b, R b + R) of slot j, R = 2048 / G, whose weights they request
+// together with the gate/up weights.  So a workgroup needs only its own
+// slot's h (F words, from the G workgroups of the slot), and each output
+// row is finished by one owner workgroup (slot 0 of the block) from the k
+// slot sums of the row (k - 1 words from other workgroups).  Measured on the
+// MI355X, such an exchange completes about 0.5 - 1.9 us after its last word
+// is written, against about 2.2 us for a kernel boundary followed by the
 // first read of data written on other dies.
 //
-// Every workgroup must be resident at once (the grid is one workgroup per
-// compute unit and a workgroup needs a fraction of one), and every wait is
-// bounded: after XWAIT_TICKS a workgroup stops waiting, sets
-// HFQ4_DEV_ERR_TIMEOUT and finishes with what it has.
+// Phases per workgroup:
+//  R  the waves that own a router row (rows wg, wg + nwg, ... ; one wave
+//     each, the router kernel's arithmetic) compute and publish its logit;
+//     the others stage x in LDS.  (Routing given: every wave stages x.)
+//  T  wave 0 polls the E logits and runs the top-k, as the gate/up kernel
+//     of the three-launch path does.
+//  G  gate/up loads of the workgroup's chunks and down loads of its rows go
+//     out together; the chunks' h values are published.
+//  D1 the workgroup polls slot j's F h words, stages them as fragments and
+//     computes its rows' slot sums (down_fast's arithmetic); non-owners
+//     publish them.
+//  D2 the owner polls the other slots' sums of its rows and writes
+//     y = res + the slot combine (combine_slots).
+// Every dot product, reduction, fragment and combine is the one the
+// three-launch kernels compute, so idx, wts and y are bit-identical to that
+// path.
+//
+// Every workgroup must be resident at once (one per compute unit, a
+// fraction of one each); every wait is bounded: after XWAIT_TICKS a
+// workgroup stops waiting, sets HFQ4_DEV_ERR_TIMEOUT and finishes with what
+// it has.
 //
 // Generations: the workspace counts the single-launch calls run on it; the
 // current call's generation is g = count + 1.  Every workgroup reads the
 // count first and then raises its start flag to g; workgroup 0 advances the
 // count only at its very end and only after it has seen every start flag at
-// g, so every workgroup of a call has read the same count: all agree on g.
-// A zeroed workspace starts at count 0 with every word at generation 0,
-// never a call's.
-//
-// Per workgroup (four waves):
-//  R  the waves that own a router row (rows wg, wg + nwg, ... ; one wave
-//     each, the same arithmetic as the router kernel) compute and publish
-//     its logit; the others stage x in LDS;
-//  T  wave 0 polls the E logits and runs the top-k (as the gate/up kernel
-//     of the three-launch path does);
-//  G  every wave issues the loads of its gate/up item and, at once, of its
-//     two down rows of every selected expert; computes the item and
-//     publishes its four h values;
-//  D  the workgroup polls all k*F h words until every one holds this
-//     call's generation, stages them as fragments, and every wave finishes
-//     its down rows (weights already in registers) with the
-//     routing-weighted slot sum.
-// Every dot product, reduction and fragment is the one the three-launch
-// kernels compute, so idx, wts and y are bit-identical to that path.
+// g, so every workgroup of a call has read the same count.  A zeroed
+// workspace starts at count 0 with every word at generation 0, never a
+// call's.
 constexpr uint64_t XWAIT_TICKS = 200000;   // 2 ms at 100 MHz
+constexpr int L1_NWG = 256;                // grid of the single-launch layer
 
 __device__ __forceinline__ void put_word(uint64_t* p, uint32_t bits, uint32_t g) {
   __hip_atomic_store(p, ((uint64_t)g << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -734,126 +767,143 @@ __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
 // Expert weights through a per-expert pointer table (the HBM expert cache):
 // entry e holds the device-visible addresses of expert e's gate, up and
 // down matrices -- an HBM slot or mapped pinned host memory -- and
-// resident[e] says which (for the hit counts).  Global loads at 8-byte
-// alignment (a block's code bytes start 8 bytes into it).
+// resident[e] says which (for the hit counts).
 struct TableArgs {
   const uint64_t* ptr;          // [E][3]
   const uint8_t* resident;      // [E] or null
   unsigned long long* hits;     // [2]: selections of resident / other experts, or null
 };
-typedef uint32_t u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
-__device__ __forceinline__ u32x4 gload16(const uint8_t* p) {
-  const u32x4a8 v = *reinterpret_cast<const u32x4a8*>(p);
-  return u32x4{v.x, v.y, v.z, v.w};
-}
-__device__ __forceinline__ u32x2 gload8(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 
-template <int PER, bool TABLE>
+// Poll n tagged words at src[0..n) into dst (LDS) until all hold generation
+// g, by the whole workgroup (at most PER_T words per thread, every load out
+// before any is used).  Returns whether the wait expired.
+template <int PER_T>
+__device__ __forceinline__ bool gather_words(const uint64_t* src, int n, uint32_t g, float* dst) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    uint64_t w[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) w[i] = get_word(src + min((int)threadIdx.x + 256 * i, n - 1));
+    int stale = 0;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int idx = (int)threadIdx.x + 256 * i;
+      if (idx < n) {
+        stale |= (uint32_t)(w[i] >> 32) != g;
+        dst[idx] = __uint_as_float((uint32_t)w[i]);
+      }
+    }
+    const int any_stale = __syncthreads_or(stale);
+    const int expired = __syncthreads_or(threadIdx.x == 0 &&
+                                         __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS);
+    if (!any_stale) return false;
+    if (expired) return true;
+  }
+}
+
+// NRL = k / 2: gate/up chunks per workgroup and row loads (of 4 rows) per wave.
+// SPLIT: the kernel stops after the gate/up phase -- h goes to ws.h and the
+// routing to ws.idx / ws.wts with plain stores, and the down kernel of the
+// three-launch chain (down_fast_kernel) follows as a second launch.
+template <int PER, int NRL, bool FROM_LOGITS, bool TABLE, bool SPLIT>
 __global__ void __launch_bounds__(256) layer1_kernel(ExpertArgs a, Ws ws, RouteArgs ra,
                                                      int32_t* idx_out, float* wts_out,
                                                      TableArgs tb) {
-  __shared__ uint64_t s_ptr[MAXK][3];
+  constexpr int K = 2 * NRL;                     // slots
+  constexpr int G = L1_NWG / K;                  // workgroups per slot
+  constexpr int R = 16 * NRL;                    // down rows per workgroup (R * G = 2048)
   __shared__ __align__(16) uint8_t xfr[frag_bytes(FAST_SEGS_D)];
-  __shared__ __align__(16) uint8_t hfr[8 * frag_bytes(FAST_SEGS_F)];
-  __shared__ __align__(16) float hval[8 * FAST_F];
+  __shared__ __align__(16) uint8_t hfr[frag_bytes(FAST_SEGS_F)];
+  __shared__ __align__(16) float hval[FAST_F];
+  __shared__ float s0v[R];                       // slot 0's sums of this block's rows (owner)
+  __shared__ float other[(K - 1) * R];           // the other slots' sums (owner)
   __shared__ int s_exp[MAXK];
   __shared__ float s_w[MAXK];
   __shared__ uint32_t s_gen;
+  __shared__ int s_started;
   const int wv = wave_id(), lane = threadIdx.x & 63;
   const int wg = blockIdx.x, nwg = gridDim.x;
-  const int k = a.k, E = a.L.E, F = a.L.F, d = a.L.d;
-  __shared__ int s_started;
+  const int E = a.L.E, F = a.L.F, d = a.L.d;
+  const int j = wg % K, b = wg / K;              // this workgroup's slot and block
   trace_point(ws.trace, TK_GATEUP, 0);
   if (threadIdx.x == 0) {
     s_gen = ws.gen[0] + 1u;
     s_started = 0;
     __hip_atomic_store(ws.xflag + wg, s_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  const uint32_t g0 = __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u;
 
-  // R: router rows, x staging
-  const int nrows = E > wg ? min(4, (E - wg + nwg - 1) / nwg) : 0;
-  if (wv < nrows) {
-    const int e = wg + nwg * wv;
-    const float l = router_row1(ra, e, lane);
-    const uint32_t g = __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u;
-    if (lane == 0) put_word(ws.xlog + e, __float_as_uint(l), g);
-  }
-  if (nrows < 4) {
-    if (wv >= nrows)
-      stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x - 64 * nrows, 256 - 64 * nrows);
+  // R + T: routing (wave 0), x staging (the other waves)
+  if (FROM_LOGITS) {
+    const int nrows = E > wg ? min(4, (E - wg + nwg - 1) / nwg) : 0;
+    if (wv < nrows) {
+      const int e = wg + nwg * wv;
+      const float l = router_row1(ra, e, lane);
+      if (lane == 0) put_word(ws.xlog + e, __float_as_uint(l), g0);
+    }
+    if (wv == 0) {
+      uint32_t key[PER];
+      int nan_seen = 0;
+      bool ok = false;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        uint64_t wd[PER];
+        // addresses clamped into the array: no branch, all loads out first
+#pragma unroll
+        for (int i = 0; i < PER; ++i) wd[i] = get_word(ws.xlog + min(lane * PER + i, E - 1));
+        bool mine = true;
+        nan_seen = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int e = lane * PER + i;
+          const float f = __uint_as_float((uint32_t)wd[i]);
+          mine &= (uint32_t)(wd[i] >> 32) == g0 || e >= E;
+          key[i] = e < E ? okey(f) : 0u;
+          nan_seen |= (e < E) & __builtin_isnan(f);
+        }
+        ok = __all(mine);
+        if (ok || __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS) break;
+      }
+      if (!ok && lane == 0)
+        __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int e;
+      float w;
+      topk_keys<PER>(key, E, K, K, e, w, ws.trace);
+      if (lane < K) {
+        s_exp[lane] = e;
+        s_w[lane] = w;
+      }
+      if (__any(nan_seen) && lane == 0 && wg == 0)
+        __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int first = max(1, nrows);   // waves without a router row stage x
+      if (wv >= first) stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x - 64 * first, 256 - 64 * first);
+    }
+    if (nrows >= 4) {   // every wave owned a router row: all stage x now
+      __syncthreads();
+      stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x, 256);
+    }
   } else {
+    if (threadIdx.x < K) {
+      const int e = a.idx[threadIdx.x];
+      s_exp[threadIdx.x] = e >= 0 && e < E ? e : -1;
+      s_w[threadIdx.x] = a.wts[threadIdx.x];
+      if ((e < 0 || e >= E) && wg == 0)
+        __hip_atomic_fetch_or(ws.err, 1u /*HFQ4_DEV_ERR_INDEX*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     stage_vector(a.x, d, FAST_SEGS_D, xfr, threadIdx.x, 256);
   }
-  __syncthreads();
-  const uint32_t g = s_gen;
-  trace_point(ws.trace, TK_GATEUP, 1);
-
-  // T: wave 0 gathers the logits and selects
-  if (wv == 0) {
-    uint32_t key[PER];
-    int nan_seen = 0;
-    bool ok = false;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (true) {
-      bool mine = true;
-      nan_seen = 0;
-      uint64_t wd[PER];
-      // addresses clamped into the array, so the loads need no branch and
-      // all go out before the first is used
-#pragma unroll
-      for (int i = 0; i < PER; ++i) wd[i] = get_word(ws.xlog + min(lane * PER + i, E - 1));
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = lane * PER + i;
-        const float f = __uint_as_float((uint32_t)wd[i]);
-        mine &= (uint32_t)(wd[i] >> 32) == g || e >= E;
-        key[i] = e < E ? okey(f) : 0u;
-        nan_seen |= (e < E) & __builtin_isnan(f);
-      }
-      ok = __all(mine);
-      if (ok || __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS) break;
-    }
-    if (!ok && lane == 0)
-      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int e;
-    float w;
-    topk_keys<PER>(key, E, k, k, e, w, ws.trace);
-    if (lane < k) {
-      s_exp[lane] = e;
-      s_w[lane] = w;
-    }
-    if (TABLE) {
-      if (lane < k) {
-        s_ptr[lane][0] = tb.ptr[3 * e];
-        s_ptr[lane][1] = tb.ptr[3 * e + 1];
-        s_ptr[lane][2] = tb.ptr[3 * e + 2];
-      }
-      if (wg == 0 && tb.hits) {   // hit accounting, once per call
-        const bool res = lane < k && tb.resident && tb.resident[lane < k ? e : 0];
-        const unsigned long long nres = __popcll(__ballot(res));
-        if (lane == 0) {
-          atomicAdd(tb.hits, nres);
-          atomicAdd(tb.hits + 1, (unsigned long long)k - nres);
-        }
-      }
-    }
-    if (__any(nan_seen) && lane == 0 && wg == 0)
-      __hip_atomic_fetch_or(ws.err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (wv == 1 && wg == 0) {
+  if (wv == 1 && wg == 0) {
     // every workgroup's start flag at g: all have read the count
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (true) {
+      uint32_t fw[L1_NWG / 64];
+#pragma unroll
+      for (int i = 0; i < L1_NWG / 64; ++i)
+        fw[i] = __hip_atomic_load(ws.xflag + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       bool mine = true;
-      uint32_t fw[XG_MAX / 64];
-      const int nfl = (nwg + 63) >> 6;
 #pragma unroll
-      for (int i = 0; i < XG_MAX / 64; ++i)
-        if (i < nfl)
-          fw[i] = __hip_atomic_load(ws.xflag + min(lane + 64 * i, nwg - 1), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int i = 0; i < XG_MAX / 64; ++i)
-        if (i < nfl) mine &= fw[i] == g;
+      for (int i = 0; i < L1_NWG / 64; ++i) mine &= fw[i] == g0;
       if (__all(mine)) {
         if (lane == 0) s_started = 1;
         break;
@@ -862,192 +912,204 @@ __global__ void __launch_bounds__(256) layer1_kernel(ExpertArgs a, Ws ws, RouteA
     }
   }
   __syncthreads();
+  const uint32_t g = s_gen;
   trace_point(ws.trace, TK_GATEUP, 2);
-  if (wg == 0 && threadIdx.x < k) {
-    idx_out[threadIdx.x] = s_exp[threadIdx.x];
-    wts_out[threadIdx.x] = s_w[threadIdx.x];
+  const int e_j = s_exp[j];                      // this workgroup's expert (-1: dead slot)
+  if (wg == 0 && threadIdx.x < K) {
+    if (FROM_LOGITS) {
+      idx_out[threadIdx.x] = s_exp[threadIdx.x];
+      wts_out[threadIdx.x] = s_w[threadIdx.x];
+      if (SPLIT) {
+        ws.idx[threadIdx.x] = s_exp[threadIdx.x];
+        ws.wts[threadIdx.x] = s_w[threadIdx.x];
+      }
+    }
+    if (TABLE && tb.hits) {
+      const int e = s_exp[threadIdx.x];
+      const bool res = e >= 0 && tb.resident && tb.resident[e];
+      atomicAdd(tb.hits + (res ? 0 : 1), 1ull);
+    }
   }
 
-  // G: gate/up item and down rows, all loads in flight together
-  const int nw = nwg * 4;
-  const int gw = wg * 4 + wv;
-  constexpr int nchunk = FAST_F / FAST_RP;
-  const int items = k * nchunk;
+  // G: gate/up chunks and down rows of slot j, all loads in flight together
   constexpr int64_t ROWB = 8 * BLK_BYTES;
+  constexpr int64_t DROWB = 2 * BLK_BYTES;
+  const uint32_t gmat = (uint32_t)((int64_t)F * ROWB);   // bytes of one gate (or up) matrix
+  const uint32_t dmat = (uint32_t)((int64_t)d * DROWB);  // bytes of one down matrix
+  __amdgpu_buffer_rsrc_t rg, ru, rd;
+  uint32_t og, ou, od;                            // the expert's offset in its tensor
+  if (TABLE) {
+    const uint64_t* pe = tb.ptr + 3 * (e_j >= 0 ? e_j : 0);
+    rg = make_rsrc(reinterpret_cast<const void*>(pe[0]), e_j >= 0 ? gmat : 0u);
+    ru = make_rsrc(reinterpret_cast<const void*>(pe[1]), e_j >= 0 ? gmat : 0u);
+    rd = make_rsrc(reinterpret_cast<const void*>(pe[2]), e_j >= 0 ? dmat : 0u);
+    og = ou = od = 0;
+  } else {
+    rg = make_rsrc(a.L.gate, a.L.gate_bytes);
+    ru = make_rsrc(a.L.up, a.L.up_bytes);
+    rd = make_rsrc(a.L.down, a.L.down_bytes);
+    og = e_j >= 0 ? (uint32_t)(e_j * a.L.sg) : a.L.gate_bytes;
+    ou = e_j >= 0 ? (uint32_t)(e_j * a.L.su) : a.L.up_bytes;
+    od = e_j >= 0 ? (uint32_t)(e_j * a.L.sd) : a.L.down_bytes;
+  }
+  const uint32_t d_oob = TABLE ? dmat : a.L.down_bytes;   // a down offset past the descriptor
+  const bool has_chunk = wv < NRL;
+  const int c = b * NRL + wv;                    // gate/up chunk of this wave
   const uint32_t hoff = (uint32_t)((lane >> 3) * BLK_BYTES);
   const uint32_t coff = hoff + 8 + 16 * (lane & 7);
   u32x4 cg[FAST_RP], cu[FAST_RP];
   u32x2 hg[FAST_RP], hu[FAST_RP];
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.L.gate, a.L.gate_bytes);
-  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.L.up, a.L.up_bytes);
-  const uint32_t gmat = (uint32_t)((int64_t)F * ROWB);   // bytes of one gate (or up) matrix
-  auto issue = [&](int item) {
-    const int u = item / nchunk, c = item - u * nchunk;
-    const int e = s_exp[u];
-    uint32_t bg, bu;
-    __amdgpu_buffer_rsrc_t qg = rg, qu = ru;
-    if (TABLE) {   // the item's expert is wave-uniform: one descriptor per matrix
-      qg = make_rsrc(reinterpret_cast<const void*>(s_ptr[u][0]), gmat);
-      qu = make_rsrc(reinterpret_cast<const void*>(s_ptr[u][1]), gmat);
-      bg = bu = (uint32_t)((int64_t)c * FAST_RP * ROWB);
-    } else {
-      bg = (uint32_t)(e * a.L.sg + (int64_t)c * FAST_RP * ROWB);
-      bu = (uint32_t)(e * a.L.su + (int64_t)c * FAST_RP * ROWB);
+  if (has_chunk) {
+    const uint32_t bg = og + (uint32_t)((int64_t)c * FAST_RP * ROWB);
+    const uint32_t bu = ou + (uint32_t)((int64_t)c * FAST_RP * ROWB);
+#pragma unroll
+    for (int r = 0; r < FAST_RP; ++r) {
+      hg[r] = bload8(rg, bg + r * ROWB + hoff);
+      cg[r] = bload16(rg, bg + r * ROWB + coff);
     }
 #pragma unroll
     for (int r = 0; r < FAST_RP; ++r) {
-      hg[r] = bload8(qg, bg + r * ROWB + hoff);
-      cg[r] = bload16(qg, bg + r * ROWB + coff);
+      hu[r] = bload8(ru, bu + r * ROWB + hoff);
+      cu[r] = bload16(ru, bu + r * ROWB + coff);
     }
-#pragma unroll
-    for (int r = 0; r < FAST_RP; ++r) {
-      hu[r] = bload8(qu, bu + r * ROWB + hoff);
-      cu[r] = bload16(qu, bu + r * ROWB + coff);
-    }
-  };
-  // down: lane group dg (16 lanes) takes slots dg and dg + 4 of the wave's
-  // row pair, as the down kernel does
-  const int dg = lane >> 4, ds = lane & 15;
-  constexpr int64_t DROWB = 2 * BLK_BYTES;
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
+  }
+  // down: wave wv takes rows rw0 + 4q + (lane >> 4), q < NRL; lane & 15 is
+  // the segment (down_fast's layout)
+  const int ds = lane & 15;
+  const int rw0 = b * R + wv * 4 * NRL;
   const uint32_t dhoff = (uint32_t)((ds >> 3) * BLK_BYTES);
   const uint32_t dcoff = dhoff + 8 + 16 * (ds & 7);
-  u32x4 dc[2][FAST_ROWS];
-  u32x2 dh[2][FAST_ROWS];
-  bool dlive[2];
-  float dwt[2];
-  auto issue_down = [&](int r0) {
+  u32x4 dc[NRL];
+  u32x2 dh[NRL];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = dg + 4 * t;
-      const int e = j < k ? s_exp[j] : -1;
-      dlive[t] = e >= 0;
-      dwt[t] = j < k ? s_w[j] : 0.f;
-      if (TABLE) {
-        // the lane groups take different experts: per-lane addresses; a
-        // dead slot reads slot 0's first rows (selected out below)
-        const bool ok = dlive[t] && r0 < d;
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(s_ptr[ok ? j : 0][2]) +
-                              (ok ? (int64_t)r0 * DROWB : 0);
-#pragma unroll
-        for (int r = 0; r < FAST_ROWS; ++r) {
-          const int rr = ok && r0 + r < d ? r : 0;
-          dh[t][r] = gload8(base + rr * DROWB + dhoff);
-          dc[t][r] = gload16(base + rr * DROWB + dcoff);
-        }
-      } else {
-        const uint32_t base = (dlive[t] && r0 < d) ? (uint32_t)(e * a.L.sd + (int64_t)r0 * DROWB)
-                                                   : a.L.down_bytes;
-#pragma unroll
-        for (int r = 0; r < FAST_ROWS; ++r) {
-          dh[t][r] = bload8(rd, base + r * DROWB + dhoff);
-          dc[t][r] = bload16(rd, base + r * DROWB + dcoff);
-        }
-      }
-    }
-  };
-  int it = gw;
-  if (it < items) issue(it);
-  issue_down(gw * FAST_ROWS);
+  for (int q = 0; q < NRL; ++q) {
+    if (SPLIT) break;
+    const int row = rw0 + 4 * q + (lane >> 4);
+    const uint32_t base = (e_j >= 0 && row < d) ? od + (uint32_t)((int64_t)row * DROWB) : d_oob;
+    dh[q] = bload8(rd, base + dhoff);
+    dc[q] = bload16(rd, base + dcoff);
+  }
   trace_point(ws.trace, TK_GATEUP, 3);
-  const int row = lane >> 4;
-  {
+  if (has_chunk) {
     Frag f;
     frag_load(xfr, FAST_SEGS_D, lane, f);
-    while (it < items) {
-      const int u = it / nchunk, c = it - u * nchunk;
-      float gs[FAST_RP], us[FAST_RP];
+    float gs[FAST_RP], us[FAST_RP];
 #pragma unroll
-      for (int r = 0; r < FAST_RP; ++r) {
-        gs[r] = dot_seg(cg[r], hg[r], f);
-        us[r] = dot_seg(cu[r], hu[r], f);
-      }
-      const float tg = row_sum16(fold16(fold32(gs[0], gs[2]), fold32(gs[1], gs[3])));
-      const float tu = row_sum16(fold16(fold32(us[0], us[2]), fold32(us[1], us[3])));
-      if ((lane & 15) == 0)
-        put_word(ws.xh + (int64_t)u * F + c * FAST_RP + row, __float_as_uint(silu_mul(tg, tu)), g);
-      it += nw;
-      if (it < items) issue(it);
+    for (int r = 0; r < FAST_RP; ++r) {
+      gs[r] = dot_seg(cg[r], hg[r], f);
+      us[r] = dot_seg(cu[r], hu[r], f);
+    }
+    const float tg = row_sum16(fold16(fold32(gs[0], gs[2]), fold32(gs[1], gs[3])));
+    const float tu = row_sum16(fold16(fold32(us[0], us[2]), fold32(us[1], us[3])));
+    const int row = lane >> 4;
+    if ((lane & 15) == 0) {
+      const float hv = e_j >= 0 ? silu_mul(tg, tu) : 0.f;
+      if (SPLIT)
+        ws.h[(int64_t)j * F + c * FAST_RP + row] = hv;
+      else
+        put_word(ws.xh + (int64_t)j * F + c * FAST_RP + row, __float_as_uint(hv), g);
     }
   }
   trace_point(ws.trace, TK_GATEUP, 4);
-
-  // D: read every workgroup's h words until all hold this call's
-  // generation (all of a thread's loads in flight before the first is
-  // used; each workgroup starts at a different word, so the polls of the
-  // grid do not all hit the same lines at once), stage them
-  const int nh = k * F;
-  {
-    constexpr int HPT = 8 * FAST_F / 256;   // words per thread (k <= 8, F = 512)
-    const int rot = (wg * 64) % nh;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    int expired = 0;
-    while (true) {
-      uint64_t hw[HPT];
-      int at[HPT];
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        int j = (int)threadIdx.x + 256 * i + rot;
-        j = j >= nh ? j - nh : j;
-        at[i] = j;
-        hw[i] = get_word(ws.xh + min(j, nh - 1));
-      }
-      int stale = 0;
-#pragma unroll
-      for (int i = 0; i < HPT; ++i) {
-        const bool in = (int)threadIdx.x + 256 * i < nh;
-        stale |= in && (uint32_t)(hw[i] >> 32) != g;
-        if (in) hval[at[i]] = __uint_as_float((uint32_t)hw[i]);
-      }
-      const int any_stale = __syncthreads_or(stale);
-      expired = __syncthreads_or(threadIdx.x == 0 &&
-                                 __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS);
-      if (!any_stale || expired) break;
+  if (SPLIT) {
+    if (wg == 0 && threadIdx.x == 0) {
+      if (s_started)
+        ws.gen[0] = g;
+      else
+        __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (expired && threadIdx.x == 0)
-      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  constexpr int fbh = frag_bytes(FAST_SEGS_F);
+
+  // D1: slot j's h, its fragments, this block's slot sums
+  bool late = gather_words<FAST_F / 256>(ws.xh + (int64_t)j * F, F, g, hval);
   {
-    const int j = threadIdx.x / FAST_SEGS_F, sg = threadIdx.x - j * FAST_SEGS_F;
-    if (j < k) {
+    const int sg = threadIdx.x;
+    if (sg < FAST_SEGS_F) {
       float buf[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) buf[i] = hval[j * F + sg * SEG + i];
+      for (int i = 0; i < 32; ++i) buf[i] = hval[sg * SEG + i];
       Frag fr;
       make_frag(buf, fr);
-      frag_store(hfr + j * fbh, FAST_SEGS_F, sg, fr);
+      frag_store(hfr, FAST_SEGS_F, sg, fr);
     }
   }
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 5);
-
-  // the down rows of this wave, then any further row pairs
-  for (int r0 = gw * FAST_ROWS; r0 < d; r0 += nw * FAST_ROWS) {
-    if (r0 != gw * FAST_ROWS) issue_down(r0);
-    float acc[FAST_ROWS];
+  {
+    Frag f;
+    frag_load(hfr, FAST_SEGS_F, ds, f);
 #pragma unroll
-    for (int r = 0; r < FAST_ROWS; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int j = dg + 4 * t;
-      Frag f;
-      frag_load(hfr + (j < k ? j : 0) * fbh, FAST_SEGS_F, ds, f);
-#pragma unroll
-      for (int r = 0; r < FAST_ROWS; ++r) {
-        const float v = __builtin_fmaf(dwt[t], dot_seg(dc[t][r], dh[t][r], f), acc[r]);
-        acc[r] = dlive[t] ? v : acc[r];
+    for (int q = 0; q < NRL; ++q) {
+      const float sum = row_sum16(dot_seg(dc[q], dh[q], f));
+      const int rl = wv * 4 * NRL + 4 * q + (lane >> 4);   // row within the block
+      const int row = b * R + rl;
+      if ((lane & 15) == 0) {
+        if (j == 0)
+          s0v[rl] = sum;
+        else if (row < d)
+          put_word(ws.xs + (int64_t)j * 2048 + row, __float_as_uint(sum), g);
       }
     }
-    const float t = row_sum16(fold16(fold32(acc[0], acc[1]), 0.f));
-    if ((lane == 0 || lane == 32)) {
-      const int rr = r0 + (lane >> 5);
-      if (rr < d) a.y[rr] = (a.res ? a.res[rr] : 0.f) + t;
+  }
+  // D2: the owner (slot 0) combines the slot sums of its rows
+  if (j == 0) {
+    constexpr int NW = (K - 1) * R;             // words from the other slots
+    // word t: slot 1 + t / R, row b R + t % R; rows past d and dead slots
+    // are not waited for
+    {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        constexpr int PT = (NW + 255) / 256;
+        uint64_t w[PT];
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+          const int t = min((int)threadIdx.x + 256 * i, NW - 1);
+          const int sl = 1 + t / R, row = min(b * R + t % R, d - 1);
+          w[i] = get_word(ws.xs + (int64_t)sl * 2048 + row);
+        }
+        int stale = 0;
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+          const int t = (int)threadIdx.x + 256 * i;
+          if (t < NW) {
+            const int sl = 1 + t / R, row = b * R + t % R;
+            const bool need = row < d && s_exp[sl] >= 0;
+            stale |= need && (uint32_t)(w[i] >> 32) != g;
+            other[t] = __uint_as_float((uint32_t)w[i]);
+          }
+        }
+        const int any_stale = __syncthreads_or(stale);
+        const int expired = __syncthreads_or(threadIdx.x == 0 &&
+                                             __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS);
+        if (!any_stale) break;
+        if (expired) {
+          late = true;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < R) {
+      const int row = b * R + threadIdx.x;
+      if (row < d) {
+        float sj[MAXK / 2], wj[MAXK / 2];
+        bool lj[MAXK / 2];
+#pragma unroll
+        for (int q = 0; q < MAXK / 2; ++q) {
+          sj[q] = q == 0 ? s0v[threadIdx.x] : (q < K ? other[(q - 1) * R + threadIdx.x] : 0.f);
+          wj[q] = q < K ? s_w[q] : 0.f;
+          lj[q] = q < K && s_exp[q] >= 0;
+        }
+        a.y[row] = combine_slots(sj, wj, lj, K, a.res ? a.res[row] : 0.f);
+      }
     }
   }
+  if (late && threadIdx.x == 0)
+    __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (wg == 0 && threadIdx.x == 0) {
-    // a workgroup that had not started by phase T would read the count
-    // after this store: never advance it then (the call reports a time-out)
+    // a workgroup that had not started by now would read the count after
+    // this store: never advance it then (the call reports a time-out)
     if (s_started)
       ws.gen[0] = g;
     else
@@ -1086,6 +1148,7 @@ WsLayout ws_layout(int64_t E, int B, int k, int64_t d, int64_t F, uint32_t flags
   l.xh = l.xlog + 8 * XL_MAX;
   l.xflag = l.xh + 8 * XH_MAX;
   l.gen = l.xflag + 4 * XG_MAX;
+  l.xs = l.gen + 256;
   o = al256(o + XREG_BYTES);
   l.logits = o;   // batched calls keep LG_KS partial logit sets
   o = al256(o + sizeof(float) * (B >= 2 ? (size_t)LG_KS : 1) * B * lg_stride((int)E));
@@ -1126,6 +1189,7 @@ Ws ws_carve(void* base, int64_t E, int B, int k, int64_t d, int64_t F, uint32_t 
   w.xh = reinterpret_cast<uint64_t*>(p + l.xh);
   w.xflag = reinterpret_cast<uint32_t*>(p + l.xflag);
   w.gen = reinterpret_cast<uint32_t*>(p + l.gen);
+  w.xs = reinterpret_cast<uint64_t*>(p + l.xs);
   return w;
 }
 
@@ -1218,45 +1282,67 @@ static int launch_fast(const ExpertArgs& a, Ws ws, const float* logits, int32_t*
   return (int)hipGetLastError();
 }
 
+// The single-launch layer serves one token of the tuned shape with k in
+// {2, 4, 8} on a device of 256 compute units (one workgroup per unit);
+// mode 2 runs its routing and gate/up phases, then the down kernel.
+static int g_single_launch = 0;
+void set_single_launch(int mode) { g_single_launch = mode; }
+bool single_launch_shape(int E, int d, int F, int k) {
+  return fast_shape(d, F, k) && (k == 2 || k == 4 || k == 8) && E <= XL_MAX &&
+         num_cus() == L1_NWG;
+}
+static bool use_layer1(const LayerDev& L, int B, int k) {
+  return g_single_launch != 0 && B == 1 && single_launch_shape(L.E, L.d, L.F, k);
+}
+
+template <bool FROM_LOGITS, bool TABLE, bool SPLIT = false>
+static int launch_layer1(const ExpertArgs& a, const RouteArgs& ra, Ws ws, TableArgs tb,
+                         hipStream_t s) {
+  const int E = a.L.E, k = a.k;
+  if (k != 2 && k != 4 && k != 8) return (int)hipErrorInvalidValue;
+#define HQ_L1(PER, NRL)                                                                 \
+  hipExtLaunchKernelGGL((layer1_kernel<PER, NRL, FROM_LOGITS, TABLE, SPLIT>), dim3(L1_NWG), \
+                        dim3(256), 0, s, g_ev_start, g_ev_stop, 0, a, ws, ra, ra.idx_out,    \
+                        ra.wts_out, tb)
+#define HQ_L1K(PER)    \
+  if (k == 2)          \
+    HQ_L1(PER, 1);     \
+  else if (k == 4)     \
+    HQ_L1(PER, 2);     \
+  else                 \
+    HQ_L1(PER, 4);
+  if (E <= 256) {
+    HQ_L1K(4)
+  } else if (E <= 512) {
+    HQ_L1K(8)
+  } else {
+    HQ_L1K(16)
+  }
+#undef HQ_L1K
+#undef HQ_L1
+  int err = (int)hipGetLastError();
+  if (err || !SPLIT) return err;
+  ExpertArgs ad = a;   // the down pass reads the routing the first launch wrote
+  ad.idx = ws.idx;
+  ad.wts = ws.wts;
+  const int waves = (a.L.d + FAST_ROWS - 1) / FAST_ROWS;
+  hipLaunchKernelGGL(down_fast_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, ad, ws);
+  return (int)hipGetLastError();
+}
+
 int launch_experts(const LayerDev& L, const float* x, int64_t ldx, int B, const int32_t* idx,
                    const float* wts, int k, const float* residual, float* y, int64_t ldy, Ws ws,
                    hipStream_t s) {
   ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
   if (fast_shape(L.d, L.F, k)) {
     if (B >= 2) return launch_experts_batched(a, ws, num_cus(), nullptr, s);
+    if (use_layer1(L, B, k) && g_single_launch == 1) {
+      RouteArgs ra{nullptr, nullptr, L.E, L.d, x, ldx, 1, k, nullptr, nullptr, nullptr};
+      return launch_layer1<false, false>(a, ra, ws, TableArgs{nullptr, nullptr, nullptr}, s);
+    }
     return launch_fast(a, ws, nullptr, nullptr, nullptr, s);
   }
   return launch_generic_experts(a, ws, s);
-}
-
-// One token, tuned shape, weights in device memory: the single-launch layer.
-template <bool TABLE>
-static int launch_layer1(const ExpertArgs& a, const RouteArgs& ra, Ws ws, TableArgs tb,
-                         hipStream_t s) {
-  const int nwg = num_cus();
-  const int E = a.L.E;
-#define HQ_L1(PER)                                                                            \
-  hipExtLaunchKernelGGL((layer1_kernel<PER, TABLE>), dim3(nwg), dim3(256), 0, s, g_ev_start, \
-                        g_ev_stop, 0, a, ws, ra, ra.idx_out, ra.wts_out, tb)
-  if (E <= 256)
-    HQ_L1(4);
-  else if (E <= 512)
-    HQ_L1(8);
-  else
-    HQ_L1(16);
-#undef HQ_L1
-  return (int)hipGetLastError();
-}
-
-// The single-launch layer serves one token of the tuned shape whose
-// weights are in device memory, when the grid (one workgroup per compute
-// unit) fits the workspace's per-workgroup state.
-static bool g_single_launch = false;
-void set_single_launch(bool on) { g_single_launch = on; }
-static bool use_layer1(const LayerDev& L, int B, int k, const Ws& ws) {
-  return g_single_launch && B == 1 && fast_shape(L.d, L.F, k) &&
-         !(L.flags & LAYER_HOST_MAPPED) && L.E <= XL_MAX && k * L.F <= XH_MAX &&
-         num_cus() <= XG_MAX;
 }
 
 int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const float* x,
@@ -1264,9 +1350,11 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  float* y, int64_t ldy, Ws ws, hipStream_t s) {
   RouteArgs ra{Wr, bias, L.E, L.d, x, ldx, B, k, idx, wts, nullptr};
   const bool fast = fast_shape(L.d, L.F, k);
-  if (use_layer1(L, B, k, ws)) {
+  if (use_layer1(L, B, k)) {
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
-    return launch_layer1<false>(a, ra, ws, TableArgs{nullptr, nullptr, nullptr}, s);
+    const TableArgs none{nullptr, nullptr, nullptr};
+    if (g_single_launch == 2) return launch_layer1<true, false, true>(a, ra, ws, none, s);
+    return launch_layer1<true, false>(a, ra, ws, none, s);
   }
   if (B >= 2) {
     // the same router and routing functions as moe_route_topk, so the
@@ -1296,10 +1384,10 @@ int launch_layer_table(const LayerDev& L, const uint64_t* ptr, const uint8_t* re
                        unsigned long long* hits, const float* Wr, const float* bias,
                        const float* x, int k, int32_t* idx, float* wts, const float* residual,
                        float* y, Ws ws, hipStream_t s) {
-  if (!fast_shape(L.d, L.F, k) || L.E > XL_MAX || num_cus() > XG_MAX) return (int)hipErrorInvalidValue;
+  if (!single_launch_shape(L.E, L.d, L.F, k)) return (int)hipErrorInvalidValue;
   RouteArgs ra{Wr, bias, L.E, L.d, x, L.d, 1, k, idx, wts, nullptr};
   ExpertArgs a{L, x, L.d, 1, k, idx, wts, residual, y, L.d};
-  return launch_layer1<true>(a, ra, ws, TableArgs{ptr, resident, hits}, s);
+  return launch_layer1<true, true>(a, ra, ws, TableArgs{ptr, resident, hits}, s);
 }
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import moe as om
 
 from _parity import REL_L2_TOL, ExpertCache, oracle_layer_check, rel_l2
 
@@ -132,20 +133,26 @@ def test_cpu_route_matches_gpu_and_oracle(q, layers):
         assert amb == 0 and e2 <= REL_L2_TOL, e2
 
 
-@pytest.mark.parametrize("En,k", [(256, 8), (100, 6), (1024, 8), (512, 2)])
+@pytest.mark.parametrize("En,k", [(256, 8), (100, 4), (1024, 8), (512, 2), (64, 8), (700, 4),
+                                  (100, 6)])
 def test_single_launch_equals_three_launch(q, En, k):
-    """The single-launch one-token kernel (which the table layers run on)
-    gives the same bits as the three-launch chain, for expert counts that
-    take every top-k width, and reports no device error."""
+    """The single-launch one-token kernel (which the table layers run on),
+    and its two-launch form (its routing and gate/up phases, then the down
+    kernel), give the same bits as the three-launch chain for expert counts
+    that take every top-k width and k = 2, 4, 8 (k = 6 runs the chain every
+    time), report no device error, and keep doing so when batched calls
+    share the workspace between one-token calls."""
     L = q.synthetic.build_layer(torch, 31, 0, En, D, F)
-    xs = synth.activations(torch, "cuda", 32, 4, D)
+    xs = synth.activations(torch, "cuda", 32, 6, D)
     outs = []
     try:
-        for single in (0, 1):
-            q.lib.hfq4_debug_set_single_launch(single)
-            ws = q.new_workspace(L, 1, k)
+        for mode in (0, 1, 2):   # three launches, one, two
+            q.lib.hfq4_debug_set_single_launch(mode)
+            ws = q.new_workspace(L, 4, k)
             got = []
             for t in range(xs.shape[0]):
+                if t == 3:   # a batched call on the same workspace
+                    q.moe_layer_decode(L, xs[:4], k, ws)
                 got.append(tuple(v.clone() for v in q.moe_layer_decode(L, xs[t:t + 1], k, ws,
                                                                         residual=xs[t:t + 1])))
             torch.cuda.synchronize()
@@ -153,6 +160,49 @@ def test_single_launch_equals_three_launch(q, En, k):
             outs.append(got)
     finally:
         q.lib.hfq4_debug_set_single_launch(0)
-    for a, b in zip(*outs):
-        for u, v in zip(a, b):
-            assert torch.equal(u, v)
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            for u, v in zip(a, b):
+                assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("k", [2, 4, 8])
+def test_single_launch_given_routing(q, k):
+    """moe_expert_decode with the routing given: the single launch equals
+    the three-launch chain bit for bit, an index out of range is a dead slot
+    on both (INDEX error bit, nothing added), and the oracle agrees."""
+    En = 128
+    L = q.synthetic.build_layer(torch, 41, 0, En, D, F)
+    rng = np.random.default_rng(k)
+    xs = synth.activations(torch, "cuda", 42, 3, D)
+    idx = torch.from_numpy(np.stack([rng.permutation(En)[:k] for _ in range(3)]).astype(np.int32)).cuda()
+    wts = torch.from_numpy(rng.uniform(0.05, 1, size=(3, k)).astype(np.float32)).cuda()
+    bad = idx.clone()
+    bad[0, k - 1] = En + 5            # out of range: a dead slot
+    res = []
+    try:
+        for single in (0, 1):
+            q.lib.hfq4_debug_set_single_launch(single)
+            ws = q.new_workspace(L, 1, k)
+            out = []
+            for t in range(3):
+                out.append(q.moe_expert_decode(L, xs[t:t + 1], idx[t:t + 1], wts[t:t + 1], ws,
+                                               residual=xs[t:t + 1]).clone())
+            torch.cuda.synchronize()
+            assert q.workspace_error(ws) == 0
+            ws2 = q.new_workspace(L, 1, k)
+            yb = q.moe_expert_decode(L, xs[0:1], bad[0:1], wts[0:1], ws2).clone()
+            torch.cuda.synchronize()
+            assert q.workspace_error(ws2) & 1
+            res.append((out, yb))
+    finally:
+        q.lib.hfq4_debug_set_single_launch(0)
+    for u, v in zip(res[0][0], res[1][0]):
+        assert torch.equal(u, v)
+    assert torch.equal(res[0][1], res[1][1])
+    cache = ExpertCache(torch, "cuda", 41, 0, D, F)
+    for t in range(2):
+        x64 = xs[t].cpu().numpy().astype(np.float64)
+        outs = [om.expert_forward(cache(int(e)), x64) for e in idx[t].cpu().numpy()]
+        ref = om.combine(outs, wts[t].cpu().numpy()) + x64
+        assert rel_l2(res[1][0][t].cpu().numpy()[0], ref) <= REL_L2_TOL, t
