@@ -462,15 +462,16 @@ def bench_cache(args, torch, q):
 
 
 def bench_turbo(args, torch, q):
-    """TurboQuant KV codec: encode and decode of 2^21 vectors of 128 f32
-    values (1 GiB) at 2, 3, 4 and 8 bits; both kernels are HBM streams, so
-    the roofline is HBM bandwidth over the bytes read plus written."""
-    N, n = 1 << 21, 128
-    V = torch.randn((N, n), dtype=torch.float32, device="cuda")
+    """TurboQuant KV codec: encode and decode of 1 GiB of f32 vectors (2^21
+    of 128 values at 2, 3, 4 and 8 bits; 64 and 256 values at 4 bits); both
+    kernels are HBM streams, so the roofline is HBM bandwidth over the bytes
+    read plus written."""
     res = {}
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    for bits in (4, 3, 2, 8):
+    for n, bits in ((128, 4), (128, 3), (128, 2), (128, 8), (64, 4), (256, 4)):
+        N = (1 << 28) // n                  # 1 GiB of f32 vectors
+        V = torch.randn((N, n), dtype=torch.float32, device="cuda")
         rec = q.turbo_record_bytes(n, bits)
         out = torch.empty((N, rec), dtype=torch.uint8, device="cuda")
         dec = torch.empty((N, n), dtype=torch.float32, device="cuda")
@@ -489,7 +490,8 @@ def bench_turbo(args, torch, q):
                 best = min(best, ev0.elapsed_time(ev1) / 1e3)
             t[name] = best
         moved = N * (4 * n + rec)
-        res[str(bits)] = {"record_bytes": rec, "ratio_vs_f32": round(4 * n / rec, 3),
+        key = str(bits) if n == 128 else "n%d_%d" % (n, bits)
+        res[key] = {"n": n, "vectors": N, "record_bytes": rec, "ratio_vs_f32": round(4 * n / rec, 3),
                           "encode_ms": round(t["encode"] * 1e3, 4),
                           "decode_ms": round(t["decode"] * 1e3, 4),
                           "encode_gbs": round(moved / t["encode"] / 1e9, 1),
@@ -497,9 +499,9 @@ def bench_turbo(args, torch, q):
                           "encode_frac": round(moved / t["encode"] / 1e9 / HBM_PEAK_GBS, 4),
                           "decode_frac": round(moved / t["decode"] / 1e9 / HBM_PEAK_GBS, 4),
                           "vectors_per_s_decode": round(N / t["decode"], 0)}
-        log("turbo%d: encode %.1f GB/s, decode %.1f GB/s" % (bits, res[str(bits)]["encode_gbs"],
-                                                             res[str(bits)]["decode_gbs"]))
-        del out, dec
+        log("turbo n=%d bits=%d: encode %.1f GB/s, decode %.1f GB/s" % (
+            n, bits, res[key]["encode_gbs"], res[key]["decode_gbs"]))
+        del out, dec, V
     r4 = res["4"]
     out = _base(args, 5, 1, r4["decode_ms"] / 1e3, r4["decode_gbs"],
                 "TurboQuant KV codec: 2^21 vectors of 128 f32 (1 GiB), 4-bit records of 68 bytes; "

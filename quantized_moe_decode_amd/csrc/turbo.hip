@@ -13,10 +13,13 @@
 // record is the codes packed LSB-first (code j at bits [j b, j b + b)) and
 // then s = |v| / |c| as an f32.
 //
-// One wave per vector, n/64 consecutive values per lane: the butterflies of
-// span h < n/64 stay in a lane, the others pair lane l with lane l ^
-// (h / (n/64)) through a DPP quad permute or __shfl_xor; every output is the
-// same sequence of exactly rounded adds and subtracts.  The level table is
+// n / 8 lanes per vector, eight values per lane in two runs of four, so a
+// wave holds 8, 4 or 2 vectors at once and the per-vector reductions are
+// short lane-group sums: the butterflies of spans 1, 2 and n/2 stay in a
+// lane, the others pair lane j with lane j ^ M through DPP (quad permutes,
+// row rotations) or the gfx950 row swap; every output is the same sequence
+// of exactly rounded adds and subtracts.  A wave takes two such sets per
+// iteration with all their loads in flight together.  The level table is
 // copied into LDS once per workgroup.  Both kernels are HBM streams: 4n
 // bytes of f32 on one side, n b / 8 + 4 on the other.
 #include <hip/hip_runtime.h>
@@ -28,56 +31,114 @@
 namespace hq {
 namespace {
 
-// value of lane l ^ m (m = 1, 2, ..., 32) in every lane: quad permutes by
-// DPP for 1 and 2, the others by __shfl_xor (ds_bpermute: the LDS crossbar,
-// no LDS memory and no barrier)
+// The value of lane l ^ M in every lane: quad permutes (M = 1, 2) and row
+// rotations (M = 4, 8) by DPP, the gfx950 row swap for 16 -- VALU only,
+// no LDS crossbar.
 template <int M>
-__device__ __forceinline__ float swap_lanes(float v) {
-  if (M == 1) return dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (M == 2) return dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  return __shfl_xor(v, M, 64);
+__device__ __forceinline__ float partner(float v, int lane) {
+  if (M == 16) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return (lane & 16) ? as_f32(r[0]) : as_f32(r[1]);   // r[0]: bit 4 clear, r[1]: set
+  }
+  if (M == 1) return dpp<0xB1>(v);     // quad_perm [1,0,3,2]
+  if (M == 2) return dpp<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (M == 8) return dpp<0x128>(v);    // row_ror:8
+  // M = 4: row_ror:N reads lane l - N (mod 16).  Both moves run in every
+  // lane (a DPP move reading a lane that is switched off would read the
+  // fallback value), then each lane keeps its partner's.
+  const float down4 = dpp<0x124>(v), up4 = dpp<0x12C>(v);
+  return (lane & 4) ? down4 : up4;
 }
 
-// In-place orthonormal Walsh-Hadamard transform of the wave's n = 64 * EL
-// values, lane l holding elements l*EL .. l*EL + EL - 1.
-template <int EL>
-__device__ __forceinline__ void fwht(float (&x)[EL], int lane) {
+// Register layout of one vector of n = 8 G values in an aligned group of G
+// lanes: lane j holds the four values 4j .. 4j + 3 in x[0..3] and the four
+// values n/2 + 4j .. n/2 + 4j + 3 in x[4..7], so each 16-byte load or store
+// instruction of a wave covers contiguous memory.
+//
+// In-place orthonormal Walsh-Hadamard transform in that layout, stages in
+// order of increasing span: spans 1 and 2 inside each run of four, spans
+// 4 M (M = 1 .. G/2) between lane j and lane j ^ M, span n/2 between the
+// two runs of a lane.  Every butterfly is (a, b) -> (a + b, a - b) with a
+// the lower index, exactly rounded (a lane's new value is fma(+-1, own,
+// partner), the same single rounding); then the 1/sqrt(n) scaling.
+template <int G>
+__device__ __forceinline__ void fwht8(float (&x)[8], int lane) {
 #pragma unroll
-  for (int h = 1; h < EL; h <<= 1) {
+  for (int h = 1; h < 4; h <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EL; ++e)
+    for (int e = 0; e < 8; ++e)
       if (!(e & h)) {
         const float a = x[e], b = x[e + h];
         x[e] = a + b;
         x[e + h] = a - b;
       }
   }
-  // spans >= EL: lanes l and l ^ m, m = h / EL
 #define HQ_STAGE(M)                                            \
-  {                                                            \
-    const bool upper = (lane & (M)) != 0;                      \
-    _Pragma("unroll") for (int e = 0; e < EL; ++e) {           \
-      const float o = swap_lanes<M>(x[e]);                     \
-      x[e] = upper ? o - x[e] : x[e] + o;                      \
-    }                                                          \
+  if (M < G) {                                                 \
+    const float sg = (lane & (M)) ? -1.f : 1.f;                \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e)              \
+      x[e] = __builtin_fmaf(sg, x[e], partner<M>(x[e], lane)); \
   }
-  HQ_STAGE(1) HQ_STAGE(2) HQ_STAGE(4) HQ_STAGE(8) HQ_STAGE(16) HQ_STAGE(32)
+  HQ_STAGE(1) HQ_STAGE(2) HQ_STAGE(4) HQ_STAGE(8) HQ_STAGE(16)
 #undef HQ_STAGE
-  const float inv = EL == 1 ? 0.125f : EL == 2 ? 0.08838834764831845f : 0.0625f;   // 1/sqrt(64 EL)
 #pragma unroll
-  for (int e = 0; e < EL; ++e) x[e] *= inv;
+  for (int e = 0; e < 4; ++e) {
+    const float a = x[e], b = x[e + 4];
+    x[e] = a + b;
+    x[e + 4] = a - b;
+  }
+  const float inv = G == 8 ? 0.125f : G == 16 ? 0.08838834764831845f : 0.0625f;   // 1/sqrt(8 G)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= inv;
 }
 
-// wave sum of per-lane values in a fixed order
-__device__ __forceinline__ float wsum(float v) { return wave_sum(v); }
+// A lane's two runs of four f32 values (16-byte loads and stores when the
+// vector start is 16-byte aligned).
+template <bool VEC>
+__device__ __forceinline__ void load8(const float* a, const float* b, float (&x)[8]) {
+  if constexpr (VEC) {
+    const f32x4 p = *reinterpret_cast<const f32x4*>(a);
+    const f32x4 q = *reinterpret_cast<const f32x4*>(b);
+    x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
+    x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[e + 4] = b[e];
+    }
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void store8(float* a, float* b, const float (&x)[8]) {
+  if constexpr (VEC) {
+    *reinterpret_cast<f32x4*>(a) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(b) = f32x4{x[4], x[5], x[6], x[7]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = x[e];
+      b[e] = x[e + 4];
+    }
+  }
+}
 
-template <int EL, int BITS>
+// Encode.  A wave holds 64 / G vectors at once (G = n / 8 lanes each) and
+// takes U such sets per iteration, every load of the iteration issued before
+// the first is used (a vector index past the end reads the last vector
+// again and writes nothing).  Norms are G-lane sums; each lane's two runs of
+// four codes go into the wave's records in LDS (value i's code at bits
+// [i b, i b + b) of its vector's code stream), and the iteration's records,
+// contiguous in memory, leave as whole words.
+template <int G, int BITS, int U, bool VEC>
 __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restrict__ v, int64_t count,
                                                            int64_t ldv, uint8_t* __restrict__ out,
                                                            TurboTable tab) {
-  constexpr int N = 64 * EL, L = 1 << BITS;
-  constexpr int REC = N * BITS / 8 + 4, CW = N * BITS / 32;   // record bytes, code words (<= 64)
-  __shared__ uint32_t pk[4][CW];
+  constexpr int N = 8 * G, L = 1 << BITS, VW = 64 / G;
+  constexpr int CW = N * BITS / 32, RW = CW + 1;   // code words, record words
+  constexpr int WW = U * VW * RW;                  // record words of one wave iteration
+  __shared__ uint32_t pk[4][WW];
   __shared__ float thr[L], cent[L];
   for (int i = threadIdx.x; i < L; i += blockDim.x) {
     cent[i] = tab.cent[i];
@@ -85,97 +146,149 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   }
   __syncthreads();
   const int wv = wave_id(), lane = threadIdx.x & 63;
-  for (int64_t vec = (int64_t)blockIdx.x * 4 + wv; vec < count; vec += (int64_t)gridDim.x * 4) {
-    float x[EL];
-    const float* src = v + vec * ldv + lane * EL;
+  const int gi = lane / G, li = lane % G;          // vector of the set, lane within the vector
+  constexpr int PER = U * VW;                      // vectors per wave iteration
+  const int64_t stride = (int64_t)gridDim.x * 4 * PER;
+  const uint32_t pa = (uint32_t)(4 * li) * BITS, pb = (uint32_t)(4 * li + N / 2) * BITS;   // run bits
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER; v0 < count; v0 += stride) {
+    float x[U][8];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) x[e] = src[e];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < EL; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-    const float norm = __builtin_sqrtf(wsum(ss));
-    const float inv = norm > 0.f ? 1.f / norm : 0.f;
-#pragma unroll
-    for (int e = 0; e < EL; ++e) x[e] *= inv;
-    fwht<EL>(x, lane);
-    // nearest level: the number of thresholds strictly below r (binary search)
-    uint32_t code[EL];
-    float cc = 0.f;
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      int lo = 0;
-#pragma unroll
-      for (int step = L / 2; step >= 1; step >>= 1)
-        if (thr[lo + step - 1] < x[e]) lo += step;
-      code[e] = norm > 0.f ? (uint32_t)lo : 0u;
-      const float c = cent[code[e]];
-      cc = __builtin_fmaf(c, c, cc);
+    for (int u = 0; u < U; ++u) {
+      const float* src = v + min(v0 + u * VW + gi, count - 1) * ldv + 4 * li;
+      load8<VEC>(src, src + N / 2, x[u]);
     }
-    const float cn = __builtin_sqrtf(wsum(cc));
-    const float s = norm > 0.f ? norm / cn : 0.f;
-    // pack: lane l's EL codes are bits [l EL BITS, (l+1) EL BITS) of the stream
-    if (lane < CW) pk[wv][lane] = 0u;
+    for (int t = lane; t < WW; t += 64) pk[wv][t] = 0u;
     __builtin_amdgcn_wave_barrier();
-    uint64_t chunk = 0;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) chunk |= (uint64_t)code[e] << (e * BITS);
-    const uint32_t bit0 = (uint32_t)lane * EL * BITS;
-    const uint32_t w0 = bit0 >> 5, sh = bit0 & 31;
-    const uint64_t placed = chunk << sh;
-    atomicOr(&pk[wv][w0], (uint32_t)placed);
-    if ((placed >> 32) != 0) atomicOr(&pk[wv][w0 + 1], (uint32_t)(placed >> 32));
+    for (int u = 0; u < U; ++u) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[u][e], x[u][e], ss);
+      const float norm = __builtin_sqrtf(group_sum<G>(ss));
+      const float inv = norm > 0.f ? 1.f / norm : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[u][e] *= inv;
+      fwht8<G>(x[u], lane);
+      // nearest level: the number of thresholds strictly below r (binary search)
+      float cc = 0.f;
+      uint32_t run[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int lo = 0;
+#pragma unroll
+        for (int step = L / 2; step >= 1; step >>= 1)
+          if (thr[lo + step - 1] < x[u][e]) lo += step;
+        const uint32_t code = norm > 0.f ? (uint32_t)lo : 0u;
+        const float c = cent[code];
+        cc = __builtin_fmaf(c, c, cc);
+        run[e >> 2] |= code << ((e & 3) * BITS);
+      }
+      const float cn = __builtin_sqrtf(group_sum<G>(cc));
+      const float s = norm > 0.f ? norm / cn : 0.f;
+      // the vector's record: code words, then s (the code stream ends on a
+      // word boundary, so no run spills into the s word)
+      uint32_t* rec = &pk[wv][(u * VW + gi) * RW];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t p = r ? pb : pa;
+        const uint64_t placed = (uint64_t)run[r] << (p & 31);
+        atomicOr(rec + (p >> 5), (uint32_t)placed);
+        if ((placed >> 32) != 0) atomicOr(rec + (p >> 5) + 1, (uint32_t)(placed >> 32));
+      }
+      if (li == 0) rec[CW] = __float_as_uint(s);
+    }
     __builtin_amdgcn_wave_barrier();
-    uint32_t* dst = reinterpret_cast<uint32_t*>(out + vec * REC);
-    if (lane < CW) dst[lane] = pk[wv][lane];
-    if (lane == 0) dst[CW] = __float_as_uint(s);
+    const int words = (int)min((int64_t)PER, count - v0) * RW;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(out + v0 * (4 * RW));
+    for (int t = lane; t < words; t += 64) dst[t] = pk[wv][t];
     __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int EL, int BITS>
+// Decode: the same vector layout; each lane reads the code words holding its
+// two runs (one word each, two for 3-bit codes) and the s word, every load
+// of the iteration in flight together.
+template <int G, int BITS, int U, bool VEC>
 __global__ void __launch_bounds__(256) turbo_decode_kernel(const uint8_t* __restrict__ in,
                                                            int64_t count, float* __restrict__ v,
                                                            int64_t ldv, TurboTable tab) {
-  constexpr int N = 64 * EL, L = 1 << BITS;
-  constexpr int REC = N * BITS / 8 + 4, CW = N * BITS / 32;   // record bytes, code words (<= 64)
+  constexpr int N = 8 * G, L = 1 << BITS, VW = 64 / G;
+  constexpr int CW = N * BITS / 32, REC = 4 * (CW + 1);
+  constexpr bool TWO = (32 % (4 * BITS)) != 0;   // a run may straddle two words
   __shared__ float cent[L];
   for (int i = threadIdx.x; i < L; i += blockDim.x) cent[i] = tab.cent[i];
   __syncthreads();
   const int wv = wave_id(), lane = threadIdx.x & 63;
-  for (int64_t vec = (int64_t)blockIdx.x * 4 + wv; vec < count; vec += (int64_t)gridDim.x * 4) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(in + vec * REC);
-    const uint32_t mine = lane < CW ? src[lane] : 0u;
-    const float s = __uint_as_float(src[CW]);
-    const uint32_t bit0 = (uint32_t)lane * EL * BITS;
-    const int w0 = (int)(bit0 >> 5), sh = (int)(bit0 & 31);
-    const uint32_t lo = __shfl(mine, w0, 64), hi = __shfl(mine, min(w0 + 1, CW - 1), 64);
-    const uint64_t chunk = (((uint64_t)hi << 32) | lo) >> sh;
-    float x[EL];
+  const int gi = lane / G, li = lane % G;
+  constexpr int PER = U * VW;
+  const int64_t stride = (int64_t)gridDim.x * 4 * PER;
+  const uint32_t pa = (uint32_t)(4 * li) * BITS, pb = (uint32_t)(4 * li + N / 2) * BITS;
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER; v0 < count; v0 += stride) {
+    const int nrec = (int)min((int64_t)PER, count - v0);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + v0 * REC, (uint32_t)(nrec * REC));
+    uint32_t wa[U][2], wb[U][2], sw[U];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) x[e] = cent[(chunk >> (e * BITS)) & ((1u << BITS) - 1)];
-    fwht<EL>(x, lane);
-    float* dst = v + vec * ldv + lane * EL;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t base = (uint32_t)(min(u * VW + gi, nrec - 1) * REC);
+      wa[u][0] = bload4(rin, base + 4u * (pa >> 5));
+      wb[u][0] = bload4(rin, base + 4u * (pb >> 5));
+      if (TWO) {   // the next word: at most the s word
+        wa[u][1] = bload4(rin, base + 4u * ((pa >> 5) + 1));
+        wb[u][1] = bload4(rin, base + 4u * ((pb >> 5) + 1));
+      } else {
+        wa[u][1] = wb[u][1] = 0u;
+      }
+      sw[u] = bload4(rin, base + 4u * CW);
+    }
 #pragma unroll
-    for (int e = 0; e < EL; ++e) dst[e] = s * x[e];
+    for (int u = 0; u < U; ++u) {
+      const uint32_t ra = (uint32_t)(((((uint64_t)wa[u][1]) << 32) | wa[u][0]) >> (pa & 31));
+      const uint32_t rb = (uint32_t)(((((uint64_t)wb[u][1]) << 32) | wb[u][0]) >> (pb & 31));
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = cent[(ra >> (e * BITS)) & (L - 1)];
+        x[e + 4] = cent[(rb >> (e * BITS)) & (L - 1)];
+      }
+      fwht8<G>(x, lane);
+      const float s = __uint_as_float(sw[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= s;
+      if (u * VW + gi < nrec) {
+        float* dst = v + (v0 + u * VW + gi) * ldv + 4 * li;
+        store8<VEC>(dst, dst + N / 2, x);
+      }
+    }
   }
 }
 
-template <int EL>
-int launch_turbo_el(bool enc, const void* src, int64_t count, int64_t ld, void* dst, int bits,
-                    const TurboTable& tab, hipStream_t s) {
-  int64_t blocks = (count + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
-#define HQ_T(B)                                                                                  \
-  if (bits == B) {                                                                               \
-    if (enc)                                                                                     \
-      hipLaunchKernelGGL((turbo_encode_kernel<EL, B>), dim3((unsigned)blocks), dim3(256), 0, s, \
-                         static_cast<const float*>(src), count, ld, static_cast<uint8_t*>(dst), tab); \
-    else                                                                                         \
-      hipLaunchKernelGGL((turbo_decode_kernel<EL, B>), dim3((unsigned)blocks), dim3(256), 0, s, \
-                         static_cast<const uint8_t*>(src), count, static_cast<float*>(dst), ld, tab); \
-    return (int)hipGetLastError();                                                               \
+template <int G>
+int launch_turbo_g(bool enc, const void* src, int64_t count, int64_t ld, void* dst, int bits,
+                   const TurboTable& tab, hipStream_t s) {
+  constexpr int U = 2;   // vector sets per wave and iteration
+  constexpr int PER = U * (64 / G);
+  int64_t blocks = (count + 4 * PER - 1) / (4 * PER);
+  if (blocks > 4096) blocks = 4096;
+  const void* fp = enc ? src : dst;   // the f32 side
+  const bool vec = (ld % 4) == 0 && (reinterpret_cast<uintptr_t>(fp) % 16) == 0;
+#define HQ_T(B, V)                                                                                  \
+  if (enc)                                                                                          \
+    hipLaunchKernelGGL((turbo_encode_kernel<G, B, U, V>), dim3((unsigned)blocks), dim3(256), 0, s, \
+                       static_cast<const float*>(src), count, ld, static_cast<uint8_t*>(dst), tab);  \
+  else                                                                                              \
+    hipLaunchKernelGGL((turbo_decode_kernel<G, B, U, V>), dim3((unsigned)blocks), dim3(256), 0, s, \
+                       static_cast<const uint8_t*>(src), count, static_cast<float*>(dst), ld, tab);  \
+  return (int)hipGetLastError();
+#define HQ_TB(B)          \
+  if (bits == B) {        \
+    if (vec) {            \
+      HQ_T(B, true)       \
+    } else {              \
+      HQ_T(B, false)      \
+    }                     \
   }
-  HQ_T(2) HQ_T(3) HQ_T(4) HQ_T(8)
+  HQ_TB(2) HQ_TB(3) HQ_TB(4) HQ_TB(8)
+#undef HQ_TB
 #undef HQ_T
   return (int)hipErrorInvalidValue;
 }
@@ -185,9 +298,9 @@ int launch_turbo_el(bool enc, const void* src, int64_t count, int64_t ld, void* 
 int launch_turbo(bool encode, const void* src, int64_t count, int n, int64_t ld, void* dst,
                  int bits, const TurboTable& tab, hipStream_t s) {
   if (count == 0) return 0;
-  if (n == 64) return launch_turbo_el<1>(encode, src, count, ld, dst, bits, tab, s);
-  if (n == 128) return launch_turbo_el<2>(encode, src, count, ld, dst, bits, tab, s);
-  if (n == 256) return launch_turbo_el<4>(encode, src, count, ld, dst, bits, tab, s);
+  if (n == 64) return launch_turbo_g<8>(encode, src, count, ld, dst, bits, tab, s);
+  if (n == 128) return launch_turbo_g<16>(encode, src, count, ld, dst, bits, tab, s);
+  if (n == 256) return launch_turbo_g<32>(encode, src, count, ld, dst, bits, tab, s);
   return (int)hipErrorInvalidValue;
 }
 
