@@ -19,7 +19,6 @@ dominant kernel's roofline and the CPU oracle timed on a bounded sample.
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -39,12 +38,8 @@ def log(*a):
 
 
 def kernel_sources_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "quantized_moe_decode_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()
+    from quantized_moe_decode_amd.profiling import kernel_sources_digest as digest
+    return digest(ROOT)
 
 
 def load_traffic():

@@ -9,8 +9,8 @@ FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch, one rocprofv3 --pmc
 run each) into HBM bytes per launch of the named kernel.  Each counter is
 scaled by what it reads for a plain device copy of known size in the same
 run (the 1 GiB copy bench.py --calib-copy issues), so the figure is in
-bytes as the copy sees them.  The JSON records the sha256 of the kernel
-sources it was taken on; bench.py reports it only while they match.
+bytes as the copy sees them.  The JSON records the sha256 of the one-token
+kernels' sources it was taken on; bench.py reports it only while they match.
 """
 
 import csv
@@ -22,10 +22,15 @@ import sys
 CALIB_BYTES = 1 << 30
 
 
+# The sources the one-token kernels are built from (the kernels of the
+# counter summary): their file and every header it includes.
+DIGEST_SOURCES = ("moe.hip", "hfq4_device.h", "topk_device.h", "moe_common.h", "launch.h", "turbo.h")
+
+
 def kernel_sources_digest(root):
     h = hashlib.sha256()
     csrc = os.path.join(root, "quantized_moe_decode_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DIGEST_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
