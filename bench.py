@@ -607,6 +607,10 @@ def main():
                          "as one launch whose workgroups exchange the logits, h and the per-slot "
                          "down sums through tagged words (1), or as that launch's routing and "
                          "gate/up phases followed by the down kernel (2); same results")
+    ap.add_argument("--xch-min-batch", type=int, default=9,
+                    help="batched calls of at least this many tokens route by exchange (one "
+                         "router workgroup per token), smaller ones in every gate/up workgroup "
+                         "(17: never; same results)")
     ap.add_argument("--replicas", type=int, default=32,
                     help="distinct layer copies cycled through (so caches cannot serve repeats)")
     ap.add_argument("--pool", type=int, default=4096, help="distinct input tokens cycled through")
@@ -648,6 +652,7 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     q.lib.hfq4_debug_set_single_launch({3: 0, 1: 1, 2: 2}[args.launches])
+    q.lib.hfq4_debug_set_route_exchange(args.xch_min_batch)
     if args.workload == "floor":
         from quantized_moe_decode_amd import probes
         out = {"workload": "latency and bandwidth probes (floor model of the one-token layer)",

@@ -40,7 +40,8 @@ EXPORTS = [
     "moe_workspace_init", "moe_expert_decode", "moe_layer_decode", "hfq4_host_device_pointer",
     "hfq4_debug_set_trace", "hfq4_debug_set_events", "moe_layer_decode_noalloc",
     "hfq4_gemv_host", "moe_expert_decode_host", "hfq4_offload_choice",
-    "hfq4_debug_set_single_launch", "moe_place_experts", "moe_layer_decode_table",
+    "hfq4_debug_set_single_launch", "hfq4_debug_set_route_exchange", "moe_place_experts",
+    "moe_layer_decode_table",
     "turbo_record_bytes", "turbo_levels", "turbo_encode", "turbo_decode",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -95,6 +96,7 @@ def _load():
                                          I64, I32, ctypes.POINTER(ctypes.c_uint32)]),
         "hfq4_offload_choice": (I32, [ctypes.c_double, ctypes.c_double, ctypes.POINTER(I32)]),
         "hfq4_debug_set_single_launch": (I32, [I32]),
+        "hfq4_debug_set_route_exchange": (I32, [I32]),
         "moe_place_experts": (I32, [I32, I64, I64, P, ctypes.c_uint64, ctypes.c_uint64,
                                     ctypes.c_uint64, P, ctypes.POINTER(ctypes.c_uint64)]),
         "moe_layer_decode_table": (I32, [ctypes.POINTER(MoeLayerTableC), P, P, P, I32, I32, P, P, P,

@@ -177,6 +177,13 @@ int hfq4_debug_set_single_launch(int on) {
   return ok();
 }
 
+int hfq4_debug_set_route_exchange(int min_batch) {
+  if (min_batch < 2 || min_batch > HFQ4_MAX_BATCH + 1)
+    return fail(HFQ4_E_INVALID, "min_batch = %d outside [2, %d]", min_batch, HFQ4_MAX_BATCH + 1);
+  hq::set_route_exchange_min_batch(min_batch);
+  return ok();
+}
+
 int hfq4_packed_bytes(int64_t rows, int64_t K, size_t* out) {
   if (!out) return fail(HFQ4_E_INVALID, "out is NULL");
   if (rows < 0) return fail(HFQ4_E_INVALID, "rows = %lld < 0", (long long)rows);

@@ -76,6 +76,9 @@ void set_timing_events(void* start, void* stop);
 // Diagnostics: whether one-token layers of the tuned shape run as one
 // launch (the default) or as the three-launch chain.
 void set_single_launch(int mode);   // 0: three launches, 1: one, 2: two
+// Diagnostics: batches of at least b tokens route by exchange (one router
+// workgroup per token); smaller ones route in every gate/up workgroup.
+void set_route_exchange_min_batch(int b);
 // Shapes the single-launch layer (and so the pointer-table layers) serve.
 bool single_launch_shape(int E, int d, int F, int k);
 

@@ -38,6 +38,7 @@
 #include "launch.h"
 #include "moe_common.h"
 #include "topk_device.h"
+#include "xchg_device.h"
 
 namespace hq {
 
@@ -704,13 +705,9 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
 // ====================================================================== single-launch layer, one token
 
 // The one-token layer of the tuned shape in one launch.  Its workgroups
-// exchange data between the layer's phases through tagged words -- the
-// value's bits with the call's generation in the high half, written and
-// read with relaxed atomics at agent scope (coherent across the chip's
-// dies) -- instead of through kernel boundaries.  A word carries its own
-// validity, so no fence orders an exchange: a reader polls until every word
-// it needs holds this call's generation, with all of its loads in flight
-// before the first is used.
+// exchange data between the layer's phases through tagged words (the
+// protocol of xchg_device.h: generation-tagged 64-bit words, start flags,
+// bounded waits) instead of through kernel boundaries.
 //
 // Work split (256 workgroups, k in {2, 4, 8}; G = 256 / k workgroups per
 // slot): workgroup w serves slot j = w % k and block b = w / k.  Its first
@@ -743,26 +740,8 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
 // path.
 //
 // Every workgroup must be resident at once (one per compute unit, a
-// fraction of one each); every wait is bounded: after XWAIT_TICKS a
-// workgroup stops waiting, sets HFQ4_DEV_ERR_TIMEOUT and finishes with what
-// it has.
-//
-// Generations: the workspace counts the single-launch calls run on it; the
-// current call's generation is g = count + 1.  Every workgroup reads the
-// count first and then raises its start flag to g; workgroup 0 advances the
-// count only at its very end and only after it has seen every start flag at
-// g, so every workgroup of a call has read the same count.  A zeroed
-// workspace starts at count 0 with every word at generation 0, never a
-// call's.
-constexpr uint64_t XWAIT_TICKS = 200000;   // 2 ms at 100 MHz
+// fraction of one each).
 constexpr int L1_NWG = 256;                // grid of the single-launch layer
-
-__device__ __forceinline__ void put_word(uint64_t* p, uint32_t bits, uint32_t g) {
-  __hip_atomic_store(p, ((uint64_t)g << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Expert weights through a per-expert pointer table (the HBM expert cache):
 // entry e holds the device-visible addresses of expert e's gate, up and
@@ -773,33 +752,6 @@ struct TableArgs {
   const uint8_t* resident;      // [E] or null
   unsigned long long* hits;     // [2]: selections of resident / other experts, or null
 };
-
-// Poll n tagged words at src[0..n) into dst (LDS) until all hold generation
-// g, by the whole workgroup (at most PER_T words per thread, every load out
-// before any is used).  Returns whether the wait expired.
-template <int PER_T>
-__device__ __forceinline__ bool gather_words(const uint64_t* src, int n, uint32_t g, float* dst) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    uint64_t w[PER_T];
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) w[i] = get_word(src + min((int)threadIdx.x + 256 * i, n - 1));
-    int stale = 0;
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = (int)threadIdx.x + 256 * i;
-      if (idx < n) {
-        stale |= (uint32_t)(w[i] >> 32) != g;
-        dst[idx] = __uint_as_float((uint32_t)w[i]);
-      }
-    }
-    const int any_stale = __syncthreads_or(stale);
-    const int expired = __syncthreads_or(threadIdx.x == 0 &&
-                                         __builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS);
-    if (!any_stale) return false;
-    if (expired) return true;
-  }
-}
 
 // NRL = k / 2: gate/up chunks per workgroup and row loads (of 4 rows) per wave.
 // SPLIT: the kernel stops after the gate/up phase -- h goes to ws.h and the
@@ -826,9 +778,8 @@ __global__ void __launch_bounds__(256) layer1_kernel(ExpertArgs a, Ws ws, RouteA
   const int E = a.L.E, F = a.L.F, d = a.L.d;
   const int j = wg % K, b = wg / K;              // this workgroup's slot and block
   trace_point(ws.trace, TK_GATEUP, 0);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == blockDim.x - 64) {   // the last wave: wave 0's loads do not wait behind this read
     s_gen = ws.gen[0] + 1u;
-    s_started = 0;
     __hip_atomic_store(ws.xflag + wg, s_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const uint32_t g0 = __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u;
@@ -895,21 +846,8 @@ __global__ void __launch_bounds__(256) layer1_kernel(ExpertArgs a, Ws ws, RouteA
   }
   if (wv == 1 && wg == 0) {
     // every workgroup's start flag at g: all have read the count
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (true) {
-      uint32_t fw[L1_NWG / 64];
-#pragma unroll
-      for (int i = 0; i < L1_NWG / 64; ++i)
-        fw[i] = __hip_atomic_load(ws.xflag + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bool mine = true;
-#pragma unroll
-      for (int i = 0; i < L1_NWG / 64; ++i) mine &= fw[i] == g0;
-      if (__all(mine)) {
-        if (lane == 0) s_started = 1;
-        break;
-      }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > XWAIT_TICKS) break;
-    }
+    const bool seen = start_flags_seen(ws.xflag, nwg, g0);
+    if (lane == 0) s_started = seen ? 1 : 0;   // its only writer
   }
   __syncthreads();
   const uint32_t g = s_gen;

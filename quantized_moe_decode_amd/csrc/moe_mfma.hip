@@ -25,18 +25,21 @@
 // per block against constant B rows, once per staged column.  Each block's
 // product starts from a zero accumulator, so scale and zero apply exactly.
 //
-// Kernels (one HIP graph node each; kernel boundaries are the only
-// grid-wide synchronisation, so no workgroup ever waits on another):
+// Kernels (one HIP graph node each; apart from the routing exchange inside
+// the gate/up kernel, kernel boundaries are the grid-wide synchronisation):
 //   logits_mfma_kernel   router GEMV as f32 MFMA (v_mfma_f32_16x16x4_f32)
 //                        for more than LG_VALU_MAXB tokens: 16 experts x 16
 //                        tokens per tile, K split over 4 workgroups x 4
 //                        waves; writes 4 partial logit sets.  Fewer tokens
 //                        take the VALU router of moe.hip, which writes whole
 //                        logits into set 0 (lg_sets).
-//   gateup_mfma_kernel   one wave per token routes it from the partial
-//                        logits (sums + bias, top-k, weights) and stages its
-//                        activations in LDS in the MFMA operand format; the
-//                        (token, slot) pairs are grouped by expert; items of
+//   gateup_mfma_kernel   workgroup b < B routes token b from the partial
+//                        logits (sums + bias, top-k, weights) and publishes
+//                        the selection, which every workgroup gathers
+//                        (tagged words, xchg_device.h) while staging every
+//                        token's activations in LDS in the MFMA operand
+//                        format; the (token, slot) pairs are grouped by
+//                        expert; items of
 //                        (group, 16 rows) in contiguous runs per workgroup,
 //                        a quad of waves computes gate and up over both K
 //                        halves, reduces through LDS and writes
@@ -52,6 +55,7 @@
 #include "launch.h"
 #include "moe_common.h"
 #include "topk_device.h"
+#include "xchg_device.h"
 
 namespace hq {
 
@@ -448,11 +452,12 @@ __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
 // item at a time: its waves compute gate K-half 0, gate K-half 1, up K-half
 // 0 and up K-half 1 (4 blocks each, all loads in flight at once), the
 // partial tiles meet in LDS, and the first wave writes h = SiLU(g) * u.
-// Before that, wave b < B stages token b's activations in LDS and, with
-// FROM_LOGITS, routes token b from the router's partial logits (every
-// workgroup routes every token, so no launch sits between the router and
-// the experts; workgroup 0 publishes the routing).
-template <bool FROM_LOGITS>
+// Before that, the tokens' activations are staged in LDS and, with
+// FROM_LOGITS, the tokens are routed from the router's partial logits by
+// one workgroup each and the selections exchanged (no launch sits between
+// the router and the experts; the routing workgroups publish idx and wts).
+// The grid is one workgroup per compute unit, all resident at once.
+template <bool FROM_LOGITS, bool XCH>
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, BatchRouteArgs r) {
   extern __shared__ __align__(16) uint8_t dyn[];
   uint8_t* xt = dyn;                                                     // [B][XT_STRIDE]
@@ -470,36 +475,68 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   int8_t* he = reinterpret_cast<int8_t*>(hq + (size_t)P * F * 2);   // [P][F / 16] exponents
   trace_point(ws.trace, TK_GATEUP, 0);
 
-  // 1. one wave per token routes it; the activations are staged by the
-  //    idle waves B..2B-1 when there are enough of them (B <= 8), otherwise
-  //    by the routing wave, its loads overlapping the routing loads
-  const bool split_stage = FROM_LOGITS && 2 * B <= (int)(blockDim.x >> 6);
-  if (FROM_LOGITS && wv < B) {
-    const bool pub = blockIdx.x == 0;
-    const float* xb = a.x + (int64_t)wv * a.ldx;
-    uint8_t* xe = xt + wv * XT_STRIDE;
+  // 1. Routing from the router's partial logits (FROM_LOGITS).
+  //    XCH (more tokens): workgroup b < B routes token b with its wave 0
+  //    and publishes the selection as tagged words (xchg_device.h), which
+  //    every workgroup then gathers -- one top-k per token in the whole
+  //    grid; meanwhile every workgroup stages every token's activations in
+  //    LDS (wave (b + 1) % 16 takes token b, so a router workgroup's wave 0
+  //    stages only after its routing).  The call counter and start flag are
+  //    handled by the last wave, so that the routing loads do not wait
+  //    behind the counter's read.
+  //    Otherwise every workgroup routes every token itself, wave b token b;
+  //    the activations are staged by the idle waves B..2B-1 when there are
+  //    enough of them (B <= 8), else by the routing wave, its loads
+  //    overlapping the routing loads.  Routing given: wave b stages token b.
+  __shared__ float s_rt[2 * MAXP];                   // gathered routing words
+  __shared__ uint32_t s_gen;
+  __shared__ int s_started;
+  if (XCH && threadIdx.x == blockDim.x - 64) {
+    s_gen = ws.gen[0] + 1u;
+    __hip_atomic_store(ws.xflag + blockIdx.x, s_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const uint32_t g0 = XCH ? __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u : 0u;
+  const bool split_stage = FROM_LOGITS && !XCH && 2 * B <= (int)(blockDim.x >> 6);
+  // routing waves: wave 0 of workgroup b < B (XCH), or wave b of every workgroup
+  const int rb = XCH ? (wv == 0 && (int)blockIdx.x < B ? (int)blockIdx.x : -1) : (wv < B ? wv : -1);
+  if (FROM_LOGITS && rb >= 0) {
+    const bool pub = XCH || blockIdx.x == 0;
+    const bool stage_here = !XCH && !split_stage;
+    const float* xb = a.x + (int64_t)rb * a.ldx;
+    uint8_t* xe = xt + rb * XT_STRIDE;
     if (E <= 256) {
       RouteLoads<4> L;
-      route_load<4>(r, wv, L);
-      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
-      route_token<4>(r, wv, L, s_idx, s_wt, pub);
+      route_load<4>(r, rb, L);
+      if (stage_here) stage_token(xb, a.L.d, xe, &s_xs[rb]);
+      route_token<4>(r, rb, L, s_idx, s_wt, pub);
     } else if (E <= 512) {
       RouteLoads<8> L;
-      route_load<8>(r, wv, L);
-      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
-      route_token<8>(r, wv, L, s_idx, s_wt, pub);
+      route_load<8>(r, rb, L);
+      if (stage_here) stage_token(xb, a.L.d, xe, &s_xs[rb]);
+      route_token<8>(r, rb, L, s_idx, s_wt, pub);
     } else {   // 16 loads per lane: route first, then stage
       RouteLoads<16> L;
-      route_load<16>(r, wv, L);
-      route_token<16>(r, wv, L, s_idx, s_wt, pub);
-      if (!split_stage) stage_token(xb, a.L.d, xe, &s_xs[wv]);
+      route_load<16>(r, rb, L);
+      route_token<16>(r, rb, L, s_idx, s_wt, pub);
+      if (stage_here) stage_token(xb, a.L.d, xe, &s_xs[rb]);
+    }
+    if (XCH && lane < k) {
+      const int p = rb * k + lane;
+      put_word(ws.xlog + p, (uint32_t)s_idx[p], g0);
+      put_word(ws.xlog + P + p, __float_as_uint(s_wt[p]), g0);
     }
   }
   {
-    // the staging wave of token b: wave B + b (split) or wave b
-    const int b = split_stage ? wv - B : wv;
-    if ((split_stage || !FROM_LOGITS) && b >= 0 && b < B)
+    // the token this wave stages: (wv + 15) % 16 (XCH), wave B + b (split),
+    // wave b (routing given)
+    const int b = XCH ? (wv + 15) & 15 : split_stage ? wv - B : wv;
+    if ((XCH || split_stage || !FROM_LOGITS) && b >= 0 && b < B)
       stage_token(a.x + (int64_t)b * a.ldx, a.L.d, xt + b * XT_STRIDE, &s_xs[b]);
+  }
+  if (XCH && blockIdx.x == 0 && wv == 1) {
+    // every workgroup's start flag at g: all have read the call counter
+    const bool seen = start_flags_seen(ws.xflag, (int)gridDim.x, g0);
+    if (lane == 0) s_started = seen ? 1 : 0;   // its only writer
   }
   if (!FROM_LOGITS && (int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
@@ -515,6 +552,12 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
         if (b < B) s_blk[b][wv] = make_float2(-(1024.f * sa[i] + 8.f * sv[i]), s_xs[b] * sv[i]);
       }
     }
+  }
+  if (XCH) {
+    const bool late = gather_words<1>(ws.xlog, 2 * P, s_gen, s_rt);
+    if (late && threadIdx.x == 0)
+      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)threadIdx.x < P) s_idx[threadIdx.x] = __float_as_int(s_rt[threadIdx.x]);
   }
   // routing from top-k holds k distinct experts per token
   build_groups_mm(s_idx, P, k, E, G, GS, ws.err, !FROM_LOGITS && blockIdx.x == 0, !FROM_LOGITS);
@@ -643,6 +686,14 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
     }
     __syncthreads();   // red is reused by the next round
     it = next;
+  }
+  if (XCH && blockIdx.x == 0 && threadIdx.x == 0) {
+    // a workgroup that had not started by now would read the counter after
+    // this store: never advance it then (the call reports a time-out)
+    if (s_started)
+      ws.gen[0] = s_gen;
+    else
+      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   trace_point(ws.trace, TK_GATEUP, 5);
 }
@@ -866,17 +917,27 @@ int launch_route_batched(const RouteArgs& ra, const float* part, uint32_t* err, 
   return (int)hipGetLastError();
 }
 
+// Batches of at least this many tokens route by exchange (one router
+// workgroup per token) instead of in every workgroup.
+static int g_xch_min_batch = 9;
+void set_route_exchange_min_batch(int b) { g_xch_min_batch = b; }
+
 int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, const RouteArgs* ra, hipStream_t s) {
   const size_t shx = (size_t)a.B * XT_STRIDE;
-  if (ra) {
+  if (ra && a.B >= g_xch_min_batch && nwg <= XG_MAX) {
     const BatchRouteArgs r{ws.logits, ra->bias, ra->E, ra->B, ra->k, ra->idx_out, ra->wts_out,
                            ra->logits_out, nullptr, nullptr, ws.err, get_trace()};
-    if (int e = allow_lds(gateup_mfma_kernel<true>, shx)) return e;
-    hipLaunchKernelGGL(gateup_mfma_kernel<true>, dim3(nwg), dim3(1024), shx, s, a, ws, r);
+    if (int e = allow_lds(gateup_mfma_kernel<true, true>, shx)) return e;
+    hipLaunchKernelGGL((gateup_mfma_kernel<true, true>), dim3(nwg), dim3(1024), shx, s, a, ws, r);
+  } else if (ra) {
+    const BatchRouteArgs r{ws.logits, ra->bias, ra->E, ra->B, ra->k, ra->idx_out, ra->wts_out,
+                           ra->logits_out, nullptr, nullptr, ws.err, get_trace()};
+    if (int e = allow_lds(gateup_mfma_kernel<true, false>, shx)) return e;
+    hipLaunchKernelGGL((gateup_mfma_kernel<true, false>), dim3(nwg), dim3(1024), shx, s, a, ws, r);
   } else {
     const BatchRouteArgs r{};
-    if (int e = allow_lds(gateup_mfma_kernel<false>, shx)) return e;
-    hipLaunchKernelGGL(gateup_mfma_kernel<false>, dim3(nwg), dim3(1024), shx, s, a, ws, r);
+    if (int e = allow_lds(gateup_mfma_kernel<false, false>, shx)) return e;
+    hipLaunchKernelGGL((gateup_mfma_kernel<false, false>), dim3(nwg), dim3(1024), shx, s, a, ws, r);
   }
   int err = (int)hipGetLastError();
   if (err) return err;

@@ -122,6 +122,48 @@ def test_batched_fused_equals_two_call_bitwise(q, B, E, skew):
     assert torch.equal(torch.sort(sel, dim=1, descending=True).values, top)
 
 
+@pytest.mark.parametrize("B,E,skew", [(2, 256, False), (5, 512, True), (8, 1024, False),
+                                      (12, 512, True), (16, 64, False)])
+def test_route_exchange_equals_per_workgroup_routing(q, B, E, skew):
+    """Routing by exchange (one router workgroup per token, selections
+    gathered through tagged words) and routing in every gate/up workgroup
+    give the same bits at every batch size, with batched calls of the other
+    mode and one-token calls sharing the workspace in between, and report no
+    device error."""
+    d, k = 2048, 8
+    bias = synth.zipf_bias(9, E) if skew else None
+    say("route exchange vs per-workgroup B=%d E=%d skew=%s" % (B, E, skew))
+    L, cache = _layer(q, 27, E, d, bias=bias)
+    x = synth.activations(torch, "cuda", 500 + B, 3 * B, d)
+    res = synth.activations(torch, "cuda", 600 + B, B, d)
+    ws = q.new_workspace(L, B, k)
+    outs = {}
+    try:
+        for mb in (2, 17, 2):                     # exchange, per workgroup, exchange again
+            q.lib.hfq4_debug_set_route_exchange(mb)
+            got = []
+            for t in range(3):
+                got.append(tuple(v.clone() for v in
+                                 q.moe_layer_decode(L, x[t * B:(t + 1) * B], k, ws, residual=res)))
+                q.moe_layer_decode(L, x[t:t + 1], k, ws)   # a one-token call in between
+            torch.cuda.synchronize()
+            assert q.workspace_error(ws) == 0, mb
+            outs.setdefault(mb, []).append(got)
+    finally:
+        q.lib.hfq4_debug_set_route_exchange(9)
+    ref = outs[17][0]
+    for runs in outs.values():
+        for got in runs:
+            for a, b in zip(ref, got):
+                for u, v in zip(a, b):
+                    assert torch.equal(u, v)
+    i, w, y = ref[0]
+    err, amb = oracle_layer_check(x[:B].cpu().numpy(), L.Wr.cpu().numpy(), bias, cache, k,
+                                  i.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy(),
+                                  residual=res.cpu().numpy())
+    assert amb == 0 and err <= REL_L2_TOL, (amb, err)
+
+
 def test_batched_duplicates_and_invalid(q):
     """Caller routing with a repeated expert inside a token and an index out
     of range: the repeat counts as its own slot, the bad slot adds nothing
