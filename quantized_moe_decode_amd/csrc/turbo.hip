@@ -124,7 +124,10 @@ __device__ __forceinline__ void store8(float* a, float* b, const float (&x)[8]) 
   }
 }
 
-// Encode.  A wave holds 64 / G vectors at once (G = n / 8 lanes each) and
+// Encode.  The nearest level is the number of thresholds below the rotated
+// value: a binary search over the thresholds in LDS, or for 8-bit codes a
+// bucket table built in LDS per workgroup (3 LDS reads instead of 8).
+// A wave holds 64 / G vectors at once (G = n / 8 lanes each) and
 // takes U such sets per iteration, every load of the iteration issued before
 // the first is used (a vector index past the end reads the last vector
 // again and writes nothing).  Norms are G-lane sums; each lane's two runs of
@@ -138,11 +141,38 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   constexpr int N = 8 * G, L = 1 << BITS, VW = 64 / G;
   constexpr int CW = N * BITS / 32, RW = CW + 1;   // code words, record words
   constexpr int WW = U * VW * RW;                  // record words of one wave iteration
+  constexpr bool LUT = BITS == 8;                  // bucketed search (8 bits)
+  constexpr int NBK = LUT ? TURBO_LUT_BUCKETS : 1;
   __shared__ uint32_t pk[4][WW];
-  __shared__ float thr[L], cent[L];
-  for (int i = threadIdx.x; i < L; i += blockDim.x) {
-    cent[i] = tab.cent[i];
+  __shared__ float thr[L + 1], cent[L];
+  __shared__ uint8_t bcnt[NBK];                    // thresholds in the buckets before bucket k
+  __shared__ int tbk[LUT ? L : 1];                 // bucket of threshold t
+  for (int i = threadIdx.x; i < L + 1; i += blockDim.x) {
+    if (i < L) cent[i] = tab.cent[i];
     thr[i] = i < L - 1 ? tab.thr[i] : INFINITY;
+  }
+  auto bucket = [&](float r) {
+    const float f = fminf(fmaxf(floorf((r - tab.lut_lo) * tab.lut_inv_w), 0.f), (float)(NBK - 1));
+    return (int)f;   // NaN -> 0 (fmaxf returns the number)
+  };
+  bool lut = false;
+  if (LUT && tab.lut_ok) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < L; t += blockDim.x) tbk[t] = t < L - 1 ? bucket(thr[t]) : NBK;
+    __syncthreads();
+    // bcnt[k] = the number of thresholds whose bucket is below k (buckets
+    // are monotone in the value, so those are exactly the ones below any
+    // value of bucket k); a bucket holding three would break the search
+    // below, so it turns the table off
+    for (int kb = threadIdx.x; kb < NBK; kb += blockDim.x) {
+      int lo = 0;
+      for (int step = L / 2; step >= 1; step >>= 1)
+        if (tbk[lo + step - 1] < kb) lo += step;
+      bcnt[kb] = (uint8_t)lo;
+    }
+    int bad = 0;
+    for (int t = threadIdx.x; t + 2 < L - 1; t += blockDim.x) bad |= tbk[t] == tbk[t + 2];
+    lut = !__syncthreads_or(bad);
   }
   __syncthreads();
   const int wv = wave_id(), lane = threadIdx.x & 63;
@@ -175,9 +205,16 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         int lo = 0;
+        if (LUT && lut) {
+          // the count below the value's bucket, plus the (at most two)
+          // thresholds of that bucket that lie below the value
+          const int c = bcnt[bucket(x[u][e])];
+          lo = c + (thr[c] < x[u][e]) + (thr[c + 1] < x[u][e]);
+        } else {
 #pragma unroll
-        for (int step = L / 2; step >= 1; step >>= 1)
-          if (thr[lo + step - 1] < x[u][e]) lo += step;
+          for (int step = L / 2; step >= 1; step >>= 1)
+            if (thr[lo + step - 1] < x[u][e]) lo += step;
+        }
         const uint32_t code = norm > 0.f ? (uint32_t)lo : 0u;
         const float c = cent[code];
         cc = __builtin_fmaf(c, c, cc);
