@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "turbo.h"
 
 namespace hq {
 
@@ -105,6 +104,7 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  float* y, int64_t ldy, Ws ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // TurboQuant: encode (f32 [count][ld] -> records) or decode (records -> f32).
+struct TurboTable;   // turbo.h
 int launch_turbo(bool encode, const void* src, int64_t count, int n, int64_t ld, void* dst,
                  int bits, const TurboTable& tab, hipStream_t s);
 // One token of the tuned shape with expert weights through a pointer table

@@ -27,6 +27,7 @@
 
 #include "hfq4_device.h"
 #include "launch.h"
+#include "turbo.h"
 
 namespace hq {
 namespace {

@@ -24,7 +24,7 @@ CALIB_BYTES = 1 << 30
 
 # The sources the one-token kernels are built from (the kernels of the
 # counter summary): their file and every header it includes.
-DIGEST_SOURCES = ("moe.hip", "hfq4_device.h", "topk_device.h", "moe_common.h", "launch.h", "turbo.h",
+DIGEST_SOURCES = ("moe.hip", "hfq4_device.h", "topk_device.h", "moe_common.h", "launch.h",
                   "xchg_device.h")
 
 
