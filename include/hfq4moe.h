@@ -92,9 +92,9 @@ extern "C" {
 #define HFQ4_DEV_ERR_INDEX     1u  /* an expert index outside [0, E); its slot is skipped */
 #define HFQ4_DEV_ERR_TIMEOUT   2u  /* a workgroup of a launch whose workgroups exchange data
                                       (pointer-table layers, the one- and two-launch one-token
-                                      forms, routing of 2..16 tokens) waited more than 2 ms for
-                                      another: the call's outputs are undefined and the workspace
-                                      must be zeroed again before its next use */
+                                      forms, the routing exchange of larger batches) waited more
+                                      than 2 ms for another: the call's outputs are undefined and
+                                      the workspace must be zeroed again before its next use */
 #define HFQ4_DEV_ERR_NONFINITE 4u  /* a non-finite router logit was seen */
 
 /* Layer flags */
@@ -386,12 +386,12 @@ int hfq4_debug_set_trace(void* dev, size_t bytes);
  * exists to compare them and is process-wide. */
 int hfq4_debug_set_single_launch(int on);
 
-/* Diagnostics: batched calls (moe_layer_decode) of at least min_batch
- * tokens (2 <= min_batch <= HFQ4_MAX_BATCH + 1; default 9) route by
- * exchange -- one workgroup per token runs the top-k and the gate/up
- * workgroups gather the selections through tagged words -- and smaller
- * ones route every token in every gate/up workgroup.  Same bits either
- * way; process-wide. */
+/* Diagnostics: batched calls (moe_layer_decode) of at least
+ * max(min_batch, 5) tokens (2 <= min_batch <= HFQ4_MAX_BATCH + 1; default
+ * 9) route by exchange -- one workgroup per token runs the top-k and the
+ * gate/up workgroups gather the selections through tagged words, whose
+ * generation the router launch advances -- and smaller ones route every
+ * token in every gate/up workgroup.  Same bits either way; process-wide. */
 int hfq4_debug_set_route_exchange(int min_batch);
 
 /* Diagnostics: hipEvent_t handles (cast to void*) recorded when each

@@ -1147,7 +1147,7 @@ int launch_route(const float* Wr, const float* bias, int E, int d, const float* 
                  int B, int k, int32_t* idx, float* wts, float* logits_out, Ws ws, hipStream_t s) {
   RouteArgs a{Wr, bias, E, d, x, ldx, B, k, idx, wts, logits_out};
   if (B >= 2) {
-    if (int e = launch_logits_batched(a, ws.logits, s)) return e;
+    if (int e = launch_logits_batched(a, ws.logits, nullptr, s)) return e;
     return launch_route_batched(a, ws.logits, ws.err, s);
   }
   int err = launch_logits_valu(a, ws.logits, E, s);
@@ -1298,7 +1298,8 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
     // the same router and routing functions as moe_route_topk, so the
     // two-call path gives the same bits; on the fast shape the gate/up
     // kernel routes the tokens itself
-    if (int e = launch_logits_batched(ra, ws.logits, s)) return e;
+    const bool xch = fast && batched_route_exchange(B);
+    if (int e = launch_logits_batched(ra, ws.logits, xch ? ws.gen : nullptr, s)) return e;
     ExpertArgs a{L, x, ldx, B, k, idx, wts, residual, y, ldy};
     if (fast) return launch_experts_batched(a, ws, num_cus(), &ra, s);
     if (int e = launch_route_batched(ra, ws.logits, ws.err, s)) return e;

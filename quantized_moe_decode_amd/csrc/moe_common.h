@@ -57,7 +57,13 @@ __host__ __device__ inline int lg_sets(int B) { return B <= LG_VALU_MAXB ? 1 : L
 // The VALU router for 1..LG_VALU_MAXB tokens: logits of token b at
 // out[b * ldl + e] (ldl = E for one token, lg_stride(E) for partial set 0).
 int launch_logits_valu(const RouteArgs& ra, float* out, int ldl, hipStream_t s);
-int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s);
+// gen (or null): the router also advances the workspace's call counter,
+// whose new value the following gate/up kernel's routing exchange uses as
+// this call's generation.
+int launch_logits_batched(const RouteArgs& ra, float* part, uint32_t* gen, hipStream_t s);
+// Whether a fused batched call of B tokens on the fast shape routes by
+// exchange (one router workgroup per token) on this device.
+bool batched_route_exchange(int B);
 // Top-k and weights from the partial logits, one wave per token (routing
 // only).
 int launch_route_batched(const RouteArgs& ra, const float* part, uint32_t* err, hipStream_t s);

@@ -247,10 +247,13 @@ __device__ void build_groups_mm(const int* s_idx, int P, int k, int E, GroupTab&
 // operands use the same K assignment.  The four waves of a workgroup take
 // consecutive quarters of the split and meet in LDS in a fixed order.
 __global__ void __launch_bounds__(256) logits_mfma_kernel(RouteArgs a, float* __restrict__ part,
-                                                          uint64_t* trace) {
+                                                          uint64_t* trace, uint32_t* gen) {
   __shared__ f32x4 red[4][64];
   const int wg = blockIdx.x + gridDim.x * blockIdx.y;
   trace_point_at(trace, TK_LOGITS, wg, 0);
+  // the call counter for the gate/up kernel's routing exchange: one writer,
+  // read after this launch ends
+  if (gen && wg == 0 && threadIdx.x == 0) gen[0] = gen[0] + 1u;
   const int wv = wave_id(), lane = threadIdx.x & 63;
   const int n16 = lane & 15, c = lane >> 4;
   const int rt = blockIdx.x, ks = blockIdx.y;
@@ -456,7 +459,7 @@ __global__ void __launch_bounds__(64) route_topk_kernel(BatchRouteArgs r) {
 // FROM_LOGITS, the tokens are routed from the router's partial logits by
 // one workgroup each and the selections exchanged (no launch sits between
 // the router and the experts; the routing workgroups publish idx and wts).
-// The grid is one workgroup per compute unit, all resident at once.
+// The grid is one workgroup per compute unit.
 template <bool FROM_LOGITS, bool XCH>
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, BatchRouteArgs r) {
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -481,21 +484,17 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
   //    every workgroup then gathers -- one top-k per token in the whole
   //    grid; meanwhile every workgroup stages every token's activations in
   //    LDS (wave (b + 1) % 16 takes token b, so a router workgroup's wave 0
-  //    stages only after its routing).  The call counter and start flag are
-  //    handled by the last wave, so that the routing loads do not wait
-  //    behind the counter's read.
+  //    stages only after its routing).  The generation of the words is the
+  //    call counter the router launch has just advanced, so no workgroup
+  //    waits for another to start: every wait is for the router
+  //    workgroups, the lowest-numbered ones.
   //    Otherwise every workgroup routes every token itself, wave b token b;
   //    the activations are staged by the idle waves B..2B-1 when there are
   //    enough of them (B <= 8), else by the routing wave, its loads
   //    overlapping the routing loads.  Routing given: wave b stages token b.
   __shared__ float s_rt[2 * MAXP];                   // gathered routing words
-  __shared__ uint32_t s_gen;
-  __shared__ int s_started;
-  if (XCH && threadIdx.x == blockDim.x - 64) {
-    s_gen = ws.gen[0] + 1u;
-    __hip_atomic_store(ws.xflag + blockIdx.x, s_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const uint32_t g0 = XCH ? __builtin_amdgcn_readfirstlane(ws.gen[0]) + 1u : 0u;
+  // this call's generation: the router launch just advanced the counter
+  const uint32_t g0 = XCH ? __builtin_amdgcn_readfirstlane(ws.gen[0]) : 0u;
   const bool split_stage = FROM_LOGITS && !XCH && 2 * B <= (int)(blockDim.x >> 6);
   // routing waves: wave 0 of workgroup b < B (XCH), or wave b of every workgroup
   const int rb = XCH ? (wv == 0 && (int)blockIdx.x < B ? (int)blockIdx.x : -1) : (wv < B ? wv : -1);
@@ -533,11 +532,6 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
     if ((XCH || split_stage || !FROM_LOGITS) && b >= 0 && b < B)
       stage_token(a.x + (int64_t)b * a.ldx, a.L.d, xt + b * XT_STRIDE, &s_xs[b]);
   }
-  if (XCH && blockIdx.x == 0 && wv == 1) {
-    // every workgroup's start flag at g: all have read the call counter
-    const bool seen = start_flags_seen(ws.xflag, (int)gridDim.x, g0);
-    if (lane == 0) s_started = seen ? 1 : 0;   // its only writer
-  }
   if (!FROM_LOGITS && (int)threadIdx.x < P) s_idx[threadIdx.x] = a.idx[threadIdx.x];
   __syncthreads();
   trace_point(ws.trace, TK_GATEUP, 2);
@@ -554,7 +548,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
     }
   }
   if (XCH) {
-    const bool late = gather_words<1>(ws.xlog, 2 * P, s_gen, s_rt);
+    const bool late = gather_words<1>(ws.xlog, 2 * P, g0, s_rt);
     if (late && threadIdx.x == 0)
       __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)threadIdx.x < P) s_idx[threadIdx.x] = __float_as_int(s_rt[threadIdx.x]);
@@ -686,14 +680,6 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
     }
     __syncthreads();   // red is reused by the next round
     it = next;
-  }
-  if (XCH && blockIdx.x == 0 && threadIdx.x == 0) {
-    // a workgroup that had not started by now would read the counter after
-    // this store: never advance it then (the call reports a time-out)
-    if (s_started)
-      ws.gen[0] = s_gen;
-    else
-      __hip_atomic_fetch_or(ws.err, 2u /*HFQ4_DEV_ERR_TIMEOUT*/, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   trace_point(ws.trace, TK_GATEUP, 5);
 }
@@ -903,10 +889,13 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
 
 // ====================================================================== host
 
-int launch_logits_batched(const RouteArgs& ra, float* part, hipStream_t s) {
-  if (lg_sets(ra.B) == 1) return launch_logits_valu(ra, part, lg_stride(ra.E), s);
+int launch_logits_batched(const RouteArgs& ra, float* part, uint32_t* gen, hipStream_t s) {
+  if (lg_sets(ra.B) == 1) {
+    if (gen) return (int)hipErrorInvalidValue;   // the exchange comes with the matrix-core router
+    return launch_logits_valu(ra, part, lg_stride(ra.E), s);
+  }
   hipLaunchKernelGGL(logits_mfma_kernel, dim3((ra.E + 15) / 16, LG_KS), dim3(256), 0, s, ra, part,
-                     get_trace());
+                     get_trace(), gen);
   return (int)hipGetLastError();
 }
 
@@ -921,10 +910,13 @@ int launch_route_batched(const RouteArgs& ra, const float* part, uint32_t* err, 
 // workgroup per token) instead of in every workgroup.
 static int g_xch_min_batch = 9;
 void set_route_exchange_min_batch(int b) { g_xch_min_batch = b; }
+bool batched_route_exchange(int B) {
+  return B >= g_xch_min_batch && lg_sets(B) > 1 && num_cus() <= XG_MAX;
+}
 
 int launch_experts_batched(const ExpertArgs& a, Ws ws, int nwg, const RouteArgs* ra, hipStream_t s) {
   const size_t shx = (size_t)a.B * XT_STRIDE;
-  if (ra && a.B >= g_xch_min_batch && nwg <= XG_MAX) {
+  if (ra && batched_route_exchange(a.B) && nwg == num_cus()) {
     const BatchRouteArgs r{ws.logits, ra->bias, ra->E, ra->B, ra->k, ra->idx_out, ra->wts_out,
                            ra->logits_out, nullptr, nullptr, ws.err, get_trace()};
     if (int e = allow_lds(gateup_mfma_kernel<true, true>, shx)) return e;

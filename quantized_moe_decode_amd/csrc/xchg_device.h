@@ -8,12 +8,14 @@
 // generation, with all of its loads in flight before the first is used.
 //
 // Generations: the workspace counts the calls of the exchanging kernels run
-// on it; a call's generation is g = count + 1.  Every workgroup reads the
-// count first and then raises its start flag to g; workgroup 0 advances the
-// count only at its very end and only after it has seen every start flag
-// at g, so every workgroup of a call has read the same count.  A zeroed
-// workspace starts at count 0 with every word at generation 0, never a
-// call's.
+// on it.  Where a launch of the same call precedes the exchanging one (the
+// batched router before the batched gate/up kernel), that launch advances
+// the count and the exchanging kernel takes the new count as g.  A single
+// launch takes g = count + 1: every workgroup reads the count first and
+// then raises its start flag to g, and workgroup 0 advances the count only
+// at its very end and only after it has seen every start flag at g, so
+// every workgroup of the call has read the same count.  A zeroed workspace
+// starts at count 0 with every word at generation 0, never a call's.
 //
 // Every workgroup of such a launch must be resident at once; every wait is
 // bounded: after XWAIT_TICKS a waiter stops, the call reports
