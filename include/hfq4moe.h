@@ -209,7 +209,8 @@ int moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
  * [0, E) sets HFQ4_DEV_ERR_INDEX and contributes nothing.
  * x: f32 [batch][ldx]; idx: int32 [batch][k]; wts: f32 [batch][k];
  * residual: f32 [batch][ldy] or NULL; y: f32 [batch][ldy], must not
- * overlap x.  d <= 2048, F <= 2048, d % 4 == 0, F % 4 == 0.
+ * overlap x.  d <= 2048, F <= 2048, d % 4 == 0, F % 4 == 0, and
+ * batch * k <= 128 (token, slot) pairs (HFQ4_E_UNSUPPORTED otherwise).
  * For 1792 < d <= 2048, F = 512, k <= 8 the work runs on tuned kernels:
  * one token on the VALU (f16 dot products), 2..16 tokens on MFMA matrix
  * cores (each expert a small GEMM over the tokens that chose it).  The two

@@ -308,6 +308,34 @@ def test_tiny_all_k_and_batches(qs):
             assert amb == 0 and err <= REL_L2_TOL, (B, k, err)
 
 
+@pytest.mark.parametrize("E,k,B", [(32, 9, 1), (32, 12, 3), (32, 16, 8), (16, 16, 2), (64, 16, 5),
+                                   (48, 11, 11)])
+def test_top_k_above_eight(qs, E, k, B):
+    """k from 9 to the maximum of 16 (the generic kernels), including k = E
+    (every expert selected) and batch * k at its limit of 128 pairs, fused
+    and two-call, against the oracle."""
+    q = qs
+    d, F, seed = 256, 128, 61
+    say("top-%d of %d, %d tokens" % (k, E, B))
+    layer = q.synthetic.build_layer(torch, seed, 0, E, d, F)
+    cache = ExpertCache(torch, "cuda", seed, 0, d, F)
+    x = synth.activations(torch, "cuda", 62 + k, B, d)
+    r = synth.activations(torch, "cuda", 63 + k, B, d)
+    ws = q.new_workspace(layer, B, k)
+    i1, w1, y1 = q.moe_layer_decode(layer, x, k, ws, residual=r)
+    i1, w1, y1 = i1.clone(), w1.clone(), y1.clone()
+    i2, w2 = q.moe_route_topk(layer.Wr, x, k, ws=ws)
+    y2 = q.moe_expert_decode(layer, x, i2, w2, ws, residual=r)
+    torch.cuda.synchronize()
+    assert q.workspace_error(ws) == 0
+    assert torch.equal(i1, i2) and torch.equal(w1, w2)
+    assert torch.equal(y1, y2)
+    err, amb = oracle_layer_check(x.cpu().numpy(), layer.Wr.cpu().numpy(), None, cache, k,
+                                  i1.cpu().numpy(), w1.cpu().numpy(), y1.cpu().numpy(),
+                                  residual=r.cpu().numpy())
+    assert amb == 0 and err <= REL_L2_TOL, (err, amb)
+
+
 def test_expert_decode_bad_index_skipped(qs):
     q = qs
     say("expert decode bad index")
