@@ -368,7 +368,10 @@ def bench_offload(args, torch, q):
     L = q.synthetic.build_layer(torch, 0, 30, EH, D, F, bias=synth.zipf_bias(0, EH),
                                 host_mapped=True)
     xs = synth.activations(torch, "cuda", 6, N, D)
-    m = measure_routes(torch, L, xs, K_TOP)
+    nthreads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit() and int(os.environ["OMP_NUM_THREADS"]) > 0:
+        nthreads = min(nthreads, int(os.environ["OMP_NUM_THREADS"]))
+    m = measure_routes(torch, L, xs, K_TOP, nthreads=nthreads, host_kernels=("avx512", "avx2"))
     best = min(m["pcie_s_per_step"], m["cpu_s_per_step"])
     out = _base(args, N, 3, best, m["expert_bytes_per_step"] / best / 1e9,
                 "host-resident expert layer (d=2048, FFN 512, 512 experts, top-8, Zipf router), "
@@ -376,14 +379,44 @@ def bench_offload(args, torch, q):
                 "fresh tokens" % N)
     out["offload"] = {k: (round(v, 8) if isinstance(v, float) else v) for k, v in m.items()}
     out["offload"]["rule"] = "CPU only when at least 15% faster than PCIe"
-    out["offload"]["cpu_threads"] = len(os.sched_getaffinity(0))
+    out["offload"]["cpu_threads"] = nthreads
     out["offload"]["cpu_model"] = _cpu_model()
-    out["roofline"] = {"bound": "pcie", "achieved": round(m["pcie_expert_gbs"], 2),
-                       "peak": round(max(zc, dma), 2), "unit": "GB/s",
-                       "frac": round(m["pcie_expert_gbs"] / max(zc, dma), 4), "traffic": None,
-                       "kernel": "PCIe route: whole layer step (router, top-k + gate/up, down)",
-                       "pcie_zero_copy_gbs": round(zc, 2), "pcie_dma_gbs": round(dma, 2)}
+    pcie_roof = {"bound": "pcie", "achieved": round(m["pcie_expert_gbs"], 2),
+                 "peak": round(max(zc, dma), 2), "unit": "GB/s",
+                 "frac": round(m["pcie_expert_gbs"] / max(zc, dma), 4), "traffic": None,
+                 "kernel": "PCIe route: whole layer step (router, top-k + gate/up, down)",
+                 "pcie_zero_copy_gbs": round(zc, 2), "pcie_dma_gbs": round(dma, 2)}
+    host_gbs = _host_read_rate(torch, nthreads)
+    cpu_roof = {"bound": "host-dram", "achieved": round(m["cpu_expert_gbs"], 2),
+                "peak": round(host_gbs, 2), "unit": "GB/s",
+                "frac": round(m["cpu_expert_gbs"] / host_gbs, 4), "traffic": None,
+                "kernel": "CPU route: whole layer step (router on the GPU, routing and x to the "
+                          "host, experts on %d host threads (%s), y back); peak = a %d-thread "
+                          "read of 1 GiB of pinned host memory" % (nthreads, m["host_kernel"],
+                                                                    nthreads)}
+    if m["route"] == "cpu":
+        out["roofline"], out["roofline_other_route"] = cpu_roof, pcie_roof
+    else:
+        out["roofline"], out["roofline_other_route"] = pcie_roof, cpu_roof
     return out
+
+
+def _host_read_rate(torch, nthreads):
+    """GB/s of a multi-threaded read (a sum) of 1 GiB of pinned host memory."""
+    old = torch.get_num_threads()
+    torch.set_num_threads(nthreads)
+    try:
+        buf = torch.ones(1 << 28, dtype=torch.float32, pin_memory=True)
+        best = None
+        for _ in range(4):
+            t0 = time.perf_counter()
+            float(buf.sum())
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        del buf
+        return (1 << 30) / best / 1e9
+    finally:
+        torch.set_num_threads(old)
 
 
 def bench_cache(args, torch, q):

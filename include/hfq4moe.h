@@ -339,9 +339,11 @@ int turbo_decode(const void* in, size_t in_bytes, int64_t count, int n, int bits
 /* ------------------------------------------------------------ host CPU execution */
 
 /* Dequantizing GEMV on the host CPU [CPUEXEC] [HFQ]: the same result as
- * hfq4_gemv (y[b] = residual[b] + W x[b]), computed in f32 with FMA (AVX2
- * where the CPU has it) on `nthreads` host threads (0 = one per hardware
- * thread; a pool created on first use serves every later call).  Every
+ * hfq4_gemv (y[b] = residual[b] + W x[b]), computed in f32 with FMA
+ * (AVX-512 or AVX2 where the CPU has it) on `nthreads` host threads (0 =
+ * one per CPU in the calling process's affinity mask, at most
+ * OMP_NUM_THREADS when that is set and at most 64; a pool created on first
+ * use serves every later call).  Every
  * pointer is host memory (pinned or pageable); nothing touches a GPU and
  * the call returns when y is written.  Each output is summed by one thread
  * in a fixed order, so results do not depend on nthreads.  batch 1..16,
@@ -367,6 +369,14 @@ int moe_expert_decode_host(const moe_layer* L, const float* x, int64_t ldx, int 
  * (cpu_seconds * 1.15 <= pcie_seconds), else 0: the decision leans to the
  * PCIe path.  Times must be positive and finite. */
 int hfq4_offload_choice(double pcie_seconds, double cpu_seconds, int* use_cpu);
+
+/* Diagnostics: the row kernel of hfq4_gemv_host and moe_expert_decode_host
+ * for later calls (process-wide): kernel = 0 the best this CPU has (the
+ * default), 1 AVX-512, 2 AVX2 + FMA, 3 portable C++.  HFQ4_E_UNSUPPORTED
+ * if the CPU lacks the instructions.  *in_use (may be NULL) receives the
+ * kernel calls now use (1..3).  Results agree to f32 rounding across
+ * kernels; each kernel alone is independent of the thread count. */
+int hfq4_debug_set_host_kernel(int kernel, int* in_use);
 
 /* Testing hook: make the device check see `arch` instead of the real
  * device ("" or NULL restores the real query).  Lets the refusal on a

@@ -41,7 +41,7 @@ EXPORTS = [
     "hfq4_debug_set_trace", "hfq4_debug_set_events", "moe_layer_decode_noalloc",
     "hfq4_gemv_host", "moe_expert_decode_host", "hfq4_offload_choice",
     "hfq4_debug_set_single_launch", "hfq4_debug_set_route_exchange", "moe_place_experts",
-    "moe_layer_decode_table",
+    "moe_layer_decode_table", "hfq4_debug_set_host_kernel",
     "turbo_record_bytes", "turbo_levels", "turbo_encode", "turbo_decode",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -97,6 +97,7 @@ def _load():
         "hfq4_offload_choice": (I32, [ctypes.c_double, ctypes.c_double, ctypes.POINTER(I32)]),
         "hfq4_debug_set_single_launch": (I32, [I32]),
         "hfq4_debug_set_route_exchange": (I32, [I32]),
+        "hfq4_debug_set_host_kernel": (I32, [I32, ctypes.POINTER(I32)]),
         "moe_place_experts": (I32, [I32, I64, I64, P, ctypes.c_uint64, ctypes.c_uint64,
                                     ctypes.c_uint64, P, ctypes.POINTER(ctypes.c_uint64)]),
         "moe_layer_decode_table": (I32, [ctypes.POINTER(MoeLayerTableC), P, P, P, I32, I32, P, P, P,
@@ -445,6 +446,18 @@ def hfq4_gemv_host(W, rows, K, x, residual=None, y=None, nthreads=0):
     _check(lib.hfq4_gemv_host(wp, rows, K, xp, xa2.strides[0] // 4, batch, rp, ldr, yp,
                               ya2.strides[0] // 4, int(nthreads)))
     return y
+
+
+HOST_KERNELS = {"best": 0, "avx512": 1, "avx2": 2, "portable": 3}
+
+
+def set_host_kernel(name="best"):
+    """Row kernel of the host CPU entry points for later calls (process-wide):
+    'best' (the default), 'avx512', 'avx2' or 'portable'.  Returns the name
+    of the kernel now in use; raises Hfq4Error if the CPU lacks it."""
+    used = ctypes.c_int(0)
+    _check(lib.hfq4_debug_set_host_kernel(HOST_KERNELS[name], ctypes.byref(used)))
+    return {v: k for k, v in HOST_KERNELS.items()}[used.value]
 
 
 class HostMoeLayer:

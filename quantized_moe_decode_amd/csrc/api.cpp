@@ -452,6 +452,15 @@ int moe_expert_decode_host(const moe_layer* L, const float* x, int64_t ldx, int 
   return ok();
 }
 
+int hfq4_debug_set_host_kernel(int kernel, int* in_use) {
+  if (kernel < 0 || kernel > 3)
+    return fail(HFQ4_E_INVALID, "host kernel %d outside [0, 3]", kernel);
+  if (!hq::set_host_kernel(kernel))
+    return fail(HFQ4_E_UNSUPPORTED, "this CPU lacks the instructions of host kernel %d", kernel);
+  if (in_use) *in_use = hq::host_kernel_in_use();
+  return ok();
+}
+
 int moe_place_experts(int mode, int64_t layers, int64_t E, const uint64_t* heat,
                       uint64_t expert_bytes, uint64_t fixed_bytes, uint64_t budget_bytes,
                       uint8_t* resident, uint64_t* placed_bytes) {

@@ -1,5 +1,5 @@
-// HFQ4 expert execution on the host CPU (x86-64, AVX2 + FMA, with a
-// portable fallback): the other side of host-resident experts.
+// HFQ4 expert execution on the host CPU (x86-64: AVX-512, or AVX2 + FMA,
+// with a portable fallback): the other side of host-resident experts.
 //
 // Host-resident experts can be computed where they live instead of being
 // read over PCIe by a GPU kernel: the hipfire expert-offload explainer,
@@ -7,11 +7,16 @@
 // runs on the CPU only when that is at least 15% faster (its "D2 measured
 // default"); the Strata user report, sections "1. Strata 是什么" and "2.
 // 硬件配置", runs the experts that miss its VRAM cache on the CPU with AVX-2
-// kernels.  Here the same HFQ4 arithmetic as the GPU path, in f32:
-//   sum_i (zero + scale q_i) x_i = zero * sum_i x_i + scale * sum_i q_i x_i
-// per 256-weight block, with the activation de-interleaved once per call so
-// that the low nibbles of 8 code bytes meet 8 even elements and the high
-// nibbles 8 odd ones (no shuffles in the inner loop).
+// kernels.  Here the same HFQ4 arithmetic as the GPU path, in f32, with the
+// activation de-interleaved once per call so that the low nibbles of a run
+// of code bytes meet the even elements and the high nibbles the odd ones
+// (no shuffles of x in the inner loops).  Two row kernels:
+//   * AVX-512: each block's 16 dequantized values zero + scale q are a
+//     register table that the nibbles index (a lane permute), products
+//     summed across the row;
+//   * AVX2 (and the portable one): per 256-weight block
+//     sum_i (zero + scale q_i) x_i = zero * sum_i x_i + scale * sum_i q_i x_i.
+// The best the CPU has runs unless a diagnostic call forces another.
 //
 // Threads: a small pool of host threads, created on first use and kept
 // until the process ends, takes contiguous row ranges; every output element
@@ -21,6 +26,7 @@
 #include <cmath>
 #include <condition_variable>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -29,6 +35,9 @@
 
 #if defined(__x86_64__)
 #include <immintrin.h>
+#endif
+#if defined(__linux__)
+#include <sched.h>
 #endif
 
 #include "host_cpu.h"
@@ -184,23 +193,10 @@ __attribute__((target("avx2,fma"))) float block_dot_avx2(const uint8_t* codes, c
 
 using BlockDot = float (*)(const uint8_t*, const float*, const float*);
 
-BlockDot pick_block_dot() {
-#if defined(__x86_64__)
-  __builtin_cpu_init();
-  if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) return block_dot_avx2;
-#endif
-  return block_dot_scalar;
-}
-
-BlockDot block_dot() {
-  static const BlockDot f = pick_block_dot();
-  return f;
-}
-
-// Rows [r0, r1) of y = W x (+ residual) for one prepared vector.
-void rows_dot(const uint8_t* W, int64_t r0, int64_t r1, int nb, const XPrep& xp, const float* res,
-              float* y) {
-  const BlockDot dot = block_dot();
+// Rows [r0, r1) of y = W x (+ residual) for one prepared vector, one block
+// dot product at a time: per block scale * sum q x + zero * sum x.
+void rows_dot_blocks(BlockDot dot, const uint8_t* W, int64_t r0, int64_t r1, int nb,
+                     const XPrep& xp, const float* res, float* y) {
   const int64_t rowb = (int64_t)nb * BLKB;
   for (int64_t r = r0; r < r1; ++r) {
     const uint8_t* row = W + r * rowb;
@@ -217,6 +213,82 @@ void rows_dot(const uint8_t* W, int64_t r0, int64_t r1, int nb, const XPrep& xp,
   }
 }
 
+#if defined(__x86_64__)
+// AVX-512 rows: per block a 16-entry table of the block's dequantized values
+// zero + scale * q (one f32 fma each, the format's definition), looked up by
+// the code nibbles with a lane permute (its index is the low 4 bits of each
+// 32-bit lane, so the low nibble needs no mask), and the products
+// accumulated in four vectors across the whole row; one horizontal sum per
+// row.  A permute pair covers 16 code bytes = 32 weights.
+__attribute__((target("avx512f"))) void rows_dot_avx512(const uint8_t* W, int64_t r0, int64_t r1,
+                                                        int nb, const XPrep& xp, const float* res,
+                                                        float* y) {
+  const __m512 iota = _mm512_setr_ps(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  const int64_t rowb = (int64_t)nb * BLKB;
+  for (int64_t r = r0; r < r1; ++r) {
+    const uint8_t* row = W + r * rowb;
+    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
+    __m512 a2 = _mm512_setzero_ps(), a3 = _mm512_setzero_ps();
+    for (int b = 0; b < nb; ++b) {
+      const uint8_t* blk = row + (int64_t)b * BLKB;
+      float scale, zero;
+      std::memcpy(&scale, blk, 4);
+      std::memcpy(&zero, blk + 4, 4);
+      const __m512 tab = _mm512_fmadd_ps(iota, _mm512_set1_ps(scale), _mm512_set1_ps(zero));
+      const uint8_t* codes = blk + 8;
+      const float* xe = &xp.xe[(size_t)b * HALF];
+      const float* xo = &xp.xo[(size_t)b * HALF];
+      for (int j = 0; j < HALF; j += 32) {
+        const __m512i v0 =
+            _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + j)));
+        const __m512i v1 =
+            _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + j + 16)));
+        a0 = _mm512_fmadd_ps(_mm512_permutexvar_ps(v0, tab), _mm512_loadu_ps(xe + j), a0);
+        a1 = _mm512_fmadd_ps(_mm512_permutexvar_ps(_mm512_srli_epi32(v0, 4), tab),
+                             _mm512_loadu_ps(xo + j), a1);
+        a2 = _mm512_fmadd_ps(_mm512_permutexvar_ps(v1, tab), _mm512_loadu_ps(xe + j + 16), a2);
+        a3 = _mm512_fmadd_ps(_mm512_permutexvar_ps(_mm512_srli_epi32(v1, 4), tab),
+                             _mm512_loadu_ps(xo + j + 16), a3);
+      }
+    }
+    const float acc =
+        _mm512_reduce_add_ps(_mm512_add_ps(_mm512_add_ps(a0, a1), _mm512_add_ps(a2, a3)));
+    y[r] = (res ? res[r] : 0.f) + acc;
+  }
+}
+#endif
+
+bool cpu_has(int kernel) {
+  if (kernel == HOST_KERNEL_SCALAR) return true;
+#if defined(__x86_64__)
+  __builtin_cpu_init();
+  if (kernel == HOST_KERNEL_AVX512) return __builtin_cpu_supports("avx512f");
+  if (kernel == HOST_KERNEL_AVX2)
+    return __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+#endif
+  return false;
+}
+
+int best_kernel() {
+  static const int k = cpu_has(HOST_KERNEL_AVX512) ? HOST_KERNEL_AVX512
+                       : cpu_has(HOST_KERNEL_AVX2) ? HOST_KERNEL_AVX2
+                                                   : HOST_KERNEL_SCALAR;
+  return k;
+}
+
+std::atomic<int> g_host_kernel{HOST_KERNEL_BEST};
+
+void rows_dot(const uint8_t* W, int64_t r0, int64_t r1, int nb, const XPrep& xp, const float* res,
+              float* y) {
+  int kern = g_host_kernel.load(std::memory_order_relaxed);
+  if (kern == HOST_KERNEL_BEST) kern = best_kernel();
+#if defined(__x86_64__)
+  if (kern == HOST_KERNEL_AVX512) return rows_dot_avx512(W, r0, r1, nb, xp, res, y);
+  if (kern == HOST_KERNEL_AVX2) return rows_dot_blocks(block_dot_avx2, W, r0, r1, nb, xp, res, y);
+#endif
+  rows_dot_blocks(block_dot_scalar, W, r0, r1, nb, xp, res, y);
+}
+
 inline void split(int64_t n, int t, int nt, int64_t& lo, int64_t& hi) {
   lo = n * t / nt;
   hi = n * (t + 1) / nt;
@@ -226,9 +298,35 @@ inline float silu_mul_host(float g, float u) { return g / (1.f + std::exp(-g)) *
 
 }  // namespace
 
+bool set_host_kernel(int kernel) {
+  if (kernel < HOST_KERNEL_BEST || kernel > HOST_KERNEL_SCALAR) return false;
+  if (kernel != HOST_KERNEL_BEST && !cpu_has(kernel)) return false;
+  g_host_kernel.store(kernel, std::memory_order_relaxed);
+  return true;
+}
+
+int host_kernel_in_use() {
+  const int k = g_host_kernel.load(std::memory_order_relaxed);
+  return k == HOST_KERNEL_BEST ? best_kernel() : k;
+}
+
 int host_threads_default() {
-  const unsigned n = std::thread::hardware_concurrency();
-  return n == 0 ? 1 : (int)(n > 64 ? 64 : n);
+  // the CPUs this process may run on (a container or a scheduler may grant
+  // far fewer than the machine has), at most OMP_NUM_THREADS when that is
+  // set, at most 64: more threads than CPUs would leave spinning workers
+  // competing with the ones that compute
+  int n = 0;
+#if defined(__linux__)
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  if (sched_getaffinity(0, sizeof set, &set) == 0) n = CPU_COUNT(&set);
+#endif
+  if (n <= 0) n = (int)std::thread::hardware_concurrency();
+  if (const char* e = std::getenv("OMP_NUM_THREADS")) {
+    const int m = std::atoi(e);
+    if (m > 0 && m < n) n = m;
+  }
+  return n < 1 ? 1 : (n > 64 ? 64 : n);
 }
 
 void gemv_host(const uint8_t* W, int64_t rows, int64_t K, const float* x, int64_t ldx, int batch,

@@ -13,6 +13,14 @@ struct HostLayer {
   int64_t stride_gate, stride_up, stride_down;
 };
 
+// Row kernels (set_host_kernel): the best the CPU has, or one forced.
+enum { HOST_KERNEL_BEST = 0, HOST_KERNEL_AVX512 = 1, HOST_KERNEL_AVX2 = 2, HOST_KERNEL_SCALAR = 3 };
+// Forces a row kernel for later calls (process-wide); false if the value is
+// out of range or the CPU lacks the instructions.
+bool set_host_kernel(int kernel);
+// The row kernel calls use now (1..3).
+int host_kernel_in_use();
+
 // Threads a call uses when the caller passes 0.
 int host_threads_default();
 

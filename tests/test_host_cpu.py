@@ -9,6 +9,7 @@ weights from the seeded generators.  Bars: relative L2 <= 2e-3 per token
 of the thread count, and the 15% rule of the route choice.
 """
 
+import ctypes
 import math
 
 import numpy as np
@@ -26,11 +27,23 @@ def q():
     return q
 
 
+@pytest.fixture(params=["avx512", "avx2", "portable"])
+def kern(q, request):
+    """Each host row kernel in turn (skipped where the CPU lacks it); the
+    best one is restored afterwards."""
+    try:
+        q.set_host_kernel(request.param)
+    except q.Hfq4Error:
+        pytest.skip("this CPU lacks the %s kernel" % request.param)
+    yield request.param
+    q.set_host_kernel("best")
+
+
 @pytest.mark.parametrize("rows,K,batch,resid", [(1, 256, 1, False), (7, 128, 1, True),
                                                 (33, 300, 2, False), (2051, 2048, 1, True),
                                                 (129, 1000, 3, True), (5, 5000, 1, False),
                                                 (512, 2048, 16, False), (2048, 512, 4, True)])
-def test_gemv_host_vs_oracle(q, rows, K, batch, resid):
+def test_gemv_host_vs_oracle(q, kern, rows, K, batch, resid):
     rng = np.random.default_rng(rows * 31 + K)
     W = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
     P = hfq4.quantize_rows(W)
@@ -45,7 +58,7 @@ def test_gemv_host_vs_oracle(q, rows, K, batch, resid):
         assert e <= REL_L2_TOL and e < 1e-5, (b, e)
 
 
-def test_gemv_host_exact_grid_and_padding(q):
+def test_gemv_host_exact_grid_and_padding(q, kern):
     # block C dequantizes exactly (sum -34 with x = 1); a K = 128 row pads
     # its block with zeros that must not contribute
     i = np.arange(256)
@@ -57,7 +70,7 @@ def test_gemv_host_exact_grid_and_padding(q):
     assert y[0, 0] == 8 * 120.0
 
 
-def test_gemv_host_thread_count_independent(q):
+def test_gemv_host_thread_count_independent(q, kern):
     rng = np.random.default_rng(3)
     W = (rng.standard_normal((777, 2048)) * 0.02).astype(np.float32)
     P = hfq4.quantize_rows(W)
@@ -84,7 +97,7 @@ def _host_layer(q, seed, E, d, F):
 
 @pytest.mark.parametrize("E,d,F,k,B", [(8, 256, 128, 2, 1), (16, 2048, 512, 8, 1),
                                        (12, 1000, 300, 3, 4), (9, 2048, 512, 8, 2)])
-def test_expert_decode_host_vs_oracle(q, E, d, F, k, B):
+def test_expert_decode_host_vs_oracle(q, kern, E, d, F, k, B):
     L, exps = _host_layer(q, E + d, E, d, F)
     rng = np.random.default_rng(E * d)
     x = rng.standard_normal((B, d)).astype(np.float32)
@@ -110,6 +123,36 @@ def test_expert_decode_host_bad_index(q):
     assert err & q.HFQ4_DEV_ERR_INDEX
     ref = 0.6 * moe.expert_forward(exps[3], x[0].astype(np.float64))
     assert rel_l2(y[0], ref) <= REL_L2_TOL
+
+
+def test_host_kernels_agree(q):
+    # the row kernels differ only in f32 rounding order
+    rng = np.random.default_rng(11)
+    W = (rng.standard_normal((300, 2048)) * 0.02).astype(np.float32)
+    P = hfq4.quantize_rows(W)
+    x = rng.standard_normal((2, 2048)).astype(np.float32)
+    ys = {}
+    for name in ("avx512", "avx2", "portable"):
+        try:
+            q.set_host_kernel(name)
+        except q.Hfq4Error:
+            continue
+        ys[name] = q.hfq4_gemv_host(P, 300, 2048, x)
+    q.set_host_kernel("best")
+    assert "portable" in ys
+    for name, y in ys.items():
+        assert rel_l2(y, ys["portable"]) < 1e-6, name
+
+
+def test_host_kernel_selection(q):
+    best = q.set_host_kernel("best")
+    assert best in ("avx512", "avx2", "portable")
+    assert q.set_host_kernel("portable") == "portable"
+    assert q.set_host_kernel("best") == best
+    used = ctypes.c_int(0)
+    for bad in (-1, 4):
+        assert q.lib.hfq4_debug_set_host_kernel(bad, ctypes.byref(used)) == q.HFQ4_E_INVALID
+    assert q.set_host_kernel("best") == best
 
 
 def test_offload_choice_rule(q):
