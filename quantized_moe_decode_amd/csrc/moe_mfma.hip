@@ -686,18 +686,28 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
 
 // ====================================================================== down + combine
 
-// A workgroup owns DR_ROWS = 16 output rows of every token.  It stages h of
-// all (token, slot) pairs once: the gate/up kernel wrote h as f16 in the
-// MFMA operand order with one power-of-two exponent per 16-row tile; here
-// each entry is brought to its block's exponent (the largest of the
-// block's 16 tiles) and stored in LDS.  Then its 16 waves take the expert groups in
-// turn (wave w: groups w, w + 16, ...): per group one 16-row MFMA tile over
-// K = F, A = the group's pairs, B = 16 rows of the expert's down matrix,
-// with the next group's weights in flight while the current one computes.
-// Each wave adds w_p * (down h_p) into its own [token][row] slice of LDS;
-// at the end the slices are summed in wave order onto the residual.  The
-// per-slot sum therefore needs no second kernel and no per-slot buffer.
-constexpr int DR_ROWS = 16;
+// A workgroup owns DR_ROWS = 8 output rows of every token (d = 2048: 256
+// workgroups, one per compute unit).  It stages h of all (token, slot)
+// pairs once: the gate/up kernel wrote h as f16 in the MFMA operand order
+// with one power-of-two exponent per 16-row tile; here each entry is
+// brought to its block's exponent (the largest of the block's 16 tiles) and
+// stored in LDS.  Then its 16 waves take the expert groups in turn (wave w:
+// groups w, w + 16, ...): per group one MFMA tile over K = F, A = the
+// group's pairs, B = the block's 8 rows of the expert's down matrix (the
+// tile's other 8 rows load nothing), with the next group's weights in
+// flight while the current one computes.  Each wave adds w_p * (down h_p)
+// into its own [token][row] slice of LDS; at the end the slices are summed
+// in wave order onto the residual.  The per-slot sum therefore needs no
+// second kernel and no per-slot buffer.
+//
+// Every workgroup brings in all of h (B k F f16 values: 128 KB at 16
+// tokens) besides its rows' weights, and a compute unit pulls a bounded
+// number of bytes per unit of time (about 25 - 40 GB/s at these
+// latencies), so the kernel is bound by the bytes per compute unit: half
+// of the MFMA tile's rows left empty buys 256 workgroups instead of 128,
+// half the weight bytes per unit (0.4 - 0.6 us faster per step at 2 - 16
+// tokens than 16-row blocks).
+constexpr int DR_ROWS = 8;    // output rows per workgroup (<= 16, the MFMA tile's rows)
 constexpr int DR_WAVES = 16;
 constexpr int DR_ENT_ITERS = MAXP * 64 / (64 * DR_WAVES);   // h entries per thread (F = 512)
 
@@ -764,10 +774,11 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   constexpr int64_t ROWB = 2 * BLK_BYTES;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
   const int row = r0 + n16;
+  const bool row_live = n16 < DR_ROWS && row < d;   // tile rows past the block load nothing
   u32x4 cdA[2][2], cdB[2][2];   // [block][half], two buffers
   u32x2 hdA[2], hdB[2];
   auto issue = [&](int u, u32x4 (&cd)[2][2], u32x2 (&hd)[2]) {
-    const uint32_t ro = row < d ? (uint32_t)(G.gexp[u] * a.L.sd + (int64_t)row * ROWB) : a.L.down_bytes;
+    const uint32_t ro = row_live ? (uint32_t)(G.gexp[u] * a.L.sd + (int64_t)row * ROWB) : a.L.down_bytes;
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
       hd[bk] = bload8(rd, ro + bk * BLK_BYTES);
@@ -857,9 +868,11 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     }
     // the pairs of a group belong to distinct tokens: the lanes of one
     // update touch distinct slots
+    if (n16 < DR_ROWS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (pc[i] >= 0) ys[wv][pc[i] / k][n16] += s_w[pc[i]] * acc[i];
+      for (int i = 0; i < 4; ++i)
+        if (pc[i] >= 0) ys[wv][pc[i] / k][n16] += s_w[pc[i]] * acc[i];
+    }
   };
   // buffers A and B hold groups u and u + 16; each is refilled with the
   // group two steps ahead as soon as it has been used
