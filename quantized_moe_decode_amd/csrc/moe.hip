@@ -657,6 +657,14 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
       c[t][r] = bload16(rd, base + r * ROWB + coff);
     }
   }
+  // the residual of the wave's rows, needed only at the end, goes out now
+  // (a null residual is a descriptor of 0 bytes: the loads read 0)
+  const uint32_t resb = a.res ? 4u * (uint32_t)d : 0u;
+  const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, resb);
+  float resv[FAST_ROWS];
+#pragma unroll
+  for (int r = 0; r < FAST_ROWS; ++r)
+    resv[r] = as_f32(bload4(rres, r0 + r < d ? 4u * (uint32_t)(r0 + r) : resb));
   trace_point(ws.trace, TK_DOWN, 1);
   if (stager) {
     float buf[32];
@@ -696,7 +704,7 @@ __global__ void __launch_bounds__(256) down_fast_kernel(ExpertArgs a, Ws ws) {
     for (int j = 0; j < MAXK / 2; ++j)
       sj[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps[j >> 2][r]), 16 * (j & 3)));
     const int rr = r0 + r;
-    if (lane == 0 && rr < d) a.y[rr] = combine_slots(sj, wj, lj, k, a.res ? a.res[rr] : 0.f);
+    if (lane == 0 && rr < d) a.y[rr] = combine_slots(sj, wj, lj, k, resv[r]);
   }
   trace_point(ws.trace, TK_DOWN, 3);
 }

@@ -750,6 +750,13 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     const int el = threadIdx.x + 64 * DR_WAVES * j;
     hv[j] = bload16(rh, el < NENT ? (uint32_t)el * 16u : hbytes);
   }
+  // the residual of output (token b, row r) for thread b * DR_ROWS + r,
+  // needed only at the end, goes out now (a null residual reads 0)
+  const int b_out = threadIdx.x / DR_ROWS, rr_out = r0 + (int)threadIdx.x - b_out * DR_ROWS;
+  const bool y_out = b_out < B && rr_out < d;
+  const uint32_t resb = a.res ? 4u * (uint32_t)((int64_t)(B - 1) * a.ldy + d) : 0u;
+  const float res_out = as_f32(bload4(make_rsrc(a.res, resb),
+                                      y_out ? 4u * (uint32_t)((int64_t)b_out * a.ldy + rr_out) : resb));
   if ((int)threadIdx.x < GT_WORDS) reinterpret_cast<uint32_t*>(&G)[threadIdx.x] = gword;
   if ((int)threadIdx.x < P) s_w[threadIdx.x] = wword;
   if ((int)threadIdx.x < EW) s_he[threadIdx.x] = eword;
@@ -887,15 +894,12 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
   __syncthreads();
 
   // 5. y = residual + the waves' slices, in wave order
-  if ((int)threadIdx.x < B * DR_ROWS) {
-    const int b = threadIdx.x / DR_ROWS, r = threadIdx.x - b * DR_ROWS;
-    const int rr = r0 + r;
-    if (rr < d) {
-      float y = a.res ? a.res[b * a.ldy + rr] : 0.f;
+  if (y_out) {
+    const int r = rr_out - r0;
+    float y = res_out;
 #pragma unroll
-      for (int w = 0; w < DR_WAVES; ++w) y += ys[w][b][r];
-      a.y[b * a.ldy + rr] = y;
-    }
+    for (int w = 0; w < DR_WAVES; ++w) y += ys[w][b_out][r];
+    a.y[(int64_t)b_out * a.ldy + rr_out] = y;
   }
   trace_point(ws.trace, TK_DOWN, 2);
 }
