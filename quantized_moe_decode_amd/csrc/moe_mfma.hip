@@ -47,7 +47,7 @@
 //                        power-of-two exponent per (pair, 16-row tile).
 //   route_topk_kernel    routing only (moe_route_topk): the same routing
 //                        functions, one single-wave workgroup per token.
-//   down_rows_kernel     16 output rows of every token per workgroup: stages
+//   down_rows_kernel     8 output rows of every token per workgroup: stages
 //                        h of all pairs, runs every group's down tile and
 //                        sums w_p * (down h_p) over the slots onto the
 //                        residual (no per-slot buffer, no combine kernel).
