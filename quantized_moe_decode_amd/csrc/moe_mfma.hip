@@ -703,8 +703,8 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(ExpertArgs a, Ws ws, 
 // Every workgroup brings in all of h (B k F f16 values: 128 KB at 16
 // tokens) besides its rows' weights, and a compute unit pulls a bounded
 // number of bytes per unit of time (about 25 - 40 GB/s at these
-// latencies), so the kernel is bound by the bytes per compute unit: half
-// of the MFMA tile's rows left empty buys 256 workgroups instead of 128,
+// latencies), so the bytes per compute unit weigh on the time: half of
+// the MFMA tile's rows left empty buys 256 workgroups instead of 128,
 // half the weight bytes per unit (0.4 - 0.6 us faster per step at 2 - 16
 // tokens than 16-row blocks).
 constexpr int DR_ROWS = 8;    // output rows per workgroup (<= 16, the MFMA tile's rows)
