@@ -777,7 +777,8 @@ __global__ void __launch_bounds__(64 * DR_WAVES) down_rows_kernel(ExpertArgs a, 
     s_xs[p][bk] = m == H_EMPTY ? 0.f : ldexpf(1.f, m);
   }
 
-  // 2. the wave's first group: its 16 rows x 2 blocks, every load in flight
+  // 2. the wave's first group: the block's DR_ROWS rows x 2 blocks, every
+  //    load in flight
   constexpr int64_t ROWB = 2 * BLK_BYTES;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.L.down, a.L.down_bytes);
   const int row = r0 + n16;
