@@ -133,6 +133,30 @@ def test_cpu_route_matches_gpu_and_oracle(q, layers):
         assert amb == 0 and e2 <= REL_L2_TOL, e2
 
 
+def test_measure_routes_choice(q, layers):
+    """The load-time route probe: both routes timed, every host row kernel
+    the CPU has timed twice, the fastest kept selected, and the route the
+    15 % rule gives for the two times."""
+    from quantized_moe_decode_amd.offload import measure_routes
+    hbm, host, bias = layers
+    say("route probe on the 64-expert host-resident layer")
+    xs = synth.activations(torch, "cuda", 57, 6, D)
+    try:
+        m = measure_routes(torch, host, xs, K, nthreads=4, warm=1)
+        by = m["cpu_us_per_step_by_host_kernel"]
+        assert "portable" in by and m["host_kernel"] in by
+        assert all(len(v) == 2 and min(v) > 0 for v in by.values())
+        assert min(by[m["host_kernel"]]) == min(min(v) for v in by.values())
+        assert abs(m["cpu_s_per_step"] * 1e6 - min(by[m["host_kernel"]])) <= 0.1
+        assert m["pcie_s_per_step"] > 0 and m["steps"] == 6
+        assert m["expert_bytes_per_step"] == K * host.expert_bytes()
+        assert m["route"] == ("cpu" if q.hfq4_offload_choice(m["pcie_s_per_step"],
+                                                              m["cpu_s_per_step"]) else "pcie")
+        assert q.set_host_kernel(m["host_kernel"]) == m["host_kernel"]
+    finally:
+        q.set_host_kernel("best")
+
+
 @pytest.mark.parametrize("En,k", [(256, 8), (100, 4), (1024, 8), (512, 2), (64, 8), (700, 4),
                                   (100, 6)])
 def test_single_launch_equals_three_launch(q, En, k):
