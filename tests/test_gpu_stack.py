@@ -198,7 +198,7 @@ def test_c5_mixed_stack_teacher_forced(q, B):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_host_mapped_layer_bitwise(q, B):
     """c5 layer shape (E=512, d=2048, F=512, k=8): host-mapped == HBM bits,
     and the host-mapped layer against the oracle."""
