@@ -807,8 +807,8 @@ def main():
               "event keeps the device busy while the host enqueues them")
     if args.mode == "graph":
         timing += ("; %d steps per graph, %d timed replays; warmup: %s"
-                   % (G, reps, "%d replays of the same graph" % (warm // G) if warm_graph
-                      else "%d eager steps" % warm))
+                   % (G, reps, "%d replay%s of the same graph" % (warm // G, "" if warm == G else "s")
+                      if warm_graph else "%d eager steps" % warm))
     err = q.workspace_error(ws)
     if err:
         raise SystemExit("device error word %d after timed run" % err)
