@@ -6,8 +6,9 @@
 
 Every source under csrc/ is compiled into one shared library next to this
 file (libhfq4moe.so, the decode library); the latency probes under probes/
-into a second one (libhfq4probe.so, measurement only).  All HIP code is
-built with packed-FP32 instructions disabled.
+into a second one (libhfq4probe.so, measurement only, and once more as
+libhfq4probe_kp.so with the kernel arguments preloaded into scalar
+registers).  All HIP code is built with packed-FP32 instructions disabled.
 """
 import os
 import subprocess
@@ -19,6 +20,10 @@ LIB = os.path.join(HERE, "libhfq4moe.so")
 SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "moe.hip", "moe_mfma.hip", "turbo.hip"]
 HOST_SOURCES = ["host_cpu.cpp", "placement.cpp", "turbo_tables.cpp"]   # host-only C++
 PROBE_LIB = os.path.join(HERE, "libhfq4probe.so")
+# the probes once more with kernel arguments preloaded into scalar registers
+# (measured against the default argument loads by the launch-chain probe)
+PROBE_LIB_KP = os.path.join(HERE, "libhfq4probe_kp.so")
+KP_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 PROBE_SOURCES = [os.path.join(HERE, "probes", "probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -47,9 +52,9 @@ def _host_objects(verbose):
     return objs
 
 
-def _hipcc(srcs, lib, verbose, objs=()):
+def _hipcc(srcs, lib, verbose, objs=(), extra=()):
     tmp = lib + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-x", "hip"] + srcs + ["-x", "none"] + list(objs) + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-x", "hip"] + srcs + ["-x", "none"] + list(objs) + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,6 +70,7 @@ def build(verbose=False):
     for o in objs:
         os.remove(o)
     _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_LIB_KP, verbose, extra=KP_FLAGS)
     return LIB
 
 

@@ -15,6 +15,9 @@ Measurement only: nothing here is on the decode path.
 * pingpong   a flag bounced between two workgroups with agent-scope
              atomics (one-way latency), on the same die and across dies,
              relaxed and as release/acquire with a payload;
+* chain      a graph of dependent minimal launches (each reads what the
+             previous one wrote): us per launch, with the default argument
+             loads and with the arguments preloaded (libhfq4probe_kp.so);
 * read       a plain streaming read of a large buffer (GB/s).
 """
 
@@ -23,21 +26,22 @@ import os
 
 HERE = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB_PATH = os.path.join(HERE, "libhfq4probe.so")
+LIB_PATH_KP = os.path.join(HERE, "libhfq4probe_kp.so")
 TICK_NS = 10.0   # s_memrealtime runs at 100 MHz
 
 
-def _lib():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libhfq4probe.so not built at %s -- run "
-                          "'python quantized_moe_decode_amd/build.py'" % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+def _lib(preload=False):
+    path = LIB_PATH_KP if preload else LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError("%s not built -- run 'python quantized_moe_decode_amd/build.py'" % path)
+    lib = ctypes.CDLL(path)
     P, I, U32, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
     for name, args in {"probe_chase": [P, U32, I, P, P], "probe_empty": [I, I, P],
                        "probe_pingpong": [P, P, I, I, I, I, P, P],
                        "probe_produce": [P, I, P, P], "probe_consume": [P, I, P, P, P],
                        "probe_read": [P, SZ, I, P, P],
                        "probe_exchange": [P, P, I, I, U32, I, P, I, I, P],
-                       "probe_spin": [ctypes.c_uint64, P]}.items():
+                       "probe_spin": [ctypes.c_uint64, P], "probe_chain": [P, P, I, P]}.items():
         f = getattr(lib, name)
         f.restype = I
         f.argtypes = args
@@ -199,6 +203,33 @@ def read(torch, nbytes=1 << 32, reps=5):
     return best
 
 
+def chain(torch, preload=False, launches=400, reps=20, n=256 * 64):
+    """us per launch of a HIP graph of dependent minimal launches (256
+    workgroups of 64 threads, each element read from the previous launch's
+    output), timed over replays after a first one."""
+    lib = _lib(preload)
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.zeros(n, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(launches):
+                src, dst = (a, b) if i % 2 == 0 else (b, a)
+                _ok(lib.probe_chain(_p(src), _p(dst), n, _s(torch)), "probe_chain")
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    if float(a[0]) != (reps + 1) * launches:
+        raise RuntimeError("chain probe: wrong count %s" % float(a[0]))
+    return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+
+
 def run_all(torch, log=print):
     """Every probe once; returns a dict of the numbers."""
     res = {}
@@ -209,6 +240,11 @@ def run_all(torch, log=print):
     res["boundary_gap_ns"], res["boundary_first_read_ns"] = round(gap, 1), round(rd, 1)
     log("graph boundary: %.0f ns from last producer store to first consumer start; "
         "consumer read of 256 values written on other dies %.0f ns" % (gap, rd))
+    res["chain_us_per_launch"] = round(chain(torch), 3)
+    res["chain_us_per_launch_kernarg_preload"] = round(chain(torch, preload=True), 3)
+    log("dependent minimal launches in a graph: %.2f us each; with the kernel arguments "
+        "preloaded into scalar registers %.2f us"
+        % (res["chain_us_per_launch"], res["chain_us_per_launch_kernarg_preload"]))
     eager, graph = empty(torch)
     res["empty_kernel_us_eager"], res["empty_kernel_us_graph"] = round(eager, 3), round(graph, 3)
     log("empty 256x256 kernel: %.2f us eager, %.2f us in a graph" % (eager, graph))

@@ -47,6 +47,15 @@ __global__ void empty_kernel(uint32_t* sink) {
   if (sink && threadIdx.x == 0 && blockIdx.x == 0x7fffffff) sink[0] = 1u;   // never taken
 }
 
+// One link of a chain of dependent launches: every thread reads the value
+// the previous launch wrote at its index and writes its own.  Plain pointer
+// arguments, so that a build with the kernel arguments preloaded into
+// scalar registers can preload them.
+__global__ void chain_kernel(const float* __restrict__ in, float* __restrict__ out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = in[i] + 1.f;
+}
+
 // ---------------------------------------------------------------- cross-XCD flags
 
 // Ping-pong between workgroup 0 and workgroup `partner` (both single-wave;
@@ -251,6 +260,12 @@ int probe_chase(const uint32_t* next, uint32_t start, int hops, uint64_t* out, h
 
 int probe_empty(int grid, int block, hipStream_t s) {
   hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(block), 0, s, (uint32_t*)nullptr);
+  return (int)hipGetLastError();
+}
+
+int probe_chain(const float* in, float* out, int n, hipStream_t s) {
+  if (n < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(chain_kernel, dim3((n + 63) / 64), dim3(64), 0, s, in, out, n);
   return (int)hipGetLastError();
 }
 
