@@ -552,7 +552,7 @@ def bench_turbo(args, torch, q):
     out["turbo"] = res
     out["roofline"] = {"bound": "hbm", "achieved": r4["decode_gbs"], "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": r4["decode_frac"], "traffic": None,
-                       "kernel": "turbo_decode_kernel<2, 4>"}
+                       "kernel": "turbo_decode_kernel<128, 4, true>"}
     return out
 
 

@@ -405,6 +405,13 @@ int hfq4_debug_set_single_launch(int on);
  * token in every gate/up workgroup.  Same bits either way; process-wide. */
 int hfq4_debug_set_route_exchange(int min_batch);
 
+/* Diagnostics: the TurboQuant encoder (turbo_encode) finds each nearest
+ * level through its bucket table (binary = 0, the default) or by binary
+ * search over the thresholds (binary != 0).  Same codes either way; the
+ * switch exists to test the search the encoder falls back to, and is
+ * process-wide. */
+int hfq4_debug_set_turbo_search(int binary);
+
 /* Diagnostics: hipEvent_t handles (cast to void*) recorded when each
  * later launch of the expert gate/up kernel starts and ends, so a caller
  * can time that kernel alone with hipEventElapsedTime; NULL, NULL turns it

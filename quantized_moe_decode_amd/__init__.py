@@ -41,7 +41,7 @@ EXPORTS = [
     "hfq4_debug_set_trace", "hfq4_debug_set_events", "moe_layer_decode_noalloc",
     "hfq4_gemv_host", "moe_expert_decode_host", "hfq4_offload_choice",
     "hfq4_debug_set_single_launch", "hfq4_debug_set_route_exchange", "moe_place_experts",
-    "moe_layer_decode_table", "hfq4_debug_set_host_kernel",
+    "moe_layer_decode_table", "hfq4_debug_set_host_kernel", "hfq4_debug_set_turbo_search",
     "turbo_record_bytes", "turbo_levels", "turbo_encode", "turbo_decode",
 ]
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -97,6 +97,7 @@ def _load():
         "hfq4_offload_choice": (I32, [ctypes.c_double, ctypes.c_double, ctypes.POINTER(I32)]),
         "hfq4_debug_set_single_launch": (I32, [I32]),
         "hfq4_debug_set_route_exchange": (I32, [I32]),
+        "hfq4_debug_set_turbo_search": (I32, [I32]),
         "hfq4_debug_set_host_kernel": (I32, [I32, ctypes.POINTER(I32)]),
         "moe_place_experts": (I32, [I32, I64, I64, P, ctypes.c_uint64, ctypes.c_uint64,
                                     ctypes.c_uint64, P, ctypes.POINTER(ctypes.c_uint64)]),

@@ -7,6 +7,7 @@
 // short and by how much instead of failing later).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -181,6 +182,14 @@ int hfq4_debug_set_route_exchange(int min_batch) {
   if (min_batch < 2 || min_batch > HFQ4_MAX_BATCH + 1)
     return fail(HFQ4_E_INVALID, "min_batch = %d outside [2, %d]", min_batch, HFQ4_MAX_BATCH + 1);
   hq::set_route_exchange_min_batch(min_batch);
+  return ok();
+}
+
+// Diagnostics: the TurboQuant encoder's nearest-level search by its bucket
+// table (binary = 0, the default) or by binary search over the thresholds.
+static std::atomic<int> g_turbo_binary_search{0};
+int hfq4_debug_set_turbo_search(int binary) {
+  g_turbo_binary_search.store(binary != 0 ? 1 : 0);
   return ok();
 }
 
@@ -581,7 +590,8 @@ int turbo_encode(const float* v, int64_t count, int n, int64_t ldv, int bits, vo
     return fail(HFQ4_E_INVALID, "out overlaps v");
   r = check_device();
   if (r) return r;
-  return hip_status(hq::launch_turbo(true, v, count, n, ldv, out, bits, turbo_table_for(n, bits), stream),
+  return hip_status(hq::launch_turbo(true, v, count, n, ldv, out, bits, turbo_table_for(n, bits),
+                                     g_turbo_binary_search.load() == 0, stream),
                     "turbo_encode launch");
 }
 
@@ -603,7 +613,7 @@ int turbo_decode(const void* in, size_t in_bytes, int64_t count, int n, int bits
     return fail(HFQ4_E_INVALID, "v overlaps in");
   r = check_device();
   if (r) return r;
-  return hip_status(hq::launch_turbo(false, in, count, n, ldv, v, bits, turbo_table_for(n, bits), stream),
+  return hip_status(hq::launch_turbo(false, in, count, n, ldv, v, bits, turbo_table_for(n, bits), true, stream),
                     "turbo_decode launch");
 }
 

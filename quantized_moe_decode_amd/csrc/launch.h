@@ -103,10 +103,12 @@ int launch_layer(const LayerDev& L, const float* Wr, const float* bias, const fl
                  int64_t ldx, int B, int k, int32_t* idx, float* wts, const float* residual,
                  float* y, int64_t ldy, Ws ws, hipStream_t s);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-// TurboQuant: encode (f32 [count][ld] -> records) or decode (records -> f32).
+// TurboQuant: encode (f32 [count][ld] -> records) or decode (records -> f32);
+// lut = false makes the encoder search the thresholds instead of using its
+// bucket table.
 struct TurboTable;   // turbo.h
 int launch_turbo(bool encode, const void* src, int64_t count, int n, int64_t ld, void* dst,
-                 int bits, const TurboTable& tab, hipStream_t s);
+                 int bits, const TurboTable& tab, bool lut, hipStream_t s);
 // One token of the tuned shape with expert weights through a pointer table
 // (ptr [E][3] device addresses of gate, up, down), hit counts into hits[2].
 int launch_layer_table(const LayerDev& L, const uint64_t* ptr, const uint8_t* resident,

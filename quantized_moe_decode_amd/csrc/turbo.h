@@ -10,14 +10,15 @@ namespace hq {
 struct TurboTable {
   float cent[256];
   float thr[255];
-  // Bucket index of a value r for the nearest-level search of the 8-bit
-  // codec: clamp(floor((r - lut_lo) * lut_inv_w), 0, TURBO_LUT_BUCKETS - 1);
-  // lut_ok = 0 when the buckets would be wider than the smallest gap
-  // between two thresholds (then the kernels search the thresholds).
-  float lut_lo, lut_inv_w;
+  // Bucket of a value r for the encoder's nearest-level search:
+  // clamp(fma(r, lut_a, lut_b), 0, TURBO_LUT_BUCKETS - 1) truncated (a
+  // monotone map).  lut_ok = 0 when the buckets would not be narrower than
+  // half the smallest gap between two thresholds (then the encoder
+  // searches the thresholds).
+  float lut_a, lut_b;
   int lut_ok;
 };
-constexpr int TURBO_LUT_BUCKETS = 1024;
+constexpr int TURBO_LUT_BUCKETS = 2048;
 
 // Lloyd-Max levels of the standard normal with 2^bits levels (host, f64).
 void lloyd_max_normal(int bits, double* levels);

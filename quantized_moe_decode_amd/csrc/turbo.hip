@@ -13,15 +13,21 @@
 // record is the codes packed LSB-first (code j at bits [j b, j b + b)) and
 // then s = |v| / |c| as an f32.
 //
-// n / 8 lanes per vector, eight values per lane in two runs of four, so a
-// wave holds 8, 4 or 2 vectors at once and the per-vector reductions are
-// short lane-group sums: the butterflies of spans 1, 2 and n/2 stay in a
-// lane, the others pair lane j with lane j ^ M through DPP (quad permutes,
-// row rotations) or the gfx950 row swap; every output is the same sequence
-// of exactly rounded adds and subtracts.  A wave takes two such sets per
-// iteration with all their loads in flight together.  The level table is
-// copied into LDS once per workgroup.  Both kernels are HBM streams: 4n
-// bytes of f32 on one side, n b / 8 + 4 on the other.
+// Both kernels are HBM streams (4n bytes of f32 on one side, n b / 8 + 4 on
+// the other) whose per-vector arithmetic must stay under the stream:
+//  - encode puts a vector on G = n / 32 lanes, 32 values per lane, so most
+//    of the transform stays inside a lane (butterflies of spans 1, 2, 4,
+//    n/4 and n/2) and the per-vector work (norm, square root, division) is
+//    shared by 32 values; only spans 8 .. 4 G pair lane j with lane j ^ M
+//    (M < G <= 8: DPP quad permutes, and for n = 256 a pair of row
+//    rotations).
+//  - decode, bound by its f32 stores, puts a vector on 8 lanes (n / 8
+//    values per lane, in runs of four) so that each store instruction
+//    writes 128 contiguous bytes per vector, fetches the next records
+//    before it transforms the current ones, and stores with the
+//    non-temporal hint (the output is not read back by the kernel).
+// Every butterfly is exactly rounded; the 1/sqrt(n) factor is folded into
+// the normalisation (encode) or the norm ratio (decode).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,289 +38,322 @@
 namespace hq {
 namespace {
 
-// The value of lane l ^ M in every lane: quad permutes (M = 1, 2) and row
-// rotations (M = 4, 8) by DPP, the gfx950 row swap for 16 -- VALU only,
-// no LDS crossbar.
+// The value of lane l ^ M in every lane, M = 1, 2 or 4.  M = 1, 2: quad
+// permutes.  M = 4: row_ror:12 gives every lane lane l + 4 (mod 16), then
+// row_ror:4, written only in banks 1 and 3 (the lanes with bit 2 set, whose
+// partner is lane l - 4), replaces it there.  Every lane's result is
+// written by one of the moves, so their old values are never read.
 template <int M>
-__device__ __forceinline__ float partner(float v, int lane) {
-  if (M == 16) {
-    const uint32_t b = __builtin_bit_cast(uint32_t, v);
-    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-    return (lane & 16) ? as_f32(r[0]) : as_f32(r[1]);   // r[0]: bit 4 clear, r[1]: set
-  }
-  if (M == 1) return dpp<0xB1>(v);     // quad_perm [1,0,3,2]
-  if (M == 2) return dpp<0x4E>(v);     // quad_perm [2,3,0,1]
-  if (M == 8) return dpp<0x128>(v);    // row_ror:8
-  // M = 4: row_ror:N reads lane l - N (mod 16).  Both moves run in every
-  // lane (a DPP move reading a lane that is switched off would read the
-  // fallback value), then each lane keeps its partner's.
-  const float down4 = dpp<0x124>(v), up4 = dpp<0x12C>(v);
-  return (lane & 4) ? down4 : up4;
+__device__ __forceinline__ float xlane(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  if (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xf, 0xf, true));
+  if (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xf, 0xf, true));
+  const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xf, 0xf, true);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(up, b, 0x124, 0xf, 0xA, false));
 }
 
-// Register layout of one vector of n = 8 G values in an aligned group of G
-// lanes: lane j holds the four values 4j .. 4j + 3 in x[0..3] and the four
-// values n/2 + 4j .. n/2 + 4j + 3 in x[4..7], so each 16-byte load or store
-// instruction of a wave covers contiguous memory.
-//
-// In-place orthonormal Walsh-Hadamard transform in that layout, stages in
-// order of increasing span: spans 1 and 2 inside each run of four, spans
-// 4 M (M = 1 .. G/2) between lane j and lane j ^ M, span n/2 between the
-// two runs of a lane.  Every butterfly is (a, b) -> (a + b, a - b) with a
-// the lower index, exactly rounded (a lane's new value is fma(+-1, own,
-// partner), the same single rounding); then the 1/sqrt(n) scaling.
+// Sum over the G lanes of a vector (aligned groups of 2, 4 or 8 lanes):
+// xor 1, xor 2, then the other quad of the eight (row_half_mirror).
 template <int G>
-__device__ __forceinline__ void fwht8(float (&x)[8], int lane) {
+__device__ __forceinline__ float lanes_sum(float v) {
+  v += dpp<0xB1>(v);
+  if (G >= 4) v += dpp<0x4E>(v);
+  if (G >= 8) v += dpp<0x141>(v);
+  return v;
+}
+
+// Register layout: a vector of n = G V values on an aligned group of G
+// lanes, V values per lane in runs of RL contiguous values: lane j holds
+// x[RL q + i] = value RL j + RL G q + i (q < V / RL, i < RL), each run one
+// or two 16-byte accesses.  In index bits: the low log2 RL bits are i, the
+// next log2 G bits the lane, the top bits q -- so all index bits but the
+// lane's are bits of the register index e = RL q + i.
+//
+// Walsh-Hadamard transform in place, unscaled (H with entries +-1): the
+// butterflies (a, b) -> (a + b, a - b), a the lower index, over the bits of
+// e, then one stage per lane bit, where the lane holding a keeps own +
+// partner and the one holding b partner - own (a single fma with a +-1
+// factor, exactly rounded).
+template <int G, int V>
+__device__ __forceinline__ void fwht(float (&x)[V], int lane) {
 #pragma unroll
-  for (int h = 1; h < 4; h <<= 1) {
+  for (int h = 1; h < V; h <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < V; ++e)
       if (!(e & h)) {
         const float a = x[e], b = x[e + h];
         x[e] = a + b;
         x[e + h] = a - b;
       }
   }
-#define HQ_STAGE(M)                                            \
-  if (M < G) {                                                 \
-    const float sg = (lane & (M)) ? -1.f : 1.f;                \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e)              \
-      x[e] = __builtin_fmaf(sg, x[e], partner<M>(x[e], lane)); \
+#define HQ_XSTAGE(M)                                         \
+  if (M < G) {                                               \
+    const float sg = (lane & (M)) ? -1.f : 1.f;              \
+    _Pragma("unroll") for (int e = 0; e < V; ++e)            \
+      x[e] = __builtin_fmaf(sg, x[e], xlane<M>(x[e]));       \
   }
-  HQ_STAGE(1) HQ_STAGE(2) HQ_STAGE(4) HQ_STAGE(8) HQ_STAGE(16)
-#undef HQ_STAGE
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = x[e], b = x[e + 4];
-    x[e] = a + b;
-    x[e + 4] = a - b;
-  }
-  const float inv = G == 8 ? 0.125f : G == 16 ? 0.08838834764831845f : 0.0625f;   // 1/sqrt(8 G)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= inv;
+  HQ_XSTAGE(1) HQ_XSTAGE(2) HQ_XSTAGE(4)
+#undef HQ_XSTAGE
 }
 
-// A lane's two runs of four f32 values (16-byte loads and stores when the
-// vector start is 16-byte aligned).
-template <bool VEC>
-__device__ __forceinline__ void load8(const float* a, const float* b, float (&x)[8]) {
-  if constexpr (VEC) {
-    const f32x4 p = *reinterpret_cast<const f32x4*>(a);
-    const f32x4 q = *reinterpret_cast<const f32x4*>(b);
-    x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
-    x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
-  } else {
+// A lane's runs: V / RL runs of RL f32 values starting at p, run q at
+// p + RL G q.
+template <int G, int V, int RL, bool VEC>
+__device__ __forceinline__ void load_runs(const float* p, float (&x)[V]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = a[e];
-      x[e + 4] = b[e];
+  for (int q = 0; q < V / RL; ++q) {
+    const float* r = p + RL * G * q;
+    if constexpr (VEC) {
+#pragma unroll
+      for (int h = 0; h < RL / 4; ++h) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(r + 4 * h);
+        x[RL * q + 4 * h + 0] = a.x;
+        x[RL * q + 4 * h + 1] = a.y;
+        x[RL * q + 4 * h + 2] = a.z;
+        x[RL * q + 4 * h + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RL; ++i) x[RL * q + i] = r[i];
     }
   }
 }
-template <bool VEC>
-__device__ __forceinline__ void store8(float* a, float* b, const float (&x)[8]) {
-  if constexpr (VEC) {
-    *reinterpret_cast<f32x4*>(a) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(b) = f32x4{x[4], x[5], x[6], x[7]};
-  } else {
+// Stores with the non-temporal hint.
+template <int G, int V, int RL, bool VEC>
+__device__ __forceinline__ void store_runs(float* p, const float (&x)[V]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = x[e];
-      b[e] = x[e + 4];
+  for (int q = 0; q < V / RL; ++q) {
+    float* r = p + RL * G * q;
+    if constexpr (VEC) {
+#pragma unroll
+      for (int h = 0; h < RL / 4; ++h) {
+        const f32x4 o{x[RL * q + 4 * h + 0], x[RL * q + 4 * h + 1], x[RL * q + 4 * h + 2],
+                      x[RL * q + 4 * h + 3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(r + 4 * h));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RL; ++i) __builtin_nontemporal_store(x[RL * q + i], r + i);
     }
   }
+}
+
+template <int N>
+constexpr float inv_sqrt_n() {
+  return N == 64 ? 0.125f : N == 128 ? 0.08838834764831845f : 0.0625f;
 }
 
 // Encode.  The nearest level is the number of thresholds below the rotated
-// value: a binary search over the thresholds in LDS, or for 8-bit codes a
-// bucket table built in LDS per workgroup (3 LDS reads instead of 8).
-// A wave holds 64 / G vectors at once (G = n / 8 lanes each) and
-// takes U such sets per iteration, every load of the iteration issued before
-// the first is used (a vector index past the end reads the last vector
-// again and writes nothing).  Norms are G-lane sums; each lane's two runs of
-// four codes go into the wave's records in LDS (value i's code at bits
-// [i b, i b + b) of its vector's code stream), and the iteration's records,
+// value r.  With the bucket table (lut): bucket(r) = clamp(fma(r, a, b), 0,
+// NBK - 1) truncated, the buckets narrower than half the smallest gap
+// between two thresholds, so at most one threshold m (the count of those in
+// lower buckets) can share r's bucket and one compare with it decides; the
+// entry {threshold m, level m, level m + 1} is one 16-byte LDS read.  The
+// workgroup builds the table in LDS and checks that no bucket holds two
+// thresholds; otherwise (or when asked) it searches the thresholds (binary
+// search, log2 L dependent LDS reads).
+// Layout: G = n / 32 lanes per vector, V = 32, runs of RL = 8.
+// A wave takes VW = 64 / G vectors per iteration (a vector index past the
+// end reads the last vector again and writes nothing).  Each lane's runs of
+// eight codes go into the wave's records in LDS (code i of the vector at
+// bits [i b, i b + b) of its code stream: whole words for b = 4 and 8,
+// or-ed into zeroed words otherwise), and the iteration's records,
 // contiguous in memory, leave as whole words.
-template <int G, int BITS, int U, bool VEC>
+template <int G, int BITS, bool VEC>
 __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restrict__ v, int64_t count,
                                                            int64_t ldv, uint8_t* __restrict__ out,
-                                                           TurboTable tab) {
-  constexpr int N = 8 * G, L = 1 << BITS, VW = 64 / G;
+                                                           TurboTable tab, int use_lut) {
+  constexpr int N = 32 * G, L = 1 << BITS, VW = 64 / G;
   constexpr int CW = N * BITS / 32, RW = CW + 1;   // code words, record words
-  constexpr int WW = U * VW * RW;                  // record words of one wave iteration
-  constexpr bool LUT = BITS == 8;                  // bucketed search (8 bits)
-  constexpr int NBK = LUT ? TURBO_LUT_BUCKETS : 1;
+  constexpr int WW = VW * RW;                      // record words of one wave iteration
+  constexpr int NBK = TURBO_LUT_BUCKETS;
+  constexpr bool WHOLE = BITS == 4 || BITS == 8;   // a run of eight codes fills whole words
+  constexpr int RUNW = BITS == 8 ? 2 : 1;          // words of a run's codes
   __shared__ uint32_t pk[4][WW];
-  __shared__ float thr[L + 1], cent[L];
-  __shared__ uint8_t bcnt[NBK];                    // thresholds in the buckets before bucket k
-  __shared__ int tbk[LUT ? L : 1];                 // bucket of threshold t
-  for (int i = threadIdx.x; i < L + 1; i += blockDim.x) {
-    if (i < L) cent[i] = tab.cent[i];
-    thr[i] = i < L - 1 ? tab.thr[i] : INFINITY;
-  }
-  auto bucket = [&](float r) {
-    const float f = fminf(fmaxf(floorf((r - tab.lut_lo) * tab.lut_inv_w), 0.f), (float)(NBK - 1));
-    return (int)f;   // NaN -> 0 (fmaxf returns the number)
+  __shared__ f32x4 qt[L];                          // {threshold m (inf for m = L - 1), level m, level m + 1, 0}
+  __shared__ int tbk[L];                           // bucket of threshold m (NBK for m = L - 1)
+  __shared__ uint8_t tb[NBK];                      // thresholds in the buckets below bucket k
+  const float la = tab.lut_a, lb = tab.lut_b;
+  auto bucket = [&](float r) -> uint32_t {
+    // NaN -> 0 (fmaxf returns the number); truncation of the clamped value
+    return (uint32_t)fminf(fmaxf(__builtin_fmaf(r, la, lb), 0.f), (float)(NBK - 1));
   };
-  bool lut = false;
-  if (LUT && tab.lut_ok) {
-    __syncthreads();
-    for (int t = threadIdx.x; t < L; t += blockDim.x) tbk[t] = t < L - 1 ? bucket(thr[t]) : NBK;
-    __syncthreads();
-    // bcnt[k] = the number of thresholds whose bucket is below k (buckets
-    // are monotone in the value, so those are exactly the ones below any
-    // value of bucket k); a bucket holding three would break the search
-    // below, so it turns the table off
-    for (int kb = threadIdx.x; kb < NBK; kb += blockDim.x) {
-      int lo = 0;
-      for (int step = L / 2; step >= 1; step >>= 1)
-        if (tbk[lo + step - 1] < kb) lo += step;
-      bcnt[kb] = (uint8_t)lo;
-    }
-    int bad = 0;
-    for (int t = threadIdx.x; t + 2 < L - 1; t += blockDim.x) bad |= tbk[t] == tbk[t + 2];
-    lut = !__syncthreads_or(bad);
+  for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    const float t = i < L - 1 ? tab.thr[i] : INFINITY;
+    qt[i] = f32x4{t, tab.cent[i], tab.cent[i < L - 1 ? i + 1 : i], 0.f};
+    tbk[i] = i < L - 1 ? (int)bucket(t) : NBK;
   }
   __syncthreads();
-  const int wv = wave_id(), lane = threadIdx.x & 63;
-  const int gi = lane / G, li = lane % G;          // vector of the set, lane within the vector
-  constexpr int PER = U * VW;                      // vectors per wave iteration
-  const int64_t stride = (int64_t)gridDim.x * 4 * PER;
-  const uint32_t pa = (uint32_t)(4 * li) * BITS, pb = (uint32_t)(4 * li + N / 2) * BITS;   // run bits
-  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER; v0 < count; v0 += stride) {
-    float x[U][8];
+  bool lut = false;
+  if (use_lut) {
+    for (int k = threadIdx.x; k < NBK; k += blockDim.x) {
+      int lo = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float* src = v + min(v0 + u * VW + gi, count - 1) * ldv + 4 * li;
-      load8<VEC>(src, src + N / 2, x[u]);
+      for (int step = L / 2; step >= 1; step >>= 1)
+        if (tbk[lo + step - 1] < k) lo += step;
+      tb[k] = (uint8_t)lo;
     }
-    for (int t = lane; t < WW; t += 64) pk[wv][t] = 0u;
-    __builtin_amdgcn_wave_barrier();
+    int bad = 0;
+    for (int t = threadIdx.x; t + 1 < L - 1; t += blockDim.x) bad |= tbk[t] == tbk[t + 1];
+    lut = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad)) == 0;   // uniform: one branch per iteration
+  }
+  const int wv = wave_id(), lane = threadIdx.x & 63;
+  const int gi = lane / G, li = lane % G;          // vector of the wave, lane within the vector
+  const int64_t stride = (int64_t)gridDim.x * 4 * VW;
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * VW; v0 < count; v0 += stride) {
+    float x[32];
+    load_runs<G, 32, 8, VEC>(v + min(v0 + gi, count - 1) * ldv + 8 * li, x);
+    if (!WHOLE) {
+      for (int t = lane; t < WW; t += 64) pk[wv][t] = 0u;
+    }
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float ss = 0.f;
+    for (int e = 0; e < 32; ++e) p4[e & 3] = __builtin_fmaf(x[e], x[e], p4[e & 3]);
+    const float norm = __builtin_sqrtf(lanes_sum<G>((p4[0] + p4[1]) + (p4[2] + p4[3])));
+    const bool live = norm > 0.f;
+    const float inv = live ? inv_sqrt_n<N>() / norm : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[u][e], x[u][e], ss);
-      const float norm = __builtin_sqrtf(group_sum<G>(ss));
-      const float inv = norm > 0.f ? 1.f / norm : 0.f;
+    for (int e = 0; e < 32; ++e) x[e] *= inv;
+    fwht<G, 32>(x, lane);
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t run[4][RUNW] = {};
+    auto put = [&](int e, uint32_t code, float cv) {
+      c4[e & 3] = __builtin_fmaf(cv, cv, c4[e & 3]);
+      const int bit = (e & 7) * BITS;
+      run[e >> 3][bit >> 5] |= code << (bit & 31);
+    };
+    if (lut) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[u][e] *= inv;
-      fwht8<G>(x[u], lane);
-      // nearest level: the number of thresholds strictly below r (binary search)
-      float cc = 0.f;
-      uint32_t run[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int lo = 0;
-        if (LUT && lut) {
-          // the count below the value's bucket, plus the (at most two)
-          // thresholds of that bucket that lie below the value
-          const int c = bcnt[bucket(x[u][e])];
-          lo = c + (thr[c] < x[u][e]) + (thr[c + 1] < x[u][e]);
-        } else {
-#pragma unroll
-          for (int step = L / 2; step >= 1; step >>= 1)
-            if (thr[lo + step - 1] < x[u][e]) lo += step;
-        }
-        const uint32_t code = norm > 0.f ? (uint32_t)lo : 0u;
-        const float c = cent[code];
-        cc = __builtin_fmaf(c, c, cc);
-        run[e >> 2] |= code << ((e & 3) * BITS);
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t c = tb[bucket(x[e])];
+        const f32x4 qv = qt[c];
+        const bool up = qv.x < x[e];
+        put(e, c + (up ? 1u : 0u), up ? qv.z : qv.y);
       }
-      const float cn = __builtin_sqrtf(group_sum<G>(cc));
-      const float s = norm > 0.f ? norm / cn : 0.f;
-      // the vector's record: code words, then s (the code stream ends on a
-      // word boundary, so no run spills into the s word)
-      uint32_t* rec = &pk[wv][(u * VW + gi) * RW];
+    } else {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t p = r ? pb : pa;
-        const uint64_t placed = (uint64_t)run[r] << (p & 31);
+      for (int e = 0; e < 32; ++e) {
+        int lo = 0;
+#pragma unroll
+        for (int step = L / 2; step >= 1; step >>= 1)
+          if (qt[lo + step - 1].x < x[e]) lo += step;
+        put(e, (uint32_t)lo, qt[lo].y);
+      }
+    }
+    const float cn = __builtin_sqrtf(lanes_sum<G>((c4[0] + c4[1]) + (c4[2] + c4[3])));
+    const float s = live ? norm / cn : 0.f;
+    // the vector's record: code words, then s (the code stream ends on a
+    // word boundary, so no run spills into the s word)
+    uint32_t* rec = &pk[wv][gi * RW];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t p = (uint32_t)(8 * li + 8 * G * q) * BITS;   // bit position of run q
+      if (WHOLE) {
+#pragma unroll
+        for (int w = 0; w < RUNW; ++w) rec[(p >> 5) + w] = live ? run[q][w] : 0u;
+      } else {
+        const uint64_t placed = (uint64_t)(live ? run[q][0] : 0u) << (p & 31);
         atomicOr(rec + (p >> 5), (uint32_t)placed);
         if ((placed >> 32) != 0) atomicOr(rec + (p >> 5) + 1, (uint32_t)(placed >> 32));
       }
-      if (li == 0) rec[CW] = __float_as_uint(s);
     }
+    if (li == 0) rec[CW] = __float_as_uint(s);
     __builtin_amdgcn_wave_barrier();
-    const int words = (int)min((int64_t)PER, count - v0) * RW;
+    const int words = (int)min((int64_t)VW, count - v0) * RW;
     uint32_t* dst = reinterpret_cast<uint32_t*>(out + v0 * (4 * RW));
     for (int t = lane; t < words; t += 64) dst[t] = pk[wv][t];
     __builtin_amdgcn_wave_barrier();
   }
 }
 
-// Decode: the same vector layout; each lane reads the code words holding its
-// two runs (one word each, two for 3-bit codes) and the s word, every load
-// of the iteration in flight together.
-template <int G, int BITS, int U, bool VEC>
+// Decode.  Layout: G = 8 lanes per vector, V = n / 8 values per lane in
+// runs of RL = 4.  A wave takes U sets of eight vectors per iteration; each
+// lane reads the code words holding its runs (the next word too where a run
+// may span two) and the s word, and fetches those of the next iteration
+// before it transforms and stores the current ones, so the loads wait for
+// nothing but themselves.
+template <int N, int BITS, bool VEC>
 __global__ void __launch_bounds__(256) turbo_decode_kernel(const uint8_t* __restrict__ in,
                                                            int64_t count, float* __restrict__ v,
                                                            int64_t ldv, TurboTable tab) {
-  constexpr int N = 8 * G, L = 1 << BITS, VW = 64 / G;
+  constexpr int G = 8, V = N / G, RL = 4, NR = V / RL, U = 2;
+  constexpr int L = 1 << BITS, VW = 64 / G, PER = U * VW;
   constexpr int CW = N * BITS / 32, REC = 4 * (CW + 1);
-  constexpr bool TWO = (32 % (4 * BITS)) != 0;   // a run may straddle two words
+  constexpr bool TWO = BITS == 3;                  // a run of four 3-bit codes may span two words
   __shared__ float cent[L];
   for (int i = threadIdx.x; i < L; i += blockDim.x) cent[i] = tab.cent[i];
   __syncthreads();
   const int wv = wave_id(), lane = threadIdx.x & 63;
   const int gi = lane / G, li = lane % G;
-  constexpr int PER = U * VW;
   const int64_t stride = (int64_t)gridDim.x * 4 * PER;
-  const uint32_t pa = (uint32_t)(4 * li) * BITS, pb = (uint32_t)(4 * li + N / 2) * BITS;
-  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER; v0 < count; v0 += stride) {
-    const int nrec = (int)min((int64_t)PER, count - v0);
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + v0 * REC, (uint32_t)(nrec * REC));
-    uint32_t wa[U][2], wb[U][2], sw[U];
+  uint32_t w0[U][NR], w1[U][NR], sw[U];
+  auto fetch = [&](int64_t b0) {   // the records of vectors b0 .. b0 + PER - 1 (those below count)
+    const int nrec = (int)min((int64_t)PER, count - b0);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + b0 * REC, (uint32_t)(nrec * REC));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t base = (uint32_t)(min(u * VW + gi, nrec - 1) * REC);
-      wa[u][0] = bload4(rin, base + 4u * (pa >> 5));
-      wb[u][0] = bload4(rin, base + 4u * (pb >> 5));
-      if (TWO) {   // the next word: at most the s word
-        wa[u][1] = bload4(rin, base + 4u * ((pa >> 5) + 1));
-        wb[u][1] = bload4(rin, base + 4u * ((pb >> 5) + 1));
-      } else {
-        wa[u][1] = wb[u][1] = 0u;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;   // bit position of run q
+        w0[u][q] = bload4(rin, base + 4u * (p >> 5));
+        w1[u][q] = TWO ? bload4(rin, base + 4u * ((p >> 5) + 1)) : 0u;   // at most the s word
       }
       sw[u] = bload4(rin, base + 4u * CW);
     }
+  };
+  int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER;
+  if (v0 < count) fetch(v0);
+  for (; v0 < count; v0 += stride) {
+    const int nrec = (int)min((int64_t)PER, count - v0);
+    uint32_t c0[U][NR], c1[U][NR], cs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t ra = (uint32_t)(((((uint64_t)wa[u][1]) << 32) | wa[u][0]) >> (pa & 31));
-      const uint32_t rb = (uint32_t)(((((uint64_t)wb[u][1]) << 32) | wb[u][0]) >> (pb & 31));
-      float x[8];
+      cs[u] = sw[u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = cent[(ra >> (e * BITS)) & (L - 1)];
-        x[e + 4] = cent[(rb >> (e * BITS)) & (L - 1)];
+      for (int q = 0; q < NR; ++q) {
+        c0[u][q] = w0[u][q];
+        c1[u][q] = w1[u][q];
       }
-      fwht8<G>(x, lane);
-      const float s = __uint_as_float(sw[u]);
+    }
+    if (v0 + stride < count) fetch(v0 + stride);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= s;
-      if (u * VW + gi < nrec) {
-        float* dst = v + (v0 + u * VW + gi) * ldv + 4 * li;
-        store8<VEC>(dst, dst + N / 2, x);
+    for (int u = 0; u < U; ++u) {
+      float x[V];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;
+        const uint64_t r = ((((uint64_t)c1[u][q]) << 32) | c0[u][q]) >> (p & 31);
+#pragma unroll
+        for (int i = 0; i < RL; ++i) x[RL * q + i] = cent[(uint32_t)(r >> (i * BITS)) & (L - 1)];
       }
+      fwht<G, V>(x, lane);
+      const float sc = __uint_as_float(cs[u]) * inv_sqrt_n<N>();
+#pragma unroll
+      for (int e = 0; e < V; ++e) x[e] *= sc;
+      if (u * VW + gi < nrec) store_runs<G, V, RL, VEC>(v + (v0 + u * VW + gi) * ldv + RL * li, x);
     }
   }
 }
 
-template <int G>
-int launch_turbo_g(bool enc, const void* src, int64_t count, int64_t ld, void* dst, int bits,
-                   const TurboTable& tab, hipStream_t s) {
-  constexpr int U = 2;   // vector sets per wave and iteration
-  constexpr int PER = U * (64 / G);
-  int64_t blocks = (count + 4 * PER - 1) / (4 * PER);
+template <int N>
+int launch_turbo_n(bool enc, const void* src, int64_t count, int64_t ld, void* dst, int bits,
+                   const TurboTable& tab, bool lut, hipStream_t s) {
+  // vectors per workgroup and iteration: 4 waves of 64 / (n / 32) (encode)
+  // or of 2 x 8 (decode)
+  const int per = enc ? 4 * (64 / (N / 32)) : 4 * 16;
+  int64_t blocks = (count + per - 1) / per;
   if (blocks > 4096) blocks = 4096;
   const void* fp = enc ? src : dst;   // the f32 side
   const bool vec = (ld % 4) == 0 && (reinterpret_cast<uintptr_t>(fp) % 16) == 0;
+  const int use_lut = lut && tab.lut_ok;
 #define HQ_T(B, V)                                                                                  \
   if (enc)                                                                                          \
-    hipLaunchKernelGGL((turbo_encode_kernel<G, B, U, V>), dim3((unsigned)blocks), dim3(256), 0, s, \
-                       static_cast<const float*>(src), count, ld, static_cast<uint8_t*>(dst), tab);  \
+    hipLaunchKernelGGL((turbo_encode_kernel<N / 32, B, V>), dim3((unsigned)blocks), dim3(256), 0, s, \
+                       static_cast<const float*>(src), count, ld, static_cast<uint8_t*>(dst), tab,  \
+                       use_lut);                                                                    \
   else                                                                                              \
-    hipLaunchKernelGGL((turbo_decode_kernel<G, B, U, V>), dim3((unsigned)blocks), dim3(256), 0, s, \
+    hipLaunchKernelGGL((turbo_decode_kernel<N, B, V>), dim3((unsigned)blocks), dim3(256), 0, s,    \
                        static_cast<const uint8_t*>(src), count, static_cast<float*>(dst), ld, tab);  \
   return (int)hipGetLastError();
 #define HQ_TB(B)          \
@@ -334,11 +373,11 @@ int launch_turbo_g(bool enc, const void* src, int64_t count, int64_t ld, void* d
 }  // namespace
 
 int launch_turbo(bool encode, const void* src, int64_t count, int n, int64_t ld, void* dst,
-                 int bits, const TurboTable& tab, hipStream_t s) {
+                 int bits, const TurboTable& tab, bool lut, hipStream_t s) {
   if (count == 0) return 0;
-  if (n == 64) return launch_turbo_g<8>(encode, src, count, ld, dst, bits, tab, s);
-  if (n == 128) return launch_turbo_g<16>(encode, src, count, ld, dst, bits, tab, s);
-  if (n == 256) return launch_turbo_g<32>(encode, src, count, ld, dst, bits, tab, s);
+  if (n == 64) return launch_turbo_n<64>(encode, src, count, ld, dst, bits, tab, lut, s);
+  if (n == 128) return launch_turbo_n<128>(encode, src, count, ld, dst, bits, tab, lut, s);
+  if (n == 256) return launch_turbo_n<256>(encode, src, count, ld, dst, bits, tab, lut, s);
   return (int)hipErrorInvalidValue;
 }
 

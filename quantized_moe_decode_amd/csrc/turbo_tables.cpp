@@ -62,22 +62,21 @@ void turbo_table(int n, int bits, TurboTable* t) {
   for (int j = 0; j < 256; ++j) t->cent[j] = j < L ? (float)(lv[j] * sc) : 0.f;
   for (int j = 0; j < 255; ++j)
     t->thr[j] = j < L - 1 ? (float)(0.5 * ((double)t->cent[j] + (double)t->cent[j + 1])) : INFINITY;
-  // buckets for the 8-bit search: TURBO_LUT_BUCKETS - 2 across the
-  // thresholds, each narrower than the smallest gap between two of them,
-  // so that a bucket holds at most one threshold (two with rounding; the
-  // kernels check that none holds three)
-  t->lut_lo = t->thr[0];
-  t->lut_inv_w = 0.f;
+  // buckets for the encoder's search: TURBO_LUT_BUCKETS - 2 across the
+  // thresholds (thr[0] near bucket 1, thr[L - 2] near the last), each
+  // narrower than half the smallest gap between two thresholds, so no two
+  // thresholds share a bucket even after rounding (the kernel checks)
+  const double lo = t->thr[0], hi = t->thr[L - 2];
+  double gap = INFINITY;
+  for (int j = 0; j + 1 < L - 1; ++j) gap = std::fmin(gap, (double)t->thr[j + 1] - (double)t->thr[j]);
+  const double w = (hi - lo) / (TURBO_LUT_BUCKETS - 2);
+  t->lut_a = 0.f;
+  t->lut_b = 0.f;
   t->lut_ok = 0;
-  if (bits == 8) {
-    const double lo = t->thr[0], hi = t->thr[L - 2];
-    double gap = INFINITY;
-    for (int j = 0; j + 1 < L - 1; ++j) gap = std::fmin(gap, (double)t->thr[j + 1] - (double)t->thr[j]);
-    const double w = (hi - lo) / (TURBO_LUT_BUCKETS - 2);
-    if (w > 0.0 && w < gap) {
-      t->lut_inv_w = (float)(1.0 / w);
-      t->lut_ok = 1;
-    }
+  if (w > 0.0 && 2.0 * w < gap) {
+    t->lut_a = (float)(1.0 / w);
+    t->lut_b = (float)(1.0 - lo / w);
+    t->lut_ok = 1;
   }
 }
 
