@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   constexpr int N = 32 * G, L = 1 << BITS, VW = 64 / G;
   constexpr int CW = N * BITS / 32, RW = CW + 1;   // code words, record words
   constexpr int WW = VW * RW;                      // record words of one wave iteration
-  constexpr int NBK = TURBO_LUT_BUCKETS;
+  constexpr int NBK = turbo_lut_buckets(BITS);
   constexpr bool WHOLE = BITS == 4 || BITS == 8;   // a run of eight codes fills whole words
   constexpr int RUNW = BITS == 8 ? 2 : 1;          // words of a run's codes
   __shared__ uint32_t pk[4][WW];

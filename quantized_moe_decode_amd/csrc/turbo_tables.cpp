@@ -62,14 +62,14 @@ void turbo_table(int n, int bits, TurboTable* t) {
   for (int j = 0; j < 256; ++j) t->cent[j] = j < L ? (float)(lv[j] * sc) : 0.f;
   for (int j = 0; j < 255; ++j)
     t->thr[j] = j < L - 1 ? (float)(0.5 * ((double)t->cent[j] + (double)t->cent[j + 1])) : INFINITY;
-  // buckets for the encoder's search: TURBO_LUT_BUCKETS - 2 across the
+  // buckets for the encoder's search: turbo_lut_buckets(bits) - 2 across the
   // thresholds (thr[0] near bucket 1, thr[L - 2] near the last), each
   // narrower than half the smallest gap between two thresholds, so no two
   // thresholds share a bucket even after rounding (the kernel checks)
   const double lo = t->thr[0], hi = t->thr[L - 2];
   double gap = INFINITY;
   for (int j = 0; j + 1 < L - 1; ++j) gap = std::fmin(gap, (double)t->thr[j + 1] - (double)t->thr[j]);
-  const double w = (hi - lo) / (TURBO_LUT_BUCKETS - 2);
+  const double w = (hi - lo) / (turbo_lut_buckets(bits) - 2);
   t->lut_a = 0.f;
   t->lut_b = 0.f;
   t->lut_ok = 0;

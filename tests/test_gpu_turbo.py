@@ -156,6 +156,32 @@ def test_turbo_strided_unaligned(q, n, bits):
     assert bool((gaps == 7.0).all()) and float(outb[0]) == 7.0
 
 
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_turbo_tiny_counts(q, n):
+    """Calls with fewer vectors than a wave takes (1, 3, 17) against the
+    oracle, and a call with none writes nothing."""
+    bits = 4
+    rec = q.turbo_record_bytes(n, bits)
+    for count in (1, 3, 17):
+        say("turbo tiny n=%d count=%d" % (n, count))
+        V = np.random.default_rng(count * n).standard_normal((count, n)).astype(np.float32)
+        go = Guarded(torch, (count, rec), torch.uint8, guard=256)
+        q.turbo_encode(torch.from_numpy(V).cuda(), bits, out=go.t)
+        gv = Guarded(torch, (count, n), torch.float32)
+        q.turbo_decode(go.t, n, bits, v=gv.t)
+        torch.cuda.synchronize()
+        go.check()
+        gv.check()
+        near, _ = _check_records(V, range(count), go.t.cpu().numpy(),
+                                 gv.t.cpu().numpy().astype(np.float64), n, bits, specials=0)
+        assert near <= 2
+    empty = torch.zeros((0, n), dtype=torch.float32, device="cuda")
+    out = torch.full((rec,), 0x5A, dtype=torch.uint8, device="cuda")
+    q.turbo_encode(empty, bits, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 0x5A).all())
+
+
 def test_turbo_full_size_sampled(q):
     """The benchmarked workload, 2^21 vectors of 128 values (1 GiB of f32)
     at 4 bits in one call each way: 96 sampled records (the first, the
