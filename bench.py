@@ -673,6 +673,9 @@ def main():
                     help="also run one device copy of 1 GiB (counter calibration)")
     ap.add_argument("--batches", default="1,4,16",
                     help="token batch sizes of the skewed workload")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="layer workload: skip the short runs of the skewed (4 and 16 tokens) "
+                         "and 40-layer stack workloads that follow the headline in the same line")
     ap.add_argument("--workload", choices=["layer", "stack", "hostmapped", "skewed", "floor",
                                            "offload", "cache", "turbo"],
                     default="layer",
@@ -979,7 +982,44 @@ def main():
         out["cpu_baseline"] = cpu_baseline(torch, 0, xs_host, routers_host, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    if not args.no_companions:
+        del layers, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["companion_workloads"] = companions(args, torch, q)
     print(json.dumps(out), flush=True)
+
+
+def companions(args, torch, q):
+    """Short runs of two other workloads after the headline, so that one
+    invocation also measures them: the skewed layer (E=512, Zipf router) at
+    4 and 16 tokens per step and the 40-layer stack at 1 token, each as its
+    own --workload reports it but with fixed step counts (1024 timed steps
+    of the skewed layer per batch, 2048 of the stack) instead of --steps."""
+    import copy
+    res = {"note": "measured in the same process after the headline; fixed step counts "
+                   "(skewed: 1024 steps per batch, cold replicas; stack: 2048 steps)"}
+    a = copy.copy(args)
+    a.steps, a.batches, a.calib_copy = 4096, "4,16", False
+    try:
+        sk = bench_skewed(a, torch, q)
+        res["skewed_E512_zipf"] = {b: {k: r[k] for k in ("ms_per_step", "tokens_per_s",
+                                                          "mean_distinct_experts", "expert_gbs",
+                                                          "pct_hbm_peak", "steps")}
+                                   for b, r in sk["per_batch"].items()}
+    except (Exception, SystemExit) as e:
+        res["skewed_E512_zipf"] = {"error": str(e)}
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    a.steps = 2048
+    try:
+        st = bench_stack(a, torch, q)
+        res["stack_40_layers"] = {"ms_per_step": st["ms_per_step"], "tokens_per_s": st["tokens_per_s"],
+                                  "expert_gbs": st["value"], "pct_hbm_peak": st["pct_hbm_peak"],
+                                  "steps": st["steps"]}
+    except (Exception, SystemExit) as e:
+        res["stack_40_layers"] = {"error": str(e)}
+    return res
 
 
 if __name__ == "__main__":
