@@ -12,14 +12,20 @@
 
 namespace hq {
 
-constexpr int GEMV_WG_PER_CU = 4;   // resident workgroups per CU of a long GEMV
+constexpr int GEMV_WG_PER_CU = 4;   // workgroups per CU in the grid of a GEMV below 512 MiB
 constexpr int GEMV_RPW_LONG = 4;    // row loads per wave and group of a long GEMV
-constexpr int GEMV_WG_PER_CU_LONG = 3;   // its resident workgroups per CU (137 VGPRs)
+// workgroups per CU in a long GEMV's grid: 3 fit at once (137 VGPRs), the
+// others queue; a queue of workgroups that each take a short stretch of the
+// matrix kept the chip's loads on fewer DRAM pages than 3 per CU striding
+// through all of it (1-4 GiB: 5.5-5.7 against 5.3 TB/s; 6: 5.4, 12: 5.5,
+// 48: 5.1-5.6, uncapped 3.4-3.6, where each workgroup's staging of x
+// dominates)
+constexpr int GEMV_WG_PER_CU_LONG = 24;
 
 // Rows of nb <= NB blocks (K <= 256*NB); SEGS = 8*NB lanes per row, G =
 // 64/SEGS rows per load instruction, RPW load instructions per wave: a
 // wave's group is RPW*G rows.  Lanes whose block index is >= nb load
-// nothing and contribute zero.  The grid is capped (a few workgroups per
+// nothing and contribute zero.  The grid is capped (4 or 24 workgroups per
 // CU), so a wave walks groups wave, wave + (waves in the grid), ... with the
 // next group's loads in flight while it computes the current one; x is
 // staged once per workgroup.
@@ -172,7 +178,7 @@ static int launch_narrow_rpw(const void* W, int64_t rows, int K, const float* x,
   constexpr int G = 64 / (8 * NB);
   const int64_t waves = (rows + RPW * G - 1) / (RPW * G);
   int64_t blocks = (waves + 3) / 4;
-  // larger matrices loop; the cap keeps every workgroup resident
+  // larger matrices loop (each wave strides over row groups)
   const int64_t cap = (int64_t)num_cus() * (RPW == 2 ? GEMV_WG_PER_CU : GEMV_WG_PER_CU_LONG);
   if (blocks > cap) blocks = cap;
   const size_t shm = (size_t)batch * frag_bytes(8 * NB);
