@@ -21,10 +21,9 @@
 //    shared by 32 values; only spans 8 .. 4 G pair lane j with lane j ^ M
 //    (M < G <= 8: DPP quad permutes, and for n = 256 a pair of row
 //    rotations).
-//  - decode, bound by its f32 stores, puts a vector on 8 lanes (n / 8
-//    values per lane, in runs of four) so that each store instruction
-//    writes 128 contiguous bytes per vector, fetches the next records
-//    before it transforms the current ones, and stores with the
+//  - decode, bound by its f32 stores, puts a vector on 8 lanes (16 at
+//    n = 256; runs of four values) so that each store instruction writes
+//    128 or 256 contiguous bytes per vector, and stores with the
 //    non-temporal hint (the output is not read back by the kernel).
 // Every butterfly is exactly rounded; the 1/sqrt(n) factor is folded into
 // the normalisation (encode) or the norm ratio (decode).
@@ -38,16 +37,18 @@
 namespace hq {
 namespace {
 
-// The value of lane l ^ M in every lane, M = 1, 2 or 4.  M = 1, 2: quad
-// permutes.  M = 4: row_ror:12 gives every lane lane l + 4 (mod 16), then
-// row_ror:4, written only in banks 1 and 3 (the lanes with bit 2 set, whose
-// partner is lane l - 4), replaces it there.  Every lane's result is
-// written by one of the moves, so their old values are never read.
+// The value of lane l ^ M in every lane, M = 1, 2, 4 or 8.  M = 1, 2: quad
+// permutes.  M = 8: row_ror:8.  M = 4: row_ror:12 gives every lane lane
+// l + 4 (mod 16), then row_ror:4, written only in banks 1 and 3 (the lanes
+// with bit 2 set, whose partner is lane l - 4), replaces it there.  Every
+// lane's result is written by one of the moves, so their old values are
+// never read.
 template <int M>
 __device__ __forceinline__ float xlane(float v) {
   const int b = __builtin_bit_cast(int, v);
   if (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xf, 0xf, true));
   if (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xf, 0xf, true));
+  if (M == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x128, 0xf, 0xf, true));
   const int up = __builtin_amdgcn_mov_dpp(b, 0x12C, 0xf, 0xf, true);
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(up, b, 0x124, 0xf, 0xA, false));
 }
@@ -92,7 +93,7 @@ __device__ __forceinline__ void fwht(float (&x)[V], int lane) {
     _Pragma("unroll") for (int e = 0; e < V; ++e)            \
       x[e] = __builtin_fmaf(sg, x[e], xlane<M>(x[e]));       \
   }
-  HQ_XSTAGE(1) HQ_XSTAGE(2) HQ_XSTAGE(4)
+  HQ_XSTAGE(1) HQ_XSTAGE(2) HQ_XSTAGE(4) HQ_XSTAGE(8)
 #undef HQ_XSTAGE
 }
 
@@ -266,18 +267,19 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   }
 }
 
-// Decode.  Layout: G = 8 lanes per vector, V = n / 8 values per lane in
-// runs of RL = 4.  A wave takes U sets of eight vectors per iteration; each
-// lane reads the code words holding its runs (the next word too where a run
-// may span two) and the s word, and fetches those of the next iteration
-// before it transforms and stores the current ones, so the loads wait for
-// nothing but themselves.
+// Decode.  Layout: G lanes per vector (8, or 16 at n = 256), V = n / G
+// values per lane in runs of RL = 4, so that each 16-byte store instruction
+// writes 16 G contiguous bytes per vector; the stores carry the
+// non-temporal hint (the kernel never reads its output).  Each lane reads
+// the code words holding its runs (the next word too where a run may span
+// two) and the s word.  The launch gives every wave one set of 64 / G
+// vectors; the loop covers any other grid.
 template <int N, int BITS, bool VEC>
 __global__ void __launch_bounds__(256) turbo_decode_kernel(const uint8_t* __restrict__ in,
                                                            int64_t count, float* __restrict__ v,
                                                            int64_t ldv, TurboTable tab) {
-  constexpr int G = 8, V = N / G, RL = 4, NR = V / RL, U = 2;
-  constexpr int L = 1 << BITS, VW = 64 / G, PER = U * VW;
+  constexpr int G = N == 256 ? 16 : 8, V = N / G, RL = 4, NR = V / RL;
+  constexpr int L = 1 << BITS, VW = 64 / G;
   constexpr int CW = N * BITS / 32, REC = 4 * (CW + 1);
   constexpr bool TWO = BITS == 3;                  // a run of four 3-bit codes may span two words
   __shared__ float cent[L];
@@ -285,63 +287,41 @@ __global__ void __launch_bounds__(256) turbo_decode_kernel(const uint8_t* __rest
   __syncthreads();
   const int wv = wave_id(), lane = threadIdx.x & 63;
   const int gi = lane / G, li = lane % G;
-  const int64_t stride = (int64_t)gridDim.x * 4 * PER;
-  uint32_t w0[U][NR], w1[U][NR], sw[U];
-  auto fetch = [&](int64_t b0) {   // the records of vectors b0 .. b0 + PER - 1 (those below count)
-    const int nrec = (int)min((int64_t)PER, count - b0);
-    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + b0 * REC, (uint32_t)(nrec * REC));
+  const int64_t stride = (int64_t)gridDim.x * 4 * VW;
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * VW; v0 < count; v0 += stride) {
+    const int nrec = (int)min((int64_t)VW, count - v0);
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in + v0 * REC, (uint32_t)(nrec * REC));
+    const uint32_t base = (uint32_t)(min(gi, nrec - 1) * REC);
+    uint32_t w0[NR], w1[NR];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t base = (uint32_t)(min(u * VW + gi, nrec - 1) * REC);
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;   // bit position of run q
-        w0[u][q] = bload4(rin, base + 4u * (p >> 5));
-        w1[u][q] = TWO ? bload4(rin, base + 4u * ((p >> 5) + 1)) : 0u;   // at most the s word
-      }
-      sw[u] = bload4(rin, base + 4u * CW);
+    for (int q = 0; q < NR; ++q) {
+      const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;   // bit position of run q
+      w0[q] = bload4(rin, base + 4u * (p >> 5));
+      w1[q] = TWO ? bload4(rin, base + 4u * ((p >> 5) + 1)) : 0u;   // at most the s word
     }
-  };
-  int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * PER;
-  if (v0 < count) fetch(v0);
-  for (; v0 < count; v0 += stride) {
-    const int nrec = (int)min((int64_t)PER, count - v0);
-    uint32_t c0[U][NR], c1[U][NR], cs[U];
+    const float s = __uint_as_float(bload4(rin, base + 4u * CW));
+    float x[V];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cs[u] = sw[u];
+    for (int q = 0; q < NR; ++q) {
+      const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;
+      const uint64_t r = ((((uint64_t)w1[q]) << 32) | w0[q]) >> (p & 31);
 #pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        c0[u][q] = w0[u][q];
-        c1[u][q] = w1[u][q];
-      }
+      for (int i = 0; i < RL; ++i) x[RL * q + i] = cent[(uint32_t)(r >> (i * BITS)) & (L - 1)];
     }
-    if (v0 + stride < count) fetch(v0 + stride);
+    fwht<G, V>(x, lane);
+    const float sc = s * inv_sqrt_n<N>();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[V];
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const uint32_t p = (uint32_t)(RL * li + RL * G * q) * BITS;
-        const uint64_t r = ((((uint64_t)c1[u][q]) << 32) | c0[u][q]) >> (p & 31);
-#pragma unroll
-        for (int i = 0; i < RL; ++i) x[RL * q + i] = cent[(uint32_t)(r >> (i * BITS)) & (L - 1)];
-      }
-      fwht<G, V>(x, lane);
-      const float sc = __uint_as_float(cs[u]) * inv_sqrt_n<N>();
-#pragma unroll
-      for (int e = 0; e < V; ++e) x[e] *= sc;
-      if (u * VW + gi < nrec) store_runs<G, V, RL, VEC>(v + (v0 + u * VW + gi) * ldv + RL * li, x);
-    }
+    for (int e = 0; e < V; ++e) x[e] *= sc;
+    if (gi < nrec) store_runs<G, V, RL, VEC>(v + (v0 + gi) * ldv + RL * li, x);
   }
 }
 
 template <int N>
 int launch_turbo_n(bool enc, const void* src, int64_t count, int64_t ld, void* dst, int bits,
                    const TurboTable& tab, bool lut, hipStream_t s) {
-  // vectors per workgroup and iteration: 4 waves of 64 / (n / 32) (encode)
-  // or of 2 x 8 (decode)
-  const int per = enc ? 4 * (64 / (N / 32)) : 4 * 16;
+  // vectors per workgroup and iteration: 4 waves of 64 / G, G = n / 32
+  // (encode) or 8, 16 at n = 256 (decode)
+  const int per = enc ? 4 * (64 / (N / 32)) : 4 * (64 / (N == 256 ? 16 : 8));
   // Grid: the decoder one iteration per wave; the encoder, which builds its
   // level tables once per workgroup, two (four at n = 256).  A queue of
   // short-lived workgroups keeps the chip's active loads on a narrow
