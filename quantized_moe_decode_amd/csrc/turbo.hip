@@ -159,7 +159,7 @@ constexpr float inv_sqrt_n() {
 // eight codes go into the wave's records in LDS (code i of the vector at
 // bits [i b, i b + b) of its code stream: whole words for b = 4 and 8,
 // or-ed into zeroed words otherwise), and the iteration's records,
-// contiguous in memory, leave as whole words.
+// contiguous in memory, leave as whole words with the non-temporal hint.
 template <int G, int BITS, bool VEC>
 __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restrict__ v, int64_t count,
                                                            int64_t ldv, uint8_t* __restrict__ out,
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
     __builtin_amdgcn_wave_barrier();
     const int words = (int)min((int64_t)VW, count - v0) * RW;
     uint32_t* dst = reinterpret_cast<uint32_t*>(out + v0 * (4 * RW));
-    for (int t = lane; t < words; t += 64) dst[t] = pk[wv][t];
+    for (int t = lane; t < words; t += 64) __builtin_nontemporal_store(pk[wv][t], dst + t);
     __builtin_amdgcn_wave_barrier();
   }
 }
