@@ -186,3 +186,47 @@ def test_noalloc_refuses_beyond_its_scratch(q):
     rc = q.lib.moe_layer_decode_noalloc(ctypes.byref(L), P(16), None, P(4096), 2048, 16, 8,
                                         P(1 << 20), P(1 << 21), None, P(1 << 22), 2048, None, None)
     assert rc == q.HFQ4_E_DEVICE
+
+
+def test_turbo_validation(q):
+    L = q.lib
+    by = ctypes.byref
+    sz = ctypes.c_size_t()
+    assert L.turbo_record_bytes(96, 4, by(sz)) == q.HFQ4_E_UNSUPPORTED
+    assert L.turbo_record_bytes(128, 5, by(sz)) == q.HFQ4_E_UNSUPPORTED
+    assert L.turbo_record_bytes(128, 4, None) == q.HFQ4_E_INVALID
+    assert L.turbo_record_bytes(128, 4, by(sz)) == 0 and sz.value == 68
+    levels = (ctypes.c_float * 16)()
+    assert L.turbo_levels(128, 4, None) == q.HFQ4_E_INVALID
+    assert L.turbo_levels(128, 4, levels) == 0
+    lv = list(levels)
+    assert all(a < b for a, b in zip(lv, lv[1:]))
+    n, bits, count, rec = 128, 4, 1000, 68
+    v, out = A, A + (1 << 30)
+
+    def enc(v=v, count=count, ldv=n, out=out, ob=rec * count, bits=bits):
+        return L.turbo_encode(P(v) if v else None, count, n, ldv, bits, P(out), ob, None)
+
+    assert enc(count=-1) == q.HFQ4_E_INVALID
+    assert enc(count=0) == 0                      # nothing to do: no device is touched
+    assert enc(v=0) == q.HFQ4_E_INVALID
+    assert enc(ldv=n - 1) == q.HFQ4_E_INVALID
+    assert enc(ob=rec * count - 1) == q.HFQ4_E_INVALID
+    assert enc(v=A + 2) == q.HFQ4_E_ALIGN
+    assert enc(out=A + 4 * 64) == q.HFQ4_E_INVALID   # the records would overlap v
+    assert enc(bits=5) == q.HFQ4_E_UNSUPPORTED
+    assert enc() == q.HFQ4_E_DEVICE
+
+    def dec(inp=out, ib=rec * count, count=count, vv=v, ldv=n, bits=bits):
+        return L.turbo_decode(P(inp) if inp else None, ib, count, n, bits, P(vv), ldv, None)
+
+    assert dec(count=-1) == q.HFQ4_E_INVALID
+    assert dec(count=0) == 0
+    assert dec(inp=0) == q.HFQ4_E_INVALID
+    assert dec(ldv=n - 1) == q.HFQ4_E_INVALID
+    assert dec(ib=rec * count - 1) == q.HFQ4_E_INVALID
+    assert dec(inp=out + 2) == q.HFQ4_E_ALIGN
+    assert dec(vv=out + 64) == q.HFQ4_E_INVALID        # v would overlap the records
+    assert dec(bits=8) == q.HFQ4_E_INVALID             # 132-byte records: 68000 bytes hold 515
+    assert dec() == q.HFQ4_E_DEVICE
+    assert L.hfq4_debug_set_turbo_search(1) == 0 and L.hfq4_debug_set_turbo_search(0) == 0
