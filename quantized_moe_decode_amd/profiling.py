@@ -110,7 +110,8 @@ def traffic(fetch_csv, write_csv, kernel_substr):
 
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
-        print(stats_table(sys.argv[2]))
+        # stats <kernel_stats.csv> [rows]
+        print(stats_table(sys.argv[2], int(sys.argv[3]) if len(sys.argv) > 3 else 12))
     elif sys.argv[1] == "durations":
         # durations <kernel_trace.csv> <kernel substring> <last N>
         v = trace_durations(sys.argv[2], sys.argv[3])
