@@ -157,8 +157,9 @@ constexpr float inv_sqrt_n() {
 // A wave takes VW = 64 / G vectors per iteration (a vector index past the
 // end reads the last vector again and writes nothing).  Each lane's runs of
 // eight codes go into the wave's records in LDS (code i of the vector at
-// bits [i b, i b + b) of its code stream: whole words for b = 4 and 8,
-// or-ed into zeroed words otherwise), and the iteration's records,
+// bits [i b, i b + b) of its code stream: whole words for b = 4 and 8, for
+// b = 3 (n >= 128) whole words assembled from a quad of lanes' runs, and
+// otherwise runs or-ed into zeroed words), and the iteration's records,
 // contiguous in memory, leave as whole words with the non-temporal hint.
 template <int G, int BITS, bool VEC>
 __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restrict__ v, int64_t count,
@@ -169,6 +170,10 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   constexpr int WW = VW * RW;                      // record words of one wave iteration
   constexpr int NBK = turbo_lut_buckets(BITS);
   constexpr bool WHOLE = BITS == 4 || BITS == 8;   // a run of eight codes fills whole words
+  // 3 bits with G >= 4: a quad of lanes holds four consecutive 24-bit runs,
+  // which fill three whole words together
+  constexpr bool QUADS = BITS == 3 && G >= 4;
+  constexpr bool ZERO = !(WHOLE || QUADS);   // runs or-ed into zeroed words
   constexpr int RUNW = BITS == 8 ? 2 : 1;          // words of a run's codes
   __shared__ uint32_t pk[4][WW];
   __shared__ f32x4 qt[L];                          // {threshold m (inf for m = L - 1), level m, level m + 1, 0}
@@ -204,7 +209,7 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   for (int64_t v0 = ((int64_t)blockIdx.x * 4 + wv) * VW; v0 < count; v0 += stride) {
     float x[32];
     load_runs<G, 32, 8, VEC>(v + min(v0 + gi, count - 1) * ldv + 8 * li, x);
-    if (!WHOLE) {
+    if (ZERO) {
       for (int t = lane; t < WW; t += 64) pk[wv][t] = 0u;
     }
     float p4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -252,6 +257,14 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
       if (WHOLE) {
 #pragma unroll
         for (int w = 0; w < RUNW; ++w) rec[(p >> 5) + w] = live ? run[q][w] : 0u;
+      } else if (QUADS) {
+        // runs m = 4 i + t (lane t of a quad) make words 3 i .. 3 i + 2: lane
+        // t < 3 writes word 3 i + t from its run and the next lane's
+        // (quad_perm [1, 2, 3, 3])
+        const int own = (int)(live ? run[q][0] : 0u);
+        const uint32_t nxt = (uint32_t)__builtin_amdgcn_mov_dpp(own, 0xF9, 0xf, 0xf, true);
+        const int t = li & 3, m = li + G * q;
+        if (t < 3) rec[3 * (m >> 2) + t] = ((uint32_t)own >> (8 * t)) | (nxt << (24 - 8 * t));
       } else {
         const uint64_t placed = (uint64_t)(live ? run[q][0] : 0u) << (p & 31);
         atomicOr(rec + (p >> 5), (uint32_t)placed);
