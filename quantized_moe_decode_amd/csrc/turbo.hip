@@ -192,12 +192,19 @@ __global__ void __launch_bounds__(256) turbo_encode_kernel(const float* __restri
   __syncthreads();
   bool lut = false;
   if (use_lut) {
-    for (int k = threadIdx.x; k < NBK; k += blockDim.x) {
+    // each thread fills KPT consecutive buckets: a binary search for the
+    // first, then a walk (tbk is sorted, and tbk[L - 1] = NBK ends it)
+    constexpr int KPT = NBK >= 2048 ? NBK / 256 : 1;
+    for (int k0 = threadIdx.x * KPT; k0 < NBK; k0 += blockDim.x * KPT) {
       int lo = 0;
 #pragma unroll
       for (int step = L / 2; step >= 1; step >>= 1)
-        if (tbk[lo + step - 1] < k) lo += step;
-      tb[k] = (uint8_t)lo;
+        if (tbk[lo + step - 1] < k0) lo += step;
+      tb[k0] = (uint8_t)lo;
+      for (int k = k0 + 1; k < k0 + KPT; ++k) {
+        while (tbk[lo] < k) ++lo;
+        tb[k] = (uint8_t)lo;
+      }
     }
     int bad = 0;
     for (int t = threadIdx.x; t + 1 < L - 1; t += blockDim.x) bad |= tbk[t] == tbk[t + 1];
